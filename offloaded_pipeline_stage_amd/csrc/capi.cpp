@@ -1,0 +1,343 @@
+// C ABI of the stage library: validation, context life cycle, bindings and
+// the thin entry points over the stage executor and the transfer engine.
+#include <cstdarg>
+#include <cstring>
+#include <new>
+
+#include "attn_flash.h"
+#include "ctx.h"
+
+namespace rp {
+
+namespace {
+thread_local char g_err[1024] = "";
+constexpr int kMaxLayers = 4096;
+}  // namespace
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+const char* last_error() { return g_err; }
+
+Shape make_shape(const rp_layer_cfg& c) {
+  Shape s{};
+  s.H = c.hidden; s.nq = c.n_q; s.nkv = c.n_kv; s.d = c.head_dim;
+  s.F = c.ffn; s.E = c.n_experts; s.topk = c.top_k; s.Fe = c.expert_ffn; s.r = c.lora_rank;
+  s.Q = c.n_q * c.head_dim; s.KV = c.n_kv * c.head_dim; s.QKV = s.Q + 2 * s.KV;
+  s.dt = c.dtype;
+  s.es = dtype_size(c.dtype);
+  return s;
+}
+
+rp_status block_layout(const rp_layer_cfg& cfg, int block, int tensor, size_t* off, size_t* bytes,
+                       size_t* total) {
+  const Shape s = make_shape(cfg);
+  struct T { int id; size_t n; };
+  std::vector<T> ts;
+  size_t es;
+  if (block == RP_BLOCK_WEIGHT || block == RP_BLOCK_GRAD) {
+    es = block == RP_BLOCK_WEIGHT ? s.es : 4;
+    const size_t H = s.H;
+    const size_t gu = s.E > 0 ? (size_t)s.E * 2 * s.Fe * H : 2 * (size_t)s.F * H;
+    const size_t dn = s.E > 0 ? (size_t)s.E * H * s.Fe : H * (size_t)s.F;
+    ts = {{RP_T_GAMMA1, H}, {RP_T_WQKV, (size_t)s.QKV * H}, {RP_T_WO, H * s.Q}, {RP_T_GAMMA2, H},
+          {RP_T_WGU, gu}, {RP_T_WD, dn}};
+  } else if (block == RP_BLOCK_LORA) {
+    RP_CHECK(s.r > 0, RP_ERR_INVALID, "layout: no LoRA block when lora_rank == 0");
+    es = 4;
+    const size_t r = s.r, H = s.H;
+    ts = {{RP_T_AQ, r * H}, {RP_T_BQ, (size_t)s.Q * r}, {RP_T_AK, r * H}, {RP_T_BK, (size_t)s.KV * r},
+          {RP_T_AV, r * H}, {RP_T_BV, (size_t)s.KV * r}, {RP_T_AO, r * s.Q}, {RP_T_BO, H * r}};
+  } else {
+    set_error("layout: unknown block %d", block);
+    return RP_ERR_INVALID;
+  }
+  size_t o = 0;
+  bool found = false;
+  for (const T& t : ts) {
+    o = align_up(o, 256);
+    if (t.id == tensor) {
+      if (off) *off = o;
+      if (bytes) *bytes = t.n * es;
+      found = true;
+    }
+    o += t.n * es;
+  }
+  if (total) *total = align_up(o, 256);
+  RP_CHECK(found || tensor < 0, RP_ERR_INVALID, "layout: block %d has no tensor %d", block, tensor);
+  return RP_OK;
+}
+
+}  // namespace rp
+
+hipEvent_t rp_ctx::new_event() {
+  if (!ev_free.empty()) {
+    hipEvent_t e = ev_free.back();
+    ev_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return nullptr;
+  all_events.push_back(e);
+  return e;
+}
+
+using namespace rp;
+
+#define CTX_CHECK(c) RP_CHECK((c) != nullptr, RP_ERR_INVALID, "null context")
+
+// Entering a context makes its device current (one thread may drive several).
+#define CTX_ENTER(c)      \
+  CTX_CHECK(c);           \
+  RP_HIP(hipSetDevice((c)->device))
+
+extern "C" {
+
+const char* rp_status_string(rp_status s) {
+  switch (s) {
+    case RP_OK: return "RP_OK";
+    case RP_ERR_INVALID: return "RP_ERR_INVALID";
+    case RP_ERR_UNSUPPORTED: return "RP_ERR_UNSUPPORTED";
+    case RP_ERR_WORKSPACE: return "RP_ERR_WORKSPACE";
+    case RP_ERR_NOT_PINNED: return "RP_ERR_NOT_PINNED";
+    case RP_ERR_HIP: return "RP_ERR_HIP";
+    case RP_ERR_STATE: return "RP_ERR_STATE";
+  }
+  return "RP_ERR_UNKNOWN";
+}
+
+const char* rp_last_error(void) { return last_error(); }
+
+const char* rp_version(void) { return "roundpipe-stage-gfx950 0.1"; }
+
+rp_status rp_block_layout(const rp_layer_cfg* cfg, int block, int tensor, size_t* offset, size_t* bytes,
+                          size_t* total) {
+  RP_CHECK(cfg, RP_ERR_INVALID, "layout: null cfg");
+  return block_layout(*cfg, block, tensor, offset, bytes, total);
+}
+
+rp_status rp_ctx_create(int device, const rp_layer_cfg* cfg, const rp_streams* streams, rp_ctx** out) {
+  RP_CHECK(cfg && out, RP_ERR_INVALID, "ctx_create: null argument");
+  *out = nullptr;
+  const rp_layer_cfg& c = *cfg;
+  RP_CHECK(c.dtype == RP_DTYPE_F32 || c.dtype == RP_DTYPE_BF16, RP_ERR_INVALID, "ctx_create: bad dtype %d",
+           c.dtype);
+  RP_CHECK(c.hidden > 0 && c.hidden % 64 == 0, RP_ERR_UNSUPPORTED, "ctx_create: hidden must be a multiple of 64");
+  RP_CHECK(c.n_q > 0 && c.n_kv > 0 && c.n_q % c.n_kv == 0, RP_ERR_UNSUPPORTED,
+           "ctx_create: n_q must be a positive multiple of n_kv");
+  RP_CHECK(c.head_dim == 64 || c.head_dim == 128, RP_ERR_UNSUPPORTED, "ctx_create: head_dim must be 64 or 128");
+  RP_CHECK(c.n_experts == 0, RP_ERR_UNSUPPORTED, "ctx_create: MoE layers are not implemented in this build");
+  RP_CHECK(c.lora_rank == 0, RP_ERR_UNSUPPORTED, "ctx_create: LoRA adapters are not implemented in this build");
+  RP_CHECK(c.ffn > 0 && c.ffn % 8 == 0, RP_ERR_UNSUPPORTED, "ctx_create: ffn must be a positive multiple of 8");
+  RP_CHECK(c.rms_eps > 0.f && c.rope_base > 1.f, RP_ERR_INVALID, "ctx_create: bad rms_eps or rope_base");
+  int n_dev = 0;
+  RP_HIP(hipGetDeviceCount(&n_dev));
+  RP_CHECK(device >= 0 && device < n_dev, RP_ERR_INVALID, "ctx_create: device %d of %d", device, n_dev);
+  RP_HIP(hipSetDevice(device));
+  rp_ctx* x = new (std::nothrow) rp_ctx();
+  RP_CHECK(x, RP_ERR_INVALID, "ctx_create: out of host memory");
+  x->device = device;
+  x->cfg = c;
+  x->sh = make_shape(c);
+  if (streams) {
+    x->compute = (hipStream_t)streams->compute;
+    x->act_h2d = (hipStream_t)streams->act_h2d;
+    x->act_d2h = (hipStream_t)streams->act_d2h;
+    x->w_h2d = (hipStream_t)streams->w_h2d;
+    x->g_d2h = (hipStream_t)streams->g_d2h;
+  }
+  x->layers.resize(kMaxLayers);  // fixed: deferred transfers keep pointers into it
+  *out = x;
+  return RP_OK;
+}
+
+rp_status rp_ctx_sync(rp_ctx* c) {
+  CTX_ENTER(c);
+  hipStream_t ss[5] = {c->compute, c->act_h2d, c->act_d2h, c->w_h2d, c->g_d2h};
+  for (hipStream_t s : ss) RP_HIP(hipStreamSynchronize(s));
+  RP_HIP(hipGetLastError());
+  RP_CHECK(c->deferred.empty(), RP_ERR_STATE, "ctx_sync: %zu transfer windows still wait for activation tickets",
+           c->deferred.size());
+  return RP_OK;
+}
+
+rp_status rp_ctx_destroy(rp_ctx* c) {
+  if (!c) return RP_OK;
+  rp_status st = RP_OK;
+  if (hipSetDevice(c->device) == hipSuccess) {
+    hipStream_t ss[5] = {c->compute, c->act_h2d, c->act_d2h, c->w_h2d, c->g_d2h};
+    for (hipStream_t s : ss)
+      if (hipStreamSynchronize(s) != hipSuccess) st = RP_ERR_HIP;
+    for (hipEvent_t e : c->all_events) (void)hipEventDestroy(e);
+  }
+  delete c;
+  return st;
+}
+
+rp_status rp_bind_layer(rp_ctx* c, int layer, const void* w_dev, float* grad_dev, const float* lora_dev,
+                        float* lora_grad_dev) {
+  CTX_CHECK(c);
+  RP_CHECK(layer >= 0 && layer < kMaxLayers, RP_ERR_INVALID, "bind_layer: layer %d out of range", layer);
+  RP_CHECK(w_dev && ((uintptr_t)w_dev & 255) == 0, RP_ERR_INVALID, "bind_layer: weights null or not 256-aligned");
+  RP_CHECK(!grad_dev || ((uintptr_t)grad_dev & 255) == 0, RP_ERR_INVALID, "bind_layer: gradient not 256-aligned");
+  (void)lora_dev;
+  (void)lora_grad_dev;
+  LayerBinding& b = c->layers[layer];
+  RP_CHECK(b.base.w_chunks_unissued == 0 && b.base.g_chunks_unissued == 0, RP_ERR_STATE,
+           "bind_layer: layer %d has deferred transfers", layer);
+  size_t wt = 0, gt = 0;
+  RP_TRY(block_layout(c->cfg, RP_BLOCK_WEIGHT, -1, nullptr, nullptr, &wt));
+  RP_TRY(block_layout(c->cfg, RP_BLOCK_GRAD, -1, nullptr, nullptr, &gt));
+  b.bound = true;
+  b.base.w = w_dev;
+  b.base.g = grad_dev;
+  b.base.w_bytes = wt;
+  b.base.g_bytes = grad_dev ? gt : 0;
+  return RP_OK;
+}
+
+rp_status rp_bind_lmhead(rp_ctx* c, int vocab, int n_shards, const void* const* w_shard, float* const* dw_shard,
+                         const void* gamma_f, float* dgamma_f) {
+  CTX_CHECK(c);
+  RP_CHECK(vocab > 0 && n_shards >= 1 && n_shards <= 64 && n_shards <= vocab, RP_ERR_INVALID,
+           "bind_lmhead: bad vocab/n_shards");
+  RP_CHECK(w_shard, RP_ERR_INVALID, "bind_lmhead: null shard list");
+  RP_CHECK(c->deferred.empty(), RP_ERR_STATE, "bind_lmhead: transfers are deferred");
+  const int base = vocab / n_shards, extra = vocab % n_shards;
+  std::vector<int> lo(n_shards + 1, 0);
+  for (int s = 0; s < n_shards; ++s) lo[s + 1] = lo[s] + base + (s < extra ? 1 : 0);
+  if (c->sh.dt == RP_DTYPE_BF16)
+    for (int s = 0; s < n_shards; ++s)
+      RP_CHECK((lo[s + 1] - lo[s]) % 8 == 0, RP_ERR_UNSUPPORTED, "bind_lmhead: bf16 shard rows must be a multiple of 8");
+  for (int s = 0; s < n_shards; ++s) {
+    RP_CHECK(w_shard[s] && ((uintptr_t)w_shard[s] & 15) == 0, RP_ERR_INVALID, "bind_lmhead: shard %d null/misaligned", s);
+    RP_CHECK(!dw_shard || !dw_shard[s] || ((uintptr_t)dw_shard[s] & 15) == 0, RP_ERR_INVALID,
+             "bind_lmhead: gradient %d misaligned", s);
+  }
+  c->vocab = vocab;
+  c->n_shards = n_shards;
+  c->shard_lo = lo;
+  c->shards.assign(n_shards, Slot{});
+  for (int s = 0; s < n_shards; ++s) {
+    Slot& sl = c->shards[s];
+    const size_t rows = lo[s + 1] - lo[s];
+    sl.w = w_shard[s];
+    sl.g = dw_shard ? dw_shard[s] : nullptr;
+    sl.w_bytes = rows * c->sh.H * c->sh.es;
+    sl.g_bytes = sl.g ? rows * c->sh.H * 4 : 0;
+  }
+  c->final_norm = Slot{};
+  if (gamma_f) {
+    c->final_norm.w = gamma_f;
+    c->final_norm.g = dgamma_f;
+    c->final_norm.w_bytes = (size_t)c->sh.H * c->sh.es;
+    c->final_norm.g_bytes = dgamma_f ? (size_t)c->sh.H * 4 : 0;
+  }
+  return RP_OK;
+}
+
+rp_status rp_workspace_size(const rp_ctx* cc, int op, int batch, int seq, int n_layers, int flags, size_t* bytes) {
+  rp_ctx* c = const_cast<rp_ctx*>(cc);
+  CTX_CHECK(c);
+  RP_CHECK(bytes, RP_ERR_INVALID, "workspace_size: null output");
+  RP_CHECK(batch >= 1 && seq >= 1 && n_layers >= 1, RP_ERR_INVALID, "workspace_size: bad sizes");
+  switch (op) {
+    case RP_OP_STAGE_FWD:
+      return stage_fwd(c, 0, n_layers, batch, seq, nullptr, nullptr, nullptr, nullptr, flags, nullptr, 0, bytes);
+    case RP_OP_STAGE_BWD:
+      return stage_bwd(c, 0, n_layers, batch, seq, nullptr, nullptr, nullptr, nullptr, flags, nullptr, 0, bytes);
+    case RP_OP_FUSED:
+      return stage_bwd(c, 0, n_layers, batch, seq, nullptr, nullptr, nullptr, nullptr, RP_USE_KEPT_ACTS, nullptr, 0,
+                       bytes);
+    case RP_OP_LMHEAD:
+      return lmhead(c, batch, seq, nullptr, nullptr, nullptr, nullptr, nullptr, 0, bytes);
+  }
+  set_error("workspace_size: unknown op %d", op);
+  return RP_ERR_INVALID;
+}
+
+rp_status rp_stage_fwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* x_in, void* y_out,
+                       void* const* ckpt_host, const float* const* router, int flags, void* ws, size_t ws_bytes) {
+  CTX_ENTER(c);
+  RP_CHECK((flags & ~RP_KEEP_ACTS) == 0, RP_ERR_INVALID, "stage_fwd: unknown flags 0x%x", flags);
+  if (flags & RP_KEEP_ACTS) {
+    // the kept internals sit in front of the backward temporaries of a fused stage
+    size_t need = 0;
+    RP_TRY(stage_bwd(c, 0, l1 - l0, batch, seq, nullptr, nullptr, nullptr, nullptr, RP_USE_KEPT_ACTS, nullptr, 0,
+                     &need));
+    RP_CHECK(ws_bytes >= need, RP_ERR_WORKSPACE, "stage_fwd(keep): workspace %zu < %zu bytes (fused size)",
+             ws_bytes, need);
+  }
+  return stage_fwd(c, l0, l1, batch, seq, x_in, y_out, ckpt_host, router, flags, ws, ws_bytes, nullptr);
+}
+
+rp_status rp_stage_bwd_recompute(rp_ctx* c, int l0, int l1, int batch, int seq, const void* const* ckpt,
+                                 const void* dy, void* dx, const float* const* router, int flags, void* ws,
+                                 size_t ws_bytes) {
+  CTX_ENTER(c);
+  RP_CHECK((flags & ~(RP_USE_KEPT_ACTS | RP_CKPT_DEVICE)) == 0, RP_ERR_INVALID, "stage_bwd: unknown flags 0x%x",
+           flags);
+  return stage_bwd(c, l0, l1, batch, seq, ckpt, dy, dx, router, flags, ws, ws_bytes, nullptr);
+}
+
+rp_status rp_lmhead_ce_fwd_bwd(rp_ctx* c, int batch, int seq, const void* x, const int32_t* labels, float* loss,
+                               void* dx, void* ws, size_t ws_bytes) {
+  CTX_ENTER(c);
+  return lmhead(c, batch, seq, x, labels, loss, dx, ws, ws_bytes, nullptr);
+}
+
+rp_status rp_embed_fwd(rp_ctx* c, int n_tokens, int vocab, const int32_t* ids, const void* table, void* x0) {
+  CTX_ENTER(c);
+  RP_CHECK(n_tokens >= 0 && vocab > 0 && ids && table && x0, RP_ERR_INVALID, "embed_fwd: bad arguments");
+  return embed_fwd(c->sh.dt, ids, table, x0, n_tokens, c->sh.H, c->compute);
+}
+
+rp_status rp_embed_bwd(rp_ctx* c, int n_tokens, int vocab, const int32_t* ids, const void* dx0, float* dtable) {
+  CTX_ENTER(c);
+  RP_CHECK(n_tokens >= 0 && vocab > 0 && ids && dx0 && dtable, RP_ERR_INVALID, "embed_bwd: bad arguments");
+  return embed_bwd(c->sh.dt, ids, dx0, dtable, n_tokens, vocab, c->sh.H, c->compute);
+}
+
+rp_status rp_act_copy(rp_ctx* c, int dir, void* dst, const void* src, size_t bytes, int64_t* ticket) {
+  CTX_ENTER(c);
+  return act_copy(c, dir, dst, src, bytes, ticket);
+}
+
+rp_status rp_op_gemm_bf16(rp_ctx* c, int M, int N, int K, const void* A, int lda, int a_kmajor, const void* B,
+                          int ldb, int b_kmajor, void* C, int ldc, int out_f32, int accumulate) {
+  CTX_ENTER(c);
+  GemmDesc d;
+  d.M = M; d.N = N; d.K = K;
+  d.A = A; d.lda = lda; d.a_kmajor = a_kmajor != 0;
+  d.B = B; d.ldb = ldb; d.b_kmajor = b_kmajor != 0;
+  d.C = C; d.ldc = ldc;
+  d.in_dtype = RP_DTYPE_BF16;
+  d.out_dtype = out_f32 ? RP_DTYPE_F32 : RP_DTYPE_BF16;
+  d.accumulate = accumulate != 0;
+  RP_CHECK(ldc >= N, RP_ERR_INVALID, "op_gemm: ldc < N");
+  return gemm(d, c->compute);
+}
+
+rp_status rp_op_attn_fwd(rp_ctx* c, int batch, int seq, const void* qkv, void* o, float* lse) {
+  CTX_ENTER(c);
+  RP_CHECK(batch >= 1 && seq >= 1 && qkv && o && lse, RP_ERR_INVALID, "op_attn_fwd: bad arguments");
+  AttnDesc a;
+  a.dt = c->sh.dt; a.batch = batch; a.seq = seq; a.n_q = c->sh.nq; a.n_kv = c->sh.nkv; a.d = c->sh.d;
+  return attn_fwd(a, qkv, o, lse, c->compute);
+}
+
+rp_status rp_op_attn_bwd(rp_ctx* c, int batch, int seq, const void* qkv, const void* o, const void* dout,
+                         const float* lse, void* dqkv, void* ws, size_t ws_bytes) {
+  CTX_ENTER(c);
+  RP_CHECK(batch >= 1 && seq >= 1 && qkv && o && dout && lse && dqkv && ws, RP_ERR_INVALID,
+           "op_attn_bwd: bad arguments");
+  AttnDesc a;
+  a.dt = c->sh.dt; a.batch = batch; a.seq = seq; a.n_q = c->sh.nq; a.n_kv = c->sh.nkv; a.d = c->sh.d;
+  RP_CHECK(ws_bytes >= attn_bwd_ws_bytes(a), RP_ERR_WORKSPACE, "op_attn_bwd: workspace too small");
+  return attn_bwd(a, qkv, o, dout, lse, (float*)ws, dqkv, c->compute);
+}
+
+}  // extern "C"

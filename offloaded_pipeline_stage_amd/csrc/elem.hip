@@ -1,0 +1,505 @@
+// Row-wise and elementwise kernels of the stage: RMSNorm forward/backward,
+// RoPE, SwiGLU (for the unfused fp32 path), the vocabulary-sharded
+// cross-entropy, token embedding. All HBM-bound: one wavefront per row with
+// 16-byte vector accesses, reductions by fixed-order butterflies so every
+// result is deterministic (recomputation must reproduce the forward exactly).
+#include "ops.h"
+
+namespace rp {
+namespace {
+
+// 16-byte vector of VEC elements
+template <class T> struct Vec;
+template <> struct Vec<float> { static constexpr int N = 4; typedef float4 type; };
+template <> struct Vec<bf16> { static constexpr int N = 8; typedef uint4 type; };
+
+template <class T>
+__device__ __forceinline__ void load_vec(const T* p, float* out);
+template <>
+__device__ __forceinline__ void load_vec<float>(const float* p, float* out) {
+  float4 v = *reinterpret_cast<const float4*>(p);
+  out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+}
+template <>
+__device__ __forceinline__ void load_vec<bf16>(const bf16* p, float* out) {
+  uint4 v = *reinterpret_cast<const uint4*>(p);
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+template <class T>
+__device__ __forceinline__ void store_vec(T* p, const float* in);
+template <>
+__device__ __forceinline__ void store_vec<float>(float* p, const float* in) {
+  *reinterpret_cast<float4*>(p) = make_float4(in[0], in[1], in[2], in[3]);
+}
+template <>
+__device__ __forceinline__ void store_vec<bf16>(bf16* p, const float* in) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = uint32_t(to_bf16(in[2 * i]).u) | (uint32_t(to_bf16(in[2 * i + 1]).u) << 16);
+  *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__global__ void fill_zero_kernel(uint4* p, size_t n16, uint8_t* tail, size_t ntail) {
+  size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (; i < n16; i += stride) p[i] = make_uint4(0, 0, 0, 0);
+  if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm
+// ---------------------------------------------------------------------------
+
+// one wave per row; 4 rows per 256-thread block
+template <class T>
+__global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const T* __restrict__ x,
+                                                          const T* __restrict__ gamma,
+                                                          T* __restrict__ y, float* __restrict__ rstd,
+                                                          int rows, int H, float eps) {
+  constexpr int V = Vec<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const T* xr = x + (int64_t)row * H;
+  float ss = 0.f;
+  for (int c = lane * V; c < H; c += 64 * V) {
+    float v[V];
+    load_vec<T>(xr + c, v);
+#pragma unroll
+    for (int i = 0; i < V; ++i) ss = fmaf(v[i], v[i], ss);
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+  if (lane == 0) rstd[row] = r;
+  T* yr = y + (int64_t)row * H;
+  for (int c = lane * V; c < H; c += 64 * V) {
+    float v[V], g[V];
+    load_vec<T>(xr + c, v);
+    load_vec<T>(gamma + c, g);
+#pragma unroll
+    for (int i = 0; i < V; ++i) v[i] = v[i] * r * g[i];
+    store_vec<T>(yr + c, v);
+  }
+}
+
+// dx = r*(g*gamma) - x * r^3 * mean(g*gamma*x) + resid
+// Each block owns RB consecutive rows (one wave per row at a time) and writes
+// its dgamma partial row; a second kernel sums the partials in block order.
+constexpr int RMS_BWD_ROWS = 32;
+
+template <class T, class TR>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
+    const float* __restrict__ g, const T* __restrict__ x, const T* __restrict__ gamma,
+    const float* __restrict__ rstd, const TR* __restrict__ resid, float* __restrict__ out_f32,
+    T* __restrict__ out_dt, float* __restrict__ part, int rows, int H) {
+  constexpr int V = Vec<T>::N;
+  extern __shared__ float sm[];  // [4][H] wave partials of dgamma
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* my = sm + wave * H;
+  for (int c = lane; c < H; c += 64) my[c] = 0.f;
+  const int r0 = blockIdx.x * RMS_BWD_ROWS;
+  for (int rr = wave; rr < RMS_BWD_ROWS; rr += 4) {
+    const int row = r0 + rr;
+    if (row >= rows) break;
+    const float r = rstd[row];
+    const T* xr = x + (int64_t)row * H;
+    const float* gr = g + (int64_t)row * H;
+    float dot = 0.f;
+    for (int c = lane * V; c < H; c += 64 * V) {
+      float xv[V], gm[V];
+      load_vec<T>(xr + c, xv);
+      load_vec<T>(gamma + c, gm);
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const float gv = gr[c + i];
+        dot = fmaf(gv * gm[i], xv[i], dot);
+        my[c + i] += gv * xv[i] * r;
+      }
+    }
+    dot = wave_sum(dot);
+    const float coef = r * r * r * dot / (float)H;
+    for (int c = lane * V; c < H; c += 64 * V) {
+      float xv[V], gm[V], o[V];
+      load_vec<T>(xr + c, xv);
+      load_vec<T>(gamma + c, gm);
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        float v = r * gr[c + i] * gm[i] - xv[i] * coef;
+        if (resid) v += to_f(resid[(int64_t)row * H + c + i]);
+        o[i] = v;
+      }
+      if (out_f32) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) out_f32[(int64_t)row * H + c + i] = o[i];
+      }
+      if (out_dt) store_vec<T>(out_dt + (int64_t)row * H + c, o);
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < H; c += 256)
+    part[(int64_t)blockIdx.x * H + c] = sm[c] + sm[H + c] + sm[2 * H + c] + sm[3 * H + c];
+}
+
+__global__ void sum_rows_kernel(const float* __restrict__ part, int nrow, int H, float* __restrict__ out) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= H) return;
+  float s = 0.f;
+  for (int r = 0; r < nrow; ++r) s += part[(int64_t)r * H + c];
+  out[c] = s;
+}
+
+// ---------------------------------------------------------------------------
+// RoPE (rotate-half pairs (i, i + d/2))
+// ---------------------------------------------------------------------------
+
+__global__ void rope_table_kernel(float2* tab, int seq, int d, double base) {
+  const int half = d / 2;
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)seq * half) return;
+  const int p = (int)(idx / half), i = (int)(idx % half);
+  const double inv = pow(base, -2.0 * (double)i / (double)d);
+  const double th = (double)p * inv;
+  tab[idx] = make_float2((float)cos(th), (float)sin(th));
+}
+
+// one thread per (row, head, pair)
+template <class T>
+__global__ void rope_apply_kernel(T* buf, int64_t ld, int rows, int seq, int n_heads, int d,
+                                  const float2* __restrict__ tab, int inverse) {
+  const int half = d / 2;
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t per_row = (int64_t)n_heads * half;
+  if (idx >= (int64_t)rows * per_row) return;
+  const int row = (int)(idx / per_row);
+  const int rem = (int)(idx % per_row);
+  const int h = rem / half, i = rem % half;
+  const int p = row % seq;
+  const float2 cs = tab[(int64_t)p * half + i];
+  const float s = inverse ? -cs.y : cs.y;
+  T* base = buf + (int64_t)row * ld + (int64_t)h * d;
+  const float a = to_f(base[i]), b = to_f(base[i + half]);
+  base[i] = from_f<T>(a * cs.x - b * s);
+  base[i + half] = from_f<T>(b * cs.x + a * s);
+}
+
+// ---------------------------------------------------------------------------
+// SwiGLU (unfused path)
+// ---------------------------------------------------------------------------
+template <class T>
+__global__ void swiglu_fwd_kernel(const T* gu, T* m, int rows, int F) {
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)rows * F) return;
+  const int64_t t = idx / F, f = idx % F;
+  const float g = to_f(gu[t * 2 * F + f]), u = to_f(gu[t * 2 * F + F + f]);
+  m[idx] = from_f<T>(g / (1.f + expf(-g)) * u);
+}
+
+template <class T>
+__global__ void swiglu_bwd_kernel(const float* dm, const T* gu, T* dgu, int rows, int F) {
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)rows * F) return;
+  const int64_t t = idx / F, f = idx % F;
+  const float g = to_f(gu[t * 2 * F + f]), u = to_f(gu[t * 2 * F + F + f]);
+  const float sg = 1.f / (1.f + expf(-g));
+  const float v = dm[idx];
+  dgu[t * 2 * F + f] = from_f<T>(v * u * sg * (1.f + g * (1.f - sg)));
+  dgu[t * 2 * F + F + f] = from_f<T>(v * g * sg);
+}
+
+// ---------------------------------------------------------------------------
+// cross-entropy
+// ---------------------------------------------------------------------------
+
+// one wave per row: online (max, sum-exp) over the shard's logits
+__global__ __launch_bounds__(256) void ce_stats_kernel(const float* __restrict__ z, int64_t ld, int rows,
+                                                       int Vs, int vlo, const int32_t* __restrict__ labels,
+                                                       int vocab, float2* part, float* zlab) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float* zr = z + (int64_t)row * ld;
+  float m = -INFINITY, l = 0.f;
+  for (int c = lane; c < Vs; c += 64) {
+    const float v = zr[c];
+    if (v > m) {
+      l = l * __expf(m - v) + 1.f;
+      m = v;
+    } else {
+      l += __expf(v - m);
+    }
+  }
+  // merge lanes in butterfly order
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float mo = __shfl_xor(m, o, 64), lo = __shfl_xor(l, o, 64);
+    const float mn = fmaxf(m, mo);
+    l = (m == -INFINITY ? 0.f : l * __expf(m - mn)) + (mo == -INFINITY ? 0.f : lo * __expf(mo - mn));
+    m = mn;
+  }
+  if (lane == 0) {
+    part[row] = make_float2(m, l);
+    const int y = labels[row];
+    if (y >= vlo && y < vlo + Vs && y < vocab) zlab[row] = zr[y - vlo];
+  }
+}
+
+// single block: per row combine shards -> lse; loss sum in fixed order
+__global__ __launch_bounds__(1024) void ce_combine_kernel(int rows, int n_shards, const float2* parts,
+                                                          const float* zlab, const int32_t* labels,
+                                                          int vocab, float* lse, float* loss,
+                                                          float* inv_n) {
+  __shared__ float s_loss[1024];
+  __shared__ int s_cnt[1024];
+  float acc = 0.f;
+  int cnt = 0;
+  for (int t = threadIdx.x; t < rows; t += 1024) {
+    float m = -INFINITY;
+    for (int s = 0; s < n_shards; ++s) m = fmaxf(m, parts[(int64_t)s * rows + t].x);
+    float l = 0.f;
+    for (int s = 0; s < n_shards; ++s) {
+      const float2 p = parts[(int64_t)s * rows + t];
+      l += p.y * __expf(p.x - m);
+    }
+    const float v = m + __logf(l);
+    lse[t] = v;
+    const int y = labels[t];
+    if (y >= 0 && y < vocab) {
+      acc += v - zlab[t];
+      cnt += 1;
+    }
+  }
+  s_loss[threadIdx.x] = acc;
+  s_cnt[threadIdx.x] = cnt;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if (threadIdx.x < o) {
+      s_loss[threadIdx.x] += s_loss[threadIdx.x + o];
+      s_cnt[threadIdx.x] += s_cnt[threadIdx.x + o];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int n = s_cnt[0];
+    loss[0] = n > 0 ? s_loss[0] / (float)n : 0.f;
+    inv_n[0] = n > 0 ? 1.f / (float)n : 0.f;
+  }
+}
+
+template <class T>
+__global__ void ce_grad_kernel(const float* __restrict__ z, int64_t ld, int rows, int Vs, int vlo,
+                               const int32_t* __restrict__ labels, int vocab, const float* __restrict__ lse,
+                               const float* __restrict__ inv_n, T* __restrict__ dz, int64_t ldz) {
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)rows * Vs) return;
+  const int t = (int)(idx / Vs), v = (int)(idx % Vs);
+  const int y = labels[t];
+  float out = 0.f;
+  if (y >= 0 && y < vocab) {
+    out = __expf(z[(int64_t)t * ld + v] - lse[t]);
+    if (vlo + v == y) out -= 1.f;
+    out *= inv_n[0];
+  }
+  dz[(int64_t)t * ldz + v] = from_f<T>(out);
+}
+
+// ---------------------------------------------------------------------------
+// embedding
+// ---------------------------------------------------------------------------
+template <class T>
+__global__ void embed_fwd_kernel(const int32_t* ids, const T* table, T* x0, int rows, int H) {
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)rows * H) return;
+  const int t = (int)(idx / H), c = (int)(idx % H);
+  x0[idx] = table[(int64_t)ids[t] * H + c];
+}
+
+// one block per vocabulary row, one thread per column: tokens scanned in order
+template <class T>
+__global__ void embed_bwd_kernel(const int32_t* ids, const T* dx0, float* dtable, int rows, int H) {
+  const int v = blockIdx.x;
+  for (int c = threadIdx.x; c < H; c += blockDim.x) {
+    float s = 0.f;
+    for (int t = 0; t < rows; ++t)
+      if (ids[t] == v) s += to_f(dx0[(int64_t)t * H + c]);
+    dtable[(int64_t)v * H + c] = s;
+  }
+}
+
+template <class T>
+__global__ void cast_kernel(const float* a, T* out, size_t n) {
+  const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  if (i < n) out[i] = from_f<T>(a[i]);
+}
+
+unsigned blocks_for(int64_t n, int per = 256) { return (unsigned)cdiv(n, per); }
+
+}  // namespace
+
+rp_status fill_zero(void* p, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return RP_OK;
+  RP_CHECK(((uintptr_t)p & 15) == 0, RP_ERR_INVALID, "fill_zero: pointer not 16-byte aligned");
+  const size_t n16 = bytes / 16, ntail = bytes % 16;
+  unsigned g = (unsigned)std::min<size_t>(std::max<size_t>(cdiv(n16, 256), 1), 8192);
+  RP_LAUNCH(fill_zero_kernel, dim3(g), dim3(256), 0, s, (uint4*)p, n16, (uint8_t*)p + n16 * 16, ntail);
+  return RP_OK;
+}
+
+rp_status rmsnorm_fwd(int dt, const void* x, const void* gamma, void* y, float* rstd, int T, int H,
+                      float eps, hipStream_t s) {
+  if (T == 0) return RP_OK;
+  RP_CHECK(H % 8 == 0, RP_ERR_UNSUPPORTED, "rmsnorm: H %% 8 != 0");
+  dim3 g(blocks_for(T, 4));
+  if (dt == RP_DTYPE_BF16)
+    RP_LAUNCH(rmsnorm_fwd_kernel<bf16>, g, dim3(256), 0, s, (const bf16*)x, (const bf16*)gamma,
+              (bf16*)y, rstd, T, H, eps);
+  else
+    RP_LAUNCH(rmsnorm_fwd_kernel<float>, g, dim3(256), 0, s, (const float*)x, (const float*)gamma,
+              (float*)y, rstd, T, H, eps);
+  return RP_OK;
+}
+
+size_t rmsnorm_bwd_part_bytes(int T, int H) {
+  return (size_t)cdiv(T, RMS_BWD_ROWS) * H * sizeof(float);
+}
+
+template <class T>
+static rp_status rmsnorm_bwd_t(const float* g, const void* x, const void* gamma, const float* rstd,
+                               const void* resid, int resid_dt, float* out_f32, void* out_dt,
+                               float* dgamma, float* part, int rows, int H, hipStream_t s) {
+  const unsigned nb = blocks_for(rows, RMS_BWD_ROWS);
+  const size_t lds = 4 * (size_t)H * sizeof(float);
+  RP_CHECK(lds <= 160 * 1024, RP_ERR_UNSUPPORTED, "rmsnorm bwd: H too large");
+  if (lds > 32 * 1024) {
+    if (resid_dt == RP_DTYPE_F32)
+      RP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&rmsnorm_bwd_kernel<T, float>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+    else
+      RP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&rmsnorm_bwd_kernel<T, bf16>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+  }
+  if (resid_dt == RP_DTYPE_F32 || resid == nullptr)
+    RP_LAUNCH((rmsnorm_bwd_kernel<T, float>), dim3(nb), dim3(256), lds, s, g, (const T*)x,
+              (const T*)gamma, rstd, (const float*)resid, out_f32, (T*)out_dt, part, rows, H);
+  else
+    RP_LAUNCH((rmsnorm_bwd_kernel<T, bf16>), dim3(nb), dim3(256), lds, s, g, (const T*)x,
+              (const T*)gamma, rstd, (const bf16*)resid, out_f32, (T*)out_dt, part, rows, H);
+  if (dgamma) RP_LAUNCH(sum_rows_kernel, dim3(blocks_for(H)), dim3(256), 0, s, part, (int)nb, H, dgamma);
+  return RP_OK;
+}
+
+rp_status rmsnorm_bwd(int dt, const float* g, const void* x, const void* gamma, const float* rstd,
+                      const void* resid, int resid_dt, float* out_f32, void* out_dt, float* dgamma,
+                      float* part, int T, int H, hipStream_t s) {
+  if (T == 0) {
+    if (dgamma) return fill_zero(dgamma, (size_t)H * 4, s);
+    return RP_OK;
+  }
+  RP_CHECK(H % 8 == 0, RP_ERR_UNSUPPORTED, "rmsnorm: H %% 8 != 0");
+  if (dt == RP_DTYPE_BF16)
+    return rmsnorm_bwd_t<bf16>(g, x, gamma, rstd, resid, resid_dt, out_f32, out_dt, dgamma, part, T, H, s);
+  return rmsnorm_bwd_t<float>(g, x, gamma, rstd, resid, resid_dt, out_f32, out_dt, dgamma, part, T, H, s);
+}
+
+rp_status rope_table(float2* tab, int seq, int d, float base, hipStream_t s) {
+  const int64_t n = (int64_t)seq * (d / 2);
+  if (n == 0) return RP_OK;
+  RP_LAUNCH(rope_table_kernel, dim3(blocks_for(n)), dim3(256), 0, s, tab, seq, d, (double)base);
+  return RP_OK;
+}
+
+rp_status rope_apply(int dt, void* buf, int64_t ld, int T, int seq, int n_heads, int d,
+                     const float2* tab, bool inverse, hipStream_t s) {
+  const int64_t n = (int64_t)T * n_heads * (d / 2);
+  if (n == 0) return RP_OK;
+  if (dt == RP_DTYPE_BF16)
+    RP_LAUNCH(rope_apply_kernel<bf16>, dim3(blocks_for(n)), dim3(256), 0, s, (bf16*)buf, ld, T, seq,
+              n_heads, d, tab, inverse ? 1 : 0);
+  else
+    RP_LAUNCH(rope_apply_kernel<float>, dim3(blocks_for(n)), dim3(256), 0, s, (float*)buf, ld, T, seq,
+              n_heads, d, tab, inverse ? 1 : 0);
+  return RP_OK;
+}
+
+rp_status swiglu_fwd(int dt, const void* gu, void* m, int T, int F, hipStream_t s) {
+  const int64_t n = (int64_t)T * F;
+  if (n == 0) return RP_OK;
+  if (dt == RP_DTYPE_BF16)
+    RP_LAUNCH(swiglu_fwd_kernel<bf16>, dim3(blocks_for(n)), dim3(256), 0, s, (const bf16*)gu, (bf16*)m, T, F);
+  else
+    RP_LAUNCH(swiglu_fwd_kernel<float>, dim3(blocks_for(n)), dim3(256), 0, s, (const float*)gu, (float*)m, T, F);
+  return RP_OK;
+}
+
+rp_status swiglu_bwd(int dt, const float* dm, const void* gu, void* dgu, int T, int F, hipStream_t s) {
+  const int64_t n = (int64_t)T * F;
+  if (n == 0) return RP_OK;
+  if (dt == RP_DTYPE_BF16)
+    RP_LAUNCH(swiglu_bwd_kernel<bf16>, dim3(blocks_for(n)), dim3(256), 0, s, dm, (const bf16*)gu, (bf16*)dgu, T, F);
+  else
+    RP_LAUNCH(swiglu_bwd_kernel<float>, dim3(blocks_for(n)), dim3(256), 0, s, dm, (const float*)gu, (float*)dgu, T, F);
+  return RP_OK;
+}
+
+rp_status ce_shard_stats(const float* logits, int64_t ld, int T, int Vs, int vlo, const int32_t* labels,
+                         int vocab, float2* part, float* zlab, hipStream_t s) {
+  if (T == 0) return RP_OK;
+  RP_LAUNCH(ce_stats_kernel, dim3(blocks_for(T, 4)), dim3(256), 0, s, logits, ld, T, Vs, vlo, labels,
+            vocab, part, zlab);
+  return RP_OK;
+}
+
+rp_status ce_combine(int T, int n_shards, const float2* parts, const float* zlab, const int32_t* labels,
+                     int vocab, float* lse, float* loss, float* inv_n, hipStream_t s) {
+  RP_LAUNCH(ce_combine_kernel, dim3(1), dim3(1024), 0, s, T, n_shards, parts, zlab, labels, vocab, lse,
+            loss, inv_n);
+  return RP_OK;
+}
+
+rp_status ce_grad(int dt, const float* logits, int64_t ld, int T, int Vs, int vlo, const int32_t* labels,
+                  int vocab, const float* lse, const float* inv_n, void* dz, int64_t ldz, hipStream_t s) {
+  const int64_t n = (int64_t)T * Vs;
+  if (n == 0) return RP_OK;
+  if (dt == RP_DTYPE_BF16)
+    RP_LAUNCH(ce_grad_kernel<bf16>, dim3(blocks_for(n)), dim3(256), 0, s, logits, ld, T, Vs, vlo, labels,
+              vocab, lse, inv_n, (bf16*)dz, ldz);
+  else
+    RP_LAUNCH(ce_grad_kernel<float>, dim3(blocks_for(n)), dim3(256), 0, s, logits, ld, T, Vs, vlo, labels,
+              vocab, lse, inv_n, (float*)dz, ldz);
+  return RP_OK;
+}
+
+rp_status embed_fwd(int dt, const int32_t* ids, const void* table, void* x0, int T, int H, hipStream_t s) {
+  const int64_t n = (int64_t)T * H;
+  if (n == 0) return RP_OK;
+  if (dt == RP_DTYPE_BF16)
+    RP_LAUNCH(embed_fwd_kernel<bf16>, dim3(blocks_for(n)), dim3(256), 0, s, ids, (const bf16*)table, (bf16*)x0, T, H);
+  else
+    RP_LAUNCH(embed_fwd_kernel<float>, dim3(blocks_for(n)), dim3(256), 0, s, ids, (const float*)table, (float*)x0, T, H);
+  return RP_OK;
+}
+
+rp_status embed_bwd(int dt, const int32_t* ids, const void* dx0, float* dtable, int T, int V, int H,
+                    hipStream_t s) {
+  if (V == 0) return RP_OK;
+  if (dt == RP_DTYPE_BF16)
+    RP_LAUNCH(embed_bwd_kernel<bf16>, dim3(V), dim3(256), 0, s, ids, (const bf16*)dx0, dtable, T, H);
+  else
+    RP_LAUNCH(embed_bwd_kernel<float>, dim3(V), dim3(256), 0, s, ids, (const float*)dx0, dtable, T, H);
+  return RP_OK;
+}
+
+rp_status cast_from_f32(int dt, const float* a, void* out, size_t n, hipStream_t s) {
+  if (n == 0) return RP_OK;
+  if (dt == RP_DTYPE_BF16)
+    RP_LAUNCH(cast_kernel<bf16>, dim3(blocks_for(n)), dim3(256), 0, s, a, (bf16*)out, n);
+  else
+    RP_LAUNCH(cast_kernel<float>, dim3(blocks_for(n)), dim3(256), 0, s, a, (float*)out, n);
+  return RP_OK;
+}
+
+}  // namespace rp

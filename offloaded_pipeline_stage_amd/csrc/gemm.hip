@@ -1,0 +1,496 @@
+// GEMMs of the stage: every projection of the decoder layer (q/k/v, o, gate/up,
+// down), their input-gradient (NN) and weight-gradient (TN) products, and the
+// LM-head shard products. These are the dense contractions that carry almost
+// all of a layer's FLOPs (the paper's appendix C counts matrix multiplies only).
+//
+// bf16 path: v_mfma_f32_32x32x16_bf16 on gfx950. 256 threads = 4 waves in a
+// 2 x 2 grid, each wave owns a (BM/2) x (BN/2) block of 32x32 MFMA tiles.
+// K advances 64 at a time through double-buffered LDS (one barrier per step):
+// the next step's global loads are issued before the current step's MFMAs.
+// LDS rows are 128 bytes (64 bf16 of K) with the 16-byte chunk index XOR-
+// swizzled by row bits 0-2 and 3-5, so the MFMA fragment reads (32 rows, same
+// chunk) and both store patterns below are free of bank conflicts.
+// Operands whose K is the contiguous dimension are copied 16 bytes at a time;
+// operands whose M/N is contiguous (the transposed operands of the backward
+// products) are loaded as 4 K-rows x 8 elements and transposed in registers
+// before the LDS store, so every layout reaches the same LDS image and the
+// same MFMA loop.
+// Epilogues fuse the residual add, the SwiGLU activation (gate and up columns
+// of one output column are held by the same lane) and its backward, and fp32
+// accumulation.
+//
+// fp32 path (and a bf16 cross-check): a plain LDS-tiled FMA kernel with the
+// same epilogue semantics.
+#include "ops.h"
+
+namespace rp {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int BK = 64;
+constexpr int NT = 256;
+
+struct GemmParams {
+  int M, N, K;
+  const bf16* A; int64_t lda;
+  const bf16* B; int64_t ldb;
+  void* C; int64_t ldc;
+  const void* R; int64_t ldr;
+  void* C2; int64_t ldc2;
+  int F;            // SwiGLU width (EPI_SWIGLU: N == 2F; EPI_SWIGLU_BWD: N == F)
+  int tiles_m, tiles_n;
+  int accumulate;
+};
+
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 7); }
+__device__ __forceinline__ int lds_off(int row, int kc) { return row * 128 + ((kc ^ swz(row)) << 4); }
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
+
+// --- global -> register -> LDS copies --------------------------------------
+
+// K-major operand: element (r, k) at g[r * ld + k]; R rows per tile.
+// rowmap: for the SwiGLU gate/up interleave, tile row -> global row.
+template <int R, bool SWIGLU>
+struct LoaderK {
+  static constexpr int NCH = R * 8 / NT;
+  u32x4_t reg[NCH];
+  __device__ __forceinline__ void load(const bf16* g, int64_t ld, int row0, int rows, int k0,
+                                       int K, int tid, int F, int wn_span) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      int c = tid + i * NT;
+      int r = c >> 3, kc = c & 7;
+      int k = k0 + kc * 8;
+      int grow;
+      bool ok;
+      if (SWIGLU) {
+        // tile row r: wave column w = r / wn_span; first half gate, second up
+        int w = r / wn_span, j = r % wn_span, half = wn_span >> 1;
+        int f = row0 + w * half + (j < half ? j : j - half);
+        ok = f < F;
+        grow = (j < half) ? f : F + f;
+      } else {
+        grow = row0 + r;
+        ok = grow < rows;
+      }
+      if (ok && k < K)
+        reg[i] = *reinterpret_cast<const u32x4_t*>(g + (int64_t)grow * ld + k);
+      else
+        reg[i] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(char* lds, int tid) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      int c = tid + i * NT;
+      int r = c >> 3, kc = c & 7;
+      *reinterpret_cast<u32x4_t*>(lds + lds_off(r, kc)) = reg[i];
+    }
+  }
+};
+
+// M-major operand: element (r, k) at g[k * ld + r]; loaded as blocks of
+// 4 K-rows x 8 r, transposed in registers into 8 rows x 4 k.
+template <int R>
+struct LoaderM {
+  static constexpr int NRB = R / 8;
+  static constexpr int NBLK = (BK / 4) * NRB / NT;
+  u32x4_t reg[NBLK][4];
+  __device__ __forceinline__ void load(const bf16* g, int64_t ld, int row0, int rows, int k0,
+                                       int K, int tid) {
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i) {
+      int b = tid + i * NT;
+      int rb = b % NRB, kb = b / NRB;
+      int r = row0 + rb * 8;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int k = k0 + kb * 4 + j;
+        if (k < K && r + 8 <= rows) {
+          reg[i][j] = *reinterpret_cast<const u32x4_t*>(g + (int64_t)k * ld + r);
+        } else if (k < K && r < rows) {
+          uint16_t e[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) e[q] = (r + q < rows) ? g[(int64_t)k * ld + r + q].u : 0;
+          reg[i][j] = u32x4_t{e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
+                              e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16)};
+        } else {
+          reg[i][j] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void store(char* lds, int tid) {
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i) {
+      int b = tid + i * NT;
+      int rb = b % NRB, kb = b / NRB;
+      int kc = kb >> 1, half = kb & 1;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // rows 2q (low halves) and 2q+1 (high halves)
+        uint32_t a0 = reg[i][0][q], a1 = reg[i][1][q], a2 = reg[i][2][q], a3 = reg[i][3][q];
+        u32x2_t lo = u32x2_t{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
+        u32x2_t hi = u32x2_t{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
+        int r0 = rb * 8 + 2 * q;
+        *reinterpret_cast<u32x2_t*>(lds + lds_off(r0, kc) + half * 8) = lo;
+        *reinterpret_cast<u32x2_t*>(lds + lds_off(r0 + 1, kc) + half * 8) = hi;
+      }
+    }
+  }
+};
+
+template <int R, bool KMAJ, bool SWIGLU>
+struct Loader;
+template <int R, bool SWIGLU>
+struct Loader<R, true, SWIGLU> : LoaderK<R, SWIGLU> {};
+template <int R, bool SWIGLU>
+struct Loader<R, false, SWIGLU> : LoaderM<R> {};
+
+// --- the MFMA kernel --------------------------------------------------------
+
+template <int BM, int BN, bool AK, bool BKM, int EPI, bool OUT_F32>
+__global__ __launch_bounds__(NT) void gemm_mfma_kernel(GemmParams p) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr bool SW = (EPI == EPI_SWIGLU);
+  extern __shared__ __align__(16) char smem[];
+  // [A buffer 0][A buffer 1][B buffer 0][B buffer 1]
+  auto sA = [&](int i) { return smem + i * (BM * 128); };
+  auto sB = [&](int i) { return smem + 2 * BM * 128 + i * (BN * 128); };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // tile order: contiguous ranges per XCD (workgroups are dealt round-robin
+  // over the 8 XCDs), grouped 8 tile-rows at a time for L2 reuse
+  int pid = blockIdx.x;
+  const int ntiles = p.tiles_m * p.tiles_n;
+  if ((ntiles & 7) == 0) pid = (pid & 7) * (ntiles >> 3) + (pid >> 3);
+  constexpr int GROUP = 8;
+  const int in_group = GROUP * p.tiles_n;
+  const int gid = pid / in_group;
+  const int first_m = gid * GROUP;
+  const int gsize = min(p.tiles_m - first_m, GROUP);
+  const int tile_m = first_m + (pid % in_group) % gsize;
+  const int tile_n = (pid % in_group) / gsize;
+
+  const int m0 = tile_m * BM;
+  const int n0 = SW ? tile_n * (BN / 2) : tile_n * BN;  // SwiGLU: F-column base
+
+  Loader<BM, AK, false> la;
+  Loader<BN, BKM, SW> lb;
+
+  auto load = [&](int k0) {
+    if constexpr (AK) la.load(p.A + 0, p.lda, m0, p.M, k0, p.K, tid, 0, 0);
+    else la.load(p.A, p.lda, m0, p.M, k0, p.K, tid);
+    if constexpr (BKM) lb.load(p.B, p.ldb, n0, p.N, k0, p.K, tid, p.F, WN);
+    else lb.load(p.B, p.ldb, n0, p.N, k0, p.K, tid);
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = (p.K + BK - 1) / BK;
+  load(0);
+  la.store(sA(0), tid);
+  lb.store(sB(0), tid);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load((kt + 1) * BK);
+    const char* a_s = sA(cur);
+    const char* b_s = sB(cur);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int kc = ks * 2 + (lane >> 5);
+      bf16x8_t af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        int row = wm * WM + i * 32 + (lane & 31);
+        af[i] = *reinterpret_cast<const bf16x8_t*>(a_s + lds_off(row, kc));
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        int row = wn * WN + j * 32 + (lane & 31);
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(b_s + lds_off(row, kc));
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) {
+      la.store(sA(cur ^ 1), tid);
+      lb.store(sB(cur ^ 1), tid);
+    }
+    __syncthreads();
+  }
+
+  // --- epilogue: lane holds column (lane & 31) of each 32x32 tile, rows
+  // 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15
+  const int lc = lane & 31, lr = (lane >> 5) * 4;
+  if constexpr (EPI == EPI_SWIGLU) {
+    bf16* gu = reinterpret_cast<bf16*>(p.C);
+    bf16* mo = reinterpret_cast<bf16*>(p.C2);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN / 2; ++j) {
+        const int f = n0 + wn * (WN / 2) + j * 32 + lc;
+        if (f >= p.F) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + lr + (r & 3);
+          if (m >= p.M) continue;
+          const float g = acc[i][j][r], u = acc[i][j + TN / 2][r];
+          gu[(int64_t)m * p.ldc + f] = to_bf16(g);
+          gu[(int64_t)m * p.ldc + p.F + f] = to_bf16(u);
+          mo[(int64_t)m * p.ldc2 + f] = to_bf16(silu_f(g) * u);
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn * WN + j * 32 + lc;
+        if (n >= p.N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + lr + (r & 3);
+          if (m >= p.M) continue;
+          float v = acc[i][j][r];
+          if constexpr (EPI == EPI_SWIGLU_BWD) {
+            const bf16* gu = reinterpret_cast<const bf16*>(p.R);
+            const float g = to_f(gu[(int64_t)m * p.ldr + n]);
+            const float u = to_f(gu[(int64_t)m * p.ldr + p.F + n]);
+            const float sg = 1.f / (1.f + __expf(-g));
+            bf16* dgu = reinterpret_cast<bf16*>(p.C);
+            dgu[(int64_t)m * p.ldc + n] = to_bf16(v * u * sg * (1.f + g * (1.f - sg)));
+            dgu[(int64_t)m * p.ldc + p.F + n] = to_bf16(v * g * sg);
+          } else if constexpr (OUT_F32) {
+            float* c = reinterpret_cast<float*>(p.C) + (int64_t)m * p.ldc + n;
+            if (EPI == EPI_RESID) v += reinterpret_cast<const float*>(p.R)[(int64_t)m * p.ldr + n];
+            *c = p.accumulate ? *c + v : v;
+          } else {
+            if (EPI == EPI_RESID) v += to_f(reinterpret_cast<const bf16*>(p.R)[(int64_t)m * p.ldr + n]);
+            reinterpret_cast<bf16*>(p.C)[(int64_t)m * p.ldc + n] = to_bf16(v);
+          }
+        }
+      }
+  }
+}
+
+// --- the generic kernel -----------------------------------------------------
+
+template <class TI>
+struct SimpleParams {
+  int M, N, K;
+  const TI* A; int64_t sam, sak;
+  const TI* B; int64_t sbn, sbk;
+};
+
+// 64x64 output tile, 16x16 threads with 4x4 outputs each; writes fp32 acc
+// through the epilogue functor
+template <class TI, class TO, int EPI>
+__global__ __launch_bounds__(256) void gemm_simple_kernel(SimpleParams<TI> p, TO* C, int64_t ldc,
+                                                          const TO* R, int64_t ldr, int accumulate) {
+  __shared__ float As[16][65];
+  __shared__ float Bs[16][65];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < p.K; k0 += 16) {
+    for (int i = threadIdx.x; i < 1024; i += 256) {
+      int kk = i & 15, mm = i >> 4;
+      int m = m0 + mm, k = k0 + kk;
+      As[kk][mm] = (m < p.M && k < p.K) ? to_f(p.A[m * p.sam + k * p.sak]) : 0.f;
+      int n = n0 + mm;
+      Bs[kk][mm] = (n < p.N && k < p.K) ? to_f(p.B[n * p.sbn + k * p.sbk]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int m = m0 + ty * 4 + i, n = n0 + tx * 4 + j;
+      if (m >= p.M || n >= p.N) continue;
+      float v = acc[i][j];
+      if (EPI == EPI_RESID) v += to_f(R[(int64_t)m * ldr + n]);
+      TO* c = C + (int64_t)m * ldc + n;
+      if (accumulate) v += to_f(*c);
+      *c = from_f<TO>(v);
+    }
+}
+
+template <class TI, class TO, int EPI>
+rp_status launch_simple(const GemmDesc& d, void* C, int64_t ldc, hipStream_t s) {
+  SimpleParams<TI> p;
+  p.M = d.M; p.N = d.N; p.K = d.K;
+  p.A = reinterpret_cast<const TI*>(d.A);
+  p.sam = d.a_kmajor ? d.lda : 1; p.sak = d.a_kmajor ? 1 : d.lda;
+  p.B = reinterpret_cast<const TI*>(d.B);
+  p.sbn = d.b_kmajor ? d.ldb : 1; p.sbk = d.b_kmajor ? 1 : d.ldb;
+  dim3 grid(cdiv(d.N, 64), cdiv(d.M, 64));
+  RP_LAUNCH((gemm_simple_kernel<TI, TO, EPI>), grid, dim3(256), 0, s, p,
+            reinterpret_cast<TO*>(C), ldc, reinterpret_cast<const TO*>(d.R), d.ldr,
+            (int)d.accumulate);
+  return RP_OK;
+}
+
+template <class TI>
+rp_status gemm_simple(const GemmDesc& d, hipStream_t s) {
+  const bool of32 = d.out_dtype == RP_DTYPE_F32;
+  switch (d.epi) {
+    case EPI_STORE:
+      if (of32) return launch_simple<TI, float, EPI_STORE>(d, d.C, d.ldc, s);
+      return launch_simple<TI, bf16, EPI_STORE>(d, d.C, d.ldc, s);
+    case EPI_RESID:
+      if (of32) return launch_simple<TI, float, EPI_RESID>(d, d.C, d.ldc, s);
+      return launch_simple<TI, bf16, EPI_RESID>(d, d.C, d.ldc, s);
+    case EPI_SWIGLU: {
+      // gu = A B^T into C, then m = silu(g) * u
+      if (of32) RP_TRY((launch_simple<TI, float, EPI_STORE>(d, d.C, d.ldc, s)));
+      else RP_TRY((launch_simple<TI, bf16, EPI_STORE>(d, d.C, d.ldc, s)));
+      RP_CHECK(d.ldc == d.N && d.ldc2 == d.N / 2, RP_ERR_UNSUPPORTED, "swiglu: packed rows required");
+      return swiglu_fwd(d.out_dtype, d.C, d.C2, d.M, d.N / 2, s);
+    }
+    case EPI_SWIGLU_BWD: {
+      RP_CHECK(d.tmp != nullptr, RP_ERR_INVALID, "swiglu bwd: fp32 scratch missing");
+      GemmDesc e = d;
+      e.accumulate = false;
+      RP_TRY((launch_simple<TI, float, EPI_STORE>(e, d.tmp, d.N, s)));
+      RP_CHECK(d.ldc == 2 * d.N && d.ldr == 2 * d.N, RP_ERR_UNSUPPORTED, "swiglu bwd: packed rows required");
+      return swiglu_bwd(d.out_dtype, d.tmp, d.R, d.C, d.M, d.N, s);
+    }
+  }
+  set_error("gemm: unknown epilogue %d", d.epi);
+  return RP_ERR_INVALID;
+}
+
+// --- MFMA dispatch ------------------------------------------------------------
+
+template <int BM, int BN, bool AK, bool BKM, int EPI, bool OF32>
+rp_status launch_mfma(const GemmDesc& d, hipStream_t s) {
+  GemmParams p;
+  p.M = d.M; p.N = d.N; p.K = d.K;
+  p.A = reinterpret_cast<const bf16*>(d.A); p.lda = d.lda;
+  p.B = reinterpret_cast<const bf16*>(d.B); p.ldb = d.ldb;
+  p.C = d.C; p.ldc = d.ldc;
+  p.R = d.R; p.ldr = d.ldr;
+  p.C2 = d.C2; p.ldc2 = d.ldc2;
+  p.accumulate = d.accumulate ? 1 : 0;
+  p.F = EPI == EPI_SWIGLU ? d.N / 2 : (EPI == EPI_SWIGLU_BWD ? d.N : 0);
+  p.tiles_m = (int)cdiv(d.M, BM);
+  p.tiles_n = EPI == EPI_SWIGLU ? (int)cdiv(d.N / 2, BN / 2) : (int)cdiv(d.N, BN);
+  const size_t lds = 2 * (BM + BN) * 128;
+  static bool attr_set = false;  // one instantiation per template: set once
+  if (!attr_set) {
+    RP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_mfma_kernel<BM, BN, AK, BKM, EPI, OF32>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+    attr_set = true;
+  }
+  const int64_t nt = (int64_t)p.tiles_m * p.tiles_n;
+  RP_LAUNCH((gemm_mfma_kernel<BM, BN, AK, BKM, EPI, OF32>), dim3((unsigned)nt), dim3(NT), lds, s, p);
+  return RP_OK;
+}
+
+template <int BM, int BN, int EPI, bool OF32>
+rp_status dispatch_layout(const GemmDesc& d, hipStream_t s) {
+  if (d.a_kmajor && d.b_kmajor) return launch_mfma<BM, BN, true, true, EPI, OF32>(d, s);
+  if (d.a_kmajor && !d.b_kmajor) return launch_mfma<BM, BN, true, false, EPI, OF32>(d, s);
+  if (!d.a_kmajor && !d.b_kmajor) return launch_mfma<BM, BN, false, false, EPI, OF32>(d, s);
+  return launch_mfma<BM, BN, false, true, EPI, OF32>(d, s);
+}
+
+template <int BM, int BN>
+rp_status dispatch_epi(const GemmDesc& d, hipStream_t s) {
+  const bool of32 = d.out_dtype == RP_DTYPE_F32;
+  switch (d.epi) {
+    case EPI_STORE:
+      return of32 ? dispatch_layout<BM, BN, EPI_STORE, true>(d, s)
+                  : dispatch_layout<BM, BN, EPI_STORE, false>(d, s);
+    case EPI_RESID:
+      return of32 ? dispatch_layout<BM, BN, EPI_RESID, true>(d, s)
+                  : dispatch_layout<BM, BN, EPI_RESID, false>(d, s);
+    case EPI_SWIGLU:
+      RP_CHECK(d.b_kmajor && !of32, RP_ERR_UNSUPPORTED, "swiglu epilogue: K-major bf16 only");
+      return dispatch_layout<BM, BN, EPI_SWIGLU, false>(d, s);
+    case EPI_SWIGLU_BWD:
+      RP_CHECK(!of32, RP_ERR_UNSUPPORTED, "swiglu bwd epilogue: bf16 only");
+      return dispatch_layout<BM, BN, EPI_SWIGLU_BWD, false>(d, s);
+  }
+  set_error("gemm: unknown epilogue %d", d.epi);
+  return RP_ERR_INVALID;
+}
+
+}  // namespace
+
+rp_status gemm_validate(const GemmDesc& d) {
+  RP_CHECK(d.M >= 0 && d.N >= 0 && d.K >= 0, RP_ERR_INVALID, "gemm: negative size");
+  RP_CHECK(d.A && d.B && d.C, RP_ERR_INVALID, "gemm: null operand");
+  RP_CHECK(d.lda >= (d.a_kmajor ? d.K : d.M) && d.ldb >= (d.b_kmajor ? d.K : d.N), RP_ERR_INVALID,
+           "gemm: leading dimension too small");
+  if (d.in_dtype == RP_DTYPE_BF16 && !d.force_simple) {
+    RP_CHECK(d.K % 8 == 0 && d.lda % 8 == 0 && d.ldb % 8 == 0, RP_ERR_UNSUPPORTED,
+             "gemm(bf16): K and leading dimensions must be multiples of 8");
+    RP_CHECK(((uintptr_t)d.A & 15) == 0 && ((uintptr_t)d.B & 15) == 0, RP_ERR_INVALID,
+             "gemm(bf16): operands must be 16-byte aligned");
+    if (d.epi == EPI_SWIGLU) RP_CHECK(d.N % 2 == 0, RP_ERR_INVALID, "swiglu: N must be even");
+  }
+  if (d.epi == EPI_RESID || d.epi == EPI_SWIGLU_BWD) RP_CHECK(d.R, RP_ERR_INVALID, "gemm: missing R");
+  if (d.epi == EPI_SWIGLU) RP_CHECK(d.C2, RP_ERR_INVALID, "gemm: missing C2");
+  RP_CHECK(!d.accumulate || d.out_dtype == RP_DTYPE_F32, RP_ERR_INVALID,
+           "gemm: accumulation needs an fp32 output");
+  return RP_OK;
+}
+
+rp_status gemm(const GemmDesc& d, hipStream_t s) {
+  RP_TRY(gemm_validate(d));
+  if (d.M == 0 || d.N == 0) return RP_OK;
+  if (d.K == 0) {
+    RP_CHECK(d.epi == EPI_STORE, RP_ERR_UNSUPPORTED, "gemm: K == 0 only for plain stores");
+    if (d.accumulate) return RP_OK;
+    // C = 0 row by row
+    for (int m = 0; m < d.M; ++m)
+      RP_TRY(fill_zero((char*)d.C + (size_t)m * d.ldc * dtype_size(d.out_dtype),
+                       (size_t)d.N * dtype_size(d.out_dtype), s));
+    return RP_OK;
+  }
+  if (d.in_dtype == RP_DTYPE_F32) return gemm_simple<float>(d, s);
+  if (d.force_simple) return gemm_simple<bf16>(d, s);
+  const int64_t n_eff = d.epi == EPI_SWIGLU ? d.N / 2 : d.N;
+  const int64_t big = cdiv(d.M, 256) * cdiv(n_eff, d.epi == EPI_SWIGLU ? 128 : 256);
+  if (big >= 240) return dispatch_epi<256, 256>(d, s);
+  return dispatch_epi<128, 128>(d, s);
+}
+
+}  // namespace rp

@@ -1,0 +1,107 @@
+// Internal launchers of the stage kernels (not part of the C ABI).
+#pragma once
+
+#include "common.h"
+
+namespace rp {
+
+// ---------------------------------------------------------------------------
+// GEMM: C[M, N] = sum_k A(m, k) * B(n, k), fp32 accumulation
+// ---------------------------------------------------------------------------
+enum Epi {
+  EPI_STORE = 0,      // C = acc (out dtype), or C += acc (fp32, accumulate)
+  EPI_RESID = 1,      // C = acc + R (out dtype; R same dtype as C)
+  EPI_SWIGLU = 2,     // B rows [0,F) gate, [F,2F) up: C = gu [M, 2F] pre-activations,
+                      // C2 = silu(g) * u [M, F]; N passed = 2F
+  EPI_SWIGLU_BWD = 3  // acc = dm [M, F]; R = gu [M, 2F]; C = dgu [M, 2F]
+};
+
+struct GemmDesc {
+  int M = 0, N = 0, K = 0;
+  const void* A = nullptr; int64_t lda = 0; bool a_kmajor = true;
+  const void* B = nullptr; int64_t ldb = 0; bool b_kmajor = true;
+  void* C = nullptr; int64_t ldc = 0;
+  int in_dtype = RP_DTYPE_BF16;   // A and B
+  int out_dtype = RP_DTYPE_BF16;  // C (and C2, R)
+  int epi = EPI_STORE;
+  bool accumulate = false;
+  const void* R = nullptr; int64_t ldr = 0;
+  void* C2 = nullptr; int64_t ldc2 = 0;
+  float* tmp = nullptr;           // fp32 [M, N] scratch for the unfused fp32 path
+  bool force_simple = false;      // use the generic kernel even for bf16
+};
+
+rp_status gemm(const GemmDesc& d, hipStream_t s);
+rp_status gemm_validate(const GemmDesc& d);
+
+// ---------------------------------------------------------------------------
+// elementwise / row kernels
+// ---------------------------------------------------------------------------
+rp_status fill_zero(void* p, size_t bytes, hipStream_t s);
+
+// y = x * rsqrt(mean(x^2) + eps) * gamma ; rstd[t] = rsqrt(...)
+rp_status rmsnorm_fwd(int dt, const void* x, const void* gamma, void* y, float* rstd, int T,
+                      int H, float eps, hipStream_t s);
+
+// dx = (r * g*gamma - x * r^3 * mean(g*gamma*x)) + resid;  g fp32 [T, H].
+// resid: nullptr, or [T, H] of dtype resid_dt. Writes out_f32 and/or out_dt.
+// dgamma[h] = sum_t g[t,h] x[t,h] r[t] through part [n_part, H] partials.
+rp_status rmsnorm_bwd(int dt, const float* g, const void* x, const void* gamma,
+                      const float* rstd, const void* resid, int resid_dt, float* out_f32,
+                      void* out_dt, float* dgamma, float* part, int T, int H, hipStream_t s);
+size_t rmsnorm_bwd_part_bytes(int T, int H);
+
+// cos/sin table [seq][d/2] (fp32 pairs) computed in fp64
+rp_status rope_table(float2* tab, int seq, int d, float base, hipStream_t s);
+// rotate (inverse=false) / rotate back (inverse=true) the first n_heads heads of
+// every row of buf [T, ld] in place; position of row t is t % seq
+rp_status rope_apply(int dt, void* buf, int64_t ld, int T, int seq, int n_heads, int d,
+                     const float2* tab, bool inverse, hipStream_t s);
+
+// m = silu(g) * u from gu [T, 2F]
+rp_status swiglu_fwd(int dt, const void* gu, void* m, int T, int F, hipStream_t s);
+// dgu from dm (fp32 [T, F]) and gu
+rp_status swiglu_bwd(int dt, const float* dm, const void* gu, void* dgu, int T, int F,
+                     hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// attention
+// ---------------------------------------------------------------------------
+struct AttnDesc {
+  int dt = RP_DTYPE_BF16;
+  int batch = 1, seq = 0, n_q = 0, n_kv = 0, d = 0;
+};
+rp_status attn_fwd(const AttnDesc& a, const void* qkv, void* o, float* lse, hipStream_t s);
+// Dbuf: fp32 [n_q, T] scratch
+rp_status attn_bwd(const AttnDesc& a, const void* qkv, const void* o, const void* dout,
+                   const float* lse, float* Dbuf, void* dqkv, hipStream_t s);
+size_t attn_bwd_ws_bytes(const AttnDesc& a);
+
+// ---------------------------------------------------------------------------
+// cross-entropy over vocabulary shards
+// ---------------------------------------------------------------------------
+// per row of one shard's fp32 logits [T, Vs]: (max, sum exp(z - max)) -> part[t],
+// and the label's logit into zlab[t] if the label falls in [vlo, vlo + Vs)
+rp_status ce_shard_stats(const float* logits, int64_t ld, int T, int Vs, int vlo,
+                         const int32_t* labels, int vocab, float2* part, float* zlab,
+                         hipStream_t s);
+// merge the shards' partials: lse[t]; loss = sum(lse - zlab) / n_valid; inv_n = 1/n_valid
+rp_status ce_combine(int T, int n_shards, const float2* parts, const float* zlab,
+                     const int32_t* labels, int vocab, float* lse, float* loss, float* inv_n,
+                     hipStream_t s);
+// dz = (exp(z - lse) - [v == label]) * inv_n (0 for ignored rows), dtype dt
+rp_status ce_grad(int dt, const float* logits, int64_t ld, int T, int Vs, int vlo,
+                  const int32_t* labels, int vocab, const float* lse, const float* inv_n,
+                  void* dz, int64_t ldz, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// misc
+// ---------------------------------------------------------------------------
+rp_status embed_fwd(int dt, const int32_t* ids, const void* table, void* x0, int T, int H,
+                    hipStream_t s);
+rp_status embed_bwd(int dt, const int32_t* ids, const void* dx0, float* dtable, int T, int V,
+                    int H, hipStream_t s);
+// out (dtype dt) = a (fp32)
+rp_status cast_from_f32(int dt, const float* a, void* out, size_t n, hipStream_t s);
+
+}  // namespace rp

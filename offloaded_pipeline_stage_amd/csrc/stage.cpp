@@ -1,0 +1,412 @@
+// Stage executor: the decoder-layer forward, recompute + backward and the
+// vocabulary-sharded LM head, expressed as a sequence of kernel launches on
+// the context's compute stream, with the checkpoint copies on the activation
+// streams (RoundPipe paper, section 2.1.1 full recomputation with layer
+// inputs offloaded to host; section 3.2 fused first backward stage;
+// section 4.2.1 compute synchronised with the activation streams by events).
+#include <algorithm>
+#include <cstring>
+
+#include "ctx.h"
+
+namespace rp {
+namespace {
+
+// internals of one layer's forward, kept for its backward
+struct Acts {
+  void* x = nullptr;      // layer input [T, H]
+  float* rstd1 = nullptr; // [T]
+  void* a = nullptr;      // RMSNorm1(x) [T, H]
+  void* qkv = nullptr;    // [T, QKV], q and k rotated
+  void* o = nullptr;      // attention output [T, Q]
+  float* lse = nullptr;   // [nq, T]
+  void* h1 = nullptr;     // x + o Wo^T [T, H]
+  float* rstd2 = nullptr; // [T]
+  void* b = nullptr;      // RMSNorm2(h1) [T, H]
+  void* gu = nullptr;     // gate/up pre-activations [T, 2F]
+  void* m = nullptr;      // silu(g) * u [T, F]
+};
+
+struct BwdTmp {
+  void* dgu = nullptr;     // [T, 2F]
+  float* gbuf = nullptr;   // fp32 [T, H] (db, then da)
+  float* dh1f = nullptr;   // fp32 [T, H]
+  void* dh1 = nullptr;     // [T, H]
+  void* dO = nullptr;      // [T, Q]
+  void* dqkv = nullptr;    // [T, QKV]
+  float* Dbuf = nullptr;   // [nq, T]
+  float* dm_tmp = nullptr; // fp32 [T, F] (unfused fp32 path)
+  float* part = nullptr;   // RMSNorm dgamma partials
+  void* gp[2] = {nullptr, nullptr};  // inter-layer gradients
+  void* ck[2] = {nullptr, nullptr};  // uploaded checkpoints
+};
+
+struct Layout {
+  float2* rope = nullptr;
+  std::vector<Acts> acts;
+  void* xb[2] = {nullptr, nullptr};
+  BwdTmp bt;
+};
+
+void carve_acts(Bump& bp, const Shape& s, int64_t T, Acts& A) {
+  A.x = bp.take(T * s.H * s.es);
+  A.rstd1 = bp.take<float>(T * 4);
+  A.a = bp.take(T * s.H * s.es);
+  A.qkv = bp.take(T * s.QKV * s.es);
+  A.o = bp.take(T * s.Q * s.es);
+  A.lse = bp.take<float>((size_t)s.nq * T * 4);
+  A.h1 = bp.take(T * s.H * s.es);
+  A.rstd2 = bp.take<float>(T * 4);
+  A.b = bp.take(T * s.H * s.es);
+  A.gu = bp.take(T * 2 * s.F * s.es);
+  A.m = bp.take(T * s.F * s.es);
+}
+
+// mode bits: 1 = keep all layers' internals, 2 = backward temporaries, 4 = fwd ping-pong
+void carve(Bump& bp, const Shape& s, int64_t T, int seq, int n_layers, bool keep, bool bwd, bool fwd_pp,
+           Layout& L) {
+  L.rope = bp.take<float2>((size_t)seq * (s.d / 2) * sizeof(float2));
+  L.acts.assign(keep ? n_layers : 1, Acts{});
+  for (auto& a : L.acts) carve_acts(bp, s, T, a);
+  if (fwd_pp) {
+    L.xb[0] = bp.take(T * s.H * s.es);
+    L.xb[1] = bp.take(T * s.H * s.es);
+  }
+  if (bwd) {
+    BwdTmp& b = L.bt;
+    b.dgu = bp.take(T * 2 * s.F * s.es);
+    b.gbuf = bp.take<float>(T * s.H * 4);
+    b.dh1f = bp.take<float>(T * s.H * 4);
+    b.dh1 = bp.take(T * s.H * s.es);
+    b.dO = bp.take(T * s.Q * s.es);
+    b.dqkv = bp.take(T * s.QKV * s.es);
+    b.Dbuf = bp.take<float>((size_t)s.nq * T * 4);
+    if (s.dt == RP_DTYPE_F32) b.dm_tmp = bp.take<float>(T * s.F * 4);
+    b.part = bp.take<float>(rmsnorm_bwd_part_bytes((int)T, s.H));
+    b.gp[0] = bp.take(T * s.H * s.es);
+    b.gp[1] = bp.take(T * s.H * s.es);
+    b.ck[0] = bp.take(T * s.H * s.es);
+    b.ck[1] = bp.take(T * s.H * s.es);
+  }
+}
+
+inline const char* wptr(const Slot& s, const rp_layer_cfg& cfg, int tensor) {
+  size_t off = 0, bytes = 0;
+  block_layout(cfg, RP_BLOCK_WEIGHT, tensor, &off, &bytes, nullptr);
+  return (const char*)s.w + off;
+}
+inline float* gptr(const Slot& s, const rp_layer_cfg& cfg, int tensor) {
+  size_t off = 0, bytes = 0;
+  block_layout(cfg, RP_BLOCK_GRAD, tensor, &off, &bytes, nullptr);
+  return (float*)((char*)s.g + off);
+}
+
+GemmDesc mk(int M, int N, int K, const void* A, int64_t lda, bool ak, const void* B, int64_t ldb, bool bk,
+            void* C, int64_t ldc, int in_dt, int out_dt, int epi = EPI_STORE) {
+  GemmDesc d;
+  d.M = M; d.N = N; d.K = K;
+  d.A = A; d.lda = lda; d.a_kmajor = ak;
+  d.B = B; d.ldb = ldb; d.b_kmajor = bk;
+  d.C = C; d.ldc = ldc;
+  d.in_dtype = in_dt; d.out_dtype = out_dt; d.epi = epi;
+  return d;
+}
+
+// forward of one layer: x -> y. With y == nullptr (recomputation before the
+// backward) the down projection is skipped: the backward reads the layer's
+// internals, never its output.
+rp_status layer_fwd(rp_ctx* c, const Slot& w, int T, int seq, const void* x, const Acts& A, void* y,
+                    const float2* rope, hipStream_t st) {
+  const Shape& s = c->sh;
+  const int dt = s.dt;
+  const rp_layer_cfg& cfg = c->cfg;
+  RP_TRY(rmsnorm_fwd(dt, x, wptr(w, cfg, RP_T_GAMMA1), A.a, A.rstd1, T, s.H, cfg.rms_eps, st));
+  RP_TRY(gemm(mk(T, s.QKV, s.H, A.a, s.H, true, wptr(w, cfg, RP_T_WQKV), s.H, true, A.qkv, s.QKV, dt, dt), st));
+  RP_TRY(rope_apply(dt, A.qkv, s.QKV, T, seq, s.nq + s.nkv, s.d, rope, false, st));
+  AttnDesc ad;
+  ad.dt = dt; ad.batch = T / seq; ad.seq = seq; ad.n_q = s.nq; ad.n_kv = s.nkv; ad.d = s.d;
+  RP_TRY(attn_fwd(ad, A.qkv, A.o, A.lse, st));
+  GemmDesc go = mk(T, s.H, s.Q, A.o, s.Q, true, wptr(w, cfg, RP_T_WO), s.Q, true, A.h1, s.H, dt, dt, EPI_RESID);
+  go.R = x; go.ldr = s.H;
+  RP_TRY(gemm(go, st));
+  RP_TRY(rmsnorm_fwd(dt, A.h1, wptr(w, cfg, RP_T_GAMMA2), A.b, A.rstd2, T, s.H, cfg.rms_eps, st));
+  GemmDesc gg = mk(T, 2 * s.F, s.H, A.b, s.H, true, wptr(w, cfg, RP_T_WGU), s.H, true, A.gu, 2 * s.F, dt, dt,
+                   EPI_SWIGLU);
+  gg.C2 = A.m; gg.ldc2 = s.F;
+  RP_TRY(gemm(gg, st));
+  if (y == nullptr) return RP_OK;
+  GemmDesc gd = mk(T, s.H, s.F, A.m, s.F, true, wptr(w, cfg, RP_T_WD), s.F, true, y, s.H, dt, dt, EPI_RESID);
+  gd.R = A.h1; gd.ldr = s.H;
+  RP_TRY(gemm(gd, st));
+  return RP_OK;
+}
+
+// backward of one layer from its forward internals: dy -> dx, weight grads
+rp_status layer_bwd(rp_ctx* c, Slot& w, int T, int seq, const void* x, const Acts& A, const BwdTmp& B,
+                    const void* dy, void* dx, const float2* rope, hipStream_t st) {
+  const Shape& s = c->sh;
+  const int dt = s.dt;
+  const rp_layer_cfg& cfg = c->cfg;
+  const int F2 = 2 * s.F;
+  RP_TRY(wait_grad_drained(c, w));
+  // MLP: dm = dy Wd -> dgu (fused SwiGLU backward)
+  GemmDesc g1 = mk(T, s.F, s.H, dy, s.H, true, wptr(w, cfg, RP_T_WD), s.F, false, B.dgu, F2, dt, dt,
+                   EPI_SWIGLU_BWD);
+  g1.R = A.gu; g1.ldr = F2; g1.tmp = B.dm_tmp;
+  RP_TRY(gemm(g1, st));
+  // dWd = dy^T m
+  RP_TRY(gemm(mk(s.H, s.F, T, dy, s.H, false, A.m, s.F, false, gptr(w, cfg, RP_T_WD), s.F, dt, RP_DTYPE_F32), st));
+  // db = dgu Wgu
+  RP_TRY(gemm(mk(T, s.H, F2, B.dgu, F2, true, wptr(w, cfg, RP_T_WGU), s.H, false, B.gbuf, s.H, dt, RP_DTYPE_F32),
+              st));
+  // dWgu = dgu^T b
+  RP_TRY(gemm(mk(F2, s.H, T, B.dgu, F2, false, A.b, s.H, false, gptr(w, cfg, RP_T_WGU), s.H, dt, RP_DTYPE_F32),
+              st));
+  // dh1 = dy + RMSNorm2^T db ; dgamma2
+  RP_TRY(rmsnorm_bwd(dt, B.gbuf, A.h1, wptr(w, cfg, RP_T_GAMMA2), A.rstd2, dy, dt, B.dh1f, B.dh1,
+                     gptr(w, cfg, RP_T_GAMMA2), B.part, T, s.H, st));
+  // attention output projection
+  RP_TRY(gemm(mk(T, s.Q, s.H, B.dh1, s.H, true, wptr(w, cfg, RP_T_WO), s.Q, false, B.dO, s.Q, dt, dt), st));
+  RP_TRY(gemm(mk(s.H, s.Q, T, B.dh1, s.H, false, A.o, s.Q, false, gptr(w, cfg, RP_T_WO), s.Q, dt, RP_DTYPE_F32),
+              st));
+  AttnDesc ad;
+  ad.dt = dt; ad.batch = T / seq; ad.seq = seq; ad.n_q = s.nq; ad.n_kv = s.nkv; ad.d = s.d;
+  RP_TRY(attn_bwd(ad, A.qkv, A.o, B.dO, A.lse, B.Dbuf, B.dqkv, st));
+  RP_TRY(rope_apply(dt, B.dqkv, s.QKV, T, seq, s.nq + s.nkv, s.d, rope, true, st));
+  // da = dqkv Wqkv ; dWqkv = dqkv^T a
+  RP_TRY(gemm(mk(T, s.H, s.QKV, B.dqkv, s.QKV, true, wptr(w, cfg, RP_T_WQKV), s.H, false, B.gbuf, s.H, dt,
+                 RP_DTYPE_F32), st));
+  RP_TRY(gemm(mk(s.QKV, s.H, T, B.dqkv, s.QKV, false, A.a, s.H, false, gptr(w, cfg, RP_T_WQKV), s.H, dt,
+                 RP_DTYPE_F32), st));
+  // dx = dh1 + RMSNorm1^T da ; dgamma1
+  RP_TRY(rmsnorm_bwd(dt, B.gbuf, x, wptr(w, cfg, RP_T_GAMMA1), A.rstd1, B.dh1f, RP_DTYPE_F32, nullptr, dx,
+                     gptr(w, cfg, RP_T_GAMMA1), B.part, T, s.H, st));
+  RP_TRY(mark_consumed(c, w));
+  RP_TRY(mark_grad_ready(c, w));
+  return RP_OK;
+}
+
+rp_status check_range(rp_ctx* c, int l0, int l1, int batch, int seq) {
+  RP_CHECK(l0 >= 0 && l1 > l0 && l1 <= (int)c->layers.size(), RP_ERR_INVALID,
+           "layer range [%d, %d) invalid or not bound", l0, l1);
+  for (int l = l0; l < l1; ++l)
+    RP_CHECK(c->layers[l].bound, RP_ERR_INVALID, "layer %d is not bound", l);
+  RP_CHECK(batch >= 1 && seq >= 1, RP_ERR_INVALID, "batch and seq must be >= 1");
+  RP_CHECK((int64_t)batch * seq < (int64_t)1 << 30, RP_ERR_UNSUPPORTED, "too many tokens");
+  return RP_OK;
+}
+
+}  // namespace
+
+rp_status stage_fwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* x_in, void* y_out,
+                    void* const* ckpt_host, const float* const* router, int flags, void* ws, size_t ws_bytes,
+                    size_t* need) {
+  (void)router;
+  const Shape& s = c->sh;
+  const bool keep = flags & RP_KEEP_ACTS;
+  const int n = l1 - l0;
+  const int64_t T = (int64_t)batch * seq;
+  Layout L;
+  Bump bp(need ? nullptr : ws);
+  carve(bp, s, T, seq, n, keep, keep, !keep, L);
+  if (need) {
+    *need = bp.off;
+    return RP_OK;
+  }
+  RP_TRY(check_range(c, l0, l1, batch, seq));
+  RP_CHECK(x_in && y_out && ws, RP_ERR_INVALID, "stage_fwd: null pointer");
+  RP_CHECK(x_in != y_out, RP_ERR_INVALID, "stage_fwd: y_out may not alias x_in");
+  RP_CHECK(ws_bytes >= bp.off, RP_ERR_WORKSPACE, "stage_fwd: workspace %zu < %zu bytes", ws_bytes, bp.off);
+  if (ckpt_host)
+    for (int i = 0; i < n; ++i)
+      RP_CHECK(ckpt_host[i] && is_pinned_host(ckpt_host[i]), RP_ERR_NOT_PINNED,
+               "stage_fwd: checkpoint %d is not pinned host memory", i);
+  hipStream_t st = c->compute;
+  if (c->last_act_d2h_valid) RP_HIP(hipStreamWaitEvent(st, c->last_act_d2h, 0));
+  RP_TRY(rope_table(L.rope, seq, s.d, c->cfg.rope_base, st));
+  const size_t xbytes = (size_t)T * s.H * s.es;
+  if (keep) RP_HIP(hipMemcpyAsync(L.acts[0].x, x_in, xbytes, hipMemcpyDeviceToDevice, st));
+  std::vector<hipEvent_t> d2h_done(n, nullptr);
+  for (int i = 0; i < n; ++i) {
+    const int l = l0 + i;
+    Slot& w = c->layers[l].base;
+    RP_TRY(wait_weights(c, w));
+    const Acts& A = keep ? L.acts[i] : L.acts[0];
+    const void* x = keep ? A.x : (i == 0 ? x_in : L.xb[(i - 1) & 1]);
+    void* y = (i == n - 1) ? y_out : (keep ? L.acts[i + 1].x : L.xb[i & 1]);
+    if (ckpt_host) {
+      int64_t tk;
+      RP_TRY(act_copy(c, RP_D2H, ckpt_host[i], x, xbytes, &tk));
+      d2h_done[i] = c->ticket_ev[tk];
+      // later calls rewrite this workspace: they start after the download
+      if (!c->last_act_d2h) c->last_act_d2h = c->new_event();
+      RP_HIP(hipEventRecord(c->last_act_d2h, c->act_d2h));
+      c->last_act_d2h_valid = true;
+    }
+    // the ping-pong buffer written by this layer held the input of layer
+    // i - 1, whose checkpoint download must have finished
+    if (!keep && ckpt_host && i >= 1 && i != n - 1) RP_HIP(hipStreamWaitEvent(st, d2h_done[i - 1], 0));
+    RP_TRY(layer_fwd(c, w, (int)T, seq, x, A, y, L.rope, st));
+    RP_TRY(mark_consumed(c, w));
+  }
+  if (keep) {
+    c->kept_ws = ws;
+    c->kept_l0 = l0; c->kept_l1 = l1; c->kept_batch = batch; c->kept_seq = seq;
+  } else if (c->kept_ws == ws) {
+    c->kept_ws = nullptr;
+  }
+  return RP_OK;
+}
+
+rp_status stage_bwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* const* ckpt, const void* dy,
+                    void* dx, const float* const* router, int flags, void* ws, size_t ws_bytes, size_t* need) {
+  (void)router;
+  const Shape& s = c->sh;
+  const bool kept = flags & RP_USE_KEPT_ACTS;
+  const bool ck_dev = flags & RP_CKPT_DEVICE;
+  const int n = l1 - l0;
+  const int64_t T = (int64_t)batch * seq;
+  Layout L;
+  Bump bp(need ? nullptr : ws);
+  carve(bp, s, T, seq, n, kept, true, false, L);
+  if (need) {
+    *need = bp.off;
+    return RP_OK;
+  }
+  RP_TRY(check_range(c, l0, l1, batch, seq));
+  RP_CHECK(dy && dx && ws, RP_ERR_INVALID, "stage_bwd: null pointer");
+  RP_CHECK(ws_bytes >= bp.off, RP_ERR_WORKSPACE, "stage_bwd: workspace %zu < %zu bytes", ws_bytes, bp.off);
+  if (kept) {
+    RP_CHECK(c->kept_ws == ws && c->kept_l0 == l0 && c->kept_l1 == l1 && c->kept_batch == batch &&
+                 c->kept_seq == seq, RP_ERR_STATE,
+             "stage_bwd: no activations kept for layers [%d, %d) on this workspace", l0, l1);
+  } else {
+    RP_CHECK(ckpt != nullptr, RP_ERR_INVALID, "stage_bwd: checkpoints required without RP_USE_KEPT_ACTS");
+    for (int i = 0; i < n; ++i) {
+      RP_CHECK(ckpt[i] != nullptr, RP_ERR_INVALID, "stage_bwd: checkpoint %d is null", i);
+      if (!ck_dev)
+        RP_CHECK(is_pinned_host(ckpt[i]), RP_ERR_NOT_PINNED, "stage_bwd: checkpoint %d is not pinned", i);
+    }
+  }
+  for (int l = l0; l < l1; ++l)
+    RP_CHECK(c->layers[l].base.g != nullptr, RP_ERR_INVALID, "stage_bwd: layer %d has no gradient buffer", l);
+  hipStream_t st = c->compute;
+  if (c->last_act_d2h_valid) RP_HIP(hipStreamWaitEvent(st, c->last_act_d2h, 0));
+  RP_TRY(rope_table(L.rope, seq, s.d, c->cfg.rope_base, st));
+  const size_t xbytes = (size_t)T * s.H * s.es;
+  // checkpoint uploads: layer i's input into ck[i & 1], one layer ahead
+  hipEvent_t ck_free[2] = {nullptr, nullptr};
+  auto upload = [&](int i) -> rp_status {
+    if (kept || ck_dev) return RP_OK;
+    if (ck_free[i & 1]) RP_HIP(hipStreamWaitEvent(c->act_h2d, ck_free[i & 1], 0));
+    int64_t tk;
+    return act_copy(c, RP_H2D, L.bt.ck[i & 1], ckpt[i], xbytes, &tk);
+  };
+  // act_copy(H2D) makes the compute stream wait at issue time, so the
+  // prefetch of layer i - 1 is issued after layer i's compute is enqueued.
+  if (!kept && !ck_dev) RP_TRY(upload(n - 1));
+  const void* g_in = dy;
+  for (int i = n - 1; i >= 0; --i) {
+    const int l = l0 + i;
+    Slot& w = c->layers[l].base;
+    RP_TRY(wait_weights(c, w));
+    const Acts& A = kept ? L.acts[i] : L.acts[0];
+    const void* x;
+    if (kept) {
+      x = A.x;
+    } else {
+      x = ck_dev ? ckpt[i] : L.bt.ck[i & 1];
+      // recompute the forward from the checkpoint (same kernels as the forward)
+      RP_TRY(layer_fwd(c, w, (int)T, seq, x, A, nullptr, L.rope, st));
+    }
+    // inter-layer gradients alternate gp[0], gp[1]; the stage input's goes to dx
+    void* g_out = (i == 0) ? dx : L.bt.gp[(n - 1 - i) & 1];
+    RP_TRY(layer_bwd(c, w, (int)T, seq, x, A, L.bt, g_in, g_out, L.rope, st));
+    if (!kept && !ck_dev) {
+      if (!ck_free[i & 1]) ck_free[i & 1] = c->new_event();
+      RP_HIP(hipEventRecord(ck_free[i & 1], st));
+      if (i >= 1) RP_TRY(upload(i - 1));
+    }
+    g_in = g_out;
+  }
+  return RP_OK;
+}
+
+// ---------------------------------------------------------------------------
+// LM head
+// ---------------------------------------------------------------------------
+rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* labels, float* loss, void* dx,
+                 void* ws, size_t ws_bytes, size_t* need) {
+  const Shape& s = c->sh;
+  const int64_t T = (int64_t)batch * seq;
+  const int ns = c->n_shards;
+  int vs_max = 0;
+  for (int i = 0; i < ns; ++i) vs_max = std::max(vs_max, c->shard_lo[i + 1] - c->shard_lo[i]);
+  const bool fnorm = c->final_norm.w != nullptr;
+  Bump bp(need ? nullptr : ws);
+  void* z = fnorm ? bp.take(T * s.H * s.es) : nullptr;
+  float* rstd = bp.take<float>(T * 4);
+  float* logits = bp.take<float>((size_t)ns * T * vs_max * 4);
+  float2* parts = bp.take<float2>((size_t)ns * T * sizeof(float2));
+  float* zlab = bp.take<float>(T * 4);
+  float* lse = bp.take<float>(T * 4);
+  float* inv_n = bp.take<float>(4);
+  void* dz = bp.take(T * vs_max * s.es);
+  float* dxf = bp.take<float>(T * s.H * 4);
+  float* part = bp.take<float>(rmsnorm_bwd_part_bytes((int)T, s.H));
+  if (need) {
+    *need = bp.off;
+    return RP_OK;
+  }
+  RP_CHECK(ns > 0, RP_ERR_STATE, "lmhead: no LM head bound");
+  RP_CHECK(batch >= 1 && seq >= 1, RP_ERR_INVALID, "lmhead: batch and seq must be >= 1");
+  RP_CHECK(x && labels && loss && dx && ws, RP_ERR_INVALID, "lmhead: null pointer");
+  RP_CHECK(ws_bytes >= bp.off, RP_ERR_WORKSPACE, "lmhead: workspace %zu < %zu bytes", ws_bytes, bp.off);
+  hipStream_t st = c->compute;
+  const int dt = s.dt;
+  if (c->last_act_d2h_valid) RP_HIP(hipStreamWaitEvent(st, c->last_act_d2h, 0));
+  const void* zz = x;
+  if (fnorm) {
+    RP_TRY(wait_weights(c, c->final_norm));
+    RP_TRY(rmsnorm_fwd(dt, x, c->final_norm.w, z, rstd, (int)T, s.H, c->cfg.rms_eps, st));
+    zz = z;
+  }
+  RP_TRY(fill_zero(zlab, T * 4, st));
+  for (int i = 0; i < ns; ++i) {
+    const int lo = c->shard_lo[i], vs = c->shard_lo[i + 1] - lo;
+    Slot& w = c->shards[i];
+    RP_TRY(wait_weights(c, w));
+    float* lg = logits + (size_t)i * T * vs_max;
+    RP_TRY(gemm(mk((int)T, vs, s.H, zz, s.H, true, w.w, s.H, true, lg, vs, dt, RP_DTYPE_F32), st));
+    RP_TRY(ce_shard_stats(lg, vs, (int)T, vs, lo, labels, c->vocab, parts + (size_t)i * T, zlab, st));
+  }
+  RP_TRY(ce_combine((int)T, ns, parts, zlab, labels, c->vocab, lse, loss, inv_n, st));
+  RP_TRY(fill_zero(dxf, (size_t)T * s.H * 4, st));
+  for (int i = 0; i < ns; ++i) {
+    const int lo = c->shard_lo[i], vs = c->shard_lo[i + 1] - lo;
+    Slot& w = c->shards[i];
+    RP_CHECK(w.g != nullptr, RP_ERR_INVALID, "lmhead: shard %d has no gradient buffer", i);
+    RP_TRY(wait_grad_drained(c, w));
+    const float* lg = logits + (size_t)i * T * vs_max;
+    RP_TRY(ce_grad(dt, lg, vs, (int)T, vs, lo, labels, c->vocab, lse, inv_n, dz, vs, st));
+    GemmDesc gx = mk((int)T, s.H, vs, dz, vs, true, w.w, s.H, false, dxf, s.H, dt, RP_DTYPE_F32);
+    gx.accumulate = true;
+    RP_TRY(gemm(gx, st));
+    RP_TRY(gemm(mk(vs, s.H, (int)T, dz, vs, false, zz, s.H, false, w.g, s.H, dt, RP_DTYPE_F32), st));
+    RP_TRY(mark_consumed(c, w));
+    RP_TRY(mark_grad_ready(c, w));
+  }
+  if (fnorm) {
+    RP_CHECK(c->final_norm.g != nullptr, RP_ERR_INVALID, "lmhead: final norm has no gradient buffer");
+    RP_TRY(wait_grad_drained(c, c->final_norm));
+    RP_TRY(rmsnorm_bwd(dt, dxf, x, c->final_norm.w, rstd, nullptr, RP_DTYPE_F32, nullptr, dx, c->final_norm.g,
+                       part, (int)T, s.H, st));
+    RP_TRY(mark_consumed(c, c->final_norm));
+    RP_TRY(mark_grad_ready(c, c->final_norm));
+  } else {
+    RP_TRY(cast_from_f32(dt, dxf, dx, (size_t)T * s.H, st));
+  }
+  return RP_OK;
+}
+
+}  // namespace rp

@@ -1,0 +1,113 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/rp.h declares, and its pure host functions (block layout, transfer
+planner) agree with the oracle bit for bit."""
+import os
+import random
+import re
+import subprocess
+
+import pytest
+
+import synth
+from oracle import sched as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rp.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from offloaded_pipeline_stage_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from offloaded_pipeline_stage_amd import build
+        build.build(verbose=False)
+    binding.lib()
+    return binding
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_stage_calls():
+    fns = header_functions()
+    for need in ("rp_stage_fwd", "rp_stage_bwd_recompute", "rp_lmhead_ce_fwd_bwd", "rp_weight_stream_submit"):
+        assert need in fns
+
+
+def test_library_exports_every_declared_function(B):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (rp_[a-z0-9_]+)\b", out))
+    missing = [f for f in header_functions() if f not in exported]
+    assert not missing, missing
+    # the binding declares exactly the header's functions
+    assert sorted(B.EXPORTS) == header_functions()
+
+
+def test_status_strings(B):
+    lib = B.lib()
+    assert lib.rp_status_string(B.RP_OK) == b"RP_OK"
+    assert lib.rp_status_string(B.RP_ERR_NOT_PINNED) == b"RP_ERR_NOT_PINNED"
+    assert lib.rp_version().startswith(b"roundpipe")
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3_1p7b", "llama3_8b", "qwen3_32b"])
+def test_block_layout_is_aligned_and_disjoint(B, name):
+    cfg = synth.config(name)
+    H, Q, KV, F = cfg.hidden, cfg.q_dim, cfg.kv_dim, cfg.ffn
+    es = 2 if cfg.dtype == "bf16" else 4
+    expect = {B.RP_T_GAMMA1: H, B.RP_T_WQKV: (Q + 2 * KV) * H, B.RP_T_WO: H * Q, B.RP_T_GAMMA2: H,
+              B.RP_T_WGU: 2 * F * H, B.RP_T_WD: H * F}
+    for block, size in ((B.RP_BLOCK_WEIGHT, es), (B.RP_BLOCK_GRAD, 4)):
+        spans = []
+        for tid, n in expect.items():
+            off, nb, tot = B.block_layout(cfg, block, tid)
+            assert off % 256 == 0 and nb == n * size
+            spans.append((off, off + nb))
+        spans.sort()
+        assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+        assert tot >= spans[-1][1] and tot % 256 == 0
+    # the paper-scale sizes: Llama-3.1-8B layer = 218.1M parameters
+    if name == "llama3_8b":
+        n = sum(expect.values())
+        assert n == 218_112_000
+
+
+def test_planner_matches_oracle_bit_for_bit(B):
+    rng = random.Random(99)
+    for _ in range(300):
+        n = rng.randint(0, 9)
+        sizes = [rng.choice([rng.randint(1, 5000), rng.randint(1, 10 ** 9)]) for _ in range(n)]
+        nw = rng.randint(1, 6)
+        cap = rng.choice([0, 0, rng.randint(1000, 10 ** 8)])
+        align = rng.choice([1, 256, 4096])
+        got = B.xfer_plan(sizes, nw, cap, align)
+        chunks = S.split_items(sizes, nw, align=align, max_chunk=cap)
+        win = S.lpt_assign([c[2] for c in chunks], nw)
+        expect = [(c[0], c[1], c[2], w) for c, w in zip(chunks, win)]
+        assert got == expect
+
+
+def test_planner_layer_blocks_into_windows(B):
+    # an 8B-shaped layer block + the 4 LM-head shards over 4 windows: LPT keeps
+    # the windows within Graham's bound of the even split
+    cfg = synth.config("llama3_8b")
+    sizes = [B.block_bytes(cfg, B.RP_BLOCK_WEIGHT)] + [32064 * 4096 * 2] * 4
+    plan = B.xfer_plan(sizes, 4)
+    load = [0] * 4
+    for _, _, nb, w in plan:
+        load[w] += nb
+    assert sum(load) == sum(sizes)
+    assert max(load) <= (4 / 3) * (sum(sizes) / 4) + max(nb for _, _, nb, _ in plan)
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="checks the no-GPU error path")
+def test_ctx_create_without_gpu_fails_cleanly(B):
+    import ctypes as C
+    cfg = B.make_cfg(synth.config("tiny"))
+    h = C.c_void_p()
+    st = B.lib().rp_ctx_create(0, C.byref(cfg), None, C.byref(h))
+    assert st in (B.RP_ERR_HIP, B.RP_ERR_INVALID)
+    assert not h.value

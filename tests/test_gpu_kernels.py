@@ -1,0 +1,127 @@
+"""Kernel-level parity on the GPU through the C ABI's single-kernel entry
+points: the bf16 MFMA GEMM in every operand layout (against a CPU fp64
+product of the same bf16 inputs) and causal GQA attention (against the
+oracle)."""
+import math
+
+import pytest
+import torch
+
+import synth
+from oracle import stage as O
+from _helpers import ensure_built, max_rel, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    return ensure_built()
+
+
+def _ctx(B, **kw):
+    base = dict(name="k", hidden=256, n_q=4, n_kv=2, head_dim=128, ffn=512, batch=1, seq=64, dtype="bf16")
+    base.update(kw)
+    return B.Context(synth.StageConfig(**base))
+
+
+def _operand(rows, cols, kmajor, seed, name):
+    """Logical [rows, K=cols] operand stored K-major ([rows, cols]) or
+    transposed ([cols, rows]); returns (storage, logical fp64)."""
+    t = synth.normal((rows, cols), seed, name, dtype=torch.bfloat16)
+    store = t if kmajor else t.t().contiguous()
+    return store, t.double()
+
+
+GEMM_CASES = [
+    # M, N, K  (ragged tiles, K tail, both tile configurations)
+    (200, 136, 264),
+    (64, 8, 8),
+    (1000, 520, 72),
+    (4096, 4096, 128),   # 256x256 tiles
+    (4104, 4232, 200),   # 256x256 tiles with ragged edges
+]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_CASES)
+@pytest.mark.parametrize("ak,bk", [(True, True), (True, False), (False, False), (False, True)])
+def test_gemm_bf16_layouts(B, M, N, K, ak, bk):
+    say("gemm", M, N, K, ak, bk)
+    ctx = _ctx(B)
+    a_s, a = _operand(M, K, ak, 11, f"A{M}{K}")
+    b_s, b = _operand(N, K, bk, 12, f"B{N}{K}")
+    ref = a @ b.T
+    dev = torch.device("cuda")
+    A, Bm = a_s.to(dev), b_s.to(dev)
+    lda = K if ak else M
+    ldb = K if bk else N
+    C32 = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
+    ctx.op_gemm_bf16(M, N, K, A, lda, ak, Bm, ldb, bk, C32, N, out_f32=True)
+    C16 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ctx.op_gemm_bf16(M, N, K, A, lda, ak, Bm, ldb, bk, C16, N, out_f32=False)
+    ctx.sync()
+    err32 = max_rel(C32, ref)
+    err16 = max_rel(C16, ref)
+    assert err32 < 1e-5, err32
+    assert err16 < 2 ** -8, err16
+    # bf16 output = fp32 output rounded once
+    assert torch.equal(C16.cpu(), C32.cpu().to(torch.bfloat16))
+
+
+def test_gemm_accumulate_and_strided_output(B):
+    say("gemm accumulate")
+    ctx = _ctx(B)
+    M, N, K = 300, 96, 128
+    a_s, a = _operand(M, K, True, 1, "a")
+    b_s, b = _operand(N, K, False, 2, "b")
+    dev = torch.device("cuda")
+    base = synth.normal((M, N + 8), 3, "c")
+    C = base.clone().to(dev)
+    ctx.op_gemm_bf16(M, N, K, a_s.to(dev), K, True, b_s.to(dev), N, False, C, N + 8, out_f32=True, accumulate=True)
+    ctx.sync()
+    ref = base.double().clone()
+    ref[:, :N] += a @ b.T
+    assert max_rel(C, ref) < 1e-5
+    assert torch.equal(C[:, N:].cpu(), base[:, N:])  # columns past N untouched
+
+
+@pytest.mark.parametrize("dtype,d,nq,nkv,batch,seq", [
+    ("f32", 64, 4, 4, 2, 50),
+    ("bf16", 128, 4, 2, 2, 200),
+    ("bf16", 128, 8, 2, 1, 333),
+    ("bf16", 128, 2, 1, 1, 1),
+])
+def test_attention_fwd_bwd(B, dtype, d, nq, nkv, batch, seq):
+    say("attention", dtype, d, nq, nkv, batch, seq)
+    ctx = _ctx(B, n_q=nq, n_kv=nkv, head_dim=d, hidden=max(256, nq * d), dtype=dtype)
+    T = batch * seq
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    W = (nq + 2 * nkv) * d
+    qkv = synth.normal((T, W), 5, f"qkv{T}{W}", dtype=dt)
+    dout = synth.normal((T, nq * d), 5, f"do{T}", dtype=dt)
+    dev = torch.device("cuda")
+    o = torch.empty(T, nq * d, dtype=dt, device=dev)
+    lse = torch.empty(nq, T, dtype=torch.float32, device=dev)
+    dqkv = torch.empty(T, W, dtype=dt, device=dev)
+    ws = torch.empty(nq * T * 4 + 256, dtype=torch.uint8, device=dev)
+    qkv_d = qkv.to(dev)
+    ctx.op_attn_fwd(batch, seq, qkv_d, o, lse)
+    ctx.op_attn_bwd(batch, seq, qkv_d, o, dout.to(dev), lse, dqkv, ws)
+    ctx.sync()
+    # oracle on the same inputs
+    x = qkv.double().requires_grad_(True)
+    q = x[:, :nq * d].reshape(T, nq, d)
+    k = x[:, nq * d:(nq + nkv) * d].reshape(T, nkv, d)
+    v = x[:, (nq + nkv) * d:].reshape(T, nkv, d)
+    ref = O.causal_attention(q, k, v, batch, seq).reshape(T, nq * d)
+    (gref,) = torch.autograd.grad((ref * dout.double()).sum(), [x])
+    tol = 1e-4 if dtype == "f32" else 2e-2
+    assert max_rel(o, ref.detach()) < tol
+    assert max_rel(dqkv, gref) < tol
+    # lse is log sum exp of the scaled causal scores
+    s = torch.einsum("thd,uhd->htu", q.detach(), k.detach().repeat_interleave(nq // nkv, dim=1)) / math.sqrt(d)
+    pos = torch.arange(seq).repeat(batch)
+    row = torch.arange(T) // seq
+    mask = (pos[None, :] <= pos[:, None]) & (row[None, :] == row[:, None])
+    lref = torch.logsumexp(s.masked_fill(~mask[None], float("-inf")), dim=-1)
+    assert (lse.cpu().double() - lref).abs().max().item() < (1e-4 if dtype == "f32" else 2e-2)

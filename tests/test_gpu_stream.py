@@ -1,0 +1,130 @@
+"""Weight streaming and the ABI's error paths on the GPU: weights uploaded
+from pinned host memory through gated transfer windows give bit-identical
+results to resident weights; gradients downloaded to pinned host memory equal
+the device copies; bad arguments are rejected before anything is enqueued."""
+import pytest
+import torch
+
+import synth
+from _helpers import ensure_built, say
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda")
+
+
+@pytest.fixture(scope="module")
+def env():
+    B = ensure_built()
+    from offloaded_pipeline_stage_amd.worker import Worker
+    return B, Worker
+
+
+def _small_cfg():
+    return synth.config("qwen3_1p7b", seq=128, hidden=512, n_q=4, n_kv=2, ffn=1024)
+
+
+def test_streamed_weights_and_grad_download_bit_identical(env):
+    B, Worker = env
+    say("weight streaming")
+    cfg = _small_cfg()
+    layers = [synth.layer_weights(cfg, l, gamma="perturbed") for l in range(2)]
+    x = synth.activation(cfg, "x")
+    dy = synth.activation(cfg, "dy")
+    T, H, b, s = cfg.tokens, cfg.hidden, cfg.batch, cfg.seq
+    bf = dict(dtype=torch.bfloat16, device=DEV)
+
+    def run(wk, xd, dyd):
+        ws = wk.ctx.workspace(B.RP_OP_FUSED, b, s, 2)
+        y, dx = torch.empty(T, H, **bf), torch.empty(T, H, **bf)
+        wk.ctx.stage_fwd(0, 2, b, s, xd, y, ws, flags=B.RP_KEEP_ACTS)
+        wk.ctx.stage_bwd_recompute(0, 2, b, s, dyd, dx, ws, flags=B.RP_USE_KEPT_ACTS)
+        return y, dx
+
+    ref = Worker(cfg)
+    for l in range(2):
+        ref.add_layer(l, layers[l])
+    y_ref, dx_ref = run(ref, x.to(DEV), dy.to(DEV))
+    ref.ctx.sync()
+
+    wk = Worker(cfg)
+    host = [wk.pack_layer(layers[l], pinned=True) for l in range(2)]
+    for l in range(2):
+        wk.add_layer(l, resident=False)
+    # activation uploads first; parameter window w is gated behind activation
+    # ticket t0 + w (window 0 behind x, window 1 behind dy, window 2 behind a
+    # third copy)
+    x_host, dy_host = x.pin_memory(), dy.pin_memory()
+    x_dev, dy_dev = torch.empty(T, H, **bf), torch.empty(T, H, **bf)
+    t0 = wk.ctx.act_copy(B.RP_H2D, x_dev, x_host)
+    items = [(B.RP_PARAM_H2D, B.RP_TGT_LAYER, l, 0, wk.w_bytes, host[l]) for l in range(2)]
+    wk.ctx.weight_stream_submit(items, n_windows=3, max_chunk=1 << 20, gate_ticket=t0)
+    wk.ctx.act_copy(B.RP_H2D, dy_dev, dy_host)
+    mark_h = torch.zeros(256, dtype=torch.uint8).pin_memory()
+    mark_d = torch.empty(256, dtype=torch.uint8, device=DEV)
+    wk.ctx.act_copy(B.RP_H2D, mark_d, mark_h)
+    y, dx = run(wk, x_dev, dy_dev)
+    gh = [torch.empty(wk.g_bytes, dtype=torch.uint8).pin_memory() for _ in range(2)]
+    wk.ctx.weight_stream_submit([(B.RP_GRAD_D2H, B.RP_TGT_LAYER, l, 0, wk.g_bytes, gh[l]) for l in range(2)],
+                                n_windows=2)
+    wk.ctx.sync()
+    assert torch.equal(y, y_ref) and torch.equal(dx, dx_ref)
+    for l in range(2):
+        assert torch.equal(wk.layers[l]["w"].cpu(), host[l])
+        assert torch.equal(gh[l], wk.layers[l]["g"].cpu())
+        assert torch.equal(gh[l], ref.layers[l]["g"].cpu())
+
+
+def test_deferred_window_waits_for_its_ticket(env):
+    B, Worker = env
+    say("deferred window")
+    cfg = _small_cfg()
+    wk = Worker(cfg)
+    wk.add_layer(0, resident=False)
+    host = wk.pack_layer(synth.layer_weights(cfg, 0), pinned=True)
+    # gate on a ticket that has not been issued yet: the stage call refuses
+    wk.ctx.weight_stream_submit([(B.RP_PARAM_H2D, B.RP_TGT_LAYER, 0, 0, wk.w_bytes, host)], gate_ticket=5)
+    T, H = cfg.tokens, cfg.hidden
+    x = torch.zeros(T, H, dtype=torch.bfloat16, device=DEV)
+    y = torch.empty_like(x)
+    ws = wk.ctx.workspace(B.RP_OP_STAGE_FWD, cfg.batch, cfg.seq, 1)
+    with pytest.raises(B.RPError) as e:
+        wk.ctx.stage_fwd(0, 1, cfg.batch, cfg.seq, x, y, ws)
+    assert e.value.status == B.RP_ERR_STATE
+    # issuing tickets 0..5 releases the window
+    hx = torch.zeros(16, dtype=torch.uint8).pin_memory()
+    dx = torch.zeros(16, dtype=torch.uint8, device=DEV)
+    for _ in range(6):
+        wk.ctx.act_copy(B.RP_H2D, dx, hx)
+    wk.ctx.stage_fwd(0, 1, cfg.batch, cfg.seq, x, y, ws)
+    wk.ctx.sync()
+    assert torch.equal(wk.layers[0]["w"].cpu(), host)
+
+
+def test_error_paths(env):
+    B, Worker = env
+    say("error paths")
+    cfg = _small_cfg()
+    wk = Worker(cfg)
+    wk.add_layer(0, synth.layer_weights(cfg, 0))
+    T, H, b, s = cfg.tokens, cfg.hidden, cfg.batch, cfg.seq
+    x = torch.zeros(T, H, dtype=torch.bfloat16, device=DEV)
+    y = torch.empty_like(x)
+    small = torch.empty(1024, dtype=torch.uint8, device=DEV)
+    with pytest.raises(B.RPError) as e:
+        wk.ctx.stage_fwd(0, 1, b, s, x, y, small)
+    assert e.value.status == B.RP_ERR_WORKSPACE
+    ws = wk.ctx.workspace(B.RP_OP_FUSED, b, s, 1)
+    with pytest.raises(B.RPError) as e:
+        wk.ctx.stage_bwd_recompute(0, 1, b, s, x, y, ws, flags=B.RP_USE_KEPT_ACTS)
+    assert e.value.status == B.RP_ERR_STATE
+    pageable = torch.zeros(T, H, dtype=torch.bfloat16)
+    with pytest.raises(B.RPError) as e:
+        wk.ctx.act_copy(B.RP_D2H, pageable, x)
+    assert e.value.status == B.RP_ERR_NOT_PINNED
+    with pytest.raises(B.RPError) as e:
+        wk.ctx.stage_fwd(0, 2, b, s, x, y, ws)  # layer 1 not bound
+    assert e.value.status == B.RP_ERR_INVALID
+    with pytest.raises(B.RPError) as e:
+        wk.ctx.stage_fwd(0, 1, b, s, x, x, ws)  # output aliases input
+    assert e.value.status == B.RP_ERR_INVALID
+    wk.ctx.sync()
