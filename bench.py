@@ -1,0 +1,295 @@
+"""Throughput of one RoundPipe GPU-worker step on one MI355X.
+
+A step is one pass of the worker's hot path over one microbatch of the
+Llama-3.1-8B-shaped stage (hidden 4096, 32 query / 8 key-value heads of 128,
+SwiGLU FFN 14336, 1 x 8192 tokens, bf16 weights and activations, fp32
+gradients):
+
+  rp_stage_fwd            layer forward; its input checkpoint goes to pinned
+                          host memory (activation offload)
+  rp_lmhead_ce_fwd_bwd    4-shard LM head (4096 x 128256) + mean cross-entropy,
+                          forward and backward -> dy
+  rp_stage_bwd_recompute  checkpoint back from host, recompute the layer,
+                          backward -> dx and the fp32 weight gradients
+
+`value` is trained tokens per second with weights resident in HBM (inputs in
+HBM when the timed region starts). With --streamed the same step also uploads
+every weight from pinned host memory and downloads every gradient to it
+through rp_weight_stream_submit; that host-link-inclusive rate is reported
+under "streamed", never as `value`.
+
+Each kernel launch in the timed region is timed by the library's own HIP
+event pairs on the compute stream (rp_trace_*); the dominant kernel is priced
+against the MI355X peak for its bound. The CPU oracle is timed on a bounded
+sample of the same step for the cpu_baseline field.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--streamed]
+                       [--no-cpu-baseline] [--cpu-seq S] [--trace-json PATH]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from collections import defaultdict
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "trained tokens/sec per GPU (fwd+recompute+bwd) + MFMA util, 8B-shaped stage"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def layer_flops(cfg, recompute: bool) -> dict:
+    """Matrix-product FLOPs of one layer (causal attention counts the causal
+    pairs): forward, and backward (dX + dW products, attention dS/dP/dQ/dK/dV
+    counted as twice the forward's two products)."""
+    T, H, Q, KV, F = cfg.tokens, cfg.hidden, cfg.q_dim, cfg.kv_dim, cfg.ffn
+    lin = 2.0 * T * H * (Q + 2 * KV) + 2.0 * T * Q * H + 2.0 * T * H * 2 * F + 2.0 * T * F * H
+    pairs = cfg.batch * cfg.seq * (cfg.seq + 1) / 2.0
+    att = 4.0 * cfg.head_dim * cfg.n_q * pairs
+    fwd = lin + att
+    bwd = 2 * lin + 2 * att
+    return {"fwd": fwd, "recompute": fwd if recompute else 0.0, "bwd": bwd}
+
+
+def lmhead_flops(cfg) -> float:
+    return 3 * 2.0 * cfg.tokens * cfg.hidden * cfg.vocab
+
+
+class Step:
+    """Buffers and calls of one worker step through the C ABI."""
+
+    def __init__(self, cfg, streamed: bool):
+        from offloaded_pipeline_stage_amd import binding as B
+        from offloaded_pipeline_stage_amd.worker import Worker
+        self.B = B
+        self.cfg = cfg
+        self.streamed = streamed
+        dev = torch.device("cuda", 0)
+        T, H = cfg.tokens, cfg.hidden
+        t0 = time.time()
+        lw = synth.layer_weights(cfg, 0)
+        head = synth.lmhead_weights(cfg)
+        self.wk = Worker(cfg)
+        ctx = self.wk.ctx
+        if streamed:
+            # weights live in pinned host memory; two device copies of the layer
+            # (ids 0 and 1) alternate between steps so that the next step's
+            # upload overlaps this step's compute
+            self.host_layer = self.wk.pack_layer(lw, pinned=True)
+            for l in (0, 1):
+                self.wk.add_layer(l, resident=False)
+            self.wk.add_lmhead(None, resident=False)
+            rows = self.wk.shard_rows()
+            self.host_shards, lo = [], 0
+            for r in rows:
+                self.host_shards.append(head["w"][lo:lo + r].contiguous().pin_memory())
+                lo += r
+            self.host_grad = [torch.empty(self.wk.g_bytes, dtype=torch.uint8).pin_memory() for _ in (0, 1)]
+            self.host_dshards = [torch.empty(r, H, dtype=torch.float32).pin_memory() for r in rows]
+        else:
+            self.wk.add_layer(0, lw)
+            self.wk.add_lmhead(head["w"])
+        del lw, head
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        self.x = synth.activation(cfg, "x").to(dev)
+        self.labels = synth.uniform_labels(cfg).to(dev)
+        self.y = torch.empty(T, H, **bf)
+        self.dy = torch.empty(T, H, **bf)
+        self.dx = torch.empty(T, H, **bf)
+        self.loss = torch.zeros(1, dtype=torch.float32, device=dev)
+        self.ckpt = [torch.empty(T, H, dtype=torch.bfloat16).pin_memory()]
+        self.ws_f = ctx.workspace(B.RP_OP_STAGE_FWD, cfg.batch, cfg.seq, 1)
+        self.ws_b = ctx.workspace(B.RP_OP_STAGE_BWD, cfg.batch, cfg.seq, 1)
+        self.ws_h = ctx.workspace(B.RP_OP_LMHEAD, cfg.batch, cfg.seq)
+        self.n = 0
+        log(f"[bench] setup {time.time() - t0:.1f}s; workspaces "
+            f"{(self.ws_f.numel() + self.ws_b.numel() + self.ws_h.numel()) / 2**30:.2f} GiB")
+
+    def _shard_items(self, kind):
+        B, out = self.B, []
+        hs = self.host_shards if kind == B.RP_PARAM_H2D else self.host_dshards
+        for sh, h in enumerate(hs):
+            out.append((kind, B.RP_TGT_LMHEAD, sh, 0, h.numel() * h.element_size(), h))
+        return out
+
+    def run(self):
+        B, cfg, wk = self.B, self.cfg, self.wk
+        ctx = wk.ctx
+        b, s = cfg.batch, cfg.seq
+        layer = self.n & 1 if self.streamed else 0
+        sub = lambda items: ctx.weight_stream_submit(items, n_windows=1, max_chunk=64 << 20)  # noqa: E731
+        if self.streamed and self.n == 0:
+            sub([(B.RP_PARAM_H2D, B.RP_TGT_LAYER, layer, 0, wk.w_bytes, self.host_layer)]
+                + self._shard_items(B.RP_PARAM_H2D))
+        ctx.stage_fwd(layer, layer + 1, b, s, self.x, self.y, self.ws_f, ckpt_host=self.ckpt)
+        if self.streamed:
+            # the next step's layer weights go up (into the other device copy)
+            # while this step computes
+            sub([(B.RP_PARAM_H2D, B.RP_TGT_LAYER, layer ^ 1, 0, wk.w_bytes, self.host_layer)])
+        ctx.lmhead_ce_fwd_bwd(b, s, self.y, self.labels, self.loss, self.dy, self.ws_h)
+        if self.streamed:
+            # shard gradients down; the next step's shards up once read
+            sub(self._shard_items(B.RP_GRAD_D2H) + self._shard_items(B.RP_PARAM_H2D))
+        ctx.stage_bwd_recompute(layer, layer + 1, b, s, self.dy, self.dx, self.ws_b, ckpt=self.ckpt)
+        if self.streamed:
+            sub([(B.RP_GRAD_D2H, B.RP_TGT_LAYER, layer, 0, wk.g_bytes, self.host_grad[layer])])
+        self.n += 1
+
+    def sync(self):
+        self.wk.ctx.sync()
+        torch.cuda.synchronize()
+
+
+def summarize_trace(recs, steps):
+    agg = defaultdict(lambda: [0, 0.0, 0.0, 0.0])
+    for name, fl, by, ms in recs:
+        a = agg[name]
+        a[0] += 1
+        a[1] += fl
+        a[2] += by
+        a[3] += ms
+    return agg
+
+
+def roofline(agg, dtype):
+    name, (cnt, fl, by, ms) = max(agg.items(), key=lambda kv: kv[1][3])
+    sec = ms / 1e3
+    if fl > 0:
+        peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS
+        ach = fl / sec / 1e12
+        return {"kernel": name, "bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": None, "launches": cnt,
+                "avg_launch_ms": round(ms / cnt, 4), "flops_per_launch": fl / cnt}
+    ach = by / sec / 1e9
+    return {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": None, "launches": cnt,
+            "avg_launch_ms": round(ms / cnt, 4), "bytes_per_launch": by / cnt}
+
+
+def cpu_baseline(cfg, seq: int):
+    """The oracle, as it stands, on `seq` tokens of the same stage: layer
+    forward, LM head + cross-entropy forward/backward, layer recompute +
+    backward, all in fp64 on the host cores."""
+    from oracle import stage as O
+    c = cfg.with_(seq=seq)
+    lw = synth.layer_weights(c, 0)
+    w = synth.lmhead_weights(c)["w"]
+    x = synth.activation(c, "x")
+    labels = synth.uniform_labels(c)
+    t0 = time.time()
+    y, ck = O.stage_forward(x, [lw], c)
+    _, dy, _, _ = O.lmhead_fwd_bwd(y, w, labels, c.n_shards)
+    O.stage_backward_recompute(ck, [lw], dy, c)
+    dt = time.time() - t0
+    return {"value": round(c.tokens / dt, 2), "unit": "tokens/s", "cores": torch.get_num_threads(),
+            "kind": "oracle",
+            "sample": f"one step of the same stage at 1 x {seq} tokens (full layer and LM-head widths), "
+                      f"fp64 torch on the host, {dt:.1f} s; attention cost grows with sequence length, "
+                      f"so the full 8192-token step would run slower per token"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_8b")
+    ap.add_argument("--streamed", action="store_true", help="also time the weight-streaming variant")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seq", type=int, default=128)
+    ap.add_argument("--trace-json", default=None, help="write the per-kernel table here")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}); "
+              f"the worker step is the per-GPU unit and is reported at N=1 only.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (HIP device)", file=sys.stderr)
+        sys.exit(1)
+    from offloaded_pipeline_stage_amd import binding
+    binding.lib()  # fails loudly when librp.so is missing
+
+    cfg = synth.config(a.workload)
+    step = Step(cfg, streamed=False)
+    for _ in range(a.warmup):
+        step.run()
+    step.sync()
+    ctx = step.wk.ctx
+    ctx.trace_begin(100000)
+    step.sync()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step.run()
+    step.sync()
+    t1 = time.perf_counter()
+    recs = ctx.trace_end()
+    ms_step = (t1 - t0) * 1e3 / a.steps
+    tok_s = cfg.tokens / (ms_step / 1e3)
+    agg = summarize_trace(recs, a.steps)
+    lf = layer_flops(cfg, recompute=True)
+    step_flops = lf["fwd"] + lf["recompute"] + lf["bwd"] + lmhead_flops(cfg)
+    traced_flops = sum(v[1] for v in agg.values()) / a.steps
+    kernels = sorted(((k, v[3] / a.steps) for k, v in agg.items()), key=lambda kv: -kv[1])
+    out = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, uniform labels)",
+        "config": {"workload": "Llama-3.1-8B-shaped stage: 1 layer fwd + recompute+bwd, 4-shard LM head + CE",
+                   "batch": cfg.batch, "seq": cfg.seq, "hidden": cfg.hidden, "n_q": cfg.n_q, "n_kv": cfg.n_kv,
+                   "head_dim": cfg.head_dim, "ffn": cfg.ffn, "vocab": cfg.vocab, "n_shards": cfg.n_shards,
+                   "weights": "resident in HBM"},
+        "step_tflop": round(step_flops / 1e12, 3),
+        "tflops": round(step_flops / (ms_step / 1e3) / 1e12, 1),
+        "mfma_util": round(step_flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "traced_tflop_per_step": round(traced_flops / 1e12, 3),
+        "roofline": roofline(agg, cfg.dtype),
+        "kernels_ms_per_step": {k: round(v, 3) for k, v in kernels[:12]},
+    }
+    if a.trace_json:
+        with open(a.trace_json, "w") as f:
+            json.dump({k: {"launches": v[0], "flops": v[1], "bytes": v[2], "ms": v[3]} for k, v in agg.items()},
+                      f, indent=1)
+    del step
+    torch.cuda.empty_cache()
+
+    if a.streamed:
+        st = Step(cfg, streamed=True)
+        for _ in range(a.warmup):
+            st.run()
+        st.sync()
+        t0 = time.perf_counter()
+        for _ in range(a.steps):
+            st.run()
+        st.sync()
+        ms_s = (time.perf_counter() - t0) * 1e3 / a.steps
+        h2d = st.wk.w_bytes + sum(h.numel() * h.element_size() for h in st.host_shards)
+        d2h = st.wk.g_bytes + sum(h.numel() * 4 for h in st.host_dshards)
+        out["streamed"] = {"tokens_per_s": round(cfg.tokens / (ms_s / 1e3), 1), "ms_per_step": round(ms_s, 3),
+                           "h2d_GB_per_step": round(h2d / 1e9, 3), "d2h_GB_per_step": round(d2h / 1e9, 3),
+                           "h2d_GBps_if_link_bound": round(h2d / 1e9 / (ms_s / 1e3), 1),
+                           "d2h_GBps_if_link_bound": round(d2h / 1e9 / (ms_s / 1e3), 1)}
+        del st
+        torch.cuda.empty_cache()
+
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, a.cpu_seq)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

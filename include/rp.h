@@ -375,6 +375,34 @@ rp_status rp_op_attn_bwd(rp_ctx* ctx, int batch, int seq, const void* qkv, const
                          const void* dout, const float* lse, void* dqkv, void* ws,
                          size_t ws_bytes);
 
+/* ------------------------------------------------------------------------ */
+/* kernel trace                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* The RoundPipe paper times every layer with device events in its profiling
+ * pass (section 4.4, "Profiling"). The same mechanism here times every kernel
+ * launch the library enqueues on the compute stream, so that each kernel can
+ * be priced against its roofline while the real stage runs.
+ *
+ * rp_trace_begin waits for the compute stream, then records a HIP event pair
+ * around each of the next max_launches launches made through this context
+ * (later launches go unrecorded). rp_trace_end stops recording;
+ * rp_trace_read then waits for the recorded events and writes one record per
+ * launch, in issue order, to out[0 .. *n). With cap == 0 it only reports the
+ * count in *n; cap < count is RP_ERR_INVALID. Event pairs add a few
+ * microseconds per launch. */
+typedef struct rp_trace_rec {
+  char name[96];  /* kernel (template instance) name                        */
+  double flops;   /* algorithmic FLOPs of the launch (matrix products)      */
+  double bytes;   /* algorithmic HBM bytes of the launch (row/elementwise)  */
+  float ms;       /* event-to-event duration on the compute stream          */
+  int32_t reserved;
+} rp_trace_rec;
+
+rp_status rp_trace_begin(rp_ctx* ctx, int max_launches);
+rp_status rp_trace_end(rp_ctx* ctx);
+rp_status rp_trace_read(rp_ctx* ctx, rp_trace_rec* out, int cap, int* n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,6 +46,11 @@ class rp_xfer(C.Structure):
                 ("offset", C.c_uint64), ("bytes", C.c_uint64), ("host", C.c_void_p)]
 
 
+class rp_trace_rec(C.Structure):
+    _fields_ = [("name", C.c_char * 96), ("flops", C.c_double), ("bytes", C.c_double), ("ms", C.c_float),
+                ("reserved", C.c_int32)]
+
+
 _P = C.c_void_p
 _SIGS = {
     "rp_status_string": (C.c_char_p, [C.c_int]),
@@ -75,6 +80,9 @@ _SIGS = {
                                   C.c_int, C.c_int, C.c_int]),
     "rp_op_attn_fwd": (C.c_int, [_P, C.c_int, C.c_int, _P, _P, _P]),
     "rp_op_attn_bwd": (C.c_int, [_P, C.c_int, C.c_int, _P, _P, _P, _P, _P, _P, C.c_size_t]),
+    "rp_trace_begin": (C.c_int, [_P, C.c_int]),
+    "rp_trace_end": (C.c_int, [_P]),
+    "rp_trace_read": (C.c_int, [_P, C.POINTER(rp_trace_rec), C.c_int, C.POINTER(C.c_int)]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -260,6 +268,19 @@ class Context:
             addr = host if isinstance(host, int) else host.data_ptr()
             arr[i] = rp_xfer(kind, tgt, ident, 0, off, nb, addr)
         check(lib().rp_weight_stream_submit(self.h, arr, len(items), n_windows, max_chunk, gate_ticket))
+
+    # -- kernel trace
+    def trace_begin(self, max_launches: int = 100000):
+        check(lib().rp_trace_begin(self.h, max_launches))
+
+    def trace_end(self):
+        """Stop recording and return [(kernel name, flops, bytes, ms)] in issue order."""
+        check(lib().rp_trace_end(self.h))
+        n = C.c_int()
+        check(lib().rp_trace_read(self.h, None, 0, C.byref(n)))
+        arr = (rp_trace_rec * max(n.value, 1))()
+        check(lib().rp_trace_read(self.h, arr, n.value, C.byref(n)))
+        return [(arr[i].name.decode(), arr[i].flops, arr[i].bytes, arr[i].ms) for i in range(n.value)]
 
     # -- single kernels
     def op_gemm_bf16(self, M, N, K, A, lda, a_kmajor, B, ldb, b_kmajor, Cm, ldc, out_f32, accumulate=False):

@@ -12,9 +12,13 @@
 // MFMA flash kernels for bf16 with head_dim 128 (attn_flash.hip).
 #include "ops.h"
 #include "attn_flash.h"
+#include "trace.h"
 
 namespace rp {
 namespace {
+
+// causal (query, key) pairs of all batch rows
+double causal_pairs(const AttnDesc& a) { return (double)a.batch * a.seq * (a.seq + 1.0) / 2.0; }
 
 template <class T, int DPL>  // DPL = head_dim / 64 elements per lane
 __global__ __launch_bounds__(256) void attn_fwd_simple(const T* __restrict__ qkv, T* __restrict__ o,
@@ -160,6 +164,7 @@ rp_status fwd_simple(const AttnDesc& a, const void* qkv, void* o, float* lse, hi
   const int T_ = a.batch * a.seq;
   const int64_t waves = (int64_t)T_ * a.n_q;
   const float scale = 1.0f / sqrtf((float)a.d);
+  TraceScope ts(s, "attn_fwd_simple", 4.0 * a.d * a.n_q * causal_pairs(a), 0.0);
   RP_LAUNCH((attn_fwd_simple<T, DPL>), dim3((unsigned)cdiv(waves, 4)), dim3(256), 0, s, (const T*)qkv, (T*)o,
             lse, T_, a.seq, a.n_q, a.n_kv, scale);
   return RP_OK;
@@ -170,6 +175,7 @@ rp_status bwd_simple(const AttnDesc& a, const void* qkv, const void* o, const vo
                      float* Dbuf, void* dqkv, hipStream_t s) {
   const int T_ = a.batch * a.seq;
   const float scale = 1.0f / sqrtf((float)a.d);
+  TraceScope ts(s, "attn_bwd_simple", 8.0 * a.d * a.n_q * causal_pairs(a), 0.0);
   RP_LAUNCH((attn_dq_simple<T, DPL>), dim3((unsigned)cdiv((int64_t)T_ * a.n_q, 4)), dim3(256), 0, s,
             (const T*)qkv, (const T*)o, (const T*)dout, lse, Dbuf, (T*)dqkv, T_, a.seq, a.n_q, a.n_kv, scale);
   RP_LAUNCH((attn_dkdv_simple<T, DPL>), dim3((unsigned)cdiv((int64_t)T_ * a.n_kv, 4)), dim3(256), 0, s,

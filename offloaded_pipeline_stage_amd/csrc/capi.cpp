@@ -90,9 +90,10 @@ using namespace rp;
 #define CTX_CHECK(c) RP_CHECK((c) != nullptr, RP_ERR_INVALID, "null context")
 
 // Entering a context makes its device current (one thread may drive several).
-#define CTX_ENTER(c)      \
-  CTX_CHECK(c);           \
-  RP_HIP(hipSetDevice((c)->device))
+#define CTX_ENTER(c)           \
+  CTX_CHECK(c);                \
+  RP_HIP(hipSetDevice((c)->device)); \
+  ::rp::trace_bind(&(c)->trace)
 
 extern "C" {
 
@@ -166,6 +167,7 @@ rp_status rp_ctx_sync(rp_ctx* c) {
 
 rp_status rp_ctx_destroy(rp_ctx* c) {
   if (!c) return RP_OK;
+  if (trace_current() == &c->trace) trace_bind(nullptr);
   rp_status st = RP_OK;
   if (hipSetDevice(c->device) == hipSuccess) {
     hipStream_t ss[5] = {c->compute, c->act_h2d, c->act_d2h, c->w_h2d, c->g_d2h};
@@ -338,6 +340,49 @@ rp_status rp_op_attn_bwd(rp_ctx* c, int batch, int seq, const void* qkv, const v
   a.dt = c->sh.dt; a.batch = batch; a.seq = seq; a.n_q = c->sh.nq; a.n_kv = c->sh.nkv; a.d = c->sh.d;
   RP_CHECK(ws_bytes >= attn_bwd_ws_bytes(a), RP_ERR_WORKSPACE, "op_attn_bwd: workspace too small");
   return attn_bwd(a, qkv, o, dout, lse, (float*)ws, dqkv, c->compute);
+}
+
+rp_status rp_trace_begin(rp_ctx* c, int max_launches) {
+  CTX_ENTER(c);
+  RP_CHECK(max_launches >= 1, RP_ERR_INVALID, "trace_begin: max_launches must be >= 1");
+  RP_CHECK(!c->trace.on, RP_ERR_STATE, "trace_begin: a trace is already running");
+  // events of the previous session are reused once the stream has passed them
+  RP_HIP(hipStreamSynchronize(c->compute));
+  c->trace.recs.clear();
+  c->trace.pool_used = 0;
+  c->trace.cap = (size_t)max_launches;
+  c->trace.on = true;
+  return RP_OK;
+}
+
+rp_status rp_trace_end(rp_ctx* c) {
+  CTX_ENTER(c);
+  c->trace.on = false;
+  return RP_OK;
+}
+
+rp_status rp_trace_read(rp_ctx* c, rp_trace_rec* out, int cap, int* n) {
+  CTX_ENTER(c);
+  RP_CHECK(n, RP_ERR_INVALID, "trace_read: null count");
+  RP_CHECK(!c->trace.on, RP_ERR_STATE, "trace_read: call rp_trace_end first");
+  const size_t nr = c->trace.recs.size();
+  *n = (int)nr;
+  RP_CHECK(out || nr == 0 || cap == 0, RP_ERR_INVALID, "trace_read: null output");
+  if (cap <= 0) return RP_OK;
+  RP_CHECK((size_t)cap >= nr, RP_ERR_INVALID, "trace_read: %zu records exceed cap %d", nr, cap);
+  for (size_t i = 0; i < nr; ++i) {
+    const TraceRec& r = c->trace.recs[i];
+    RP_HIP(hipEventSynchronize(r.b));
+    float ms = 0.f;
+    RP_HIP(hipEventElapsedTime(&ms, r.a, r.b));
+    rp_trace_rec& o = out[i];
+    memset(&o, 0, sizeof(o));
+    snprintf(o.name, sizeof(o.name), "%s", r.name.c_str());
+    o.flops = r.flops;
+    o.bytes = r.bytes;
+    o.ms = ms;
+  }
+  return RP_OK;
 }
 
 }  // extern "C"

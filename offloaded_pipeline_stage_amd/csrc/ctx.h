@@ -6,6 +6,7 @@
 #include <vector>
 
 #include "ops.h"
+#include "trace.h"
 
 struct rp_ctx;
 
@@ -96,6 +97,8 @@ struct rp_ctx {
   // kept-activation bookkeeping for RP_USE_KEPT_ACTS
   const void* kept_ws = nullptr;
   int kept_l0 = -1, kept_l1 = -1, kept_batch = 0, kept_seq = 0;
+  // per-launch kernel timing (rp_trace_begin / rp_trace_read)
+  rp::Trace trace;
 
   hipEvent_t new_event();
 };

@@ -4,6 +4,7 @@
 // 16-byte vector accesses, reductions by fixed-order butterflies so every
 // result is deterministic (recomputation must reproduce the forward exactly).
 #include "ops.h"
+#include "trace.h"
 
 namespace rp {
 namespace {
@@ -345,6 +346,7 @@ rp_status fill_zero(void* p, size_t bytes, hipStream_t s) {
   RP_CHECK(((uintptr_t)p & 15) == 0, RP_ERR_INVALID, "fill_zero: pointer not 16-byte aligned");
   const size_t n16 = bytes / 16, ntail = bytes % 16;
   unsigned g = (unsigned)std::min<size_t>(std::max<size_t>(cdiv(n16, 256), 1), 8192);
+  TraceScope ts(s, "fill_zero_kernel", 0.0, (double)bytes);
   RP_LAUNCH(fill_zero_kernel, dim3(g), dim3(256), 0, s, (uint4*)p, n16, (uint8_t*)p + n16 * 16, ntail);
   return RP_OK;
 }
@@ -354,6 +356,7 @@ rp_status rmsnorm_fwd(int dt, const void* x, const void* gamma, void* y, float* 
   if (T == 0) return RP_OK;
   RP_CHECK(H % 8 == 0, RP_ERR_UNSUPPORTED, "rmsnorm: H %% 8 != 0");
   dim3 g(blocks_for(T, 4));
+  TraceScope ts(s, "rmsnorm_fwd_kernel", 0.0, (double)T * H * 2 * dtype_size(dt) + H * dtype_size(dt) + 4.0 * T);
   if (dt == RP_DTYPE_BF16)
     RP_LAUNCH(rmsnorm_fwd_kernel<bf16>, g, dim3(256), 0, s, (const bf16*)x, (const bf16*)gamma,
               (bf16*)y, rstd, T, H, eps);
@@ -373,6 +376,11 @@ static rp_status rmsnorm_bwd_t(const float* g, const void* x, const void* gamma,
                                float* dgamma, float* part, int rows, int H, hipStream_t s) {
   const unsigned nb = blocks_for(rows, RMS_BWD_ROWS);
   const size_t lds = 4 * (size_t)H * sizeof(float);
+  // g (fp32), x, out, resid read/written once; dgamma partials
+  const double es = sizeof(T);
+  TraceScope ts(s, "rmsnorm_bwd_kernel", 0.0,
+                (double)rows * H * (4.0 + 2 * es + (resid ? (resid_dt == RP_DTYPE_F32 ? 4.0 : 2.0) : 0.0) +
+                                    (out_f32 ? 4.0 : 0.0) - (out_dt ? 0.0 : es)) + 4.0 * rows);
   RP_CHECK(lds <= 160 * 1024, RP_ERR_UNSUPPORTED, "rmsnorm bwd: H too large");
   if (lds > 32 * 1024) {
     if (resid_dt == RP_DTYPE_F32)
@@ -416,6 +424,7 @@ rp_status rope_apply(int dt, void* buf, int64_t ld, int T, int seq, int n_heads,
                      const float2* tab, bool inverse, hipStream_t s) {
   const int64_t n = (int64_t)T * n_heads * (d / 2);
   if (n == 0) return RP_OK;
+  TraceScope ts(s, "rope_apply_kernel", 0.0, (double)n * 4 * dtype_size(dt));
   if (dt == RP_DTYPE_BF16)
     RP_LAUNCH(rope_apply_kernel<bf16>, dim3(blocks_for(n)), dim3(256), 0, s, (bf16*)buf, ld, T, seq,
               n_heads, d, tab, inverse ? 1 : 0);
@@ -428,6 +437,7 @@ rp_status rope_apply(int dt, void* buf, int64_t ld, int T, int seq, int n_heads,
 rp_status swiglu_fwd(int dt, const void* gu, void* m, int T, int F, hipStream_t s) {
   const int64_t n = (int64_t)T * F;
   if (n == 0) return RP_OK;
+  TraceScope ts(s, "swiglu_fwd_kernel", 0.0, (double)n * 3 * dtype_size(dt));
   if (dt == RP_DTYPE_BF16)
     RP_LAUNCH(swiglu_fwd_kernel<bf16>, dim3(blocks_for(n)), dim3(256), 0, s, (const bf16*)gu, (bf16*)m, T, F);
   else
@@ -438,6 +448,7 @@ rp_status swiglu_fwd(int dt, const void* gu, void* m, int T, int F, hipStream_t 
 rp_status swiglu_bwd(int dt, const float* dm, const void* gu, void* dgu, int T, int F, hipStream_t s) {
   const int64_t n = (int64_t)T * F;
   if (n == 0) return RP_OK;
+  TraceScope ts(s, "swiglu_bwd_kernel", 0.0, (double)n * (4 + 4 * dtype_size(dt)));
   if (dt == RP_DTYPE_BF16)
     RP_LAUNCH(swiglu_bwd_kernel<bf16>, dim3(blocks_for(n)), dim3(256), 0, s, dm, (const bf16*)gu, (bf16*)dgu, T, F);
   else
@@ -448,6 +459,7 @@ rp_status swiglu_bwd(int dt, const float* dm, const void* gu, void* dgu, int T, 
 rp_status ce_shard_stats(const float* logits, int64_t ld, int T, int Vs, int vlo, const int32_t* labels,
                          int vocab, float2* part, float* zlab, hipStream_t s) {
   if (T == 0) return RP_OK;
+  TraceScope ts(s, "ce_stats_kernel", 0.0, (double)T * Vs * 4 + 16.0 * T);
   RP_LAUNCH(ce_stats_kernel, dim3(blocks_for(T, 4)), dim3(256), 0, s, logits, ld, T, Vs, vlo, labels,
             vocab, part, zlab);
   return RP_OK;
@@ -455,6 +467,7 @@ rp_status ce_shard_stats(const float* logits, int64_t ld, int T, int Vs, int vlo
 
 rp_status ce_combine(int T, int n_shards, const float2* parts, const float* zlab, const int32_t* labels,
                      int vocab, float* lse, float* loss, float* inv_n, hipStream_t s) {
+  TraceScope ts(s, "ce_combine_kernel", 0.0, (double)T * (8.0 * n_shards + 12.0));
   RP_LAUNCH(ce_combine_kernel, dim3(1), dim3(1024), 0, s, T, n_shards, parts, zlab, labels, vocab, lse,
             loss, inv_n);
   return RP_OK;
@@ -464,6 +477,7 @@ rp_status ce_grad(int dt, const float* logits, int64_t ld, int T, int Vs, int vl
                   int vocab, const float* lse, const float* inv_n, void* dz, int64_t ldz, hipStream_t s) {
   const int64_t n = (int64_t)T * Vs;
   if (n == 0) return RP_OK;
+  TraceScope ts(s, "ce_grad_kernel", 0.0, (double)n * (4 + dtype_size(dt)) + 8.0 * T);
   if (dt == RP_DTYPE_BF16)
     RP_LAUNCH(ce_grad_kernel<bf16>, dim3(blocks_for(n)), dim3(256), 0, s, logits, ld, T, Vs, vlo, labels,
               vocab, lse, inv_n, (bf16*)dz, ldz);
@@ -495,6 +509,7 @@ rp_status embed_bwd(int dt, const int32_t* ids, const void* dx0, float* dtable, 
 
 rp_status cast_from_f32(int dt, const float* a, void* out, size_t n, hipStream_t s) {
   if (n == 0) return RP_OK;
+  TraceScope ts(s, "cast_kernel", 0.0, (double)n * (4 + dtype_size(dt)));
   if (dt == RP_DTYPE_BF16)
     RP_LAUNCH(cast_kernel<bf16>, dim3(blocks_for(n)), dim3(256), 0, s, a, (bf16*)out, n);
   else

@@ -22,6 +22,7 @@
 // fp32 path (and a bf16 cross-check): a plain LDS-tiled FMA kernel with the
 // same epilogue semantics.
 #include "ops.h"
+#include "trace.h"
 
 namespace rp {
 namespace {
@@ -360,6 +361,7 @@ rp_status launch_simple(const GemmDesc& d, void* C, int64_t ldc, hipStream_t s) 
   p.B = reinterpret_cast<const TI*>(d.B);
   p.sbn = d.b_kmajor ? d.ldb : 1; p.sbk = d.b_kmajor ? 1 : d.ldb;
   dim3 grid(cdiv(d.N, 64), cdiv(d.M, 64));
+  TraceScope ts(s, "gemm_simple_kernel", 2.0 * d.M * d.N * d.K, 0.0);
   RP_LAUNCH((gemm_simple_kernel<TI, TO, EPI>), grid, dim3(256), 0, s, p,
             reinterpret_cast<TO*>(C), ldc, reinterpret_cast<const TO*>(d.R), d.ldr,
             (int)d.accumulate);
@@ -419,6 +421,9 @@ rp_status launch_mfma(const GemmDesc& d, hipStream_t s) {
     attr_set = true;
   }
   const int64_t nt = (int64_t)p.tiles_m * p.tiles_n;
+  char name[96];
+  snprintf(name, sizeof(name), "gemm_mfma_kernel<%d, %d, %d, %d, %d, %d>", BM, BN, (int)AK, (int)BKM, EPI, (int)OF32);
+  TraceScope ts(s, name, 2.0 * d.M * d.N * d.K, 0.0);
   RP_LAUNCH((gemm_mfma_kernel<BM, BN, AK, BKM, EPI, OF32>), dim3((unsigned)nt), dim3(NT), lds, s, p);
   return RP_OK;
 }
