@@ -210,7 +210,7 @@ def main():
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--streamed", action="store_true", help="also time the weight-streaming variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seq", type=int, default=128)
+    ap.add_argument("--cpu-seq", type=int, default=1024)
     ap.add_argument("--trace-json", default=None, help="write the per-kernel table here")
     a = ap.parse_args()
     if a.gpus != 1:

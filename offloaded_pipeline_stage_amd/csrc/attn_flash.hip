@@ -1,28 +1,502 @@
-// MFMA flash attention for bf16, head_dim 128 (forward and backward).
+// MFMA flash attention for bf16, head_dim 128 (forward and backward) on gfx950.
+//
+// Causal GQA attention of the decoder layer (query head h reads kv head
+// floor(h * n_kv / n_q), scale 1/sqrt(d), keys at positions <= the query's
+// within its own batch row), on the packed qkv buffer [T, (n_q + 2 n_kv) 128].
+// The forward never materialises the scores: it streams 64-key tiles and keeps
+// a running (max, sum) per query, and stores lse = log-sum-exp of the scaled
+// scores so the backward can rebuild the probabilities (FlashAttention, which
+// the paper's appendix B.1 assumes for the attention activations).
+//
+// Building block: v_mfma_f32_32x32x16_bf16. Operand A lane l holds row l%32,
+// k = 8*(l/32)..+7; operand B lane l holds column l%32, the same k; the 32x32
+// fp32 result lane l holds column l%32, rows 8*(r/4) + 4*(l/32) + r%4.
+//
+// Orientation: every product is arranged so that the 32 rows the wave owns
+// (queries in the forward and dQ kernels, keys in the dK/dV kernel) are the
+// MFMA *column* index, i.e. one row per lane. Then
+//   - the softmax statistics of a query need only an in-lane reduction over
+//     its 16 scores of a tile plus one exchange with lane l^32;
+//   - a score tile (rows = streamed keys/queries held in registers) is the B
+//     operand of the next product directly: the 16-element k-step j of a
+//     32-row tile is registers 8j..8j+7, which hold rows 16j + {4h..4h+3,
+//     8+4h..8+4h+3} for lane half h. The A operand read from LDS uses the same
+//     row permutation, so the sum over k is unchanged.
+// Streamed tiles live in LDS in two layouts: row-major [rows][128] with the
+// 16-byte chunk index XOR-swizzled by row%16 (A operand of QK^T-type products,
+// 16-byte reads), and transposed [128][64 rows] with the 8-byte chunk index
+// XOR-swizzled by d%16 (A operand of PV-type products, 8-byte reads). Both
+// read patterns and the store patterns are free of bank conflicts.
+//
+// The backward is two deterministic kernels (no atomics): dK/dV per key block
+// (summing over the query heads of its kv group and all later queries), and
+// dQ per query block; both recompute the probabilities from lse.
 #include "attn_flash.h"
+#include "trace.h"
 
 namespace rp {
 
 namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int D = 128;        // head dim
+constexpr int NT = 256;       // threads per workgroup (4 waves)
+constexpr int WROWS = 32;     // rows owned by one wave
+constexpr int BROWS = 128;    // rows owned by one workgroup
+constexpr int TILE = 64;      // streamed rows per LDS tile
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
 bool g_flash_on = true;
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+
+__device__ __forceinline__ f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return uint32_t(to_bf16(a).u) | (uint32_t(to_bf16(b).u) << 16);
+}
+
+// registers 8j..8j+7 of a score tile as a bf16x8 B operand
+__device__ __forceinline__ bf16x8_t to_operand(const f32x16_t& c, int j) {
+  u32x4_t u;
+  u[0] = pack_bf16x2(c[8 * j + 0], c[8 * j + 1]);
+  u[1] = pack_bf16x2(c[8 * j + 2], c[8 * j + 3]);
+  u[2] = pack_bf16x2(c[8 * j + 4], c[8 * j + 5]);
+  u[3] = pack_bf16x2(c[8 * j + 6], c[8 * j + 7]);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// --- LDS layouts -------------------------------------------------------------
+
+// row-major tile [rows][128] bf16: 256-byte rows of 16 chunks of 16 bytes
+__device__ __forceinline__ int rm_off(int row, int c16) { return row * 256 + ((c16 ^ (row & 15)) << 4); }
+// transposed tile [128][64] bf16: 128-byte rows (one per d) of 16 chunks of 8 bytes
+__device__ __forceinline__ int tr_off(int d, int c8) { return d * 128 + ((c8 ^ (d & 15)) << 3); }
+
+// Copy rows [r0, r0 + 64) of a strided bf16 matrix (row stride ld elements,
+// columns [col, col + 128)) into a row-major LDS tile; rows >= rmax are zero.
+__device__ __forceinline__ void load_rm(char* lds, const bf16* g, int64_t ld, int r0, int rmax, int col, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = tid + i * NT;
+    const int row = id >> 4, c = id & 15;
+    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+    if (r0 + row < rmax) v = *reinterpret_cast<const u32x4_t*>(g + (int64_t)(r0 + row) * ld + col + 8 * c);
+    *reinterpret_cast<u32x4_t*>(lds + rm_off(row, c)) = v;
+  }
+}
+
+// Same rows into a transposed LDS tile [128][64]: each thread loads 4 rows x 8
+// columns and transposes them in registers into 8 columns x 4 rows.
+__device__ __forceinline__ void load_tr(char* lds, const bf16* g, int64_t ld, int r0, int rmax, int col, int tid) {
+  const int kg = tid & 15, db = tid >> 4;
+  u32x4_t v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = r0 + 4 * kg + j;
+    v[j] = u32x4_t{0u, 0u, 0u, 0u};
+    if (row < rmax) v[j] = *reinterpret_cast<const u32x4_t*>(g + (int64_t)row * ld + col + 8 * db);
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t a0 = v[0][p], a1 = v[1][p], a2 = v[2][p], a3 = v[3][p];
+    const u32x2_t lo = u32x2_t{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
+    const u32x2_t hi = u32x2_t{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
+    const int d0 = 8 * db + 2 * p;
+    *reinterpret_cast<u32x2_t*>(lds + tr_off(d0, kg)) = lo;
+    *reinterpret_cast<u32x2_t*>(lds + tr_off(d0 + 1, kg)) = hi;
+  }
+}
+
+// A operand of a QK^T-type product: rows 32t + (lane%32) of a row-major tile,
+// d-step s
+__device__ __forceinline__ bf16x8_t rd_rm(const char* lds, int t, int s, int lane) {
+  const int row = 32 * t + (lane & 31);
+  return *reinterpret_cast<const bf16x8_t*>(lds + rm_off(row, 2 * s + (lane >> 5)));
+}
+
+// A operand of a PV-type product: d-row 32dt + (lane%32) of a transposed tile,
+// k-step j of 32-row subtile t (rows 32t + 16j + {4h..4h+3, 8+4h..8+4h+3})
+__device__ __forceinline__ bf16x8_t rd_tr(const char* lds, int dt, int t, int j, int lane) {
+  const int d = 32 * dt + (lane & 31), h = lane >> 5;
+  const int c = 8 * t + 4 * j + h;
+  u32x4_t u;
+  const u32x2_t a = *reinterpret_cast<const u32x2_t*>(lds + tr_off(d, c));
+  const u32x2_t b = *reinterpret_cast<const u32x2_t*>(lds + tr_off(d, c + 2));
+  u[0] = a[0]; u[1] = a[1]; u[2] = b[0]; u[3] = b[1];
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// B operand held in registers: row `row` (< rmax, else zero) of a strided
+// matrix, columns [col, col + 128), d-step s for lane half h
+__device__ __forceinline__ void load_rows_b(bf16x8_t (&f)[8], const bf16* g, int64_t ld, int row, int rmax, int col,
+                                            int h) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+    if (row < rmax) v = *reinterpret_cast<const u32x4_t*>(g + (int64_t)row * ld + col + 16 * s + 8 * h);
+    f[s] = __builtin_bit_cast(bf16x8_t, v);
+  }
+}
+
+// store a [128 d x 32 rows] accumulator (rows on lanes) scaled by `mul` into
+// row `row` of a strided bf16 matrix at column col
+__device__ __forceinline__ void store_acc_rows(const f32x16_t (&acc)[4], float mul, bf16* g, int64_t ld, int row,
+                                               int rmax, int col, int h) {
+  if (row >= rmax) return;
+  bf16* out = g + (int64_t)row * ld + col;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d = 32 * dt + 8 * q + 4 * h;
+      u32x2_t u;
+      u[0] = pack_bf16x2(acc[dt][4 * q + 0] * mul, acc[dt][4 * q + 1] * mul);
+      u[1] = pack_bf16x2(acc[dt][4 * q + 2] * mul, acc[dt][4 * q + 3] * mul);
+      *reinterpret_cast<u32x2_t*>(out + d) = u;
+    }
+}
+
+struct FlashParams {
+  const bf16* qkv;   // [T, ld]
+  int64_t ld;        // (n_q + 2 n_kv) * 128
+  int seq, nq, nkv;
+  float c2;          // scale * log2(e)
+  float scale;
+  int n_blocks;      // row blocks of 128 per sequence
+};
+
+// ---------------------------------------------------------------------------
+// forward: one workgroup = 128 queries of one head; wave w owns 32 of them
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT) void flash_fwd_kernel(FlashParams p, bf16* __restrict__ o, float* __restrict__ lse) {
+  __shared__ __align__(16) char smem[2 * TILE * 256];
+  char* sK = smem;
+  char* sV = smem + TILE * 256;  // transposed [128][64]
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
+  const int head = blockIdx.x, b = blockIdx.z;
+  const int qb = p.n_blocks - 1 - blockIdx.y;  // longest rows first
+  const int hk = head / (p.nq / p.nkv);
+  const bf16* base = p.qkv + (int64_t)b * p.seq * p.ld;
+  const int q0 = qb * BROWS, qw = q0 + w * WROWS, qpos = qw + n;
+  const int kcol = (p.nq + hk) * D, vcol = (p.nq + p.nkv + hk) * D;
+
+  bf16x8_t qf[8];
+  load_rows_b(qf, base, p.ld, qpos, p.seq, head * D, h);
+  f32x16_t acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = zero16();
+  float m = -INFINITY, l = 0.f;
+
+  const int klast = min(q0 + BROWS, p.seq) - 1;
+  for (int k0 = 0; k0 <= klast; k0 += TILE) {
+    __syncthreads();
+    load_rm(sK, base, p.ld, k0, p.seq, kcol, tid);
+    load_tr(sV, base, p.ld, k0, p.seq, vcol, tid);
+    __syncthreads();
+    if (k0 > qw + WROWS - 1) continue;  // every key of the tile is after every query of the wave
+    f32x16_t st[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      st[t] = zero16();
+#pragma unroll
+      for (int s = 0; s < 8; ++s) st[t] = mfma(rd_rm(sK, t, s, lane), qf[s], st[t]);
+    }
+    const bool diag = k0 + TILE - 1 > qw;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = st[t][r] * p.c2;
+        if (diag) {
+          const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (key > qpos) v = -INFINITY;
+        }
+        st[t][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m, mx);
+    const float alpha = fexp2(m - mn);
+    float sum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fexp2(st[t][r] - mn);
+        st[t][r] = e;
+        sum += e;
+      }
+    sum += __shfl_xor(sum, 32, 64);
+    l = l * alpha + sum;
+    m = mn;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8_t pb = to_operand(st[t], j);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(rd_tr(sV, dt, t, j, lane), pb, acc[dt]);
+      }
+  }
+  const float inv = 1.f / l;
+  store_acc_rows(acc, inv, o + (int64_t)b * p.seq * p.nq * D, (int64_t)p.nq * D, qpos, p.seq, head * D, h);
+  if (h == 0 && qpos < p.seq) lse[(int64_t)head * gridDim.z * p.seq + (int64_t)b * p.seq + qpos] = (m + __log2f(l)) * LN2;
+}
+
+// ---------------------------------------------------------------------------
+// backward preprocessing: Dr[h][t] = sum_d dO[t, h, d] * O[t, h, d]
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT) void flash_bwd_dot_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout,
+                                                           float* __restrict__ Dr, int T, int nq) {
+  // 16 threads per (token, head) row of 128 elements
+  const int64_t row = (int64_t)blockIdx.x * (NT / 16) + (threadIdx.x >> 4);
+  const int c = threadIdx.x & 15;
+  float s = 0.f;
+  if (row < (int64_t)T * nq) {
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(o + row * D + 8 * c);
+    const u32x4_t g = *reinterpret_cast<const u32x4_t*>(dout + row * D + 8 * c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s = fmaf(__uint_as_float(a[i] << 16), __uint_as_float(g[i] << 16), s);
+      s = fmaf(__uint_as_float(a[i] & 0xffff0000u), __uint_as_float(g[i] & 0xffff0000u), s);
+    }
+  }
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) s += __shfl_xor(s, off, 16);
+  if (c == 0 && row < (int64_t)T * nq) {
+    const int64_t t = row / nq, hh = row % nq;
+    Dr[hh * T + t] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup = 128 queries of one head, streaming 64-key tiles
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT) void flash_dq_kernel(FlashParams p, const bf16* __restrict__ dout,
+                                                      const float* __restrict__ lse, const float* __restrict__ Dr,
+                                                      bf16* __restrict__ dqkv) {
+  __shared__ __align__(16) char smem[3 * TILE * 256];
+  char* sK = smem;
+  char* sV = smem + TILE * 256;
+  char* sKt = smem + 2 * TILE * 256;  // transposed K
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
+  const int head = blockIdx.x, b = blockIdx.z;
+  const int qb = p.n_blocks - 1 - blockIdx.y;
+  const int hk = head / (p.nq / p.nkv);
+  const int T = gridDim.z * p.seq;
+  const bf16* base = p.qkv + (int64_t)b * p.seq * p.ld;
+  const int q0 = qb * BROWS, qw = q0 + w * WROWS, qpos = qw + n;
+  const int kcol = (p.nq + hk) * D, vcol = (p.nq + p.nkv + hk) * D;
+  const int64_t ldo = (int64_t)p.nq * D;
+
+  bf16x8_t qf[8], dof[8];
+  load_rows_b(qf, base, p.ld, qpos, p.seq, head * D, h);
+  load_rows_b(dof, dout + (int64_t)b * p.seq * ldo, ldo, qpos, p.seq, head * D, h);
+  const int64_t si = (int64_t)head * T + (int64_t)b * p.seq + min(qpos, p.seq - 1);
+  const float l2 = lse[si] * LOG2E, dd = Dr[si];
+  f32x16_t acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = zero16();
+
+  const int klast = min(q0 + BROWS, p.seq) - 1;
+  for (int k0 = 0; k0 <= klast; k0 += TILE) {
+    __syncthreads();
+    load_rm(sK, base, p.ld, k0, p.seq, kcol, tid);
+    load_rm(sV, base, p.ld, k0, p.seq, vcol, tid);
+    load_tr(sKt, base, p.ld, k0, p.seq, kcol, tid);
+    __syncthreads();
+    if (k0 > qw + WROWS - 1) continue;
+    const bool diag = k0 + TILE - 1 > qw;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x16_t st = zero16(), dp = zero16();
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        st = mfma(rd_rm(sK, t, s, lane), qf[s], st);
+        dp = mfma(rd_rm(sV, t, s, lane), dof[s], dp);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = fexp2(st[r] * p.c2 - l2);
+        if (diag) {
+          const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (key > qpos) pr = 0.f;
+        }
+        st[r] = pr * (dp[r] - dd);  // dS
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8_t sb = to_operand(st, j);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(rd_tr(sKt, dt, t, j, lane), sb, acc[dt]);
+      }
+    }
+  }
+  store_acc_rows(acc, p.scale, dqkv + (int64_t)b * p.seq * p.ld, p.ld, qpos, p.seq, head * D, h);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup = 128 keys of one kv head, streaming 64-query tiles of
+// every query head of the group; wave w owns 32 keys
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf16* __restrict__ dout,
+                                                        const float* __restrict__ lse, const float* __restrict__ Dr,
+                                                        bf16* __restrict__ dqkv) {
+  __shared__ __align__(16) char smem[4 * TILE * 256 + 2 * TILE * 4];
+  char* sQ = smem;
+  char* sO = smem + TILE * 256;        // dO row-major
+  char* sQt = smem + 2 * TILE * 256;   // Q transposed
+  char* sOt = smem + 3 * TILE * 256;   // dO transposed
+  float* sL = reinterpret_cast<float*>(smem + 4 * TILE * 256);  // lse * log2(e)
+  float* sD = sL + TILE;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
+  const int hk = blockIdx.x, b = blockIdx.z;
+  const int kb = blockIdx.y;  // earliest keys (most queries) first
+  const int G = p.nq / p.nkv;
+  const int T = gridDim.z * p.seq;
+  const bf16* base = p.qkv + (int64_t)b * p.seq * p.ld;
+  const bf16* dob = dout + (int64_t)b * p.seq * p.nq * D;
+  const int64_t ldo = (int64_t)p.nq * D;
+  const int k0 = kb * BROWS, kw = k0 + w * WROWS, kpos = kw + n;
+  const int kcol = (p.nq + hk) * D, vcol = (p.nq + p.nkv + hk) * D;
+
+  bf16x8_t kf[8], vf[8];
+  load_rows_b(kf, base, p.ld, kpos, p.seq, kcol, h);
+  load_rows_b(vf, base, p.ld, kpos, p.seq, vcol, h);
+  f32x16_t dk[4], dv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dk[i] = dv[i] = zero16();
+
+  for (int g = 0; g < G; ++g) {
+    const int head = hk * G + g;
+    for (int q0 = k0; q0 < p.seq; q0 += TILE) {
+      __syncthreads();
+      load_rm(sQ, base, p.ld, q0, p.seq, head * D, tid);
+      load_rm(sO, dob, ldo, q0, p.seq, head * D, tid);
+      load_tr(sQt, base, p.ld, q0, p.seq, head * D, tid);
+      load_tr(sOt, dob, ldo, q0, p.seq, head * D, tid);
+      if (tid < TILE) {
+        const int q = min(q0 + tid, p.seq - 1);
+        const int64_t si = (int64_t)head * T + (int64_t)b * p.seq + q;
+        sL[tid] = lse[si] * LOG2E;
+        sD[tid] = Dr[si];
+      }
+      __syncthreads();
+      if (q0 + TILE - 1 < kw) continue;  // every query of the tile is before every key of the wave
+      const bool diag = q0 < kw + WROWS - 1;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        f32x16_t st = zero16(), dp = zero16();
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          st = mfma(rd_rm(sQ, u, s, lane), kf[s], st);
+          dp = mfma(rd_rm(sO, u, s, lane), vf[s], dp);
+        }
+        f32x16_t ds;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = 32 * u + 8 * (r >> 2) + 4 * h + (r & 3);
+          float pr = fexp2(st[r] * p.c2 - sL[qi]);
+          if (diag && kpos > q0 + qi) pr = 0.f;
+          if (q0 + qi >= p.seq) pr = 0.f;
+          st[r] = pr;
+          ds[r] = pr * (dp[r] - sD[qi]);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const bf16x8_t pb = to_operand(st, j), sb = to_operand(ds, j);
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            dv[dt] = mfma(rd_tr(sOt, dt, u, j, lane), pb, dv[dt]);
+            dk[dt] = mfma(rd_tr(sQt, dt, u, j, lane), sb, dk[dt]);
+          }
+        }
+      }
+    }
+  }
+  bf16* dst = dqkv + (int64_t)b * p.seq * p.ld;
+  store_acc_rows(dk, p.scale, dst, p.ld, kpos, p.seq, kcol, h);
+  store_acc_rows(dv, 1.f, dst, p.ld, kpos, p.seq, vcol, h);
+}
+
+FlashParams make_params(const AttnDesc& a, const void* qkv) {
+  FlashParams p;
+  p.qkv = reinterpret_cast<const bf16*>(qkv);
+  p.ld = (int64_t)(a.n_q + 2 * a.n_kv) * D;
+  p.seq = a.seq;
+  p.nq = a.n_q;
+  p.nkv = a.n_kv;
+  p.scale = 1.0f / sqrtf((float)D);
+  p.c2 = p.scale * LOG2E;
+  p.n_blocks = (int)cdiv(a.seq, BROWS);
+  return p;
+}
+
+double causal_pairs(const AttnDesc& a) { return (double)a.batch * a.seq * (a.seq + 1.0) / 2.0; }
+
+}  // namespace
 
 void flash_enable(bool on) { g_flash_on = on; }
 
 bool flash_supported(const AttnDesc& a) {
-  (void)a;
-  return false;  // the reference-grade kernels in attn.hip cover every shape until these land
+  return g_flash_on && a.dt == RP_DTYPE_BF16 && a.d == D && a.n_kv > 0 && a.n_q % a.n_kv == 0 && a.seq >= 1;
 }
 
-rp_status flash_fwd(const AttnDesc&, const void*, void*, float*, hipStream_t) {
-  set_error("flash attention forward not available");
-  return RP_ERR_UNSUPPORTED;
+rp_status flash_fwd(const AttnDesc& a, const void* qkv, void* o, float* lse, hipStream_t s) {
+  RP_CHECK(((uintptr_t)qkv & 15) == 0 && ((uintptr_t)o & 15) == 0, RP_ERR_INVALID,
+           "flash attention: qkv and o must be 16-byte aligned");
+  const FlashParams p = make_params(a, qkv);
+  TraceScope ts(s, "flash_fwd_kernel", 4.0 * D * a.n_q * causal_pairs(a), 0.0);
+  RP_LAUNCH(flash_fwd_kernel, dim3(a.n_q, p.n_blocks, a.batch), dim3(NT), 0, s, p, (bf16*)o, lse);
+  return RP_OK;
 }
 
-rp_status flash_bwd(const AttnDesc&, const void*, const void*, const void*, const float*, float*, void*,
-                    hipStream_t) {
-  set_error("flash attention backward not available");
-  return RP_ERR_UNSUPPORTED;
+rp_status flash_bwd(const AttnDesc& a, const void* qkv, const void* o, const void* dout, const float* lse,
+                    float* Dbuf, void* dqkv, hipStream_t s) {
+  RP_CHECK(((uintptr_t)qkv & 15) == 0 && ((uintptr_t)o & 15) == 0 && ((uintptr_t)dout & 15) == 0 &&
+               ((uintptr_t)dqkv & 15) == 0,
+           RP_ERR_INVALID, "flash attention: buffers must be 16-byte aligned");
+  const FlashParams p = make_params(a, qkv);
+  const int T = a.batch * a.seq;
+  const int64_t rows = (int64_t)T * a.n_q;
+  {
+    TraceScope ts(s, "flash_bwd_dot_kernel", 0.0, (double)rows * (2 * D * 2 + 4));
+    RP_LAUNCH(flash_bwd_dot_kernel, dim3((unsigned)cdiv(rows, NT / 16)), dim3(NT), 0, s, (const bf16*)o,
+              (const bf16*)dout, Dbuf, T, a.n_q);
+  }
+  {
+    // dV = P^T dO and dK = dS^T Q: two of the four backward products
+    TraceScope ts(s, "flash_dkdv_kernel", 4.0 * D * a.n_q * causal_pairs(a), 0.0);
+    RP_LAUNCH(flash_dkdv_kernel, dim3(a.n_kv, p.n_blocks, a.batch), dim3(NT), 0, s, p, (const bf16*)dout, lse,
+              Dbuf, (bf16*)dqkv);
+  }
+  {
+    // dQ = dS K and dP = dO V^T: the other two
+    TraceScope ts(s, "flash_dq_kernel", 4.0 * D * a.n_q * causal_pairs(a), 0.0);
+    RP_LAUNCH(flash_dq_kernel, dim3(a.n_q, p.n_blocks, a.batch), dim3(NT), 0, s, p, (const bf16*)dout, lse, Dbuf,
+              (bf16*)dqkv);
+  }
+  return RP_OK;
 }
 
 }  // namespace rp

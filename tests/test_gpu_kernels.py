@@ -90,6 +90,10 @@ def test_gemm_accumulate_and_strided_output(B):
     ("bf16", 128, 4, 2, 2, 200),
     ("bf16", 128, 8, 2, 1, 333),
     ("bf16", 128, 2, 1, 1, 1),
+    ("bf16", 128, 2, 1, 1, 64),
+    ("bf16", 128, 4, 4, 3, 130),
+    ("bf16", 128, 8, 2, 1, 1000),
+    ("bf16", 128, 4, 1, 1, 2049),
 ])
 def test_attention_fwd_bwd(B, dtype, d, nq, nkv, batch, seq):
     say("attention", dtype, d, nq, nkv, batch, seq)
