@@ -331,6 +331,39 @@ __global__ void embed_bwd_kernel(const int32_t* ids, const T* dx0, float* dtable
   }
 }
 
+// 64 x 64 tile per 256-thread block through LDS: 16-byte loads along the
+// source rows, 16-byte stores along the destination rows
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src, int64_t lds,
+                                                             uint16_t* __restrict__ dst, int64_t ldd, int rows,
+                                                             int cols) {
+  __shared__ uint16_t tile[64][64 + 2];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int id = threadIdx.x + 256 * i;
+    const int r = id >> 3, c = (id & 7) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r0 + r < rows && c0 + c < cols) v = *reinterpret_cast<const uint4*>(src + (int64_t)(r0 + r) * lds + c0 + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[r][c + 2 * e] = (uint16_t)(w[e] & 0xffffu);
+      tile[r][c + 2 * e + 1] = (uint16_t)(w[e] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int id = threadIdx.x + 256 * i;
+    const int c = id >> 3, r = (id & 7) * 8;  // destination row c, columns r..r+7
+    if (c0 + c >= cols || r0 + r >= rows) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = uint32_t(tile[r + 2 * e][c]) | (uint32_t(tile[r + 2 * e + 1][c]) << 16);
+    *reinterpret_cast<uint4*>(dst + (int64_t)(c0 + c) * ldd + r0 + r) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 template <class T>
 __global__ void cast_kernel(const float* a, T* out, size_t n) {
   const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
@@ -504,6 +537,17 @@ rp_status embed_bwd(int dt, const int32_t* ids, const void* dx0, float* dtable, 
     RP_LAUNCH(embed_bwd_kernel<bf16>, dim3(V), dim3(256), 0, s, ids, (const bf16*)dx0, dtable, T, H);
   else
     RP_LAUNCH(embed_bwd_kernel<float>, dim3(V), dim3(256), 0, s, ids, (const float*)dx0, dtable, T, H);
+  return RP_OK;
+}
+
+rp_status transpose_bf16(const void* src, int64_t lds, void* dst, int64_t ldd, int rows, int cols, hipStream_t s) {
+  if (rows == 0 || cols == 0) return RP_OK;
+  RP_CHECK(rows % 8 == 0 && cols % 8 == 0 && lds % 8 == 0 && ldd % 8 == 0 && ((uintptr_t)src & 15) == 0 &&
+               ((uintptr_t)dst & 15) == 0,
+           RP_ERR_UNSUPPORTED, "transpose: sizes and leading dimensions must be multiples of 8, 16-byte aligned");
+  TraceScope ts(s, "transpose_bf16_kernel", 0.0, 4.0 * rows * cols);
+  RP_LAUNCH(transpose_bf16_kernel, dim3((unsigned)cdiv(cols, 64), (unsigned)cdiv(rows, 64)), dim3(256), 0, s,
+            (const uint16_t*)src, lds, (uint16_t*)dst, ldd, rows, cols);
   return RP_OK;
 }
 

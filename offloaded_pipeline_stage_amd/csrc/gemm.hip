@@ -21,6 +21,8 @@
 //
 // fp32 path (and a bf16 cross-check): a plain LDS-tiled FMA kernel with the
 // same epilogue semantics.
+#include <type_traits>
+
 #include "ops.h"
 #include "trace.h"
 
@@ -33,7 +35,6 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int BK = 64;
-constexpr int NT = 256;
 
 struct GemmParams {
   int M, N, K;
@@ -42,132 +43,163 @@ struct GemmParams {
   void* C; int64_t ldc;
   const void* R; int64_t ldr;
   void* C2; int64_t ldc2;
+  uint32_t a_bytes, b_bytes;  // extent of A and B (loads beyond read as zero)
   int F;            // SwiGLU width (EPI_SWIGLU: N == 2F; EPI_SWIGLU_BWD: N == F)
   int tiles_m, tiles_n;
   int accumulate;
 };
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 7); }
-__device__ __forceinline__ int lds_off(int row, int kc) { return row * 128 + ((kc ^ swz(row)) << 4); }
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
 
+// Buffer resource over `bytes` bytes at p: loads at offsets >= bytes return 0
+// (the hardware range check), so tile rows past the matrix edge read as zeros
+// without a branch. The whole offset goes in the per-lane voffset (the range
+// check covers it); OOB_SHIFT pushes a chunk that must read as zero out of
+// range (operand extents stay below 2^31, so the sum cannot wrap).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t OOB_SHIFT = 0x80000000u;
+__device__ __forceinline__ u32x4_t bload(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+
+// --- LDS layouts ---------------------------------------------------------------
+// A tile holds R rows (M or N index) x 64 k of bf16.
+// K-major operands: rows padded to 144 bytes (16-byte chunk kc at row*144 +
+// 16*kc); the 8 lanes of a read phase hit 8 distinct 16-byte bank groups and
+// fragment addresses step by immediates.
+// M-major operands (written after an in-register transpose): 128-byte rows,
+// chunk index XOR-swizzled by row bits, which keeps the 8-byte transposed
+// stores and the 16-byte fragment reads conflict-free.
+template <bool KM> struct Lay;
+template <> struct Lay<true> {
+  static constexpr int RS = 144;
+  __device__ __forceinline__ static int off(int row, int kc) { return row * 144 + kc * 16; }
+};
+template <> struct Lay<false> {
+  static constexpr int RS = 128;
+  __device__ __forceinline__ static int off(int row, int kc) { return row * 128 + ((kc ^ swz(row)) << 4); }
+};
+
 // --- global -> register -> LDS copies --------------------------------------
 
-// K-major operand: element (r, k) at g[r * ld + k]; R rows per tile.
-// rowmap: for the SwiGLU gate/up interleave, tile row -> global row.
-template <int R, bool SWIGLU>
+// K-major operand: element (r, k) at g[r * ld + k]; R rows per tile, NT
+// threads. SWIGLU: tile row r of wave column w = r / wn_span holds gate row f
+// (first half of the span) or up row F + f (second half), so one lane ends up
+// with the gate and up pre-activations of the same output column.
+template <int R, bool SWIGLU, int NT>
 struct LoaderK {
+  static_assert(R * 8 % NT == 0, "tile rows x 8 chunks must split evenly over the threads");
   static constexpr int NCH = R * 8 / NT;
   u32x4_t reg[NCH];
-  __device__ __forceinline__ void load(const bf16* g, int64_t ld, int row0, int rows, int k0,
-                                       int K, int tid, int F, int wn_span) {
+  uint32_t voff[SWIGLU ? NCH : 1];
+  uint32_t rstride;    // bytes between this thread's consecutive rows
+  int kcol;            // first k of this thread's chunk
+  __device__ __forceinline__ void init(int64_t ld, int row0, int tid, int F, int wn_span) {
+    kcol = (tid & 7) * 8;
+    rstride = (uint32_t)((NT / 8) * ld * 2);
+    if constexpr (SWIGLU) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      int c = tid + i * NT;
-      int r = c >> 3, kc = c & 7;
-      int k = k0 + kc * 8;
-      int grow;
-      bool ok;
-      if (SWIGLU) {
-        // tile row r: wave column w = r / wn_span; first half gate, second up
-        int w = r / wn_span, j = r % wn_span, half = wn_span >> 1;
-        int f = row0 + w * half + (j < half ? j : j - half);
-        ok = f < F;
-        grow = (j < half) ? f : F + f;
-      } else {
-        grow = row0 + r;
-        ok = grow < rows;
+      for (int i = 0; i < NCH; ++i) {
+        const int r = (tid >> 3) + i * (NT / 8);
+        const int w = r / wn_span, j = r % wn_span, half = wn_span >> 1;
+        const int f = row0 + w * half + (j < half ? j : j - half);
+        // rows f >= F read garbage of valid rows (or zeros): they only feed
+        // output columns >= F, which are never stored
+        const int grow = (j < half) ? f : F + f;
+        voff[i] = (uint32_t)(((int64_t)grow * ld + (tid & 7) * 8) * 2);
       }
-      if (ok && k < K)
-        reg[i] = *reinterpret_cast<const u32x4_t*>(g + (int64_t)grow * ld + k);
-      else
-        reg[i] = u32x4_t{0u, 0u, 0u, 0u};
+    } else {
+      voff[0] = (uint32_t)(((int64_t)(row0 + (tid >> 3)) * ld + (tid & 7) * 8) * 2);
     }
+  }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int k0, int K) {
+    // a chunk past K (the K tail) reads as zeros
+    const uint32_t base = (uint32_t)(k0 * 2) + (k0 + kcol < K ? 0u : OOB_SHIFT);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+      reg[i] = bload(rs, base + (SWIGLU ? voff[i] : voff[0] + (uint32_t)i * rstride));
   }
   __device__ __forceinline__ void store(char* lds, int tid) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      int c = tid + i * NT;
-      int r = c >> 3, kc = c & 7;
-      *reinterpret_cast<u32x4_t*>(lds + lds_off(r, kc)) = reg[i];
+      const int r = (tid >> 3) + i * (NT / 8);
+      *reinterpret_cast<u32x4_t*>(lds + Lay<true>::off(r, tid & 7)) = reg[i];
     }
   }
 };
 
 // M-major operand: element (r, k) at g[k * ld + r]; loaded as blocks of
-// 4 K-rows x 8 r, transposed in registers into 8 rows x 4 k.
-template <int R>
+// 4 K-rows x 8 r, transposed in registers into 8 rows x 4 k. Rows k >= K lie
+// past the end of the buffer and read as zeros.
+template <int R, int NT>
 struct LoaderM {
   static constexpr int NRB = R / 8;
+  static_assert((BK / 4) * NRB % NT == 0, "4x8 blocks must split evenly over the threads");
   static constexpr int NBLK = (BK / 4) * NRB / NT;
   u32x4_t reg[NBLK][4];
-  __device__ __forceinline__ void load(const bf16* g, int64_t ld, int row0, int rows, int k0,
-                                       int K, int tid) {
+  uint32_t voff[NBLK];
+  __device__ __forceinline__ void init(int64_t ld, int row0, int tid) {
 #pragma unroll
     for (int i = 0; i < NBLK; ++i) {
-      int b = tid + i * NT;
-      int rb = b % NRB, kb = b / NRB;
-      int r = row0 + rb * 8;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int k = k0 + kb * 4 + j;
-        if (k < K && r + 8 <= rows) {
-          reg[i][j] = *reinterpret_cast<const u32x4_t*>(g + (int64_t)k * ld + r);
-        } else if (k < K && r < rows) {
-          uint16_t e[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) e[q] = (r + q < rows) ? g[(int64_t)k * ld + r + q].u : 0;
-          reg[i][j] = u32x4_t{e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
-                              e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16)};
-        } else {
-          reg[i][j] = u32x4_t{0u, 0u, 0u, 0u};
-        }
-      }
+      const int b = tid + i * NT;
+      const int rb = b % NRB, kb = b / NRB;
+      voff[i] = (uint32_t)(((int64_t)(kb * 4) * ld + row0 + rb * 8) * 2);
     }
+  }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int k0) {
+#pragma unroll
+    for (int i = 0; i < NBLK; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        reg[i][j] = bload(rs, voff[i] + (uint32_t)(((int64_t)(k0 + j) * ld) * 2));
   }
   __device__ __forceinline__ void store(char* lds, int tid) {
 #pragma unroll
     for (int i = 0; i < NBLK; ++i) {
-      int b = tid + i * NT;
-      int rb = b % NRB, kb = b / NRB;
-      int kc = kb >> 1, half = kb & 1;
+      const int b = tid + i * NT;
+      const int rb = b % NRB, kb = b / NRB;
+      const int kc = kb >> 1, half = kb & 1;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         // rows 2q (low halves) and 2q+1 (high halves)
-        uint32_t a0 = reg[i][0][q], a1 = reg[i][1][q], a2 = reg[i][2][q], a3 = reg[i][3][q];
-        u32x2_t lo = u32x2_t{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-        u32x2_t hi = u32x2_t{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-        int r0 = rb * 8 + 2 * q;
-        *reinterpret_cast<u32x2_t*>(lds + lds_off(r0, kc) + half * 8) = lo;
-        *reinterpret_cast<u32x2_t*>(lds + lds_off(r0 + 1, kc) + half * 8) = hi;
+        const uint32_t a0 = reg[i][0][q], a1 = reg[i][1][q], a2 = reg[i][2][q], a3 = reg[i][3][q];
+        const u32x2_t lo = u32x2_t{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
+        const u32x2_t hi = u32x2_t{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
+        const int r0 = rb * 8 + 2 * q;
+        *reinterpret_cast<u32x2_t*>(lds + Lay<false>::off(r0, kc) + half * 8) = lo;
+        *reinterpret_cast<u32x2_t*>(lds + Lay<false>::off(r0 + 1, kc) + half * 8) = hi;
       }
     }
   }
 };
 
-template <int R, bool KMAJ, bool SWIGLU>
-struct Loader;
-template <int R, bool SWIGLU>
-struct Loader<R, true, SWIGLU> : LoaderK<R, SWIGLU> {};
-template <int R, bool SWIGLU>
-struct Loader<R, false, SWIGLU> : LoaderM<R> {};
-
 // --- the MFMA kernel --------------------------------------------------------
 
-template <int BM, int BN, bool AK, bool BKM, int EPI, bool OUT_F32>
-__global__ __launch_bounds__(NT) void gemm_mfma_kernel(GemmParams p) {
-  constexpr int WM = BM / 2, WN = BN / 2;
+// WGM x WGN waves, each owning a (BM / WGM) x (BN / WGN) block of 32x32 tiles.
+// Per 64-wide k step: the next step's global loads are issued first, the
+// fragments of k-substep s + 1 are read from LDS while the MFMAs of substep s
+// run, and the loaded registers are written to the other LDS buffer in the
+// middle of the MFMA stream; one barrier per step.
+template <int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool OUT_F32>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(GemmParams p) {
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
+  static_assert(TM >= 1 && TN >= 1 && (EPI != EPI_SWIGLU || TN % 2 == 0), "bad wave tile");
   constexpr bool SW = (EPI == EPI_SWIGLU);
+  constexpr int A_BUF = BM * Lay<AK>::RS, B_BUF = BN * Lay<BKM>::RS;
   extern __shared__ __align__(16) char smem[];
   // [A buffer 0][A buffer 1][B buffer 0][B buffer 1]
-  auto sA = [&](int i) { return smem + i * (BM * 128); };
-  auto sB = [&](int i) { return smem + 2 * BM * 128 + i * (BN * 128); };
+  char* const sA0 = smem;
+  char* const sB0 = smem + 2 * A_BUF;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
   // tile order: contiguous ranges per XCD (workgroups are dealt round-robin
   // over the 8 XCDs), grouped 8 tile-rows at a time for L2 reuse
@@ -185,14 +217,20 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(GemmParams p) {
   const int m0 = tile_m * BM;
   const int n0 = SW ? tile_n * (BN / 2) : tile_n * BN;  // SwiGLU: F-column base
 
-  Loader<BM, AK, false> la;
-  Loader<BN, BKM, SW> lb;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_bytes);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, p.b_bytes);
+  std::conditional_t<AK, LoaderK<BM, false, NT>, LoaderM<BM, NT>> la;
+  std::conditional_t<BKM, LoaderK<BN, SW, NT>, LoaderM<BN, NT>> lb;
+  if constexpr (AK) la.init(p.lda, m0, tid, 0, 1);
+  else la.init(p.lda, m0, tid);
+  if constexpr (BKM) lb.init(p.ldb, n0, tid, p.F, WN);
+  else lb.init(p.ldb, n0, tid);
 
   auto load = [&](int k0) {
-    if constexpr (AK) la.load(p.A + 0, p.lda, m0, p.M, k0, p.K, tid, 0, 0);
-    else la.load(p.A, p.lda, m0, p.M, k0, p.K, tid);
-    if constexpr (BKM) lb.load(p.B, p.ldb, n0, p.N, k0, p.K, tid, p.F, WN);
-    else lb.load(p.B, p.ldb, n0, p.N, k0, p.K, tid);
+    if constexpr (AK) la.load(ra, p.lda, k0, p.K);
+    else la.load(ra, p.lda, k0);
+    if constexpr (BKM) lb.load(rb, p.ldb, k0, p.K);
+    else lb.load(rb, p.ldb, k0);
   };
 
   f32x16_t acc[TM][TN];
@@ -203,42 +241,58 @@ __global__ __launch_bounds__(NT) void gemm_mfma_kernel(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // fragment rows of this lane
+  const int arow = wm * WM + (lane & 31), brow = wn * WN + (lane & 31), kh = lane >> 5;
+  // fragment q of k-substep ks: q < TM reads A row block q, else B row block q - TM
+  auto read_one = [&](const char* a_s, const char* b_s, int ks, int q, bf16x8_t (&af)[TM], bf16x8_t (&bfr)[TN]) {
+    const int kc = ks * 2 + kh;
+    if (q < TM) af[q] = *reinterpret_cast<const bf16x8_t*>(a_s + Lay<AK>::off(arow + q * 32, kc));
+    else bfr[q - TM] = *reinterpret_cast<const bf16x8_t*>(b_s + Lay<BKM>::off(brow + (q - TM) * 32, kc));
+  };
+
+  // The k loop body is one basic block issued in a fixed order: the next
+  // tile's global loads first, then each substep's MFMAs with the following
+  // substep's fragment reads interleaved one by one, and in the last substep
+  // the LDS stores of the next tile interleaved. The last step's prefetch of
+  // the tile past K is harmless (rows past the operand read as zeros, the K
+  // tail is masked) and never read back.
+  constexpr int NKS = BK / 16;
+  constexpr int NMF = TM * TN;  // MFMAs per k-substep
+  constexpr int NRD = TM + TN;  // fragment reads per k-substep
+  static_assert(NRD <= NMF, "fewer MFMAs than fragment reads per substep");
   const int nk = (p.K + BK - 1) / BK;
   load(0);
-  la.store(sA(0), tid);
-  lb.store(sB(0), tid);
+  la.store(sA0, tid);
+  lb.store(sB0, tid);
   __syncthreads();
+  bf16x8_t af[2][TM], bfr[2][TN];
+#pragma unroll
+  for (int q = 0; q < NRD; ++q) read_one(sA0, sB0, 0, q, af[0], bfr[0]);
 
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) load((kt + 1) * BK);
-    const char* a_s = sA(cur);
-    const char* b_s = sB(cur);
+    load((kt + 1) * BK);
+    __builtin_amdgcn_sched_barrier(0);
+    const char* a_s = sA0 + cur * A_BUF;
+    const char* b_s = sB0 + cur * B_BUF;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int kc = ks * 2 + (lane >> 5);
-      bf16x8_t af[TM], bfr[TN];
+    for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        int row = wm * WM + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const bf16x8_t*>(a_s + lds_off(row, kc));
+      for (int t = 0; t < NMF; ++t) {
+        const int i = t / TN, j = t % TN;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j], 0, 0, 0);
+        if (ks + 1 < NKS && t < NRD) read_one(a_s, b_s, ks + 1, t, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+        if (ks + 1 == NKS && t == 0) {
+          // the other buffer was last read before the previous barrier
+          la.store(sA0 + (cur ^ 1) * A_BUF, tid);
+          lb.store(sB0 + (cur ^ 1) * B_BUF, tid);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        int row = wn * WN + j * 32 + (lane & 31);
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(b_s + lds_off(row, kc));
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) {
-      la.store(sA(cur ^ 1), tid);
-      lb.store(sB(cur ^ 1), tid);
     }
     __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NRD; ++q) read_one(sA0 + (cur ^ 1) * A_BUF, sB0 + (cur ^ 1) * B_BUF, 0, q, af[0], bfr[0]);
   }
 
   // --- epilogue: lane holds column (lane & 31) of each 32x32 tile, rows
@@ -400,7 +454,13 @@ rp_status gemm_simple(const GemmDesc& d, hipStream_t s) {
 
 // --- MFMA dispatch ------------------------------------------------------------
 
-template <int BM, int BN, bool AK, bool BKM, int EPI, bool OF32>
+// bytes spanned by an operand of `rows` x `k` stored with leading dimension ld
+inline uint64_t operand_bytes(bool kmajor, int64_t rows, int64_t k, int64_t ld) {
+  if (rows == 0 || k == 0) return 0;
+  return (uint64_t)(kmajor ? (rows - 1) * ld + k : (k - 1) * ld + rows) * 2;
+}
+
+template <int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool OF32>
 rp_status launch_mfma(const GemmDesc& d, hipStream_t s) {
   GemmParams p;
   p.M = d.M; p.N = d.N; p.K = d.K;
@@ -413,45 +473,52 @@ rp_status launch_mfma(const GemmDesc& d, hipStream_t s) {
   p.F = EPI == EPI_SWIGLU ? d.N / 2 : (EPI == EPI_SWIGLU_BWD ? d.N : 0);
   p.tiles_m = (int)cdiv(d.M, BM);
   p.tiles_n = EPI == EPI_SWIGLU ? (int)cdiv(d.N / 2, BN / 2) : (int)cdiv(d.N, BN);
-  const size_t lds = 2 * (BM + BN) * 128;
+  const uint64_t ab = operand_bytes(AK, d.M, d.K, d.lda), bb = operand_bytes(BKM, d.N, d.K, d.ldb);
+  RP_CHECK(ab < (1ull << 31) && bb < (1ull << 31), RP_ERR_UNSUPPORTED,
+           "gemm(bf16): each operand must span less than 2 GiB");
+  p.a_bytes = (uint32_t)ab;
+  p.b_bytes = (uint32_t)bb;
+  const size_t lds = 2 * ((size_t)BM * (AK ? 144 : 128) + (size_t)BN * (BKM ? 144 : 128));
   static bool attr_set = false;  // one instantiation per template: set once
   if (!attr_set) {
-    RP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_mfma_kernel<BM, BN, AK, BKM, EPI, OF32>),
+    RP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_mfma_kernel<BM, BN, WGM, WGN, AK, BKM, EPI, OF32>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
     attr_set = true;
   }
   const int64_t nt = (int64_t)p.tiles_m * p.tiles_n;
   char name[96];
-  snprintf(name, sizeof(name), "gemm_mfma_kernel<%d, %d, %d, %d, %d, %d>", BM, BN, (int)AK, (int)BKM, EPI, (int)OF32);
+  snprintf(name, sizeof(name), "gemm_mfma_kernel<%d, %d, %d, %d, %d, %d, %d, %d>", BM, BN, WGM, WGN, (int)AK, (int)BKM,
+           EPI, (int)OF32);
   TraceScope ts(s, name, 2.0 * d.M * d.N * d.K, 0.0);
-  RP_LAUNCH((gemm_mfma_kernel<BM, BN, AK, BKM, EPI, OF32>), dim3((unsigned)nt), dim3(NT), lds, s, p);
+  RP_LAUNCH((gemm_mfma_kernel<BM, BN, WGM, WGN, AK, BKM, EPI, OF32>), dim3((unsigned)nt), dim3(64 * WGM * WGN), lds, s,
+            p);
   return RP_OK;
 }
 
-template <int BM, int BN, int EPI, bool OF32>
+template <int BM, int BN, int WGM, int WGN, int EPI, bool OF32>
 rp_status dispatch_layout(const GemmDesc& d, hipStream_t s) {
-  if (d.a_kmajor && d.b_kmajor) return launch_mfma<BM, BN, true, true, EPI, OF32>(d, s);
-  if (d.a_kmajor && !d.b_kmajor) return launch_mfma<BM, BN, true, false, EPI, OF32>(d, s);
-  if (!d.a_kmajor && !d.b_kmajor) return launch_mfma<BM, BN, false, false, EPI, OF32>(d, s);
-  return launch_mfma<BM, BN, false, true, EPI, OF32>(d, s);
+  if (d.a_kmajor && d.b_kmajor) return launch_mfma<BM, BN, WGM, WGN, true, true, EPI, OF32>(d, s);
+  if (d.a_kmajor && !d.b_kmajor) return launch_mfma<BM, BN, WGM, WGN, true, false, EPI, OF32>(d, s);
+  if (!d.a_kmajor && !d.b_kmajor) return launch_mfma<BM, BN, WGM, WGN, false, false, EPI, OF32>(d, s);
+  return launch_mfma<BM, BN, WGM, WGN, false, true, EPI, OF32>(d, s);
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WGM, int WGN>
 rp_status dispatch_epi(const GemmDesc& d, hipStream_t s) {
   const bool of32 = d.out_dtype == RP_DTYPE_F32;
   switch (d.epi) {
     case EPI_STORE:
-      return of32 ? dispatch_layout<BM, BN, EPI_STORE, true>(d, s)
-                  : dispatch_layout<BM, BN, EPI_STORE, false>(d, s);
+      return of32 ? dispatch_layout<BM, BN, WGM, WGN, EPI_STORE, true>(d, s)
+                  : dispatch_layout<BM, BN, WGM, WGN, EPI_STORE, false>(d, s);
     case EPI_RESID:
-      return of32 ? dispatch_layout<BM, BN, EPI_RESID, true>(d, s)
-                  : dispatch_layout<BM, BN, EPI_RESID, false>(d, s);
+      return of32 ? dispatch_layout<BM, BN, WGM, WGN, EPI_RESID, true>(d, s)
+                  : dispatch_layout<BM, BN, WGM, WGN, EPI_RESID, false>(d, s);
     case EPI_SWIGLU:
       RP_CHECK(d.b_kmajor && !of32, RP_ERR_UNSUPPORTED, "swiglu epilogue: K-major bf16 only");
-      return dispatch_layout<BM, BN, EPI_SWIGLU, false>(d, s);
+      return dispatch_layout<BM, BN, WGM, WGN, EPI_SWIGLU, false>(d, s);
     case EPI_SWIGLU_BWD:
       RP_CHECK(!of32, RP_ERR_UNSUPPORTED, "swiglu bwd epilogue: bf16 only");
-      return dispatch_layout<BM, BN, EPI_SWIGLU_BWD, false>(d, s);
+      return dispatch_layout<BM, BN, WGM, WGN, EPI_SWIGLU_BWD, false>(d, s);
   }
   set_error("gemm: unknown epilogue %d", d.epi);
   return RP_ERR_INVALID;
@@ -494,8 +561,29 @@ rp_status gemm(const GemmDesc& d, hipStream_t s) {
   if (d.force_simple) return gemm_simple<bf16>(d, s);
   const int64_t n_eff = d.epi == EPI_SWIGLU ? d.N / 2 : d.N;
   const int64_t big = cdiv(d.M, 256) * cdiv(n_eff, d.epi == EPI_SWIGLU ? 128 : 256);
-  if (big >= 240) return dispatch_epi<256, 256>(d, s);
-  return dispatch_epi<128, 128>(d, s);
+  if (big < 240) return dispatch_epi<128, 128, 2, 2>(d, s);
+  if (!d.a_kmajor && !d.b_kmajor) {
+    // both operands M-major (weight gradients): transpose both through the
+    // scratch and run the K-major kernel, which is far faster than
+    // transposing tiles in registers on the way to LDS
+    if (d.tr && d.tr_bytes >= gemm_tr_bytes(d.M, d.N, d.K) && d.M % 8 == 0 && d.N % 8 == 0) {
+      GemmDesc e = d;
+      char* ta = reinterpret_cast<char*>(d.tr);
+      char* tb = ta + align_up((size_t)d.M * d.K * 2, 256);
+      RP_TRY(transpose_bf16(d.A, d.lda, ta, d.K, d.K, d.M, s));
+      RP_TRY(transpose_bf16(d.B, d.ldb, tb, d.K, d.K, d.N, s));
+      e.A = ta; e.lda = d.K; e.a_kmajor = true;
+      e.B = tb; e.ldb = d.K; e.b_kmajor = true;
+      e.tr = nullptr;
+      return dispatch_epi<256, 256, 2, 4>(e, s);
+    }
+    return dispatch_epi<256, 256, 2, 2>(d, s);
+  }
+  return dispatch_epi<256, 256, 2, 4>(d, s);
+}
+
+size_t gemm_tr_bytes(int64_t M, int64_t N, int64_t K) {
+  return align_up((size_t)M * K * 2, 256) + align_up((size_t)N * K * 2, 256);
 }
 
 }  // namespace rp

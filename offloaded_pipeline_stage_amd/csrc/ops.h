@@ -29,7 +29,14 @@ struct GemmDesc {
   void* C2 = nullptr; int64_t ldc2 = 0;
   float* tmp = nullptr;           // fp32 [M, N] scratch for the unfused fp32 path
   bool force_simple = false;      // use the generic kernel even for bf16
+  // scratch for bf16 products whose operands are both M-major (the weight
+  // gradients dY^T X): both are transposed into it (gemm_tr_bytes) and the
+  // K-major kernel runs on the copies
+  void* tr = nullptr; size_t tr_bytes = 0;
 };
+
+// scratch gemm() uses to transpose both operands of an M x N x K product
+size_t gemm_tr_bytes(int64_t M, int64_t N, int64_t K);
 
 rp_status gemm(const GemmDesc& d, hipStream_t s);
 rp_status gemm_validate(const GemmDesc& d);
@@ -101,6 +108,9 @@ rp_status embed_fwd(int dt, const int32_t* ids, const void* table, void* x0, int
                     hipStream_t s);
 rp_status embed_bwd(int dt, const int32_t* ids, const void* dx0, float* dtable, int T, int V,
                     int H, hipStream_t s);
+// dst [cols, rows] (leading dimension ldd) = src [rows, cols]^T (leading
+// dimension lds), bf16; rows, cols, lds, ldd multiples of 8, 16-byte aligned
+rp_status transpose_bf16(const void* src, int64_t lds, void* dst, int64_t ldd, int rows, int cols, hipStream_t s);
 // out (dtype dt) = a (fp32)
 rp_status cast_from_f32(int dt, const float* a, void* out, size_t n, hipStream_t s);
 

@@ -37,6 +37,8 @@ struct BwdTmp {
   float* Dbuf = nullptr;   // [nq, T]
   float* dm_tmp = nullptr; // fp32 [T, F] (unfused fp32 path)
   float* part = nullptr;   // RMSNorm dgamma partials
+  void* tr = nullptr;      // operand transposes of the weight-gradient products
+  size_t tr_bytes = 0;
   void* gp[2] = {nullptr, nullptr};  // inter-layer gradients
   void* ck[2] = {nullptr, nullptr};  // uploaded checkpoints
 };
@@ -83,6 +85,14 @@ void carve(Bump& bp, const Shape& s, int64_t T, int seq, int n_layers, bool keep
     b.Dbuf = bp.take<float>((size_t)s.nq * T * 4);
     if (s.dt == RP_DTYPE_F32) b.dm_tmp = bp.take<float>(T * s.F * 4);
     b.part = bp.take<float>(rmsnorm_bwd_part_bytes((int)T, s.H));
+    if (s.dt == RP_DTYPE_BF16) {
+      // largest weight-gradient product: dW_gu [2F, H] over T tokens
+      size_t need = 0;
+      const int64_t shapes[4][2] = {{s.H, s.F}, {2 * (int64_t)s.F, s.H}, {s.H, s.Q}, {s.QKV, s.H}};
+      for (auto& mn : shapes) need = std::max(need, gemm_tr_bytes(mn[0], mn[1], T));
+      b.tr = bp.take(need);
+      b.tr_bytes = need;
+    }
     b.gp[0] = bp.take(T * s.H * s.es);
     b.gp[1] = bp.take(T * s.H * s.es);
     b.ck[0] = bp.take(T * s.H * s.es);
@@ -155,20 +165,33 @@ rp_status layer_bwd(rp_ctx* c, Slot& w, int T, int seq, const void* x, const Act
   g1.R = A.gu; g1.ldr = F2; g1.tmp = B.dm_tmp;
   RP_TRY(gemm(g1, st));
   // dWd = dy^T m
-  RP_TRY(gemm(mk(s.H, s.F, T, dy, s.H, false, A.m, s.F, false, gptr(w, cfg, RP_T_WD), s.F, dt, RP_DTYPE_F32), st));
+  {
+    GemmDesc gw = mk(s.H, s.F, T, dy, s.H, false, A.m, s.F, false, gptr(w, cfg, RP_T_WD), s.F, dt, RP_DTYPE_F32);
+    gw.tr = B.tr;
+    gw.tr_bytes = B.tr_bytes;
+    RP_TRY(gemm(gw, st));
+  }
   // db = dgu Wgu
   RP_TRY(gemm(mk(T, s.H, F2, B.dgu, F2, true, wptr(w, cfg, RP_T_WGU), s.H, false, B.gbuf, s.H, dt, RP_DTYPE_F32),
               st));
   // dWgu = dgu^T b
-  RP_TRY(gemm(mk(F2, s.H, T, B.dgu, F2, false, A.b, s.H, false, gptr(w, cfg, RP_T_WGU), s.H, dt, RP_DTYPE_F32),
-              st));
+  {
+    GemmDesc gw = mk(F2, s.H, T, B.dgu, F2, false, A.b, s.H, false, gptr(w, cfg, RP_T_WGU), s.H, dt, RP_DTYPE_F32);
+    gw.tr = B.tr;
+    gw.tr_bytes = B.tr_bytes;
+    RP_TRY(gemm(gw, st));
+  }
   // dh1 = dy + RMSNorm2^T db ; dgamma2
   RP_TRY(rmsnorm_bwd(dt, B.gbuf, A.h1, wptr(w, cfg, RP_T_GAMMA2), A.rstd2, dy, dt, B.dh1f, B.dh1,
                      gptr(w, cfg, RP_T_GAMMA2), B.part, T, s.H, st));
   // attention output projection
   RP_TRY(gemm(mk(T, s.Q, s.H, B.dh1, s.H, true, wptr(w, cfg, RP_T_WO), s.Q, false, B.dO, s.Q, dt, dt), st));
-  RP_TRY(gemm(mk(s.H, s.Q, T, B.dh1, s.H, false, A.o, s.Q, false, gptr(w, cfg, RP_T_WO), s.Q, dt, RP_DTYPE_F32),
-              st));
+  {
+    GemmDesc gw = mk(s.H, s.Q, T, B.dh1, s.H, false, A.o, s.Q, false, gptr(w, cfg, RP_T_WO), s.Q, dt, RP_DTYPE_F32);
+    gw.tr = B.tr;
+    gw.tr_bytes = B.tr_bytes;
+    RP_TRY(gemm(gw, st));
+  }
   AttnDesc ad;
   ad.dt = dt; ad.batch = T / seq; ad.seq = seq; ad.n_q = s.nq; ad.n_kv = s.nkv; ad.d = s.d;
   RP_TRY(attn_bwd(ad, A.qkv, A.o, B.dO, A.lse, B.Dbuf, B.dqkv, st));
@@ -176,8 +199,13 @@ rp_status layer_bwd(rp_ctx* c, Slot& w, int T, int seq, const void* x, const Act
   // da = dqkv Wqkv ; dWqkv = dqkv^T a
   RP_TRY(gemm(mk(T, s.H, s.QKV, B.dqkv, s.QKV, true, wptr(w, cfg, RP_T_WQKV), s.H, false, B.gbuf, s.H, dt,
                  RP_DTYPE_F32), st));
-  RP_TRY(gemm(mk(s.QKV, s.H, T, B.dqkv, s.QKV, false, A.a, s.H, false, gptr(w, cfg, RP_T_WQKV), s.H, dt,
-                 RP_DTYPE_F32), st));
+  {
+    GemmDesc gw = mk(s.QKV, s.H, T, B.dqkv, s.QKV, false, A.a, s.H, false, gptr(w, cfg, RP_T_WQKV), s.H, dt,
+                 RP_DTYPE_F32);
+    gw.tr = B.tr;
+    gw.tr_bytes = B.tr_bytes;
+    RP_TRY(gemm(gw, st));
+  }
   // dx = dh1 + RMSNorm1^T da ; dgamma1
   RP_TRY(rmsnorm_bwd(dt, B.gbuf, x, wptr(w, cfg, RP_T_GAMMA1), A.rstd1, B.dh1f, RP_DTYPE_F32, nullptr, dx,
                      gptr(w, cfg, RP_T_GAMMA1), B.part, T, s.H, st));
@@ -354,6 +382,8 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
   void* dz = bp.take(T * vs_max * s.es);
   float* dxf = bp.take<float>(T * s.H * 4);
   float* part = bp.take<float>(rmsnorm_bwd_part_bytes((int)T, s.H));
+  const size_t tr_bytes = s.dt == RP_DTYPE_BF16 ? gemm_tr_bytes(vs_max, s.H, T) : 0;
+  void* tr = tr_bytes ? bp.take(tr_bytes) : nullptr;
   if (need) {
     *need = bp.off;
     return RP_OK;
@@ -392,7 +422,10 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
     GemmDesc gx = mk((int)T, s.H, vs, dz, vs, true, w.w, s.H, false, dxf, s.H, dt, RP_DTYPE_F32);
     gx.accumulate = true;
     RP_TRY(gemm(gx, st));
-    RP_TRY(gemm(mk(vs, s.H, (int)T, dz, vs, false, zz, s.H, false, w.g, s.H, dt, RP_DTYPE_F32), st));
+    GemmDesc gw = mk(vs, s.H, (int)T, dz, vs, false, zz, s.H, false, w.g, s.H, dt, RP_DTYPE_F32);
+    gw.tr = tr;
+    gw.tr_bytes = tr_bytes;
+    RP_TRY(gemm(gw, st));
     RP_TRY(mark_consumed(c, w));
     RP_TRY(mark_grad_ready(c, w));
   }
