@@ -131,7 +131,9 @@ rp_status rp_ctx_create(int device, const rp_layer_cfg* cfg, const rp_streams* s
            "ctx_create: n_q must be a positive multiple of n_kv");
   RP_CHECK(c.head_dim == 64 || c.head_dim == 128, RP_ERR_UNSUPPORTED, "ctx_create: head_dim must be 64 or 128");
   RP_CHECK(c.n_experts == 0, RP_ERR_UNSUPPORTED, "ctx_create: MoE layers are not implemented in this build");
-  RP_CHECK(c.lora_rank == 0, RP_ERR_UNSUPPORTED, "ctx_create: LoRA adapters are not implemented in this build");
+  RP_CHECK(c.lora_rank == 0 || (c.lora_rank > 0 && c.lora_rank % 8 == 0 && c.lora_rank <= 128 &&
+                                 c.dtype == RP_DTYPE_BF16),
+           RP_ERR_UNSUPPORTED, "ctx_create: LoRA rank must be a multiple of 8 up to 128, with bf16 layers");
   RP_CHECK(c.ffn > 0 && c.ffn % 8 == 0, RP_ERR_UNSUPPORTED, "ctx_create: ffn must be a positive multiple of 8");
   RP_CHECK(c.rms_eps > 0.f && c.rope_base > 1.f, RP_ERR_INVALID, "ctx_create: bad rms_eps or rope_base");
   int n_dev = 0;
@@ -185,11 +187,24 @@ rp_status rp_bind_layer(rp_ctx* c, int layer, const void* w_dev, float* grad_dev
   RP_CHECK(layer >= 0 && layer < kMaxLayers, RP_ERR_INVALID, "bind_layer: layer %d out of range", layer);
   RP_CHECK(w_dev && ((uintptr_t)w_dev & 255) == 0, RP_ERR_INVALID, "bind_layer: weights null or not 256-aligned");
   RP_CHECK(!grad_dev || ((uintptr_t)grad_dev & 255) == 0, RP_ERR_INVALID, "bind_layer: gradient not 256-aligned");
-  (void)lora_dev;
-  (void)lora_grad_dev;
   LayerBinding& b = c->layers[layer];
-  RP_CHECK(b.base.w_chunks_unissued == 0 && b.base.g_chunks_unissued == 0, RP_ERR_STATE,
-           "bind_layer: layer %d has deferred transfers", layer);
+  RP_CHECK(b.base.w_chunks_unissued == 0 && b.base.g_chunks_unissued == 0 && b.lora.w_chunks_unissued == 0 &&
+               b.lora.g_chunks_unissued == 0,
+           RP_ERR_STATE, "bind_layer: layer %d has deferred transfers", layer);
+  if (c->cfg.lora_rank > 0) {
+    RP_CHECK(lora_dev && ((uintptr_t)lora_dev & 255) == 0, RP_ERR_INVALID,
+             "bind_layer: LoRA layers need a 256-aligned adapter block");
+    RP_CHECK(!lora_grad_dev || ((uintptr_t)lora_grad_dev & 255) == 0, RP_ERR_INVALID,
+             "bind_layer: adapter gradient not 256-aligned");
+    size_t lt = 0;
+    RP_TRY(block_layout(c->cfg, RP_BLOCK_LORA, -1, nullptr, nullptr, &lt));
+    b.lora.w = lora_dev;
+    b.lora.g = lora_grad_dev;
+    b.lora.w_bytes = lt;
+    b.lora.g_bytes = lora_grad_dev ? lt : 0;
+  } else {
+    RP_CHECK(!lora_dev && !lora_grad_dev, RP_ERR_INVALID, "bind_layer: adapters given for a context without LoRA");
+  }
   size_t wt = 0, gt = 0;
   RP_TRY(block_layout(c->cfg, RP_BLOCK_WEIGHT, -1, nullptr, nullptr, &wt));
   RP_TRY(block_layout(c->cfg, RP_BLOCK_GRAD, -1, nullptr, nullptr, &gt));

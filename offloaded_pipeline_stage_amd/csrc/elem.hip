@@ -364,6 +364,17 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
   }
 }
 
+__global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N, float* __restrict__ C,
+                                     int64_t ldc, int accumulate) {
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)M * N) return;
+  const int64_t m = idx / N, n = idx % N;
+  float v = 0.f;
+  for (int sp = 0; sp < splits; ++sp) v += part[(int64_t)sp * M * N + idx];
+  float* c = C + m * ldc + n;
+  *c = accumulate ? *c + v : v;
+}
+
 template <class T>
 __global__ void cast_kernel(const float* a, T* out, size_t n) {
   const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
@@ -548,6 +559,15 @@ rp_status transpose_bf16(const void* src, int64_t lds, void* dst, int64_t ldd, i
   TraceScope ts(s, "transpose_bf16_kernel", 0.0, 4.0 * rows * cols);
   RP_LAUNCH(transpose_bf16_kernel, dim3((unsigned)cdiv(cols, 64), (unsigned)cdiv(rows, 64)), dim3(256), 0, s,
             (const uint16_t*)src, lds, (uint16_t*)dst, ldd, rows, cols);
+  return RP_OK;
+}
+
+rp_status splitk_reduce(const float* part, int splits, int M, int N, float* C, int64_t ldc, bool accumulate,
+                        hipStream_t s) {
+  const int64_t n = (int64_t)M * N;
+  if (n == 0) return RP_OK;
+  TraceScope ts(s, "splitk_reduce_kernel", 0.0, (double)n * 4 * (splits + 1 + (accumulate ? 1 : 0)));
+  RP_LAUNCH(splitk_reduce_kernel, dim3(blocks_for(n)), dim3(256), 0, s, part, splits, M, N, C, ldc, accumulate ? 1 : 0);
   return RP_OK;
 }
 

@@ -47,6 +47,9 @@ struct GemmParams {
   int F;            // SwiGLU width (EPI_SWIGLU: N == 2F; EPI_SWIGLU_BWD: N == F)
   int tiles_m, tiles_n;
   int accumulate;
+  float alpha;      // C = alpha * A B^T (+ R) for the store and residual epilogues
+  int kc;           // k extent of one split (blockIdx.y); K when not split
+  int64_t c_split;  // element stride between the splits' partial outputs
 };
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 7); }
@@ -142,20 +145,25 @@ struct LoaderM {
   static constexpr int NBLK = (BK / 4) * NRB / NT;
   u32x4_t reg[NBLK][4];
   uint32_t voff[NBLK];
+  int krow[NBLK];  // first k row of each block
   __device__ __forceinline__ void init(int64_t ld, int row0, int tid) {
 #pragma unroll
     for (int i = 0; i < NBLK; ++i) {
       const int b = tid + i * NT;
       const int rb = b % NRB, kb = b / NRB;
+      krow[i] = kb * 4;
       voff[i] = (uint32_t)(((int64_t)(kb * 4) * ld + row0 + rb * 8) * 2);
     }
   }
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int k0) {
+  // k rows >= kend (past K, or past this split's range) read as zeros
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int k0, int kend) {
 #pragma unroll
     for (int i = 0; i < NBLK; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        reg[i][j] = bload(rs, voff[i] + (uint32_t)(((int64_t)(k0 + j) * ld) * 2));
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t oob = (k0 + krow[i] + j < kend) ? 0u : OOB_SHIFT;
+        reg[i][j] = bload(rs, voff[i] + (uint32_t)(((int64_t)(k0 + j) * ld) * 2) + oob);
+      }
   }
   __device__ __forceinline__ void store(char* lds, int tid) {
 #pragma unroll
@@ -226,11 +234,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(GemmParams p)
   if constexpr (BKM) lb.init(p.ldb, n0, tid, p.F, WN);
   else lb.init(p.ldb, n0, tid);
 
+  // k range of this split (the whole K unless the product is split along K)
+  const int kbeg = blockIdx.y * p.kc;
+  const int kend = min(p.K, kbeg + p.kc);
   auto load = [&](int k0) {
-    if constexpr (AK) la.load(ra, p.lda, k0, p.K);
-    else la.load(ra, p.lda, k0);
-    if constexpr (BKM) lb.load(rb, p.ldb, k0, p.K);
-    else lb.load(rb, p.ldb, k0);
+    la.load(ra, p.lda, k0, kend);
+    lb.load(rb, p.ldb, k0, kend);
   };
 
   f32x16_t acc[TM][TN];
@@ -260,8 +269,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(GemmParams p)
   constexpr int NMF = TM * TN;  // MFMAs per k-substep
   constexpr int NRD = TM + TN;  // fragment reads per k-substep
   static_assert(NRD <= NMF, "fewer MFMAs than fragment reads per substep");
-  const int nk = (p.K + BK - 1) / BK;
-  load(0);
+  const int nk = (kend - kbeg + BK - 1) / BK;
+  load(kbeg);
   la.store(sA0, tid);
   lb.store(sB0, tid);
   __syncthreads();
@@ -271,7 +280,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(GemmParams p)
 
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    load((kt + 1) * BK);
+    load(kbeg + (kt + 1) * BK);
     __builtin_amdgcn_sched_barrier(0);
     const char* a_s = sA0 + cur * A_BUF;
     const char* b_s = sB0 + cur * B_BUF;
@@ -328,7 +337,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(GemmParams p)
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + lr + (r & 3);
           if (m >= p.M) continue;
-          float v = acc[i][j][r];
+          float v = acc[i][j][r] * p.alpha;
           if constexpr (EPI == EPI_SWIGLU_BWD) {
             const bf16* gu = reinterpret_cast<const bf16*>(p.R);
             const float g = to_f(gu[(int64_t)m * p.ldr + n]);
@@ -338,7 +347,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(GemmParams p)
             dgu[(int64_t)m * p.ldc + n] = to_bf16(v * u * sg * (1.f + g * (1.f - sg)));
             dgu[(int64_t)m * p.ldc + p.F + n] = to_bf16(v * g * sg);
           } else if constexpr (OUT_F32) {
-            float* c = reinterpret_cast<float*>(p.C) + (int64_t)m * p.ldc + n;
+            float* c = reinterpret_cast<float*>(p.C) + blockIdx.y * p.c_split + (int64_t)m * p.ldc + n;
             if (EPI == EPI_RESID) v += reinterpret_cast<const float*>(p.R)[(int64_t)m * p.ldr + n];
             *c = p.accumulate ? *c + v : v;
           } else {
@@ -363,7 +372,7 @@ struct SimpleParams {
 // through the epilogue functor
 template <class TI, class TO, int EPI>
 __global__ __launch_bounds__(256) void gemm_simple_kernel(SimpleParams<TI> p, TO* C, int64_t ldc,
-                                                          const TO* R, int64_t ldr, int accumulate) {
+                                                          const TO* R, int64_t ldr, int accumulate, float alpha) {
   __shared__ float As[16][65];
   __shared__ float Bs[16][65];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
@@ -398,7 +407,7 @@ __global__ __launch_bounds__(256) void gemm_simple_kernel(SimpleParams<TI> p, TO
     for (int j = 0; j < 4; ++j) {
       int m = m0 + ty * 4 + i, n = n0 + tx * 4 + j;
       if (m >= p.M || n >= p.N) continue;
-      float v = acc[i][j];
+      float v = acc[i][j] * alpha;
       if (EPI == EPI_RESID) v += to_f(R[(int64_t)m * ldr + n]);
       TO* c = C + (int64_t)m * ldc + n;
       if (accumulate) v += to_f(*c);
@@ -418,7 +427,7 @@ rp_status launch_simple(const GemmDesc& d, void* C, int64_t ldc, hipStream_t s) 
   TraceScope ts(s, "gemm_simple_kernel", 2.0 * d.M * d.N * d.K, 0.0);
   RP_LAUNCH((gemm_simple_kernel<TI, TO, EPI>), grid, dim3(256), 0, s, p,
             reinterpret_cast<TO*>(C), ldc, reinterpret_cast<const TO*>(d.R), d.ldr,
-            (int)d.accumulate);
+            (int)d.accumulate, d.alpha);
   return RP_OK;
 }
 
@@ -470,6 +479,19 @@ rp_status launch_mfma(const GemmDesc& d, hipStream_t s) {
   p.R = d.R; p.ldr = d.ldr;
   p.C2 = d.C2; p.ldc2 = d.ldc2;
   p.accumulate = d.accumulate ? 1 : 0;
+  p.alpha = d.alpha;
+  p.kc = d.K;
+  p.c_split = 0;
+  int splits = 1;
+  if (d.split_k > 1) {
+    // split K into ranges of whole 64-wide steps; each writes an fp32 partial
+    p.kc = (int)(cdiv(cdiv(d.K, d.split_k), BK) * BK);
+    splits = (int)cdiv(d.K, p.kc);
+    p.C = d.partial;
+    p.ldc = d.N;
+    p.c_split = (int64_t)d.M * d.N;
+    p.accumulate = 0;
+  }
   p.F = EPI == EPI_SWIGLU ? d.N / 2 : (EPI == EPI_SWIGLU_BWD ? d.N : 0);
   p.tiles_m = (int)cdiv(d.M, BM);
   p.tiles_n = EPI == EPI_SWIGLU ? (int)cdiv(d.N / 2, BN / 2) : (int)cdiv(d.N, BN);
@@ -490,8 +512,9 @@ rp_status launch_mfma(const GemmDesc& d, hipStream_t s) {
   snprintf(name, sizeof(name), "gemm_mfma_kernel<%d, %d, %d, %d, %d, %d, %d, %d>", BM, BN, WGM, WGN, (int)AK, (int)BKM,
            EPI, (int)OF32);
   TraceScope ts(s, name, 2.0 * d.M * d.N * d.K, 0.0);
-  RP_LAUNCH((gemm_mfma_kernel<BM, BN, WGM, WGN, AK, BKM, EPI, OF32>), dim3((unsigned)nt), dim3(64 * WGM * WGN), lds, s,
-            p);
+  RP_LAUNCH((gemm_mfma_kernel<BM, BN, WGM, WGN, AK, BKM, EPI, OF32>), dim3((unsigned)nt, (unsigned)splits),
+            dim3(64 * WGM * WGN), lds, s, p);
+  if (splits > 1) return splitk_reduce(d.partial, splits, d.M, d.N, reinterpret_cast<float*>(d.C), d.ldc, d.accumulate, s);
   return RP_OK;
 }
 
@@ -542,10 +565,29 @@ rp_status gemm_validate(const GemmDesc& d) {
   if (d.epi == EPI_SWIGLU) RP_CHECK(d.C2, RP_ERR_INVALID, "gemm: missing C2");
   RP_CHECK(!d.accumulate || d.out_dtype == RP_DTYPE_F32, RP_ERR_INVALID,
            "gemm: accumulation needs an fp32 output");
+  if (d.split_k > 1)
+    RP_CHECK(d.in_dtype == RP_DTYPE_BF16 && d.out_dtype == RP_DTYPE_F32 && d.epi == EPI_STORE && d.partial &&
+                 d.partial_bytes >= splitk_bytes(d.M, d.N, d.K, d.split_k),
+             RP_ERR_INVALID, "gemm: split-K needs bf16 operands, a plain fp32 store and its partial scratch");
+  RP_CHECK(d.alpha == 1.f || d.epi == EPI_STORE || d.epi == EPI_RESID, RP_ERR_INVALID,
+           "gemm: alpha applies to the store and residual epilogues only");
   return RP_OK;
 }
 
-rp_status gemm(const GemmDesc& d, hipStream_t s) {
+rp_status gemm(const GemmDesc& dd, hipStream_t s) {
+  GemmDesc d = dd;
+  if (d.split_k == 0) {
+    // automatic split-K for products with few output tiles and a long K (the
+    // LoRA adapter gradients): enough ranges to give ~512 workgroups
+    d.split_k = 1;
+    const int64_t tiles = cdiv(d.M, 128) * cdiv(d.N, 128);
+    if (d.in_dtype == RP_DTYPE_BF16 && d.out_dtype == RP_DTYPE_F32 && d.epi == EPI_STORE && d.partial &&
+        tiles < 128 && d.K >= 1024) {
+      int sk = (int)std::min<int64_t>(cdiv(512, tiles), d.K / 256);
+      while (sk > 1 && splitk_bytes(d.M, d.N, d.K, sk) > d.partial_bytes) --sk;
+      d.split_k = std::max(sk, 1);
+    }
+  }
   RP_TRY(gemm_validate(d));
   if (d.M == 0 || d.N == 0) return RP_OK;
   if (d.K == 0) {
@@ -559,6 +601,7 @@ rp_status gemm(const GemmDesc& d, hipStream_t s) {
   }
   if (d.in_dtype == RP_DTYPE_F32) return gemm_simple<float>(d, s);
   if (d.force_simple) return gemm_simple<bf16>(d, s);
+  if (d.split_k > 1) return dispatch_epi<128, 128, 2, 2>(d, s);
   const int64_t n_eff = d.epi == EPI_SWIGLU ? d.N / 2 : d.N;
   const int64_t big = cdiv(d.M, 256) * cdiv(n_eff, d.epi == EPI_SWIGLU ? 128 : 256);
   if (big < 240) return dispatch_epi<128, 128, 2, 2>(d, s);
@@ -580,6 +623,12 @@ rp_status gemm(const GemmDesc& d, hipStream_t s) {
     return dispatch_epi<256, 256, 2, 2>(d, s);
   }
   return dispatch_epi<256, 256, 2, 4>(d, s);
+}
+
+size_t splitk_bytes(int64_t M, int64_t N, int64_t K, int split_k) {
+  if (split_k <= 1) return 0;
+  const int64_t kc = cdiv(cdiv(K, split_k), BK) * BK;
+  return (size_t)cdiv(K, kc) * M * N * sizeof(float);
 }
 
 size_t gemm_tr_bytes(int64_t M, int64_t N, int64_t K) {

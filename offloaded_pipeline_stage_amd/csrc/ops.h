@@ -33,7 +33,19 @@ struct GemmDesc {
   // gradients dY^T X): both are transposed into it (gemm_tr_bytes) and the
   // K-major kernel runs on the copies
   void* tr = nullptr; size_t tr_bytes = 0;
+  float alpha = 1.f;              // C = alpha * A B^T (+ R): store / residual epilogues
+  // split-K (bf16 operands, plain fp32 store): K is cut into split_k ranges,
+  // each writes an fp32 partial into `partial` (splitk_bytes), and a fixed-
+  // order reduction sums them into C (adding to C with accumulate).
+  // split_k == 0: chosen from the tile count when `partial` is given
+  int split_k = 1;
+  float* partial = nullptr; size_t partial_bytes = 0;
 };
+
+size_t splitk_bytes(int64_t M, int64_t N, int64_t K, int split_k);
+// C[m, n] (+)= sum over s < splits of part[s][m][n], in split order
+rp_status splitk_reduce(const float* part, int splits, int M, int N, float* C, int64_t ldc, bool accumulate,
+                        hipStream_t s);
 
 // scratch gemm() uses to transpose both operands of an M x N x K product
 size_t gemm_tr_bytes(int64_t M, int64_t N, int64_t K);

@@ -25,6 +25,19 @@ struct Acts {
   void* b = nullptr;      // RMSNorm2(h1) [T, H]
   void* gu = nullptr;     // gate/up pre-activations [T, 2F]
   void* m = nullptr;      // silu(g) * u [T, F]
+  // LoRA: s * (a A^T) for q|k|v [T, 3r] and s * (o Ao^T) [T, r], s = alpha / r
+  void* us_qkv = nullptr;
+  void* us_o = nullptr;
+};
+
+// bf16 copies of one layer's LoRA adapters, in the orientation the products use
+struct LoraBf16 {
+  void* aqkv = nullptr;  // [3r, H]: A_q, A_k, A_v stacked
+  void* bq = nullptr;    // [Q, r]
+  void* bk = nullptr;    // [KV, r]
+  void* bv = nullptr;    // [KV, r]
+  void* ao = nullptr;    // [r, Q]
+  void* bo = nullptr;    // [H, r]
 };
 
 struct BwdTmp {
@@ -39,12 +52,17 @@ struct BwdTmp {
   float* part = nullptr;   // RMSNorm dgamma partials
   void* tr = nullptr;      // operand transposes of the weight-gradient products
   size_t tr_bytes = 0;
+  void* g_qkv = nullptr;   // LoRA: dq|dk|dv times B_q|B_k|B_v [T, 3r]
+  void* g_o = nullptr;     // LoRA: dh1 B_o [T, r]
+  float* splitk = nullptr; // split-K partials of the adapter-gradient products
+  size_t splitk_bytes = 0;
   void* gp[2] = {nullptr, nullptr};  // inter-layer gradients
   void* ck[2] = {nullptr, nullptr};  // uploaded checkpoints
 };
 
 struct Layout {
   float2* rope = nullptr;
+  LoraBf16 lw;
   std::vector<Acts> acts;
   void* xb[2] = {nullptr, nullptr};
   BwdTmp bt;
@@ -62,12 +80,28 @@ void carve_acts(Bump& bp, const Shape& s, int64_t T, Acts& A) {
   A.b = bp.take(T * s.H * s.es);
   A.gu = bp.take(T * 2 * s.F * s.es);
   A.m = bp.take(T * s.F * s.es);
+  if (s.r > 0) {
+    A.us_qkv = bp.take(T * 3 * s.r * s.es);
+    A.us_o = bp.take(T * s.r * s.es);
+  }
 }
+
+// split-K partial scratch of the adapter-gradient products
+constexpr size_t kLoraSplitBytes = 64u << 20;
 
 // mode bits: 1 = keep all layers' internals, 2 = backward temporaries, 4 = fwd ping-pong
 void carve(Bump& bp, const Shape& s, int64_t T, int seq, int n_layers, bool keep, bool bwd, bool fwd_pp,
            Layout& L) {
   L.rope = bp.take<float2>((size_t)seq * (s.d / 2) * sizeof(float2));
+  if (s.r > 0) {
+    const size_t r = s.r, e = s.es;
+    L.lw.aqkv = bp.take(3 * r * s.H * e);
+    L.lw.bq = bp.take((size_t)s.Q * r * e);
+    L.lw.bk = bp.take((size_t)s.KV * r * e);
+    L.lw.bv = bp.take((size_t)s.KV * r * e);
+    L.lw.ao = bp.take(r * s.Q * e);
+    L.lw.bo = bp.take((size_t)s.H * r * e);
+  }
   L.acts.assign(keep ? n_layers : 1, Acts{});
   for (auto& a : L.acts) carve_acts(bp, s, T, a);
   if (fwd_pp) {
@@ -93,6 +127,12 @@ void carve(Bump& bp, const Shape& s, int64_t T, int seq, int n_layers, bool keep
       b.tr = bp.take(need);
       b.tr_bytes = need;
     }
+    if (s.r > 0) {
+      b.g_qkv = bp.take(T * 3 * s.r * s.es);
+      b.g_o = bp.take(T * s.r * s.es);
+      b.splitk = bp.take<float>(kLoraSplitBytes);
+      b.splitk_bytes = kLoraSplitBytes;
+    }
     b.gp[0] = bp.take(T * s.H * s.es);
     b.gp[1] = bp.take(T * s.H * s.es);
     b.ck[0] = bp.take(T * s.H * s.es);
@@ -111,6 +151,34 @@ inline float* gptr(const Slot& s, const rp_layer_cfg& cfg, int tensor) {
   return (float*)((char*)s.g + off);
 }
 
+inline const float* lptr(const Slot& s, const rp_layer_cfg& cfg, int tensor) {
+  size_t off = 0, bytes = 0;
+  block_layout(cfg, RP_BLOCK_LORA, tensor, &off, &bytes, nullptr);
+  return (const float*)((const char*)s.w + off);
+}
+inline float* lgptr(const Slot& s, const rp_layer_cfg& cfg, int tensor) {
+  size_t off = 0, bytes = 0;
+  block_layout(cfg, RP_BLOCK_LORA, tensor, &off, &bytes, nullptr);
+  return (float*)((char*)s.g + off);
+}
+
+// the layer's fp32 adapters -> bf16 operand copies
+rp_status lora_cast(rp_ctx* c, const Slot& ls, const LoraBf16& lw, hipStream_t st) {
+  const Shape& s = c->sh;
+  const rp_layer_cfg& cfg = c->cfg;
+  const size_t r = s.r, rh = r * s.H;
+  char* aqkv = (char*)lw.aqkv;
+  RP_TRY(cast_from_f32(s.dt, lptr(ls, cfg, RP_T_AQ), aqkv, rh, st));
+  RP_TRY(cast_from_f32(s.dt, lptr(ls, cfg, RP_T_AK), aqkv + rh * s.es, rh, st));
+  RP_TRY(cast_from_f32(s.dt, lptr(ls, cfg, RP_T_AV), aqkv + 2 * rh * s.es, rh, st));
+  RP_TRY(cast_from_f32(s.dt, lptr(ls, cfg, RP_T_BQ), lw.bq, (size_t)s.Q * r, st));
+  RP_TRY(cast_from_f32(s.dt, lptr(ls, cfg, RP_T_BK), lw.bk, (size_t)s.KV * r, st));
+  RP_TRY(cast_from_f32(s.dt, lptr(ls, cfg, RP_T_BV), lw.bv, (size_t)s.KV * r, st));
+  RP_TRY(cast_from_f32(s.dt, lptr(ls, cfg, RP_T_AO), lw.ao, r * s.Q, st));
+  RP_TRY(cast_from_f32(s.dt, lptr(ls, cfg, RP_T_BO), lw.bo, (size_t)s.H * r, st));
+  return RP_OK;
+}
+
 GemmDesc mk(int M, int N, int K, const void* A, int64_t lda, bool ak, const void* B, int64_t ldb, bool bk,
             void* C, int64_t ldc, int in_dt, int out_dt, int epi = EPI_STORE) {
   GemmDesc d;
@@ -124,14 +192,34 @@ GemmDesc mk(int M, int N, int K, const void* A, int64_t lda, bool ak, const void
 
 // forward of one layer: x -> y. With y == nullptr (recomputation before the
 // backward) the down projection is skipped: the backward reads the layer's
-// internals, never its output.
-rp_status layer_fwd(rp_ctx* c, const Slot& w, int T, int seq, const void* x, const Acts& A, void* y,
-                    const float2* rope, hipStream_t st) {
+// internals, never its output. LoRA layers add s (x A^T) B^T to the q, k, v
+// and o projections (s = alpha / r), in place on the bf16 projection output.
+rp_status layer_fwd(rp_ctx* c, const LayerBinding& lb, const LoraBf16& lw, int T, int seq, const void* x,
+                    const Acts& A, void* y, const float2* rope, hipStream_t st) {
   const Shape& s = c->sh;
   const int dt = s.dt;
   const rp_layer_cfg& cfg = c->cfg;
+  const Slot& w = lb.base;
+  const int r = s.r;
+  const float ls = r > 0 ? cfg.lora_alpha / (float)r : 0.f;
   RP_TRY(rmsnorm_fwd(dt, x, wptr(w, cfg, RP_T_GAMMA1), A.a, A.rstd1, T, s.H, cfg.rms_eps, st));
   RP_TRY(gemm(mk(T, s.QKV, s.H, A.a, s.H, true, wptr(w, cfg, RP_T_WQKV), s.H, true, A.qkv, s.QKV, dt, dt), st));
+  if (r > 0) {
+    RP_TRY(lora_cast(c, lb.lora, lw, st));
+    // us = s a [A_q; A_k; A_v]^T, then q|k|v += us_x B_x^T
+    GemmDesc gu = mk(T, 3 * r, s.H, A.a, s.H, true, lw.aqkv, s.H, true, A.us_qkv, 3 * r, dt, dt);
+    gu.alpha = ls;
+    RP_TRY(gemm(gu, st));
+    const void* bx[3] = {lw.bq, lw.bk, lw.bv};
+    const int nx[3] = {s.Q, s.KV, s.KV}, cx[3] = {0, s.Q, s.Q + s.KV};
+    for (int xi = 0; xi < 3; ++xi) {
+      char* col = (char*)A.qkv + (size_t)cx[xi] * s.es;
+      GemmDesc g = mk(T, nx[xi], r, (const char*)A.us_qkv + (size_t)xi * r * s.es, 3 * r, true, bx[xi], r, true, col,
+                      s.QKV, dt, dt, EPI_RESID);
+      g.R = col; g.ldr = s.QKV;
+      RP_TRY(gemm(g, st));
+    }
+  }
   RP_TRY(rope_apply(dt, A.qkv, s.QKV, T, seq, s.nq + s.nkv, s.d, rope, false, st));
   AttnDesc ad;
   ad.dt = dt; ad.batch = T / seq; ad.seq = seq; ad.n_q = s.nq; ad.n_kv = s.nkv; ad.d = s.d;
@@ -139,6 +227,15 @@ rp_status layer_fwd(rp_ctx* c, const Slot& w, int T, int seq, const void* x, con
   GemmDesc go = mk(T, s.H, s.Q, A.o, s.Q, true, wptr(w, cfg, RP_T_WO), s.Q, true, A.h1, s.H, dt, dt, EPI_RESID);
   go.R = x; go.ldr = s.H;
   RP_TRY(gemm(go, st));
+  if (r > 0) {
+    // us_o = s o A_o^T ; h1 += us_o B_o^T
+    GemmDesc gu = mk(T, r, s.Q, A.o, s.Q, true, lw.ao, s.Q, true, A.us_o, r, dt, dt);
+    gu.alpha = ls;
+    RP_TRY(gemm(gu, st));
+    GemmDesc g = mk(T, s.H, r, A.us_o, r, true, lw.bo, r, true, A.h1, s.H, dt, dt, EPI_RESID);
+    g.R = A.h1; g.ldr = s.H;
+    RP_TRY(gemm(g, st));
+  }
   RP_TRY(rmsnorm_fwd(dt, A.h1, wptr(w, cfg, RP_T_GAMMA2), A.b, A.rstd2, T, s.H, cfg.rms_eps, st));
   GemmDesc gg = mk(T, 2 * s.F, s.H, A.b, s.H, true, wptr(w, cfg, RP_T_WGU), s.H, true, A.gu, 2 * s.F, dt, dt,
                    EPI_SWIGLU);
@@ -151,46 +248,64 @@ rp_status layer_fwd(rp_ctx* c, const Slot& w, int T, int seq, const void* x, con
   return RP_OK;
 }
 
-// backward of one layer from its forward internals: dy -> dx, weight grads
-rp_status layer_bwd(rp_ctx* c, Slot& w, int T, int seq, const void* x, const Acts& A, const BwdTmp& B,
-                    const void* dy, void* dx, const float2* rope, hipStream_t st) {
+// a weight-gradient product dW = X^T Y (both operands M-major, fp32 out)
+rp_status wgrad(int M, int N, int K, const void* A, int64_t lda, const void* Bm, int64_t ldb, float* C, int64_t ldc,
+                int dt, const BwdTmp& B, float alpha, hipStream_t st) {
+  GemmDesc g = mk(M, N, K, A, lda, false, Bm, ldb, false, C, ldc, dt, RP_DTYPE_F32);
+  g.tr = B.tr;
+  g.tr_bytes = B.tr_bytes;
+  g.alpha = alpha;
+  if (B.splitk) {
+    g.split_k = 0;  // automatic for the skinny adapter products
+    g.partial = B.splitk;
+    g.partial_bytes = B.splitk_bytes;
+  }
+  return gemm(g, st);
+}
+
+// backward of one layer from its forward internals: dy -> dx and the weight
+// gradients (every weight and gain for a full fine-tune; with LoRA the base is
+// frozen and only the adapters get gradients)
+rp_status layer_bwd(rp_ctx* c, LayerBinding& lb, const LoraBf16& lw, int T, int seq, const void* x, const Acts& A,
+                    const BwdTmp& B, const void* dy, void* dx, const float2* rope, hipStream_t st) {
   const Shape& s = c->sh;
   const int dt = s.dt;
   const rp_layer_cfg& cfg = c->cfg;
+  Slot& w = lb.base;
+  const int r = s.r;
+  const bool full = r == 0;  // full fine-tune: base weights are trainable
+  const float ls = r > 0 ? cfg.lora_alpha / (float)r : 0.f;
+  Slot& gs = full ? w : lb.lora;  // the slot whose gradient block this backward writes
   const int F2 = 2 * s.F;
-  RP_TRY(wait_grad_drained(c, w));
+  RP_TRY(wait_grad_drained(c, gs));
+  if (r > 0) RP_TRY(lora_cast(c, lb.lora, lw, st));
   // MLP: dm = dy Wd -> dgu (fused SwiGLU backward)
   GemmDesc g1 = mk(T, s.F, s.H, dy, s.H, true, wptr(w, cfg, RP_T_WD), s.F, false, B.dgu, F2, dt, dt,
                    EPI_SWIGLU_BWD);
   g1.R = A.gu; g1.ldr = F2; g1.tmp = B.dm_tmp;
   RP_TRY(gemm(g1, st));
   // dWd = dy^T m
-  {
-    GemmDesc gw = mk(s.H, s.F, T, dy, s.H, false, A.m, s.F, false, gptr(w, cfg, RP_T_WD), s.F, dt, RP_DTYPE_F32);
-    gw.tr = B.tr;
-    gw.tr_bytes = B.tr_bytes;
-    RP_TRY(gemm(gw, st));
-  }
+  if (full) RP_TRY(wgrad(s.H, s.F, T, dy, s.H, A.m, s.F, gptr(w, cfg, RP_T_WD), s.F, dt, B, 1.f, st));
   // db = dgu Wgu
   RP_TRY(gemm(mk(T, s.H, F2, B.dgu, F2, true, wptr(w, cfg, RP_T_WGU), s.H, false, B.gbuf, s.H, dt, RP_DTYPE_F32),
               st));
   // dWgu = dgu^T b
-  {
-    GemmDesc gw = mk(F2, s.H, T, B.dgu, F2, false, A.b, s.H, false, gptr(w, cfg, RP_T_WGU), s.H, dt, RP_DTYPE_F32);
-    gw.tr = B.tr;
-    gw.tr_bytes = B.tr_bytes;
-    RP_TRY(gemm(gw, st));
-  }
+  if (full) RP_TRY(wgrad(F2, s.H, T, B.dgu, F2, A.b, s.H, gptr(w, cfg, RP_T_WGU), s.H, dt, B, 1.f, st));
   // dh1 = dy + RMSNorm2^T db ; dgamma2
   RP_TRY(rmsnorm_bwd(dt, B.gbuf, A.h1, wptr(w, cfg, RP_T_GAMMA2), A.rstd2, dy, dt, B.dh1f, B.dh1,
-                     gptr(w, cfg, RP_T_GAMMA2), B.part, T, s.H, st));
-  // attention output projection
+                     full ? gptr(w, cfg, RP_T_GAMMA2) : nullptr, B.part, T, s.H, st));
+  // attention output projection: dO = dh1 Wo ; dWo = dh1^T o
   RP_TRY(gemm(mk(T, s.Q, s.H, B.dh1, s.H, true, wptr(w, cfg, RP_T_WO), s.Q, false, B.dO, s.Q, dt, dt), st));
-  {
-    GemmDesc gw = mk(s.H, s.Q, T, B.dh1, s.H, false, A.o, s.Q, false, gptr(w, cfg, RP_T_WO), s.Q, dt, RP_DTYPE_F32);
-    gw.tr = B.tr;
-    gw.tr_bytes = B.tr_bytes;
-    RP_TRY(gemm(gw, st));
+  if (full) RP_TRY(wgrad(s.H, s.Q, T, B.dh1, s.H, A.o, s.Q, gptr(w, cfg, RP_T_WO), s.Q, dt, B, 1.f, st));
+  if (r > 0) {
+    const Slot& L = lb.lora;
+    // g_o = dh1 B_o ; dO += s g_o A_o ; dA_o = s g_o^T o ; dB_o = dh1^T us_o
+    RP_TRY(gemm(mk(T, r, s.H, B.dh1, s.H, true, lw.bo, r, false, B.g_o, r, dt, dt), st));
+    GemmDesc g = mk(T, s.Q, r, B.g_o, r, true, lw.ao, s.Q, false, B.dO, s.Q, dt, dt, EPI_RESID);
+    g.R = B.dO; g.ldr = s.Q; g.alpha = ls;
+    RP_TRY(gemm(g, st));
+    RP_TRY(wgrad(r, s.Q, T, B.g_o, r, A.o, s.Q, lgptr(L, cfg, RP_T_AO), s.Q, dt, B, ls, st));
+    RP_TRY(wgrad(s.H, r, T, B.dh1, s.H, A.us_o, r, lgptr(L, cfg, RP_T_BO), r, dt, B, 1.f, st));
   }
   AttnDesc ad;
   ad.dt = dt; ad.batch = T / seq; ad.seq = seq; ad.n_q = s.nq; ad.n_kv = s.nkv; ad.d = s.d;
@@ -199,18 +314,37 @@ rp_status layer_bwd(rp_ctx* c, Slot& w, int T, int seq, const void* x, const Act
   // da = dqkv Wqkv ; dWqkv = dqkv^T a
   RP_TRY(gemm(mk(T, s.H, s.QKV, B.dqkv, s.QKV, true, wptr(w, cfg, RP_T_WQKV), s.H, false, B.gbuf, s.H, dt,
                  RP_DTYPE_F32), st));
-  {
-    GemmDesc gw = mk(s.QKV, s.H, T, B.dqkv, s.QKV, false, A.a, s.H, false, gptr(w, cfg, RP_T_WQKV), s.H, dt,
-                 RP_DTYPE_F32);
-    gw.tr = B.tr;
-    gw.tr_bytes = B.tr_bytes;
-    RP_TRY(gemm(gw, st));
+  if (full) RP_TRY(wgrad(s.QKV, s.H, T, B.dqkv, s.QKV, A.a, s.H, gptr(w, cfg, RP_T_WQKV), s.H, dt, B, 1.f, st));
+  if (r > 0) {
+    const Slot& L = lb.lora;
+    // g_x = d{q,k,v} B_x ; da += s [g_q g_k g_v] [A_q; A_k; A_v] ;
+    // dA_x = s g_x^T a ; dB_x = d{q,k,v}^T us_x
+    const void* bx[3] = {lw.bq, lw.bk, lw.bv};
+    const int nx[3] = {s.Q, s.KV, s.KV}, cx[3] = {0, s.Q, s.Q + s.KV};
+    const int ta[3] = {RP_T_AQ, RP_T_AK, RP_T_AV}, tb[3] = {RP_T_BQ, RP_T_BK, RP_T_BV};
+    for (int xi = 0; xi < 3; ++xi) {
+      const char* dcol = (const char*)B.dqkv + (size_t)cx[xi] * s.es;
+      char* gcol = (char*)B.g_qkv + (size_t)xi * r * s.es;
+      RP_TRY(gemm(mk(T, r, nx[xi], dcol, s.QKV, true, bx[xi], r, false, gcol, 3 * r, dt, dt), st));
+    }
+    GemmDesc g = mk(T, s.H, 3 * r, B.g_qkv, 3 * r, true, lw.aqkv, s.H, false, B.gbuf, s.H, dt, RP_DTYPE_F32);
+    g.accumulate = true;
+    g.alpha = ls;
+    RP_TRY(gemm(g, st));
+    for (int xi = 0; xi < 3; ++xi) {
+      const char* dcol = (const char*)B.dqkv + (size_t)cx[xi] * s.es;
+      const char* gcol = (const char*)B.g_qkv + (size_t)xi * r * s.es;
+      const char* ucol = (const char*)A.us_qkv + (size_t)xi * r * s.es;
+      RP_TRY(wgrad(r, s.H, T, gcol, 3 * r, A.a, s.H, lgptr(L, cfg, ta[xi]), s.H, dt, B, ls, st));
+      RP_TRY(wgrad(nx[xi], r, T, dcol, s.QKV, ucol, 3 * r, lgptr(L, cfg, tb[xi]), r, dt, B, 1.f, st));
+    }
   }
   // dx = dh1 + RMSNorm1^T da ; dgamma1
   RP_TRY(rmsnorm_bwd(dt, B.gbuf, x, wptr(w, cfg, RP_T_GAMMA1), A.rstd1, B.dh1f, RP_DTYPE_F32, nullptr, dx,
-                     gptr(w, cfg, RP_T_GAMMA1), B.part, T, s.H, st));
+                     full ? gptr(w, cfg, RP_T_GAMMA1) : nullptr, B.part, T, s.H, st));
   RP_TRY(mark_consumed(c, w));
-  RP_TRY(mark_grad_ready(c, w));
+  if (r > 0) RP_TRY(mark_consumed(c, lb.lora));
+  RP_TRY(mark_grad_ready(c, gs));
   return RP_OK;
 }
 
@@ -257,8 +391,10 @@ rp_status stage_fwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* x
   std::vector<hipEvent_t> d2h_done(n, nullptr);
   for (int i = 0; i < n; ++i) {
     const int l = l0 + i;
-    Slot& w = c->layers[l].base;
+    LayerBinding& lb = c->layers[l];
+    Slot& w = lb.base;
     RP_TRY(wait_weights(c, w));
+    if (s.r > 0) RP_TRY(wait_weights(c, lb.lora));
     const Acts& A = keep ? L.acts[i] : L.acts[0];
     const void* x = keep ? A.x : (i == 0 ? x_in : L.xb[(i - 1) & 1]);
     void* y = (i == n - 1) ? y_out : (keep ? L.acts[i + 1].x : L.xb[i & 1]);
@@ -274,8 +410,9 @@ rp_status stage_fwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* x
     // the ping-pong buffer written by this layer held the input of layer
     // i - 1, whose checkpoint download must have finished
     if (!keep && ckpt_host && i >= 1 && i != n - 1) RP_HIP(hipStreamWaitEvent(st, d2h_done[i - 1], 0));
-    RP_TRY(layer_fwd(c, w, (int)T, seq, x, A, y, L.rope, st));
+    RP_TRY(layer_fwd(c, lb, L.lw, (int)T, seq, x, A, y, L.rope, st));
     RP_TRY(mark_consumed(c, w));
+    if (s.r > 0) RP_TRY(mark_consumed(c, lb.lora));
   }
   if (keep) {
     c->kept_ws = ws;
@@ -316,8 +453,13 @@ rp_status stage_bwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* c
         RP_CHECK(is_pinned_host(ckpt[i]), RP_ERR_NOT_PINNED, "stage_bwd: checkpoint %d is not pinned", i);
     }
   }
-  for (int l = l0; l < l1; ++l)
-    RP_CHECK(c->layers[l].base.g != nullptr, RP_ERR_INVALID, "stage_bwd: layer %d has no gradient buffer", l);
+  for (int l = l0; l < l1; ++l) {
+    if (s.r > 0)
+      RP_CHECK(c->layers[l].lora.w != nullptr && c->layers[l].lora.g != nullptr, RP_ERR_INVALID,
+               "stage_bwd: layer %d has no LoRA adapter / adapter-gradient buffer", l);
+    else
+      RP_CHECK(c->layers[l].base.g != nullptr, RP_ERR_INVALID, "stage_bwd: layer %d has no gradient buffer", l);
+  }
   hipStream_t st = c->compute;
   if (c->last_act_d2h_valid) RP_HIP(hipStreamWaitEvent(st, c->last_act_d2h, 0));
   RP_TRY(rope_table(L.rope, seq, s.d, c->cfg.rope_base, st));
@@ -336,8 +478,9 @@ rp_status stage_bwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* c
   const void* g_in = dy;
   for (int i = n - 1; i >= 0; --i) {
     const int l = l0 + i;
-    Slot& w = c->layers[l].base;
-    RP_TRY(wait_weights(c, w));
+    LayerBinding& lb = c->layers[l];
+    RP_TRY(wait_weights(c, lb.base));
+    if (s.r > 0) RP_TRY(wait_weights(c, lb.lora));
     const Acts& A = kept ? L.acts[i] : L.acts[0];
     const void* x;
     if (kept) {
@@ -345,11 +488,11 @@ rp_status stage_bwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* c
     } else {
       x = ck_dev ? ckpt[i] : L.bt.ck[i & 1];
       // recompute the forward from the checkpoint (same kernels as the forward)
-      RP_TRY(layer_fwd(c, w, (int)T, seq, x, A, nullptr, L.rope, st));
+      RP_TRY(layer_fwd(c, lb, L.lw, (int)T, seq, x, A, nullptr, L.rope, st));
     }
     // inter-layer gradients alternate gp[0], gp[1]; the stage input's goes to dx
     void* g_out = (i == 0) ? dx : L.bt.gp[(n - 1 - i) & 1];
-    RP_TRY(layer_bwd(c, w, (int)T, seq, x, A, L.bt, g_in, g_out, L.rope, st));
+    RP_TRY(layer_bwd(c, lb, L.lw, (int)T, seq, x, A, L.bt, g_in, g_out, L.rope, st));
     if (!kept && !ck_dev) {
       if (!ck_free[i & 1]) ck_free[i & 1] = c->new_event();
       RP_HIP(hipEventRecord(ck_free[i & 1], st));

@@ -51,15 +51,44 @@ class Worker:
             return host.pin_memory()
         return host.to(self.dev)
 
+    LORA_IDS = (("aq", B.RP_T_AQ), ("bq", B.RP_T_BQ), ("ak", B.RP_T_AK), ("bk", B.RP_T_BK),
+                ("av", B.RP_T_AV), ("bv", B.RP_T_BV), ("ao", B.RP_T_AO), ("bo", B.RP_T_BO))
+
+    def pack_lora(self, lora: Dict[str, torch.Tensor], pinned: bool = False) -> torch.Tensor:
+        """fp32 adapter block (A_q, B_q, ..., B_o at the library's offsets)."""
+        host = torch.zeros(self.ctx.block_bytes(B.RP_BLOCK_LORA), dtype=torch.uint8)
+        self.ctx.pack(B.RP_BLOCK_LORA, {tid: lora[n].float().cpu() for n, tid in self.LORA_IDS}, host)
+        return host.pin_memory() if pinned else host.to(self.dev)
+
     def add_layer(self, layer: int, w: Optional[Dict[str, torch.Tensor]] = None, resident: bool = True,
-                  grads: bool = True, wbuf: Optional[torch.Tensor] = None):
-        """Allocate (and fill, if resident) the layer's device buffers and bind them."""
+                  grads: bool = True, wbuf: Optional[torch.Tensor] = None,
+                  lora: Optional[Dict[str, torch.Tensor]] = None):
+        """Allocate (and fill, if resident) the layer's device buffers and bind them.
+        LoRA contexts freeze the base: no base-gradient block, an adapter block
+        and its fp32 gradient block instead."""
         if wbuf is None:
             wbuf = self.pack_layer(w) if resident else torch.empty(self.w_bytes, dtype=torch.uint8, device=self.dev)
-        gbuf = torch.zeros(self.g_bytes, dtype=torch.uint8, device=self.dev) if grads else None
-        self.ctx.bind_layer(layer, wbuf, gbuf)
-        self.layers[layer] = {"w": wbuf, "g": gbuf}
+        lbuf = lgbuf = gbuf = None
+        if self.cfg.lora_rank > 0:
+            nb = self.ctx.block_bytes(B.RP_BLOCK_LORA)
+            lbuf = self.pack_lora(lora) if lora is not None else torch.zeros(nb, dtype=torch.uint8, device=self.dev)
+            lgbuf = torch.zeros(nb, dtype=torch.uint8, device=self.dev) if grads else None
+        elif grads:
+            gbuf = torch.zeros(self.g_bytes, dtype=torch.uint8, device=self.dev)
+        self.ctx.bind_layer(layer, wbuf, gbuf, lbuf, lgbuf)
+        self.layers[layer] = {"w": wbuf, "g": gbuf, "lora": lbuf, "lora_g": lgbuf}
         return wbuf, gbuf
+
+    def unpack_lora_grads(self, lgbuf: torch.Tensor) -> Dict[str, torch.Tensor]:
+        cfg = self.cfg
+        r, H, Q, KV = cfg.lora_rank, cfg.hidden, cfg.q_dim, cfg.kv_dim
+        shapes = {"aq": (r, H), "bq": (Q, r), "ak": (r, H), "bk": (KV, r), "av": (r, H), "bv": (KV, r),
+                  "ao": (r, Q), "bo": (H, r)}
+        out = {}
+        for n, tid in self.LORA_IDS:
+            off, nb = self.ctx.layout(B.RP_BLOCK_LORA, tid)
+            out[n] = lgbuf[off:off + nb].view(torch.float32).view(*shapes[n])
+        return out
 
     def unpack_grads(self, gbuf: torch.Tensor) -> Dict[str, torch.Tensor]:
         cfg = self.cfg

@@ -190,3 +190,50 @@ def test_recompute_equals_kept_and_split_invariance_bf16(W):
     dx_ref, _ = O.stage_backward_recompute(ck_ref, layers, dy, cfg)
     assert max_rel(y1, y_ref) < GRAD_TOL["bf16"]
     assert max_rel(dx1, dx_ref) < GRAD_TOL["bf16"]
+
+
+@pytest.mark.parametrize("b_zero", [False, True])
+def test_bf16_lora_layer_matches_oracle(W, b_zero):
+    """LoRA r16 alpha32 on q, k, v, o over a frozen bf16 layer (Qwen3-235B
+    attention widths: 64 query / 4 kv heads, hidden 4096; dense MLP here, the
+    MoE MLP has its own test), ragged sequence: output, dx and the eight
+    adapter gradients against the oracle. B = 0 (the initialisation) must give
+    the base output and dA exactly zero."""
+    say("bf16 lora layer", b_zero)
+    cfg = synth.config("qwen3_235b_moe", seq=200, n_experts=0, top_k=0, expert_ffn=0, ffn=1536)
+    lw = synth.layer_weights(cfg, 0, gamma="perturbed")
+    lora = synth.lora_weights(cfg, 0, b_zero=b_zero)
+    x = synth.activation(cfg, "x")
+    dy = synth.activation(cfg, "dy")
+    wk = W(cfg)
+    wk.add_layer(0, lw, lora=lora)
+    T, H = cfg.tokens, cfg.hidden
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+    dx = torch.empty_like(y)
+    from offloaded_pipeline_stage_amd import binding as Bd
+    ws = wk.ctx.workspace(Bd.RP_OP_FUSED, cfg.batch, cfg.seq, 1)
+    wk.ctx.stage_fwd(0, 1, cfg.batch, cfg.seq, x.to(DEV), y, ws, flags=Bd.RP_KEEP_ACTS)
+    wk.ctx.stage_bwd_recompute(0, 1, cfg.batch, cfg.seq, dy.to(DEV), dx, ws, flags=Bd.RP_USE_KEPT_ACTS)
+    wk.ctx.sync()
+    y_ref, _ = O.stage_forward(x, [lw], cfg, loras=[lora])
+    dx_ref, g_ref, _ = O.layer_backward(x, lw, dy, cfg, lora)
+    tol = GRAD_TOL["bf16"]
+    assert max_rel(y, y_ref) < tol
+    assert max_rel(dx, dx_ref) < tol
+    got = wk.unpack_lora_grads(wk.layers[0]["lora_g"])
+    for n, r in g_ref.items():
+        if b_zero and n.startswith("a"):
+            assert torch.count_nonzero(got[n]).item() == 0, n
+            continue
+        e = max_rel(got[n], r)
+        assert e < tol, (n, e)
+    if b_zero:
+        # B = 0: the adapters change nothing, so y equals the base layer's output
+        base_cfg = cfg.with_(lora_rank=0, lora_alpha=0.0)
+        wb = W(base_cfg)
+        wb.add_layer(0, lw)
+        yb = torch.empty_like(y)
+        wsb = wb.ctx.workspace(Bd.RP_OP_STAGE_FWD, cfg.batch, cfg.seq, 1)
+        wb.ctx.stage_fwd(0, 1, cfg.batch, cfg.seq, x.to(DEV), yb, wsb)
+        wb.ctx.sync()
+        assert torch.equal(y, yb)
