@@ -182,11 +182,24 @@ class Context:
         h = _P()
         check(lib().rp_ctx_create(device, C.byref(self._c), C.byref(s), C.byref(h)))
         self.h = h
-        self._keep = []  # tensors the library may still read
+        # every tensor handed to an enqueueing call stays referenced until
+        # sync(): the library reads and writes them asynchronously on its own
+        # streams, so torch must not recycle their memory before then
+        self._keep = []
 
     # -- life cycle
+    def _hold(self, *objs):
+        for o in objs:
+            if o is None:
+                continue
+            if isinstance(o, (list, tuple)):
+                self._hold(*o)
+            elif isinstance(o, torch.Tensor):
+                self._keep.append(o)
+
     def sync(self):
         check(lib().rp_ctx_sync(self.h))
+        self._keep.clear()
 
     def close(self):
         if self.h:
@@ -220,11 +233,15 @@ class Context:
     def bind_layer(self, layer: int, w: torch.Tensor, g: Optional[torch.Tensor] = None,
                    lora: Optional[torch.Tensor] = None, lora_g: Optional[torch.Tensor] = None):
         check(lib().rp_bind_layer(self.h, layer, ptr(w), ptr(g), ptr(lora), ptr(lora_g)))
+        self._bound = getattr(self, "_bound", {})
+        self._bound[("layer", layer)] = (w, g, lora, lora_g)  # bindings live as long as the context
 
     def bind_lmhead(self, vocab: int, shards: Sequence[torch.Tensor], dshards: Optional[Sequence[torch.Tensor]],
                     gamma_f: Optional[torch.Tensor] = None, dgamma_f: Optional[torch.Tensor] = None):
         check(lib().rp_bind_lmhead(self.h, vocab, len(shards), ptr_array(shards),
                                    ptr_array(dshards) if dshards is not None else None, ptr(gamma_f), ptr(dgamma_f)))
+        self._bound = getattr(self, "_bound", {})
+        self._bound["lmhead"] = (list(shards), list(dshards or []), gamma_f, dgamma_f)
 
     def workspace_size(self, op: int, batch: int, seq: int, n_layers: int = 1, flags: int = 0) -> int:
         n = C.c_size_t()
@@ -239,26 +256,32 @@ class Context:
     def stage_fwd(self, l0, l1, batch, seq, x, y, ws, ckpt_host=None, router=None, flags=0):
         check(lib().rp_stage_fwd(self.h, l0, l1, batch, seq, ptr(x), ptr(y), ptr_array(ckpt_host),
                                  ptr_array(router), flags, ptr(ws), ws.numel()))
+        self._hold(x, y, ws, ckpt_host, router)
 
     def stage_bwd_recompute(self, l0, l1, batch, seq, dy, dx, ws, ckpt=None, router=None, flags=0):
         check(lib().rp_stage_bwd_recompute(self.h, l0, l1, batch, seq, ptr_array(ckpt), ptr(dy), ptr(dx),
                                            ptr_array(router), flags, ptr(ws), ws.numel()))
+        self._hold(dy, dx, ws, ckpt, router)
 
     def lmhead_ce_fwd_bwd(self, batch, seq, x, labels, loss, dx, ws):
         check(lib().rp_lmhead_ce_fwd_bwd(self.h, batch, seq, ptr(x), ptr(labels), ptr(loss), ptr(dx), ptr(ws),
                                          ws.numel()))
+        self._hold(x, labels, loss, dx, ws)
 
     def embed_fwd(self, ids, table, x0):
         check(lib().rp_embed_fwd(self.h, ids.numel(), table.shape[0], ptr(ids), ptr(table), ptr(x0)))
+        self._hold(ids, table, x0)
 
     def embed_bwd(self, ids, dx0, dtable):
         check(lib().rp_embed_bwd(self.h, ids.numel(), dtable.shape[0], ptr(ids), ptr(dx0), ptr(dtable)))
+        self._hold(ids, dx0, dtable)
 
     # -- transfers
     def act_copy(self, direction: int, dst: torch.Tensor, src: torch.Tensor, nbytes: Optional[int] = None) -> int:
         t = C.c_int64()
         nb = nbytes if nbytes is not None else src.numel() * src.element_size()
         check(lib().rp_act_copy(self.h, direction, ptr(dst), ptr(src), nb, C.byref(t)))
+        self._hold(dst, src)
         return t.value
 
     def weight_stream_submit(self, items, n_windows: int = 1, max_chunk: int = 0, gate_ticket: int = -1):
@@ -268,6 +291,7 @@ class Context:
             addr = host if isinstance(host, int) else host.data_ptr()
             arr[i] = rp_xfer(kind, tgt, ident, 0, off, nb, addr)
         check(lib().rp_weight_stream_submit(self.h, arr, len(items), n_windows, max_chunk, gate_ticket))
+        self._hold([it[5] for it in items])
 
     # -- kernel trace
     def trace_begin(self, max_launches: int = 100000):
@@ -286,10 +310,13 @@ class Context:
     def op_gemm_bf16(self, M, N, K, A, lda, a_kmajor, B, ldb, b_kmajor, Cm, ldc, out_f32, accumulate=False):
         check(lib().rp_op_gemm_bf16(self.h, M, N, K, ptr(A), lda, int(a_kmajor), ptr(B), ldb, int(b_kmajor),
                                     ptr(Cm), ldc, int(out_f32), int(accumulate)))
+        self._hold(A, B, Cm)
 
     def op_attn_fwd(self, batch, seq, qkv, o, lse):
         check(lib().rp_op_attn_fwd(self.h, batch, seq, ptr(qkv), ptr(o), ptr(lse)))
+        self._hold(qkv, o, lse)
 
     def op_attn_bwd(self, batch, seq, qkv, o, dout, lse, dqkv, ws):
         check(lib().rp_op_attn_bwd(self.h, batch, seq, ptr(qkv), ptr(o), ptr(dout), ptr(lse), ptr(dqkv), ptr(ws),
                                    ws.numel()))
+        self._hold(qkv, o, dout, lse, dqkv, ws)

@@ -130,11 +130,17 @@ rp_status rp_ctx_create(int device, const rp_layer_cfg* cfg, const rp_streams* s
   RP_CHECK(c.n_q > 0 && c.n_kv > 0 && c.n_q % c.n_kv == 0, RP_ERR_UNSUPPORTED,
            "ctx_create: n_q must be a positive multiple of n_kv");
   RP_CHECK(c.head_dim == 64 || c.head_dim == 128, RP_ERR_UNSUPPORTED, "ctx_create: head_dim must be 64 or 128");
-  RP_CHECK(c.n_experts == 0, RP_ERR_UNSUPPORTED, "ctx_create: MoE layers are not implemented in this build");
+  RP_CHECK(c.n_experts == 0 || (c.n_experts <= 256 && c.top_k >= 1 && c.top_k <= 16 && c.top_k <= c.n_experts &&
+                                 c.expert_ffn > 0 && c.expert_ffn % 8 == 0 && c.ffn == 0 &&
+                                 c.dtype == RP_DTYPE_BF16),
+           RP_ERR_UNSUPPORTED,
+           "ctx_create: MoE layers need bf16, up to 256 experts, 1 <= top_k <= 16, expert_ffn a multiple of 8 "
+           "and ffn == 0");
   RP_CHECK(c.lora_rank == 0 || (c.lora_rank > 0 && c.lora_rank % 8 == 0 && c.lora_rank <= 128 &&
                                  c.dtype == RP_DTYPE_BF16),
            RP_ERR_UNSUPPORTED, "ctx_create: LoRA rank must be a multiple of 8 up to 128, with bf16 layers");
-  RP_CHECK(c.ffn > 0 && c.ffn % 8 == 0, RP_ERR_UNSUPPORTED, "ctx_create: ffn must be a positive multiple of 8");
+  RP_CHECK(c.n_experts > 0 || (c.ffn > 0 && c.ffn % 8 == 0), RP_ERR_UNSUPPORTED,
+           "ctx_create: ffn must be a positive multiple of 8");
   RP_CHECK(c.rms_eps > 0.f && c.rope_base > 1.f, RP_ERR_INVALID, "ctx_create: bad rms_eps or rope_base");
   int n_dev = 0;
   RP_HIP(hipGetDeviceCount(&n_dev));

@@ -50,6 +50,14 @@ struct GemmParams {
   float alpha;      // C = alpha * A B^T (+ R) for the store and residual epilogues
   int kc;           // k extent of one split (blockIdx.y); K when not split
   int64_t c_split;  // element stride between the splits' partial outputs
+  // grouped mode (one product per expert over its rows; see GemmGroup)
+  const int* g_tile_e;    // [tiles_m] expert of each 128/256-row tile, -1 = idle
+  const int* g_tile_m0;   // [tiles_m] first row of the tile within its expert
+  const int* g_off;       // [E] first row of each expert
+  const int* g_cnt;       // [E] rows of each expert
+  const int* g_rows;      // gathered A: operand row of each grouped row
+  const float* row_scale; // [rows] per-row factor of the epilogue (or null)
+  int64_t b_stride;       // elements between consecutive experts' B
 };
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 7); }
@@ -93,18 +101,31 @@ template <> struct Lay<false> {
 // threads. SWIGLU: tile row r of wave column w = r / wn_span holds gate row f
 // (first half of the span) or up row F + f (second half), so one lane ends up
 // with the gate and up pre-activations of the same output column.
-template <int R, bool SWIGLU, int NT>
+// Row maps of a K-major operand tile
+enum RowMode {
+  ROWS_CONTIG = 0,  // tile row r is operand row row0 + r
+  ROWS_SWIGLU = 1,  // gate/up interleave (see LoaderK)
+  ROWS_GATHER = 2   // tile row r is operand row rows[row0 + r] (rows past nrows read as zeros)
+};
+
+// K-major operand: element (r, k) at g[r * ld + k]; R rows per tile, NT
+// threads. ROWS_SWIGLU: tile row r of wave column w = r / wn_span holds gate
+// row f (first half of the span) or up row F + f (second half), so one lane
+// ends up with the gate and up pre-activations of the same output column.
+template <int R, int MODE, int NT>
 struct LoaderK {
   static_assert(R * 8 % NT == 0, "tile rows x 8 chunks must split evenly over the threads");
   static constexpr int NCH = R * 8 / NT;
+  static constexpr bool MAPPED = MODE != ROWS_CONTIG;
   u32x4_t reg[NCH];
-  uint32_t voff[SWIGLU ? NCH : 1];
+  uint32_t voff[MAPPED ? NCH : 1];
   uint32_t rstride;    // bytes between this thread's consecutive rows
   int kcol;            // first k of this thread's chunk
-  __device__ __forceinline__ void init(int64_t ld, int row0, int tid, int F, int wn_span) {
+  __device__ __forceinline__ void init(int64_t ld, int row0, int tid, int F, int wn_span, const int* rows = nullptr,
+                                       int nrows = 0) {
     kcol = (tid & 7) * 8;
     rstride = (uint32_t)((NT / 8) * ld * 2);
-    if constexpr (SWIGLU) {
+    if constexpr (MODE == ROWS_SWIGLU) {
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
         const int r = (tid >> 3) + i * (NT / 8);
@@ -115,6 +136,12 @@ struct LoaderK {
         const int grow = (j < half) ? f : F + f;
         voff[i] = (uint32_t)(((int64_t)grow * ld + (tid & 7) * 8) * 2);
       }
+    } else if constexpr (MODE == ROWS_GATHER) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int r = row0 + (tid >> 3) + i * (NT / 8);
+        voff[i] = r < nrows ? (uint32_t)(((int64_t)rows[r] * ld + (tid & 7) * 8) * 2) : OOB_SHIFT;
+      }
     } else {
       voff[0] = (uint32_t)(((int64_t)(row0 + (tid >> 3)) * ld + (tid & 7) * 8) * 2);
     }
@@ -124,7 +151,7 @@ struct LoaderK {
     const uint32_t base = (uint32_t)(k0 * 2) + (k0 + kcol < K ? 0u : OOB_SHIFT);
 #pragma unroll
     for (int i = 0; i < NCH; ++i)
-      reg[i] = bload(rs, base + (SWIGLU ? voff[i] : voff[0] + (uint32_t)i * rstride));
+      reg[i] = bload(rs, base + (MAPPED ? voff[i] : voff[0] + (uint32_t)i * rstride));
   }
   __device__ __forceinline__ void store(char* lds, int tid) {
 #pragma unroll
@@ -192,7 +219,9 @@ struct LoaderM {
 // fragments of k-substep s + 1 are read from LDS while the MFMAs of substep s
 // run, and the loaded registers are written to the other LDS buffer in the
 // middle of the MFMA stream; one barrier per step.
-template <int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool OUT_F32>
+// GRP: 0 = one product; 1 = grouped, A rows contiguous per expert; 2 =
+// grouped, A rows gathered through g_rows.
+template <int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool OUT_F32, int GRP>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(GemmParams p) {
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -222,14 +251,38 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(GemmParams p)
   const int tile_m = first_m + (pid % in_group) % gsize;
   const int tile_n = (pid % in_group) / gsize;
 
-  const int m0 = tile_m * BM;
+  int m0 = tile_m * BM;
   const int n0 = SW ? tile_n * (BN / 2) : tile_n * BN;  // SwiGLU: F-column base
+
+  if constexpr (GRP != 0) {
+    // grouped: this tile covers rows [m0, m0 + BM) of expert e; C, C2, R and
+    // the row factors are shifted to the expert's first row, B to its weights
+    const int e = p.g_tile_e[tile_m];
+    if (e < 0) return;  // idle tile (uniform over the workgroup, before any barrier)
+    const int offe = p.g_off[e];
+    m0 = p.g_tile_m0[tile_m];
+    p.M = p.g_cnt[e];
+    const size_t oes = OUT_F32 ? 4 : 2;
+    p.C = (char*)p.C + (size_t)offe * p.ldc * oes;
+    if (p.C2) p.C2 = (char*)p.C2 + (size_t)offe * p.ldc2 * 2;
+    if (p.R) p.R = (const char*)p.R + (size_t)offe * p.ldr * oes;
+    if (p.row_scale) p.row_scale += offe;
+    p.B += (int64_t)e * p.b_stride;
+    if constexpr (GRP == 1) {
+      p.A += (int64_t)offe * p.lda;
+      p.a_bytes -= (uint32_t)((int64_t)offe * p.lda * 2);
+    } else {
+      p.g_rows += offe;
+    }
+  }
 
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_bytes);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, p.b_bytes);
-  std::conditional_t<AK, LoaderK<BM, false, NT>, LoaderM<BM, NT>> la;
-  std::conditional_t<BKM, LoaderK<BN, SW, NT>, LoaderM<BN, NT>> lb;
-  if constexpr (AK) la.init(p.lda, m0, tid, 0, 1);
+  constexpr int AMODE = GRP == 2 ? ROWS_GATHER : ROWS_CONTIG;
+  std::conditional_t<AK, LoaderK<BM, AMODE, NT>, LoaderM<BM, NT>> la;
+  std::conditional_t<BKM, LoaderK<BN, SW ? ROWS_SWIGLU : ROWS_CONTIG, NT>, LoaderM<BN, NT>> lb;
+  static_assert(GRP != 2 || AK, "gathered rows need a K-major A");
+  if constexpr (AK) la.init(p.lda, m0, tid, 0, 1, p.g_rows, p.M);
   else la.init(p.lda, m0, tid);
   if constexpr (BKM) lb.init(p.ldb, n0, tid, p.F, WN);
   else lb.init(p.ldb, n0, tid);
@@ -338,6 +391,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(GemmParams p)
           const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + lr + (r & 3);
           if (m >= p.M) continue;
           float v = acc[i][j][r] * p.alpha;
+          if (p.row_scale) v *= p.row_scale[m];
           if constexpr (EPI == EPI_SWIGLU_BWD) {
             const bf16* gu = reinterpret_cast<const bf16*>(p.R);
             const float g = to_f(gu[(int64_t)m * p.ldr + n]);
@@ -469,9 +523,9 @@ inline uint64_t operand_bytes(bool kmajor, int64_t rows, int64_t k, int64_t ld) 
   return (uint64_t)(kmajor ? (rows - 1) * ld + k : (k - 1) * ld + rows) * 2;
 }
 
-template <int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool OF32>
+template <int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool OF32, int GRP = 0>
 rp_status launch_mfma(const GemmDesc& d, hipStream_t s) {
-  GemmParams p;
+  GemmParams p{};
   p.M = d.M; p.N = d.N; p.K = d.K;
   p.A = reinterpret_cast<const bf16*>(d.A); p.lda = d.lda;
   p.B = reinterpret_cast<const bf16*>(d.B); p.ldb = d.ldb;
@@ -495,7 +549,20 @@ rp_status launch_mfma(const GemmDesc& d, hipStream_t s) {
   p.F = EPI == EPI_SWIGLU ? d.N / 2 : (EPI == EPI_SWIGLU_BWD ? d.N : 0);
   p.tiles_m = (int)cdiv(d.M, BM);
   p.tiles_n = EPI == EPI_SWIGLU ? (int)cdiv(d.N / 2, BN / 2) : (int)cdiv(d.N, BN);
-  const uint64_t ab = operand_bytes(AK, d.M, d.K, d.lda), bb = operand_bytes(BKM, d.N, d.K, d.ldb);
+  p.row_scale = d.row_scale;
+  uint64_t ab = operand_bytes(AK, d.M, d.K, d.lda), bb = operand_bytes(BKM, d.N, d.K, d.ldb);
+  if constexpr (GRP != 0) {
+    const GemmGroup& g = *d.group;
+    p.tiles_m = g.max_tiles_m;
+    p.g_tile_e = g.tile_e;
+    p.g_tile_m0 = g.tile_m0;
+    p.g_off = g.off;
+    p.g_cnt = g.cnt;
+    p.g_rows = g.rows;
+    p.b_stride = g.b_stride;
+    ab = operand_bytes(AK, g.a_rows, d.K, d.lda);  // the whole operand: rows are per expert
+    // d.N x d.K is one expert's B
+  }
   RP_CHECK(ab < (1ull << 31) && bb < (1ull << 31), RP_ERR_UNSUPPORTED,
            "gemm(bf16): each operand must span less than 2 GiB");
   p.a_bytes = (uint32_t)ab;
@@ -503,16 +570,17 @@ rp_status launch_mfma(const GemmDesc& d, hipStream_t s) {
   const size_t lds = 2 * ((size_t)BM * (AK ? 144 : 128) + (size_t)BN * (BKM ? 144 : 128));
   static bool attr_set = false;  // one instantiation per template: set once
   if (!attr_set) {
-    RP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_mfma_kernel<BM, BN, WGM, WGN, AK, BKM, EPI, OF32>),
+    RP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_mfma_kernel<BM, BN, WGM, WGN, AK, BKM, EPI, OF32, GRP>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
     attr_set = true;
   }
   const int64_t nt = (int64_t)p.tiles_m * p.tiles_n;
   char name[96];
-  snprintf(name, sizeof(name), "gemm_mfma_kernel<%d, %d, %d, %d, %d, %d, %d, %d>", BM, BN, WGM, WGN, (int)AK, (int)BKM,
-           EPI, (int)OF32);
+  snprintf(name, sizeof(name), "gemm_mfma_kernel<%d, %d, %d, %d, %d, %d, %d, %d, %d>", BM, BN, WGM, WGN, (int)AK,
+           (int)BKM, EPI, (int)OF32, GRP);
+  // grouped products: d.M is the total of the experts' rows
   TraceScope ts(s, name, 2.0 * d.M * d.N * d.K, 0.0);
-  RP_LAUNCH((gemm_mfma_kernel<BM, BN, WGM, WGN, AK, BKM, EPI, OF32>), dim3((unsigned)nt, (unsigned)splits),
+  RP_LAUNCH((gemm_mfma_kernel<BM, BN, WGM, WGN, AK, BKM, EPI, OF32, GRP>), dim3((unsigned)nt, (unsigned)splits),
             dim3(64 * WGM * WGN), lds, s, p);
   if (splits > 1) return splitk_reduce(d.partial, splits, d.M, d.N, reinterpret_cast<float*>(d.C), d.ldc, d.accumulate, s);
   return RP_OK;
@@ -549,14 +617,19 @@ rp_status dispatch_epi(const GemmDesc& d, hipStream_t s) {
 
 }  // namespace
 
+// both operands M-major: K is a row index of each, any value works
+#define K_MULT_FREE(d) (!(d).a_kmajor && !(d).b_kmajor)
+
 rp_status gemm_validate(const GemmDesc& d) {
   RP_CHECK(d.M >= 0 && d.N >= 0 && d.K >= 0, RP_ERR_INVALID, "gemm: negative size");
   RP_CHECK(d.A && d.B && d.C, RP_ERR_INVALID, "gemm: null operand");
   RP_CHECK(d.lda >= (d.a_kmajor ? d.K : d.M) && d.ldb >= (d.b_kmajor ? d.K : d.N), RP_ERR_INVALID,
            "gemm: leading dimension too small");
   if (d.in_dtype == RP_DTYPE_BF16 && !d.force_simple) {
-    RP_CHECK(d.K % 8 == 0 && d.lda % 8 == 0 && d.ldb % 8 == 0, RP_ERR_UNSUPPORTED,
-             "gemm(bf16): K and leading dimensions must be multiples of 8");
+    // 16-byte chunks run along K for K-major operands (a chunk may not
+    // straddle K) and along M / N for M-major ones (rows start 16-byte aligned)
+    RP_CHECK((K_MULT_FREE(d) || d.K % 8 == 0) && d.lda % 8 == 0 && d.ldb % 8 == 0, RP_ERR_UNSUPPORTED,
+             "gemm(bf16): leading dimensions, and K when an operand is K-major, must be multiples of 8");
     RP_CHECK(((uintptr_t)d.A & 15) == 0 && ((uintptr_t)d.B & 15) == 0, RP_ERR_INVALID,
              "gemm(bf16): operands must be 16-byte aligned");
     if (d.epi == EPI_SWIGLU) RP_CHECK(d.N % 2 == 0, RP_ERR_INVALID, "swiglu: N must be even");
@@ -609,7 +682,7 @@ rp_status gemm(const GemmDesc& dd, hipStream_t s) {
     // both operands M-major (weight gradients): transpose both through the
     // scratch and run the K-major kernel, which is far faster than
     // transposing tiles in registers on the way to LDS
-    if (d.tr && d.tr_bytes >= gemm_tr_bytes(d.M, d.N, d.K) && d.M % 8 == 0 && d.N % 8 == 0) {
+    if (d.tr && d.tr_bytes >= gemm_tr_bytes(d.M, d.N, d.K) && d.M % 8 == 0 && d.N % 8 == 0 && d.K % 8 == 0) {
       GemmDesc e = d;
       char* ta = reinterpret_cast<char*>(d.tr);
       char* tb = ta + align_up((size_t)d.M * d.K * 2, 256);
@@ -623,6 +696,28 @@ rp_status gemm(const GemmDesc& dd, hipStream_t s) {
     return dispatch_epi<256, 256, 2, 2>(d, s);
   }
   return dispatch_epi<256, 256, 2, 4>(d, s);
+}
+
+rp_status gemm_grouped(const GemmDesc& d, hipStream_t s) {
+  RP_CHECK(d.group && d.in_dtype == RP_DTYPE_BF16 && d.out_dtype == RP_DTYPE_BF16 && d.split_k == 1 && !d.accumulate,
+           RP_ERR_INVALID, "gemm_grouped: bf16 in/out, no split, no accumulation");
+  RP_CHECK(d.K % 8 == 0 && d.lda % 8 == 0 && d.ldb % 8 == 0 && ((uintptr_t)d.A & 15) == 0 &&
+               ((uintptr_t)d.B & 15) == 0 && d.a_kmajor && d.A && d.B && d.C,
+           RP_ERR_INVALID, "gemm_grouped: K-major A, aligned operands");
+  if (d.M == 0 || d.N == 0 || d.group->max_tiles_m == 0) return RP_OK;
+  const bool gather = d.group->rows != nullptr;
+  if (d.epi == EPI_SWIGLU && d.b_kmajor)
+    return gather ? launch_mfma<GROUP_BM, 256, 2, 4, true, true, EPI_SWIGLU, false, 2>(d, s)
+                  : launch_mfma<GROUP_BM, 256, 2, 4, true, true, EPI_SWIGLU, false, 1>(d, s);
+  if (d.epi == EPI_STORE && d.b_kmajor && !gather)
+    return launch_mfma<GROUP_BM, 256, 2, 4, true, true, EPI_STORE, false, 1>(d, s);
+  if (d.epi == EPI_SWIGLU_BWD && !d.b_kmajor && gather)
+    return launch_mfma<GROUP_BM, 256, 2, 4, true, false, EPI_SWIGLU_BWD, false, 2>(d, s);
+  if (d.epi == EPI_STORE && !d.b_kmajor && !gather)
+    return launch_mfma<GROUP_BM, 256, 2, 4, true, false, EPI_STORE, false, 1>(d, s);
+  set_error("gemm_grouped: unsupported combination (epilogue %d, B %s, A %s)", d.epi,
+            d.b_kmajor ? "K-major" : "M-major", gather ? "gathered" : "contiguous");
+  return RP_ERR_UNSUPPORTED;
 }
 
 size_t splitk_bytes(int64_t M, int64_t N, int64_t K, int split_k) {

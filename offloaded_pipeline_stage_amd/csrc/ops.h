@@ -16,6 +16,21 @@ enum Epi {
   EPI_SWIGLU_BWD = 3  // acc = dm [M, F]; R = gu [M, 2F]; C = dgu [M, 2F]
 };
 
+// Grouped product: one GEMM per expert over that expert's rows, in one launch.
+// Row tiles of GROUP_BM rows are mapped to (expert, first row) by tile_e /
+// tile_m0 (built on the device from the routing); idle tiles have expert -1.
+constexpr int GROUP_BM = 256;
+struct GemmGroup {
+  const int* tile_e = nullptr;
+  const int* tile_m0 = nullptr;
+  const int* off = nullptr;     // [E] first grouped row of each expert
+  const int* cnt = nullptr;     // [E] rows of each expert
+  const int* rows = nullptr;    // gathered A: operand row of each grouped row (null: A is grouped rows)
+  int max_tiles_m = 0;          // size of the tile map
+  int64_t a_rows = 0;           // rows of the A operand buffer
+  int64_t b_stride = 0;         // elements between consecutive experts' B (N x K each)
+};
+
 struct GemmDesc {
   int M = 0, N = 0, K = 0;
   const void* A = nullptr; int64_t lda = 0; bool a_kmajor = true;
@@ -40,7 +55,15 @@ struct GemmDesc {
   // split_k == 0: chosen from the tile count when `partial` is given
   int split_k = 1;
   float* partial = nullptr; size_t partial_bytes = 0;
+  const float* row_scale = nullptr;  // per-row factor applied in the epilogue (grouped rows)
+  const GemmGroup* group = nullptr;  // gemm_grouped only
 };
+
+// grouped product over experts (see GemmGroup): M = total grouped rows (for
+// accounting), N x K = one expert's B; C (and C2 / R) have one row per grouped
+// row. Supported: SwiGLU and plain-store forwards (K-major B), SwiGLU-backward
+// and plain-store input gradients (M-major B).
+rp_status gemm_grouped(const GemmDesc& d, hipStream_t s);
 
 size_t splitk_bytes(int64_t M, int64_t N, int64_t K, int split_k);
 // C[m, n] (+)= sum over s < splits of part[s][m][n], in split order
@@ -112,6 +135,31 @@ rp_status ce_combine(int T, int n_shards, const float2* parts, const float* zlab
 rp_status ce_grad(int dt, const float* logits, int64_t ld, int T, int Vs, int vlo,
                   const int32_t* labels, int vocab, const float* lse, const float* inv_n,
                   void* dz, int64_t ldz, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// mixture of experts
+// ---------------------------------------------------------------------------
+// routing state of one MoE layer call (device buffers carved by the caller)
+struct MoeRouting {
+  int* idx = nullptr;       // [T, k] selected experts, descending logit
+  float* wgt = nullptr;     // [T, k] softmax weights over the selected
+  int* cnt = nullptr;       // [E] rows per expert
+  int* off = nullptr;       // [E + 1] first grouped row per expert
+  int* tile_e = nullptr;    // [max_tiles] tile map of the grouped products
+  int* tile_m0 = nullptr;
+  int max_tiles = 0;
+  int* perm_row = nullptr;  // [T k] token of each grouped row
+  float* perm_w = nullptr;  // [T k] routing weight of each grouped row
+  int* inv = nullptr;       // [T k] grouped row of each (token, slot)
+};
+int moe_max_tiles(int64_t T, int k, int E);
+// top-k routing, counting sort by expert, tile map
+rp_status moe_route(const MoeRouting& m, const float* logits, int T, int E, int k, hipStream_t s);
+// y = h1 + sum_s w * ye[row(t, s)]
+rp_status moe_combine(const void* h1, const void* ye, const MoeRouting& m, int T, int k, int H, void* y,
+                      hipStream_t s);
+// db (fp32) = sum_s dbe[row(t, s)]
+rp_status moe_uncombine(const void* dbe, const MoeRouting& m, int T, int k, int H, float* db, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // misc

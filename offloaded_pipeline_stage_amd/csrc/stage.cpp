@@ -23,8 +23,9 @@ struct Acts {
   void* h1 = nullptr;     // x + o Wo^T [T, H]
   float* rstd2 = nullptr; // [T]
   void* b = nullptr;      // RMSNorm2(h1) [T, H]
-  void* gu = nullptr;     // gate/up pre-activations [T, 2F]
-  void* m = nullptr;      // silu(g) * u [T, F]
+  void* gu = nullptr;     // gate/up pre-activations [T, 2F] (MoE: [T k, 2Fe] grouped rows)
+  void* m = nullptr;      // silu(g) * u [T, F] (MoE: [T k, Fe])
+  MoeRouting mr;          // MoE routing of this layer's tokens
   // LoRA: s * (a A^T) for q|k|v [T, 3r] and s * (o Ao^T) [T, r], s = alpha / r
   void* us_qkv = nullptr;
   void* us_o = nullptr;
@@ -56,6 +57,7 @@ struct BwdTmp {
   void* g_o = nullptr;     // LoRA: dh1 B_o [T, r]
   float* splitk = nullptr; // split-K partials of the adapter-gradient products
   size_t splitk_bytes = 0;
+  void* dbe = nullptr;     // MoE: input gradients per grouped row [T k, H]
   void* gp[2] = {nullptr, nullptr};  // inter-layer gradients
   void* ck[2] = {nullptr, nullptr};  // uploaded checkpoints
 };
@@ -63,6 +65,7 @@ struct BwdTmp {
 struct Layout {
   float2* rope = nullptr;
   LoraBf16 lw;
+  void* ye = nullptr;     // MoE: expert outputs [T k, H] (grouped rows)
   std::vector<Acts> acts;
   void* xb[2] = {nullptr, nullptr};
   BwdTmp bt;
@@ -78,8 +81,23 @@ void carve_acts(Bump& bp, const Shape& s, int64_t T, Acts& A) {
   A.h1 = bp.take(T * s.H * s.es);
   A.rstd2 = bp.take<float>(T * 4);
   A.b = bp.take(T * s.H * s.es);
-  A.gu = bp.take(T * 2 * s.F * s.es);
-  A.m = bp.take(T * s.F * s.es);
+  const int64_t rows = s.E > 0 ? T * s.topk : T;  // MLP rows (grouped rows for MoE)
+  const int64_t F = s.E > 0 ? s.Fe : s.F;
+  A.gu = bp.take(rows * 2 * F * s.es);
+  A.m = bp.take(rows * F * s.es);
+  if (s.E > 0) {
+    MoeRouting& m = A.mr;
+    m.max_tiles = moe_max_tiles(T, s.topk, s.E);
+    m.idx = bp.take<int>(rows * 4);
+    m.wgt = bp.take<float>(rows * 4);
+    m.cnt = bp.take<int>((size_t)s.E * 4);
+    m.off = bp.take<int>((size_t)(s.E + 1) * 4);
+    m.tile_e = bp.take<int>((size_t)m.max_tiles * 4);
+    m.tile_m0 = bp.take<int>((size_t)m.max_tiles * 4);
+    m.perm_row = bp.take<int>(rows * 4);
+    m.perm_w = bp.take<float>(rows * 4);
+    m.inv = bp.take<int>(rows * 4);
+  }
   if (s.r > 0) {
     A.us_qkv = bp.take(T * 3 * s.r * s.es);
     A.us_o = bp.take(T * s.r * s.es);
@@ -104,13 +122,19 @@ void carve(Bump& bp, const Shape& s, int64_t T, int seq, int n_layers, bool keep
   }
   L.acts.assign(keep ? n_layers : 1, Acts{});
   for (auto& a : L.acts) carve_acts(bp, s, T, a);
+  if (s.E > 0) L.ye = bp.take(T * s.topk * s.H * s.es);
   if (fwd_pp) {
     L.xb[0] = bp.take(T * s.H * s.es);
     L.xb[1] = bp.take(T * s.H * s.es);
   }
   if (bwd) {
     BwdTmp& b = L.bt;
-    b.dgu = bp.take(T * 2 * s.F * s.es);
+    if (s.E > 0) {
+      b.dgu = bp.take(T * s.topk * 2 * s.Fe * s.es);
+      b.dbe = bp.take(T * s.topk * s.H * s.es);
+    } else {
+      b.dgu = bp.take(T * 2 * s.F * s.es);
+    }
     b.gbuf = bp.take<float>(T * s.H * 4);
     b.dh1f = bp.take<float>(T * s.H * 4);
     b.dh1 = bp.take(T * s.H * s.es);
@@ -194,8 +218,8 @@ GemmDesc mk(int M, int N, int K, const void* A, int64_t lda, bool ak, const void
 // backward) the down projection is skipped: the backward reads the layer's
 // internals, never its output. LoRA layers add s (x A^T) B^T to the q, k, v
 // and o projections (s = alpha / r), in place on the bf16 projection output.
-rp_status layer_fwd(rp_ctx* c, const LayerBinding& lb, const LoraBf16& lw, int T, int seq, const void* x,
-                    const Acts& A, void* y, const float2* rope, hipStream_t st) {
+rp_status layer_fwd(rp_ctx* c, const LayerBinding& lb, const LoraBf16& lw, void* ye, const float* router, int T,
+                    int seq, const void* x, const Acts& A, void* y, const float2* rope, hipStream_t st) {
   const Shape& s = c->sh;
   const int dt = s.dt;
   const rp_layer_cfg& cfg = c->cfg;
@@ -237,6 +261,33 @@ rp_status layer_fwd(rp_ctx* c, const LayerBinding& lb, const LoraBf16& lw, int T
     RP_TRY(gemm(g, st));
   }
   RP_TRY(rmsnorm_fwd(dt, A.h1, wptr(w, cfg, RP_T_GAMMA2), A.b, A.rstd2, T, s.H, cfg.rms_eps, st));
+  if (s.E > 0) {
+    // MoE: route, then per expert gu = b_e W_gu,e^T with the SwiGLU epilogue
+    // (rows of b gathered through the routing), ye = m_e W_d,e^T, and
+    // y = h1 + sum_s w_s ye[row(t, s)]
+    const int k = s.topk, Fe = s.Fe;
+    RP_TRY(moe_route(A.mr, router, T, s.E, k, st));
+    GemmGroup grp;
+    grp.tile_e = A.mr.tile_e; grp.tile_m0 = A.mr.tile_m0; grp.off = A.mr.off; grp.cnt = A.mr.cnt;
+    grp.max_tiles_m = A.mr.max_tiles;
+    grp.rows = A.mr.perm_row;
+    grp.a_rows = T;
+    grp.b_stride = (int64_t)2 * Fe * s.H;
+    GemmDesc gg = mk(T * k, 2 * Fe, s.H, A.b, s.H, true, wptr(w, cfg, RP_T_WGU), s.H, true, A.gu, 2 * Fe, dt, dt,
+                     EPI_SWIGLU);
+    gg.C2 = A.m; gg.ldc2 = Fe;
+    gg.group = &grp;
+    RP_TRY(gemm_grouped(gg, st));
+    if (y == nullptr) return RP_OK;
+    GemmGroup g2 = grp;
+    g2.rows = nullptr;
+    g2.a_rows = (int64_t)T * k;
+    g2.b_stride = (int64_t)s.H * Fe;
+    GemmDesc gd = mk(T * k, s.H, Fe, A.m, Fe, true, wptr(w, cfg, RP_T_WD), Fe, true, ye, s.H, dt, dt);
+    gd.group = &g2;
+    RP_TRY(gemm_grouped(gd, st));
+    return moe_combine(A.h1, ye, A.mr, T, k, s.H, y, st);
+  }
   GemmDesc gg = mk(T, 2 * s.F, s.H, A.b, s.H, true, wptr(w, cfg, RP_T_WGU), s.H, true, A.gu, 2 * s.F, dt, dt,
                    EPI_SWIGLU);
   gg.C2 = A.m; gg.ldc2 = s.F;
@@ -279,18 +330,45 @@ rp_status layer_bwd(rp_ctx* c, LayerBinding& lb, const LoraBf16& lw, int T, int 
   const int F2 = 2 * s.F;
   RP_TRY(wait_grad_drained(c, gs));
   if (r > 0) RP_TRY(lora_cast(c, lb.lora, lw, st));
-  // MLP: dm = dy Wd -> dgu (fused SwiGLU backward)
-  GemmDesc g1 = mk(T, s.F, s.H, dy, s.H, true, wptr(w, cfg, RP_T_WD), s.F, false, B.dgu, F2, dt, dt,
-                   EPI_SWIGLU_BWD);
-  g1.R = A.gu; g1.ldr = F2; g1.tmp = B.dm_tmp;
-  RP_TRY(gemm(g1, st));
-  // dWd = dy^T m
-  if (full) RP_TRY(wgrad(s.H, s.F, T, dy, s.H, A.m, s.F, gptr(w, cfg, RP_T_WD), s.F, dt, B, 1.f, st));
-  // db = dgu Wgu
-  RP_TRY(gemm(mk(T, s.H, F2, B.dgu, F2, true, wptr(w, cfg, RP_T_WGU), s.H, false, B.gbuf, s.H, dt, RP_DTYPE_F32),
-              st));
-  // dWgu = dgu^T b
-  if (full) RP_TRY(wgrad(F2, s.H, T, B.dgu, F2, A.b, s.H, gptr(w, cfg, RP_T_WGU), s.H, dt, B, 1.f, st));
+  if (s.E > 0) {
+    // MoE with frozen experts: input gradient only. Per expert
+    // dgu = SwiGLU'(w_s dy_e W_d,e) (routing weight as a row factor, rows of
+    // dy gathered through the routing), dbe = dgu W_gu,e, db = sum_s dbe.
+    const int k = s.topk, Fe = s.Fe;
+    GemmGroup grp;
+    grp.tile_e = A.mr.tile_e; grp.tile_m0 = A.mr.tile_m0; grp.off = A.mr.off; grp.cnt = A.mr.cnt;
+    grp.max_tiles_m = A.mr.max_tiles;
+    grp.rows = A.mr.perm_row;
+    grp.a_rows = T;
+    grp.b_stride = (int64_t)s.H * Fe;
+    GemmDesc g1 = mk(T * k, Fe, s.H, dy, s.H, true, wptr(w, cfg, RP_T_WD), Fe, false, B.dgu, 2 * Fe, dt, dt,
+                     EPI_SWIGLU_BWD);
+    g1.R = A.gu; g1.ldr = 2 * Fe;
+    g1.row_scale = A.mr.perm_w;
+    g1.group = &grp;
+    RP_TRY(gemm_grouped(g1, st));
+    GemmGroup g2 = grp;
+    g2.rows = nullptr;
+    g2.a_rows = (int64_t)T * k;
+    g2.b_stride = (int64_t)2 * Fe * s.H;
+    GemmDesc gb = mk(T * k, s.H, 2 * Fe, B.dgu, 2 * Fe, true, wptr(w, cfg, RP_T_WGU), s.H, false, B.dbe, s.H, dt, dt);
+    gb.group = &g2;
+    RP_TRY(gemm_grouped(gb, st));
+    RP_TRY(moe_uncombine(B.dbe, A.mr, T, k, s.H, B.gbuf, st));
+  } else {
+    // MLP: dm = dy Wd -> dgu (fused SwiGLU backward)
+    GemmDesc g1 = mk(T, s.F, s.H, dy, s.H, true, wptr(w, cfg, RP_T_WD), s.F, false, B.dgu, F2, dt, dt,
+                     EPI_SWIGLU_BWD);
+    g1.R = A.gu; g1.ldr = F2; g1.tmp = B.dm_tmp;
+    RP_TRY(gemm(g1, st));
+    // dWd = dy^T m
+    if (full) RP_TRY(wgrad(s.H, s.F, T, dy, s.H, A.m, s.F, gptr(w, cfg, RP_T_WD), s.F, dt, B, 1.f, st));
+    // db = dgu Wgu
+    RP_TRY(gemm(mk(T, s.H, F2, B.dgu, F2, true, wptr(w, cfg, RP_T_WGU), s.H, false, B.gbuf, s.H, dt, RP_DTYPE_F32),
+                st));
+    // dWgu = dgu^T b
+    if (full) RP_TRY(wgrad(F2, s.H, T, B.dgu, F2, A.b, s.H, gptr(w, cfg, RP_T_WGU), s.H, dt, B, 1.f, st));
+  }
   // dh1 = dy + RMSNorm2^T db ; dgamma2
   RP_TRY(rmsnorm_bwd(dt, B.gbuf, A.h1, wptr(w, cfg, RP_T_GAMMA2), A.rstd2, dy, dt, B.dh1f, B.dh1,
                      full ? gptr(w, cfg, RP_T_GAMMA2) : nullptr, B.part, T, s.H, st));
@@ -363,7 +441,6 @@ rp_status check_range(rp_ctx* c, int l0, int l1, int batch, int seq) {
 rp_status stage_fwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* x_in, void* y_out,
                     void* const* ckpt_host, const float* const* router, int flags, void* ws, size_t ws_bytes,
                     size_t* need) {
-  (void)router;
   const Shape& s = c->sh;
   const bool keep = flags & RP_KEEP_ACTS;
   const int n = l1 - l0;
@@ -378,6 +455,10 @@ rp_status stage_fwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* x
   RP_TRY(check_range(c, l0, l1, batch, seq));
   RP_CHECK(x_in && y_out && ws, RP_ERR_INVALID, "stage_fwd: null pointer");
   RP_CHECK(x_in != y_out, RP_ERR_INVALID, "stage_fwd: y_out may not alias x_in");
+  if (s.E > 0) {
+    RP_CHECK(router != nullptr, RP_ERR_INVALID, "stage_fwd: MoE layers need router logits");
+    for (int i = 0; i < n; ++i) RP_CHECK(router[i] != nullptr, RP_ERR_INVALID, "stage_fwd: router %d is null", i);
+  }
   RP_CHECK(ws_bytes >= bp.off, RP_ERR_WORKSPACE, "stage_fwd: workspace %zu < %zu bytes", ws_bytes, bp.off);
   if (ckpt_host)
     for (int i = 0; i < n; ++i)
@@ -410,7 +491,7 @@ rp_status stage_fwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* x
     // the ping-pong buffer written by this layer held the input of layer
     // i - 1, whose checkpoint download must have finished
     if (!keep && ckpt_host && i >= 1 && i != n - 1) RP_HIP(hipStreamWaitEvent(st, d2h_done[i - 1], 0));
-    RP_TRY(layer_fwd(c, lb, L.lw, (int)T, seq, x, A, y, L.rope, st));
+    RP_TRY(layer_fwd(c, lb, L.lw, L.ye, s.E > 0 ? router[i] : nullptr, (int)T, seq, x, A, y, L.rope, st));
     RP_TRY(mark_consumed(c, w));
     if (s.r > 0) RP_TRY(mark_consumed(c, lb.lora));
   }
@@ -425,7 +506,6 @@ rp_status stage_fwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* x
 
 rp_status stage_bwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* const* ckpt, const void* dy,
                     void* dx, const float* const* router, int flags, void* ws, size_t ws_bytes, size_t* need) {
-  (void)router;
   const Shape& s = c->sh;
   const bool kept = flags & RP_USE_KEPT_ACTS;
   const bool ck_dev = flags & RP_CKPT_DEVICE;
@@ -440,6 +520,12 @@ rp_status stage_bwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* c
   }
   RP_TRY(check_range(c, l0, l1, batch, seq));
   RP_CHECK(dy && dx && ws, RP_ERR_INVALID, "stage_bwd: null pointer");
+  RP_CHECK(s.E == 0 || s.r > 0, RP_ERR_UNSUPPORTED,
+           "stage_bwd: MoE expert weights are frozen here; MoE layers train through LoRA adapters");
+  if (s.E > 0 && !kept) {
+    RP_CHECK(router != nullptr, RP_ERR_INVALID, "stage_bwd: recomputing MoE layers needs router logits");
+    for (int i = 0; i < n; ++i) RP_CHECK(router[i] != nullptr, RP_ERR_INVALID, "stage_bwd: router %d is null", i);
+  }
   RP_CHECK(ws_bytes >= bp.off, RP_ERR_WORKSPACE, "stage_bwd: workspace %zu < %zu bytes", ws_bytes, bp.off);
   if (kept) {
     RP_CHECK(c->kept_ws == ws && c->kept_l0 == l0 && c->kept_l1 == l1 && c->kept_batch == batch &&
@@ -488,7 +574,7 @@ rp_status stage_bwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* c
     } else {
       x = ck_dev ? ckpt[i] : L.bt.ck[i & 1];
       // recompute the forward from the checkpoint (same kernels as the forward)
-      RP_TRY(layer_fwd(c, lb, L.lw, (int)T, seq, x, A, nullptr, L.rope, st));
+      RP_TRY(layer_fwd(c, lb, L.lw, L.ye, s.E > 0 ? router[i] : nullptr, (int)T, seq, x, A, nullptr, L.rope, st));
     }
     // inter-layer gradients alternate gp[0], gp[1]; the stage input's goes to dx
     void* g_out = (i == 0) ? dx : L.bt.gp[(n - 1 - i) & 1];

@@ -77,6 +77,9 @@ class Worker:
             gbuf = torch.zeros(self.g_bytes, dtype=torch.uint8, device=self.dev)
         self.ctx.bind_layer(layer, wbuf, gbuf, lbuf, lgbuf)
         self.layers[layer] = {"w": wbuf, "g": gbuf, "lora": lbuf, "lora_g": lgbuf}
+        # torch filled / copied these on its own stream; the library's streams
+        # must not see them before that work is done
+        torch.cuda.current_stream(self.dev).synchronize()
         return wbuf, gbuf
 
     def unpack_lora_grads(self, lgbuf: torch.Tensor) -> Dict[str, torch.Tensor]:
@@ -132,6 +135,7 @@ class Worker:
             dgf = torch.zeros(H, dtype=torch.float32, device=self.dev)
         self.ctx.bind_lmhead(self.cfg.vocab, shards, dshards, gf, dgf)
         self.head = {"w": shards, "dw": dshards, "gamma_f": gf, "dgamma_f": dgf}
+        torch.cuda.current_stream(self.dev).synchronize()
         return self.head
 
     # ------------------------------------------------------------------ calls
