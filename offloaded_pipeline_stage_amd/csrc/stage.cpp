@@ -558,6 +558,9 @@ rp_status stage_bwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* c
     int64_t tk;
     return act_copy(c, RP_H2D, L.bt.ck[i & 1], ckpt[i], xbytes, &tk);
   };
+  // the checkpoints may have been written to host memory by this context's
+  // earlier downloads (the forward stage): uploads start after those
+  if (!kept && !ck_dev && c->last_act_d2h_valid) RP_HIP(hipStreamWaitEvent(c->act_h2d, c->last_act_d2h, 0));
   // act_copy(H2D) makes the compute stream wait at issue time, so the
   // prefetch of layer i - 1 is issued after layer i's compute is enqueued.
   if (!kept && !ck_dev) RP_TRY(upload(n - 1));

@@ -151,13 +151,10 @@ def _positions(batch: int, seq: int) -> Tensor:
     return torch.arange(seq).repeat(batch)
 
 
-def layer_forward(x: Tensor, w: Dict[str, Tensor], cfg, lora: Optional[Dict[str, Tensor]] = None,
-                  router: Optional[Tensor] = None, keep: bool = False):
-    """One pre-norm decoder layer, x [T, H] -> y [T, H].
-
-    With keep=True also returns the internals (normed inputs, rotated q/k, v,
-    attention output, residual h1, MLP input).
-    """
+def attention_block(x: Tensor, w: Dict[str, Tensor], cfg, lora: Optional[Dict[str, Tensor]] = None):
+    """The attention half of the layer and the MLP's input: returns
+    (a, q, k, v, o, h1, b) with a = RMSNorm1(x), rotated q/k, v, attention
+    output o, h1 = x + o Wo^T (+ LoRA) and b = RMSNorm2(h1)."""
     T, H = x.shape
     nq, nkv, d = cfg.n_q, cfg.n_kv, cfg.head_dim
     pos = _positions(cfg.batch, T // cfg.batch)
@@ -180,6 +177,19 @@ def layer_forward(x: Tensor, w: Dict[str, Tensor], cfg, lora: Optional[Dict[str,
         proj = proj + lora_delta(o, lora["ao"], lora["bo"], scale)
     h1 = x + proj
     bn = rmsnorm(h1, w["gamma2"], cfg.rms_eps)
+    return a, q, kk, v, o, h1, bn
+
+
+def layer_forward(x: Tensor, w: Dict[str, Tensor], cfg, lora: Optional[Dict[str, Tensor]] = None,
+                  router: Optional[Tensor] = None, keep: bool = False):
+    """One pre-norm decoder layer, x [T, H] -> y [T, H].
+
+    With keep=True also returns the internals (normed inputs, rotated q/k, v,
+    attention output, residual h1, MLP input).
+    """
+    T = x.shape[0]
+    nq, nkv, d = cfg.n_q, cfg.n_kv, cfg.head_dim
+    a, q, kk, v, o, h1, bn = attention_block(x, w, cfg, lora)
     if cfg.is_moe:
         mlp = moe_mlp(bn, router, w["wg"], w["wu"], w["wd"], cfg.top_k)
     else:
@@ -189,6 +199,105 @@ def layer_forward(x: Tensor, w: Dict[str, Tensor], cfg, lora: Optional[Dict[str,
         return y
     return y, {"a": a, "q": q.reshape(T, nq * d), "k": kk.reshape(T, nkv * d),
                "v": v.reshape(T, nkv * d), "o": o, "h1": h1, "b": bn}
+
+
+def layer_forward_rows(x: Tensor, w: Dict[str, Tensor], cfg, rows: Sequence[int],
+                       lora: Optional[Dict[str, Tensor]] = None,
+                       router: Optional[Tensor] = None) -> Tensor:
+    """The same layer as layer_forward, evaluated only at the token rows
+    `rows`: keys and values are projected for every token (a query attends to
+    all earlier tokens of its batch row), everything else only for the listed
+    rows. Returns y[rows] [len(rows), H]. Lets the full-size workloads be
+    checked one output row at a time."""
+    T, H = x.shape
+    nq, nkv, d = cfg.n_q, cfg.n_kv, cfg.head_dim
+    seq = T // cfg.batch
+    pos = _positions(cfg.batch, seq)
+    scale = (cfg.lora_alpha / cfg.lora_rank) if lora is not None else 0.0
+    a = rmsnorm(x, w["gamma1"], cfg.rms_eps)
+    kk = a @ w["wk"].T
+    v = a @ w["wv"].T
+    if lora is not None:
+        kk = kk + lora_delta(a, lora["ak"], lora["bk"], scale)
+        v = v + lora_delta(a, lora["av"], lora["bv"], scale)
+    kk = rope(kk.reshape(T, nkv, d), pos, cfg.rope_base)
+    v = v.reshape(T, nkv, d)
+    out = []
+    for t in rows:
+        at = a[t:t + 1]
+        q = at @ w["wq"].T
+        if lora is not None:
+            q = q + lora_delta(at, lora["aq"], lora["bq"], scale)
+        q = rope(q.reshape(1, nq, d), pos[t:t + 1], cfg.rope_base)[0]
+        r0 = (t // seq) * seq
+        o = torch.empty(nq, d, dtype=x.dtype)
+        for h in range(nq):
+            hk = (h * nkv) // nq
+            s = (kk[r0:t + 1, hk, :] @ q[h]) / math.sqrt(d)
+            o[h] = torch.softmax(s, dim=0) @ v[r0:t + 1, hk, :]
+        o = o.reshape(1, nq * d)
+        proj = o @ w["wo"].T
+        if lora is not None:
+            proj = proj + lora_delta(o, lora["ao"], lora["bo"], scale)
+        h1 = x[t:t + 1] + proj
+        bn = rmsnorm(h1, w["gamma2"], cfg.rms_eps)
+        if cfg.is_moe:
+            mlp = moe_mlp(bn, router[t:t + 1], w["wg"], w["wu"], w["wd"], cfg.top_k)
+        else:
+            mlp = swiglu(bn, w["wg"], w["wu"], w["wd"])
+        out.append(h1 + mlp)
+    return torch.cat(out, dim=0)
+
+
+def mlp_weight_grad_columns(b: Tensor, dy: Tensor, w: Dict[str, Tensor], cols: Sequence[int]):
+    """Gradients of sum(y * dy) for the dense SwiGLU MLP
+    y = h1 + (silu(b Wg^T) * (b Wu^T)) Wd^T, at the FFN columns `cols` only:
+    dWd[:, cols], dWg[cols, :], dWu[cols, :]. Column f of the FFN involves
+    only row f of Wg / Wu and column f of Wd, so each is exact on its own."""
+    g = b @ w["wg"][cols].T
+    u = b @ w["wu"][cols].T
+    sg = torch.sigmoid(g)
+    m = g * sg * u
+    dm = dy @ w["wd"][:, cols]
+    dg = dm * u * (sg + g * sg * (1 - sg))      # d silu(g) / dg = sg (1 + g (1 - sg))
+    du = dm * g * sg
+    return dy.T @ m, dg.T @ b, du.T @ b
+
+
+def lmhead_rows(x: Tensor, w: Tensor, labels: Tensor, rows: Sequence[int], vocab_rows: Sequence[int],
+                chunk: int = 1024):
+    """Full-size LM-head checks without the [T, V] gradient: the mean
+    cross-entropy over all labelled rows (logits built a row chunk at a time),
+    dloss/dx at the token rows `rows`, and dloss/dW at the vocabulary rows
+    `vocab_rows`. Same definition as lmhead_loss_unsharded (no final norm)."""
+    T = x.shape[0]
+    valid = labels >= 0
+    n_valid = int(valid.sum())
+    lse = torch.empty(T, dtype=x.dtype)
+    total = torch.zeros((), dtype=x.dtype)
+    for c0 in range(0, T, chunk):
+        z = x[c0:c0 + chunk] @ w.T
+        lse[c0:c0 + chunk] = torch.logsumexp(z, dim=-1)
+        lab = labels[c0:c0 + chunk]
+        ok = lab >= 0
+        zl = z.gather(1, torch.where(ok, lab, torch.zeros_like(lab)).long()[:, None])[:, 0]
+        total = total + torch.where(ok, lse[c0:c0 + chunk] - zl, torch.zeros((), dtype=x.dtype)).sum()
+    loss = total / n_valid
+    dx = []
+    for t in rows:
+        p = torch.softmax(x[t] @ w.T, dim=0)
+        if labels[t] >= 0:
+            p[int(labels[t])] -= 1.0
+            dx.append((p @ w) / n_valid)
+        else:
+            dx.append(torch.zeros(w.shape[1], dtype=x.dtype))
+    dw = []
+    for vr in vocab_rows:
+        pv = torch.exp(x @ w[vr] - lse)            # softmax column vr over all tokens
+        pv = pv - (labels == vr).to(x.dtype)
+        pv = torch.where(valid, pv, torch.zeros((), dtype=x.dtype))
+        dw.append((pv @ x) / n_valid)
+    return loss, torch.stack(dx), torch.stack(dw)
 
 
 def trainable_names(cfg) -> List[str]:

@@ -400,3 +400,58 @@ def test_fp32_oracle_close_to_fp64_on_tiny_model():
         for n in a:
             err = (a[n].double() - b[n]).abs().max() / b[n].abs().max()
             assert err.item() < 1e-5, n
+
+
+@pytest.mark.parametrize("variant", ["dense", "lora_moe"])
+def test_layer_forward_rows_equals_full_forward(variant):
+    """The row-sampled layer forward (used for full-size checks) equals the
+    full forward at the sampled rows, including rows of the second batch row."""
+    kw = dict(n_q=4, n_kv=2)
+    if variant == "lora_moe":
+        kw.update(lora_rank=3, lora_alpha=6.0, ffn=0, n_experts=4, top_k=2, expert_ffn=12)
+    cfg = tiny_cfg(**kw)
+    w = f64(synth.layer_weights(cfg, 0, gamma="perturbed"))
+    for k in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"):
+        w[k] = w[k] * 10
+    lora = f64(synth.lora_weights(cfg, 0, b_zero=False)) if cfg.lora_rank else None
+    router = synth.router_logits(cfg, 0).to(D64) if cfg.is_moe else None
+    x = synth.activation(cfg, "x").to(D64)
+    y = O.layer_forward(x, w, cfg, lora, router)
+    rows = [0, 3, 7, 8, 15]
+    yr = O.layer_forward_rows(x, w, cfg, rows, lora, router)
+    assert torch.allclose(yr, y[rows], rtol=1e-12, atol=1e-12)
+
+
+def test_lmhead_rows_equals_full_gradients():
+    """Chunked loss, row-sampled dx and vocabulary-sampled dW equal the full
+    autograd LM head (ignored labels included)."""
+    g = torch.Generator().manual_seed(3)
+    T, H, V = 40, 12, 50
+    x = torch.randn(T, H, generator=g, dtype=D64)
+    w = torch.randn(V, H, generator=g, dtype=D64) * 0.3
+    labels = torch.randint(0, V, (T,), generator=g)
+    labels[5] = -1
+    loss, dx, dw, _ = O.lmhead_fwd_bwd(x, w, labels, 1)
+    rows, vrows = [0, 5, 17, 39], [0, 3, int(labels[2]), 49]
+    l2, dxr, dwr = O.lmhead_rows(x, w, labels, rows, vrows, chunk=16)
+    assert torch.allclose(l2, loss, rtol=1e-12)
+    assert torch.allclose(dxr, dx[rows], rtol=1e-10, atol=1e-14)
+    assert torch.allclose(dwr, dw[vrows], rtol=1e-10, atol=1e-14)
+
+
+def test_mlp_weight_grad_columns_equals_autograd():
+    """Column-sampled MLP weight gradients (used at full size) equal the
+    autograd gradients of sum(y * dy) at those columns."""
+    g = torch.Generator().manual_seed(4)
+    T, H, Fd = 20, 8, 12
+    b = torch.randn(T, H, generator=g, dtype=D64)
+    dy = torch.randn(T, H, generator=g, dtype=D64)
+    w = {k: (torch.randn(*sh, generator=g, dtype=D64) * 0.5).requires_grad_(True)
+         for k, sh in (("wg", (Fd, H)), ("wu", (Fd, H)), ("wd", (H, Fd)))}
+    y = O.swiglu(b, w["wg"], w["wu"], w["wd"])
+    gg, gu, gd = torch.autograd.grad((y * dy).sum(), [w["wg"], w["wu"], w["wd"]])
+    cols = [0, 5, 11]
+    dwd, dwg, dwu = O.mlp_weight_grad_columns(b, dy, {k: v.detach() for k, v in w.items()}, cols)
+    assert torch.allclose(dwd, gd[:, cols], rtol=1e-12, atol=1e-12)
+    assert torch.allclose(dwg, gg[cols], rtol=1e-12, atol=1e-12)
+    assert torch.allclose(dwu, gu[cols], rtol=1e-12, atol=1e-12)
