@@ -23,8 +23,14 @@ event pairs on the compute stream (rp_trace_*); the dominant kernel is priced
 against the MI355X peak for its bound. The CPU oracle is timed on a bounded
 sample of the same step for the cpu_baseline field.
 
+`roofline.traffic` comes from two rocprofv3 counter runs of this script
+(FETCH_SIZE, then WRITE_SIZE, with --copy-calibration-mib for the scale),
+reduced by offloaded_pipeline_stage_amd/pmc.py into
+profiles/<workload>_step_traffic.txt.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--streamed]
                        [--no-cpu-baseline] [--cpu-seq S] [--trace-json PATH]
+                       [--copy-calibration-mib M]
 """
 from __future__ import annotations
 
@@ -165,19 +171,38 @@ def summarize_trace(recs, steps):
     return agg
 
 
-def roofline(agg, dtype):
+def roofline(agg, dtype, traffic_file):
+    """The dominant kernel (most time per step) against its MI355X peak.
+    `traffic` is its calibrated HBM bytes per launch from the committed
+    FETCH_SIZE/WRITE_SIZE summary, or None when that summary is absent or
+    was taken from another version of the kernel's source."""
+    from offloaded_pipeline_stage_amd import pmc
     name, (cnt, fl, by, ms) = max(agg.items(), key=lambda kv: kv[1][3])
     sec = ms / 1e3
+    traffic = pmc.traffic_for(traffic_file, name)
+    traffic = None if traffic is None else round(traffic)
     if fl > 0:
         peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS
         ach = fl / sec / 1e12
         return {"kernel": name, "bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": None, "launches": cnt,
+                "frac": round(ach / peak, 4), "traffic": traffic, "launches": cnt,
                 "avg_launch_ms": round(ms / cnt, 4), "flops_per_launch": fl / cnt}
     ach = by / sec / 1e9
     return {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": None, "launches": cnt,
+            "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic, "launches": cnt,
             "avg_launch_ms": round(ms / cnt, 4), "bytes_per_launch": by / cnt}
+
+
+def copy_calibration(ctx, mib: int):
+    """One plain device-to-device copy of `mib` MiB through the library's
+    16-byte-per-lane copy kernel (rp_op_copy), the reference that the
+    FETCH_SIZE / WRITE_SIZE counter runs are scaled by."""
+    src = torch.ones(mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ctx.op_copy(dst, src)
+    ctx.sync()
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 def cpu_baseline(cfg, seq: int):
@@ -212,6 +237,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seq", type=int, default=1024)
     ap.add_argument("--trace-json", default=None, help="write the per-kernel table here")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one device copy of this size (for the HBM counter runs)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}); "
@@ -224,7 +251,10 @@ def main():
     binding.lib()  # fails loudly when librp.so is missing
 
     cfg = synth.config(a.workload)
+    traffic_file = os.path.join(ROOT, "profiles", f"{a.workload}_step_traffic.txt")
     step = Step(cfg, streamed=False)
+    if a.copy_calibration_mib > 0:
+        copy_calibration(step.wk.ctx, a.copy_calibration_mib)
     for _ in range(a.warmup):
         step.run()
     step.sync()
@@ -257,7 +287,7 @@ def main():
         "tflops": round(step_flops / (ms_step / 1e3) / 1e12, 1),
         "mfma_util": round(step_flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "traced_tflop_per_step": round(traced_flops / 1e12, 3),
-        "roofline": roofline(agg, cfg.dtype),
+        "roofline": roofline(agg, cfg.dtype, traffic_file),
         "kernels_ms_per_step": {k: round(v, 3) for k, v in kernels[:12]},
     }
     if a.trace_json:

@@ -375,6 +375,13 @@ rp_status rp_op_attn_bwd(rp_ctx* ctx, int batch, int seq, const void* qkv, const
                          const void* dout, const float* lse, void* dqkv, void* ws,
                          size_t ws_bytes);
 
+/* Plain device-to-device copy of `bytes` (a multiple of 16; both pointers
+ * 16-byte aligned, non-overlapping device memory), 16 bytes per lane. Its
+ * known traffic is the scale for HBM byte counters (FETCH_SIZE, WRITE_SIZE)
+ * read on the library's other kernels. Enqueued on the compute stream;
+ * RP_ERR_INVALID on misaligned arguments. */
+rp_status rp_op_copy(rp_ctx* ctx, void* dst, const void* src, size_t bytes);
+
 /* ------------------------------------------------------------------------ */
 /* kernel trace                                                              */
 /* ------------------------------------------------------------------------ */

@@ -79,6 +79,7 @@ _SIGS = {
     "rp_op_gemm_bf16": (C.c_int, [_P, C.c_int, C.c_int, C.c_int, _P, C.c_int, C.c_int, _P, C.c_int, C.c_int, _P,
                                   C.c_int, C.c_int, C.c_int]),
     "rp_op_attn_fwd": (C.c_int, [_P, C.c_int, C.c_int, _P, _P, _P]),
+    "rp_op_copy": (C.c_int, [_P, _P, _P, C.c_size_t]),
     "rp_op_attn_bwd": (C.c_int, [_P, C.c_int, C.c_int, _P, _P, _P, _P, _P, _P, C.c_size_t]),
     "rp_trace_begin": (C.c_int, [_P, C.c_int]),
     "rp_trace_end": (C.c_int, [_P]),
@@ -311,6 +312,13 @@ class Context:
         check(lib().rp_op_gemm_bf16(self.h, M, N, K, ptr(A), lda, int(a_kmajor), ptr(B), ldb, int(b_kmajor),
                                     ptr(Cm), ldc, int(out_f32), int(accumulate)))
         self._hold(A, B, Cm)
+
+    def op_copy(self, dst, src):
+        n = src.numel() * src.element_size()
+        if dst.numel() * dst.element_size() < n:
+            raise ValueError("op_copy: dst smaller than src")
+        check(lib().rp_op_copy(self.h, ptr(dst), ptr(src), n))
+        self._hold(dst, src)
 
     def op_attn_fwd(self, batch, seq, qkv, o, lse):
         check(lib().rp_op_attn_fwd(self.h, batch, seq, ptr(qkv), ptr(o), ptr(lse)))

@@ -344,6 +344,12 @@ rp_status rp_op_gemm_bf16(rp_ctx* c, int M, int N, int K, const void* A, int lda
   return gemm(d, c->compute);
 }
 
+rp_status rp_op_copy(rp_ctx* c, void* dst, const void* src, size_t bytes) {
+  CTX_ENTER(c);
+  RP_CHECK(bytes == 0 || (dst && src), RP_ERR_INVALID, "op_copy: null pointer");
+  return copy16(dst, src, bytes, c->compute);
+}
+
 rp_status rp_op_attn_fwd(rp_ctx* c, int batch, int seq, const void* qkv, void* o, float* lse) {
   CTX_ENTER(c);
   RP_CHECK(batch >= 1 && seq >= 1 && qkv && o && lse, RP_ERR_INVALID, "op_attn_fwd: bad arguments");

@@ -52,6 +52,14 @@ __global__ void fill_zero_kernel(uint4* p, size_t n16, uint8_t* tail, size_t nta
   if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
 }
 
+// plain 16-byte-per-lane copy: the reference that HBM byte counters are
+// scaled by, with the same load and store width as the library's kernels
+__global__ void copy16_kernel(uint4* __restrict__ dst, const uint4* __restrict__ src, size_t n16) {
+  size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (; i < n16; i += stride) dst[i] = src[i];
+}
+
 // ---------------------------------------------------------------------------
 // RMSNorm
 // ---------------------------------------------------------------------------
@@ -392,6 +400,17 @@ rp_status fill_zero(void* p, size_t bytes, hipStream_t s) {
   unsigned g = (unsigned)std::min<size_t>(std::max<size_t>(cdiv(n16, 256), 1), 8192);
   TraceScope ts(s, "fill_zero_kernel", 0.0, (double)bytes);
   RP_LAUNCH(fill_zero_kernel, dim3(g), dim3(256), 0, s, (uint4*)p, n16, (uint8_t*)p + n16 * 16, ntail);
+  return RP_OK;
+}
+
+rp_status copy16(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return RP_OK;
+  RP_CHECK((((uintptr_t)dst | (uintptr_t)src | bytes) & 15) == 0, RP_ERR_INVALID,
+           "copy: pointers and size must be multiples of 16 bytes");
+  const size_t n16 = bytes / 16;
+  unsigned g = (unsigned)std::min<size_t>(std::max<size_t>(cdiv(n16, 256), 1), 8192);
+  TraceScope ts(s, "copy16_kernel", 0.0, 2.0 * bytes);
+  RP_LAUNCH(copy16_kernel, dim3(g), dim3(256), 0, s, (uint4*)dst, (const uint4*)src, n16);
   return RP_OK;
 }
 

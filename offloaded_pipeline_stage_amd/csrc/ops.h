@@ -80,6 +80,7 @@ rp_status gemm_validate(const GemmDesc& d);
 // elementwise / row kernels
 // ---------------------------------------------------------------------------
 rp_status fill_zero(void* p, size_t bytes, hipStream_t s);
+rp_status copy16(void* dst, const void* src, size_t bytes, hipStream_t s);
 
 // y = x * rsqrt(mean(x^2) + eps) * gamma ; rstd[t] = rsqrt(...)
 rp_status rmsnorm_fwd(int dt, const void* x, const void* gamma, void* y, float* rstd, int T,

@@ -1,0 +1,174 @@
+"""HBM traffic of the step's kernels from rocprofv3 counter runs.
+
+Two `rocprofv3 --pmc` passes of the same bench command, one collecting
+FETCH_SIZE and one WRITE_SIZE (KiB per dispatch), are reduced here to
+bytes per launch for every kernel. Both counters are calibrated against a
+plain device-to-device copy of known size (the library's copy16_kernel,
+16 bytes per lane like its other kernels) that the bench command runs before
+its steps (`--copy-calibration-mib`): the scale factor is the copy's known bytes
+divided by what the counter reports for it.
+
+The summary records, for each kernel, a hash of the source file that
+defines it; `traffic_for` returns None when that file has changed since the
+counters were taken, so a stale figure is never reported for a new kernel.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+from collections import defaultdict
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+COPY_KERNEL = "copy16_kernel"
+
+
+def norm_name(name: str) -> str:
+    """rocprofv3's demangled name -> the library's trace name form:
+    no return type, namespaces or argument list; bools as 0/1."""
+    n = name.strip()
+    if n.startswith("void "):
+        n = n[5:]
+    depth = 0
+    for i, ch in enumerate(n):  # cut the argument list (the first '(' outside <>)
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0 and not n.startswith("(anonymous", i):
+            n = n[:i]
+            break
+    n = n.replace("(anonymous namespace)::", "")
+    n = re.sub(r"\brp::", "", n)
+    n = re.sub(r"\btrue\b", "1", n)
+    n = re.sub(r"\bfalse\b", "0", n)
+    return n
+
+
+def base_name(n: str) -> str:
+    return n.split("<", 1)[0]
+
+
+def kernel_source(base: str) -> str | None:
+    """The csrc file that defines __global__ `base`."""
+    pat = re.compile(r"__global__[^;{]*?\b" + re.escape(base) + r"\s*\(", re.S)
+    for p in sorted(glob.glob(os.path.join(CSRC, "*.hip"))):
+        if pat.search(open(p).read()):
+            return p
+    return None
+
+
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def _dispatches(path: str, counter: str):
+    """[(dispatch_id, kernel_name, value)] of one counter, in dispatch order."""
+    out = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name", counter) != counter:
+                continue
+            out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    out.sort()
+    return out
+
+
+def _find_csv(d: str) -> str:
+    hits = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not hits:
+        raise FileNotFoundError(f"no counter_collection.csv under {d}")
+    return hits[0]
+
+
+def summarize(fetch_dir: str, write_dir: str, copy_mib: int, title: str, commands: list[str]) -> str:
+    """Text summary of the two counter runs (one table + one JSON line)."""
+    copy_kib = copy_mib * 1024.0
+    per = {}
+    factors = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _dispatches(_find_csv(d), counter)
+        cal = [v for _, k, v in rows if COPY_KERNEL in k]
+        if not cal:
+            raise RuntimeError(f"{counter}: the calibration copy is missing from {d}")
+        # the calibration copy is the process's first copy16_kernel launch
+        factors[counter] = copy_kib / cal[0]
+        agg = defaultdict(lambda: [0, 0.0])
+        for _, k, v in rows:
+            a = agg[norm_name(k)]
+            a[0] += 1
+            a[1] += v
+        per[counter] = agg
+    names = sorted(set(per["FETCH_SIZE"]) | set(per["WRITE_SIZE"]))
+    table = {}
+    for n in names:
+        cf, sf = per["FETCH_SIZE"].get(n, [0, 0.0])
+        cw, sw = per["WRITE_SIZE"].get(n, [0, 0.0])
+        if cf == 0 or cw == 0:
+            continue
+        src = kernel_source(base_name(n))
+        table[n] = {
+            "launches": cf,
+            "fetch_bytes": sf / cf * 1024.0 * factors["FETCH_SIZE"],
+            "write_bytes": sw / cw * 1024.0 * factors["WRITE_SIZE"],
+            "fetch_kib_raw": sf / cf, "write_kib_raw": sw / cw,
+            "source": os.path.basename(src) if src else None,
+            "source_sha": source_hash(src) if src else None,
+        }
+    lines = [f"# {title}", ""]
+    lines += [f"command: {c}" for c in commands]
+    lines += ["",
+              f"calibration: {COPY_KERNEL} of {copy_mib} MiB; scale FETCH_SIZE x{factors['FETCH_SIZE']:.4f}, "
+              f"WRITE_SIZE x{factors['WRITE_SIZE']:.4f} (known bytes / counter)", "",
+              f"{'launches':>8} {'fetch_MB':>10} {'write_MB':>10}  kernel (per launch, calibrated)"]
+    for n, t in sorted(table.items(), key=lambda kv: -(kv[1]["fetch_bytes"] + kv[1]["write_bytes"]) * kv[1]["launches"]):
+        lines.append(f"{t['launches']:8d} {t['fetch_bytes'] / 1e6:10.2f} {t['write_bytes'] / 1e6:10.2f}  {n}")
+    lines += ["", "traffic_json: " + json.dumps({"factors": factors, "kernels": table}, sort_keys=True)]
+    return "\n".join(lines) + "\n"
+
+
+def load(path: str) -> dict | None:
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("traffic_json: "):
+            return json.loads(line[len("traffic_json: "):])
+    return None
+
+
+def traffic_for(path: str, kernel: str) -> float | None:
+    """Calibrated HBM bytes per launch of `kernel` (trace-name form) from the
+    summary at `path`, or None when absent or taken from other source."""
+    d = load(path)
+    if d is None:
+        return None
+    t = d["kernels"].get(kernel)
+    if t is None:
+        # the trace may name a kernel by its base only
+        hits = [v for k, v in d["kernels"].items() if base_name(k) == kernel]
+        if len(hits) != 1:
+            return None
+        t = hits[0]
+    src = kernel_source(base_name(kernel))
+    if src is None or t.get("source_sha") != source_hash(src):
+        return None
+    return t["fetch_bytes"] + t["write_bytes"]
+
+
+if __name__ == "__main__":
+    import argparse
+    ap = argparse.ArgumentParser(description="summarise FETCH_SIZE / WRITE_SIZE counter runs")
+    ap.add_argument("fetch_dir")
+    ap.add_argument("write_dir")
+    ap.add_argument("--copy-mib", type=int, required=True)
+    ap.add_argument("--title", required=True)
+    ap.add_argument("--command", action="append", default=[])
+    ap.add_argument("--out", required=True)
+    a = ap.parse_args()
+    txt = summarize(a.fetch_dir, a.write_dir, a.copy_mib, a.title, a.command)
+    with open(a.out, "w") as f:
+        f.write(txt)
+    print(txt)

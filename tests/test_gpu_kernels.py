@@ -129,3 +129,20 @@ def test_attention_fwd_bwd(B, dtype, d, nq, nkv, batch, seq):
     mask = (pos[None, :] <= pos[:, None]) & (row[None, :] == row[:, None])
     lref = torch.logsumexp(s.masked_fill(~mask[None], float("-inf")), dim=-1)
     assert (lse.cpu().double() - lref).abs().max().item() < (1e-4 if dtype == "f32" else 2e-2)
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 16, (3 << 20) + 48])
+def test_copy_is_bit_exact(B, nbytes):
+    ctx = _ctx(B)
+    g = torch.Generator().manual_seed(nbytes)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g)
+    dst = torch.zeros(nbytes + 32, dtype=torch.uint8, device="cuda")
+    s = src.to("cuda")
+    say(f"copy {nbytes} bytes")
+    ctx.op_copy(dst, s)
+    ctx.sync()
+    out = dst.cpu()
+    assert torch.equal(out[:nbytes], src)
+    assert not out[nbytes:].any()  # nothing written past the end
+    with pytest.raises(B.RPError):
+        ctx.op_copy(dst[1:17], s[:16])  # misaligned destination
