@@ -146,19 +146,24 @@ struct LoaderK {
       voff[0] = (uint32_t)(((int64_t)(row0 + (tid >> 3)) * ld + (tid & 7) * 8) * 2);
     }
   }
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int k0, int K) {
+  // issue units: unit u is one 16-byte chunk (load) / one LDS store
+  static constexpr int NUNIT = NCH;
+  __device__ __forceinline__ void load_unit(__amdgpu_buffer_rsrc_t rs, int64_t ld, int k0, int K, int i) {
     // a chunk past K (the K tail) reads as zeros
     const uint32_t base = (uint32_t)(k0 * 2) + (k0 + kcol < K ? 0u : OOB_SHIFT);
+    reg[i] = bload(rs, base + (MAPPED ? voff[i] : voff[0] + (uint32_t)i * rstride));
+  }
+  __device__ __forceinline__ void store_unit(char* lds, int tid, int i) {
+    const int r = (tid >> 3) + i * (NT / 8);
+    *reinterpret_cast<u32x4_t*>(lds + Lay<true>::off(r, tid & 7)) = reg[i];
+  }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int k0, int K) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i)
-      reg[i] = bload(rs, base + (MAPPED ? voff[i] : voff[0] + (uint32_t)i * rstride));
+    for (int i = 0; i < NCH; ++i) load_unit(rs, ld, k0, K, i);
   }
   __device__ __forceinline__ void store(char* lds, int tid) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int r = (tid >> 3) + i * (NT / 8);
-      *reinterpret_cast<u32x4_t*>(lds + Lay<true>::off(r, tid & 7)) = reg[i];
-    }
+    for (int i = 0; i < NCH; ++i) store_unit(lds, tid, i);
   }
 };
 
@@ -182,43 +187,45 @@ struct LoaderM {
       voff[i] = (uint32_t)(((int64_t)(kb * 4) * ld + row0 + rb * 8) * 2);
     }
   }
+  // issue units: unit i is one 4 x 8 block (four loads / its transposed stores)
+  static constexpr int NUNIT = NBLK;
   // k rows >= kend (past K, or past this split's range) read as zeros
+  __device__ __forceinline__ void load_unit(__amdgpu_buffer_rsrc_t rs, int64_t ld, int k0, int kend, int i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t oob = (k0 + krow[i] + j < kend) ? 0u : OOB_SHIFT;
+      reg[i][j] = bload(rs, voff[i] + (uint32_t)(((int64_t)(k0 + j) * ld) * 2) + oob);
+    }
+  }
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int k0, int kend) {
 #pragma unroll
-    for (int i = 0; i < NBLK; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t oob = (k0 + krow[i] + j < kend) ? 0u : OOB_SHIFT;
-        reg[i][j] = bload(rs, voff[i] + (uint32_t)(((int64_t)(k0 + j) * ld) * 2) + oob);
-      }
+    for (int i = 0; i < NBLK; ++i) load_unit(rs, ld, k0, kend, i);
   }
   __device__ __forceinline__ void store(char* lds, int tid) {
 #pragma unroll
-    for (int i = 0; i < NBLK; ++i) {
-      const int b = tid + i * NT;
-      const int rb = b % NRB, kb = b / NRB;
-      const int kc = kb >> 1, half = kb & 1;
+    for (int i = 0; i < NBLK; ++i) store_unit(lds, tid, i);
+  }
+  __device__ __forceinline__ void store_unit(char* lds, int tid, int i) {
+    const int b = tid + i * NT;
+    const int rb = b % NRB, kb = b / NRB;
+    const int kc = kb >> 1, half = kb & 1;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        // rows 2q (low halves) and 2q+1 (high halves)
-        const uint32_t a0 = reg[i][0][q], a1 = reg[i][1][q], a2 = reg[i][2][q], a3 = reg[i][3][q];
-        const u32x2_t lo = u32x2_t{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-        const u32x2_t hi = u32x2_t{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-        const int r0 = rb * 8 + 2 * q;
-        *reinterpret_cast<u32x2_t*>(lds + Lay<false>::off(r0, kc) + half * 8) = lo;
-        *reinterpret_cast<u32x2_t*>(lds + Lay<false>::off(r0 + 1, kc) + half * 8) = hi;
-      }
+    for (int q = 0; q < 4; ++q) {
+      // rows 2q (low halves) and 2q+1 (high halves)
+      const uint32_t a0 = reg[i][0][q], a1 = reg[i][1][q], a2 = reg[i][2][q], a3 = reg[i][3][q];
+      const u32x2_t lo = u32x2_t{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
+      const u32x2_t hi = u32x2_t{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
+      const int r0 = rb * 8 + 2 * q;
+      *reinterpret_cast<u32x2_t*>(lds + Lay<false>::off(r0, kc) + half * 8) = lo;
+      *reinterpret_cast<u32x2_t*>(lds + Lay<false>::off(r0 + 1, kc) + half * 8) = hi;
     }
   }
 };
 
 // --- the MFMA kernel --------------------------------------------------------
 
-// WGM x WGN waves, each owning a (BM / WGM) x (BN / WGN) block of 32x32 tiles.
-// Per 64-wide k step: the next step's global loads are issued first, the
-// fragments of k-substep s + 1 are read from LDS while the MFMAs of substep s
-// run, and the loaded registers are written to the other LDS buffer in the
-// middle of the MFMA stream; one barrier per step.
+// WGM x WGN waves, each owning a (BM / WGM) x (BN / WGN) block of 32x32 tiles;
+// the k loop's schedule is described above it.
 // GRP: 0 = one product; 1 = grouped, A rows contiguous per expert; 2 =
 // grouped, A rows gathered through g_rows.
 template <int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool OUT_F32, int GRP>
@@ -305,27 +312,44 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(GemmParams p)
 
   // fragment rows of this lane
   const int arow = wm * WM + (lane & 31), brow = wn * WN + (lane & 31), kh = lane >> 5;
-  // fragment q of k-substep ks: q < TM reads A row block q, else B row block q - TM
+  // fragment q of k-substep ks, in the order the MFMAs consume them (A row
+  // block 0, B row blocks 0 .. TN-1, then A row blocks 1 .. TM-1), so the
+  // first MFMA of a substep waits for two reads only
   auto read_one = [&](const char* a_s, const char* b_s, int ks, int q, bf16x8_t (&af)[TM], bf16x8_t (&bfr)[TN]) {
     const int kc = ks * 2 + kh;
-    if (q < TM) af[q] = *reinterpret_cast<const bf16x8_t*>(a_s + Lay<AK>::off(arow + q * 32, kc));
-    else bfr[q - TM] = *reinterpret_cast<const bf16x8_t*>(b_s + Lay<BKM>::off(brow + (q - TM) * 32, kc));
+    if (q >= 1 && q <= TN) bfr[q - 1] = *reinterpret_cast<const bf16x8_t*>(b_s + Lay<BKM>::off(brow + (q - 1) * 32, kc));
+    else {
+      const int i = q == 0 ? 0 : q - TN;
+      af[i] = *reinterpret_cast<const bf16x8_t*>(a_s + Lay<AK>::off(arow + i * 32, kc));
+    }
   };
 
-  // The k loop body is one basic block issued in a fixed order: the next
-  // tile's global loads first, then each substep's MFMAs with the following
-  // substep's fragment reads interleaved one by one, and in the last substep
-  // the LDS stores of the next tile interleaved. The last step's prefetch of
-  // the tile past K is harmless (rows past the operand read as zeros, the K
-  // tail is masked) and never read back.
+  // Software pipeline over 64-wide k tiles, two LDS buffers, one barrier per
+  // tile. Entering tile kt: LDS[cur] holds tile kt, the registers hold its
+  // substep-0 fragments, and the loaders' registers hold tile kt + 1 (loaded
+  // one tile earlier). Substep s runs its MFMAs with substep s + 1's fragment
+  // reads interleaved; substep 0 also writes tile kt + 1 into LDS[cur ^ 1]
+  // and then issues the global loads of tile kt + 2. The barrier closes
+  // substep 2, the last one that reads LDS[cur]; after it tile kt + 1 is
+  // visible, so substep 3 reads tile kt + 1's substep-0 fragments under its
+  // MFMAs and no wave waits on LDS at the top of the next tile. The next
+  // tile's stores (into LDS[cur]) come after that same barrier. Prefetches
+  // past the end read zeros (rows past the operand, the masked K tail) and
+  // are never consumed.
   constexpr int NKS = BK / 16;
   constexpr int NMF = TM * TN;  // MFMAs per k-substep
   constexpr int NRD = TM + TN;  // fragment reads per k-substep
+  static_assert(NKS == 4, "the barrier placement assumes four substeps");
   static_assert(NRD <= NMF, "fewer MFMAs than fragment reads per substep");
+  // the loaders' issue units (A's, then B's) are spread over substep 0's MFMA
+  // slots: slot t stores units [t * NU / NMF, (t + 1) * NU / NMF) into the
+  // other buffer and reissues their global loads for the tile after
+  constexpr int NUA = decltype(la)::NUNIT, NU = NUA + decltype(lb)::NUNIT;
   const int nk = (kend - kbeg + BK - 1) / BK;
   load(kbeg);
   la.store(sA0, tid);
   lb.store(sB0, tid);
+  load(kbeg + BK);
   __syncthreads();
   bf16x8_t af[2][TM], bfr[2][TN];
 #pragma unroll
@@ -333,28 +357,36 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(GemmParams p)
 
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    load(kbeg + (kt + 1) * BK);
-    __builtin_amdgcn_sched_barrier(0);
     const char* a_s = sA0 + cur * A_BUF;
     const char* b_s = sB0 + cur * B_BUF;
+    char* a_n = sA0 + (cur ^ 1) * A_BUF;
+    char* b_n = sB0 + (cur ^ 1) * B_BUF;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
       for (int t = 0; t < NMF; ++t) {
         const int i = t / TN, j = t % TN;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j], 0, 0, 0);
-        if (ks + 1 < NKS && t < NRD) read_one(a_s, b_s, ks + 1, t, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
-        if (ks + 1 == NKS && t == 0) {
-          // the other buffer was last read before the previous barrier
-          la.store(sA0 + (cur ^ 1) * A_BUF, tid);
-          lb.store(sB0 + (cur ^ 1) * B_BUF, tid);
+        if (t < NRD) {
+          if (ks + 1 < NKS) read_one(a_s, b_s, ks + 1, t, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+          else read_one(a_n, b_n, 0, t, af[0], bfr[0]);
+        }
+        if (ks == 0) {
+#pragma unroll
+          for (int u = t * NU / NMF; u < (t + 1) * NU / NMF; ++u) {
+            if (u < NUA) {
+              la.store_unit(a_n, tid, u);
+              la.load_unit(ra, p.lda, kbeg + (kt + 2) * BK, kend, u);
+            } else {
+              lb.store_unit(b_n, tid, u - NUA);
+              lb.load_unit(rb, p.ldb, kbeg + (kt + 2) * BK, kend, u - NUA);
+            }
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (ks == 2) __syncthreads();
     }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < NRD; ++q) read_one(sA0 + (cur ^ 1) * A_BUF, sB0 + (cur ^ 1) * B_BUF, 0, q, af[0], bfr[0]);
   }
 
   // --- epilogue: lane holds column (lane & 31) of each 32x32 tile, rows
