@@ -82,44 +82,23 @@ __device__ __forceinline__ bf16x8_t to_operand(const f32x16_t& c, int j) {
 
 // --- LDS layouts -------------------------------------------------------------
 
-// row-major tile [rows][128] bf16: 256-byte rows of 16 chunks of 16 bytes
-__device__ __forceinline__ int rm_off(int row, int c16) { return row * 256 + ((c16 ^ (row & 15)) << 4); }
-// transposed tile [128][64] bf16: 128-byte rows (one per d) of 16 chunks of 8 bytes
-__device__ __forceinline__ int tr_off(int d, int c8) { return d * 128 + ((c8 ^ (d & 15)) << 3); }
-
-// Copy rows [r0, r0 + 64) of a strided bf16 matrix (row stride ld elements,
-// columns [col, col + 128)) into a row-major LDS tile; rows >= rmax are zero.
-__device__ __forceinline__ void load_rm(char* lds, const bf16* g, int64_t ld, int r0, int rmax, int col, int tid) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int id = tid + i * NT;
-    const int row = id >> 4, c = id & 15;
-    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-    if (r0 + row < rmax) v = *reinterpret_cast<const u32x4_t*>(g + (int64_t)(r0 + row) * ld + col + 8 * c);
-    *reinterpret_cast<u32x4_t*>(lds + rm_off(row, c)) = v;
-  }
+// row-major tile [rows][128] bf16: 256-byte rows of 16 chunks of 16 bytes,
+// chunk index XOR (row%16 ^ (row/16)%4): 16 consecutive rows (a fragment read)
+// and rows {4i + j : i < 16} (a store of the 4-row loads below) both spread
+// over all 16 chunk positions
+__device__ __forceinline__ int rm_off(int row, int c16) {
+  return row * 256 + ((c16 ^ ((row & 15) ^ ((row >> 4) & 3))) << 4);
 }
-
-// Same rows into a transposed LDS tile [128][64]: each thread loads 4 rows x 8
-// columns and transposes them in registers into 8 columns x 4 rows.
-__device__ __forceinline__ void load_tr(char* lds, const bf16* g, int64_t ld, int r0, int rmax, int col, int tid) {
-  const int kg = tid & 15, db = tid >> 4;
-  u32x4_t v[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = r0 + 4 * kg + j;
-    v[j] = u32x4_t{0u, 0u, 0u, 0u};
-    if (row < rmax) v[j] = *reinterpret_cast<const u32x4_t*>(g + (int64_t)row * ld + col + 8 * db);
-  }
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t a0 = v[0][p], a1 = v[1][p], a2 = v[2][p], a3 = v[3][p];
-    const u32x2_t lo = u32x2_t{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-    const u32x2_t hi = u32x2_t{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-    const int d0 = 8 * db + 2 * p;
-    *reinterpret_cast<u32x2_t*>(lds + tr_off(d0, kg)) = lo;
-    *reinterpret_cast<u32x2_t*>(lds + tr_off(d0 + 1, kg)) = hi;
-  }
+// transposed tile [128][64] bf16: 128-byte rows (one per d) of 8 chunks of 16
+// bytes, chunk index XOR (d/2)%8, so that 16 consecutive d rows (a fragment
+// read) hit 16 distinct bank groups. Within each 16-key block the four 4-key
+// groups are stored in the order 0, 2, 1, 3: the 8 keys that one lane needs
+// for an operand (groups h and 2 + h of the block) then form one 16-byte chunk.
+__device__ __forceinline__ int tr_off(int d, int c16) { return d * 128 + ((c16 ^ ((d >> 1) & 7)) << 4); }
+// byte offset of the 8-byte slot of key group kg (keys 4kg .. 4kg + 3) in row d
+__device__ __forceinline__ int tr_slot(int d, int kg) {
+  const int kp = (kg & ~3) | ((kg & 1) << 1) | ((kg >> 1) & 1);
+  return tr_off(d, kp >> 1) + ((kp & 1) << 3);
 }
 
 // A operand of a QK^T-type product: rows 32t + (lane%32) of a row-major tile,
@@ -130,15 +109,11 @@ __device__ __forceinline__ bf16x8_t rd_rm(const char* lds, int t, int s, int lan
 }
 
 // A operand of a PV-type product: d-row 32dt + (lane%32) of a transposed tile,
-// k-step j of 32-row subtile t (rows 32t + 16j + {4h..4h+3, 8+4h..8+4h+3})
+// k-step j of 32-row subtile t (rows 32t + 16j + {4h..4h+3, 8+4h..8+4h+3}):
+// key groups 8t + 4j + h and 8t + 4j + 2 + h, one 16-byte chunk
 __device__ __forceinline__ bf16x8_t rd_tr(const char* lds, int dt, int t, int j, int lane) {
   const int d = 32 * dt + (lane & 31), h = lane >> 5;
-  const int c = 8 * t + 4 * j + h;
-  u32x4_t u;
-  const u32x2_t a = *reinterpret_cast<const u32x2_t*>(lds + tr_off(d, c));
-  const u32x2_t b = *reinterpret_cast<const u32x2_t*>(lds + tr_off(d, c + 2));
-  u[0] = a[0]; u[1] = a[1]; u[2] = b[0]; u[3] = b[1];
-  return __builtin_bit_cast(bf16x8_t, u);
+  return *reinterpret_cast<const bf16x8_t*>(lds + tr_off(d, 2 * (2 * t + j) + h));
 }
 
 // B operand held in registers: row `row` (< rmax, else zero) of a strided
@@ -180,13 +155,58 @@ struct FlashParams {
   int n_blocks;      // row blocks of 128 per sequence
 };
 
+// Streamed 64-row tiles of NM matrices in flight between global memory and
+// LDS. Each thread loads 4 consecutive rows x 8 columns of every matrix; the
+// same registers then fill a row-major tile (four 16-byte stores) and/or a
+// transposed tile (transposed in registers, eight 8-byte stores). Loads and
+// stores are separate calls so that a later tile's loads can be issued a whole
+// tile of compute before their stores.
+template <int NM>
+struct TileSet {
+  u32x4_t v[NM][4];
+  __device__ __forceinline__ void load(const bf16* const (&g)[NM], const int64_t (&ld)[NM], const int (&col)[NM],
+                                       int r0, int rmax, int tid) {
+    const int kg = tid & 15, db = tid >> 4;
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = r0 + 4 * kg + j;
+        v[m][j] = u32x4_t{0u, 0u, 0u, 0u};
+        if (row < rmax) v[m][j] = *reinterpret_cast<const u32x4_t*>(g[m] + (int64_t)row * ld[m] + col[m] + 8 * db);
+      }
+  }
+  __device__ __forceinline__ void store_rm(int m, char* t, int tid) const {
+    const int kg = tid & 15, db = tid >> 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4_t*>(t + rm_off(4 * kg + j, db)) = v[m][j];
+  }
+  __device__ __forceinline__ void store_tr(int m, char* t, int tid) const {
+    const int kg = tid & 15, db = tid >> 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t a0 = v[m][0][q], a1 = v[m][1][q], a2 = v[m][2][q], a3 = v[m][3][q];
+      const u32x2_t lo = u32x2_t{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
+      const u32x2_t hi = u32x2_t{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
+      const int d0 = 8 * db + 2 * q;
+      *reinterpret_cast<u32x2_t*>(t + tr_slot(d0, kg)) = lo;
+      *reinterpret_cast<u32x2_t*>(t + tr_slot(d0 + 1, kg)) = hi;
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
-// forward: one workgroup = 128 queries of one head; wave w owns 32 of them
+// forward: one workgroup = 128 queries of one head; wave w owns 32 of them.
+// K (row-major) and V (transposed) tiles are double-buffered in LDS: while
+// tile kt is computed, tile kt + 1 (loaded during tile kt - 1) is written to
+// the other buffer and tile kt + 2's global loads are issued; one barrier per
+// tile. Registers are capped for two waves per SIMD, so two workgroups share
+// a CU and one's softmax overlaps the other's MFMAs.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(NT) void flash_fwd_kernel(FlashParams p, bf16* __restrict__ o, float* __restrict__ lse) {
-  __shared__ __align__(16) char smem[2 * TILE * 256];
-  char* sK = smem;
-  char* sV = smem + TILE * 256;  // transposed [128][64]
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_fwd_kernel(
+    FlashParams p, bf16* __restrict__ o, float* __restrict__ lse) {
+  constexpr int STAGE = 2 * TILE * 256;
+  __shared__ __align__(16) char smem[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
   const int head = blockIdx.x, b = blockIdx.z;
   const int qb = p.n_blocks - 1 - blockIdx.y;  // longest rows first
@@ -203,60 +223,79 @@ __global__ __launch_bounds__(NT) void flash_fwd_kernel(FlashParams p, bf16* __re
   float m = -INFINITY, l = 0.f;
 
   const int klast = min(q0 + BROWS, p.seq) - 1;
-  for (int k0 = 0; k0 <= klast; k0 += TILE) {
-    __syncthreads();
-    load_rm(sK, base, p.ld, k0, p.seq, kcol, tid);
-    load_tr(sV, base, p.ld, k0, p.seq, vcol, tid);
-    __syncthreads();
-    if (k0 > qw + WROWS - 1) continue;  // every key of the tile is after every query of the wave
-    f32x16_t st[2];
+  const int ntile = klast / TILE + 1;
+  const bf16* const gsrc[2] = {base, base};
+  const int64_t gld[2] = {p.ld, p.ld};
+  const int gcol[2] = {kcol, vcol};
+  TileSet<2> tp;
+  auto put = [&](char* st) {
+    tp.store_rm(0, st, tid);
+    tp.store_tr(1, st + TILE * 256, tid);
+  };
+  tp.load(gsrc, gld, gcol, 0, p.seq, tid);
+  put(smem);
+  if (ntile > 1) tp.load(gsrc, gld, gcol, TILE, p.seq, tid);
+  __syncthreads();
+  for (int kt = 0; kt < ntile; ++kt) {
+    const int k0 = kt * TILE;
+    char* sK = smem + (kt & 1) * STAGE;
+    char* sV = sK + TILE * 256;
+    if (k0 <= qw + WROWS - 1) {  // else every key of the tile is after every query of the wave
+      f32x16_t st[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      st[t] = zero16();
+      for (int t = 0; t < 2; ++t) {
+        st[t] = zero16();
 #pragma unroll
-      for (int s = 0; s < 8; ++s) st[t] = mfma(rd_rm(sK, t, s, lane), qf[s], st[t]);
-    }
-    const bool diag = k0 + TILE - 1 > qw;
-    float mx = -INFINITY;
+        for (int s = 0; s < 8; ++s) st[t] = mfma(rd_rm(sK, t, s, lane), qf[s], st[t]);
+      }
+      const bool diag = k0 + TILE - 1 > qw;
+      float mx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = st[t][r] * p.c2;
-        if (diag) {
-          const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key > qpos) v = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          float v = st[t][r] * p.c2;
+          if (diag) {
+            const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (key > qpos) v = -INFINITY;
+          }
+          st[t][r] = v;
+          mx = fmaxf(mx, v);
         }
-        st[t][r] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m, mx);
-    const float alpha = fexp2(m - mn);
-    float sum = 0.f;
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m, mx);
+      const float alpha = fexp2(m - mn);
+      float sum = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = fexp2(st[t][r] - mn);
-        st[t][r] = e;
-        sum += e;
-      }
-    sum += __shfl_xor(sum, 32, 64);
-    l = l * alpha + sum;
-    m = mn;
+        for (int r = 0; r < 16; ++r) {
+          const float e = fexp2(st[t][r] - mn);
+          st[t][r] = e;
+          sum += e;
+        }
+      sum += __shfl_xor(sum, 32, 64);
+      l = l * alpha + sum;
+      m = mn;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bf16x8_t pb = to_operand(st[t], j);
+        for (int j = 0; j < 2; ++j) {
+          const bf16x8_t pb = to_operand(st[t], j);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(rd_tr(sV, dt, t, j, lane), pb, acc[dt]);
-      }
+          for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(rd_tr(sV, dt, t, j, lane), pb, acc[dt]);
+        }
+    }
+    if (kt + 1 < ntile) {
+      // the other buffer was last read before the previous barrier
+      put(smem + ((kt + 1) & 1) * STAGE);
+      if (kt + 2 < ntile) tp.load(gsrc, gld, gcol, k0 + 2 * TILE, p.seq, tid);
+    }
+    __syncthreads();
   }
   const float inv = 1.f / l;
   store_acc_rows(acc, inv, o + (int64_t)b * p.seq * p.nq * D, (int64_t)p.nq * D, qpos, p.seq, head * D, h);
@@ -290,15 +329,14 @@ __global__ __launch_bounds__(NT) void flash_bwd_dot_kernel(const bf16* __restric
 }
 
 // ---------------------------------------------------------------------------
-// dQ: one workgroup = 128 queries of one head, streaming 64-key tiles
+// dQ: one workgroup = 128 queries of one head, streaming 64-key tiles (K and V
+// row-major, K transposed) double-buffered in LDS like the forward
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(NT) void flash_dq_kernel(FlashParams p, const bf16* __restrict__ dout,
                                                       const float* __restrict__ lse, const float* __restrict__ Dr,
                                                       bf16* __restrict__ dqkv) {
-  __shared__ __align__(16) char smem[3 * TILE * 256];
-  char* sK = smem;
-  char* sV = smem + TILE * 256;
-  char* sKt = smem + 2 * TILE * 256;  // transposed K
+  constexpr int STAGE = 3 * TILE * 256;
+  extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
   const int head = blockIdx.x, b = blockIdx.z;
   const int qb = p.n_blocks - 1 - blockIdx.y;
@@ -318,57 +356,72 @@ __global__ __launch_bounds__(NT) void flash_dq_kernel(FlashParams p, const bf16*
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = zero16();
 
+  const bf16* const gsrc[2] = {base, base};
+  const int64_t gld[2] = {p.ld, p.ld};
+  const int gcol[2] = {kcol, vcol};
   const int klast = min(q0 + BROWS, p.seq) - 1;
-  for (int k0 = 0; k0 <= klast; k0 += TILE) {
-    __syncthreads();
-    load_rm(sK, base, p.ld, k0, p.seq, kcol, tid);
-    load_rm(sV, base, p.ld, k0, p.seq, vcol, tid);
-    load_tr(sKt, base, p.ld, k0, p.seq, kcol, tid);
-    __syncthreads();
-    if (k0 > qw + WROWS - 1) continue;
-    const bool diag = k0 + TILE - 1 > qw;
+  const int ntile = klast / TILE + 1;
+  TileSet<2> ts;
+  auto put = [&](char* st) {
+    ts.store_rm(0, st, tid);
+    ts.store_rm(1, st + TILE * 256, tid);
+    ts.store_tr(0, st + 2 * TILE * 256, tid);
+  };
+  ts.load(gsrc, gld, gcol, 0, p.seq, tid);
+  put(smem);
+  if (ntile > 1) ts.load(gsrc, gld, gcol, TILE, p.seq, tid);
+  __syncthreads();
+  for (int kt = 0; kt < ntile; ++kt) {
+    const int k0 = kt * TILE;
+    const char* sK = smem + (kt & 1) * STAGE;
+    const char* sV = sK + TILE * 256;
+    const char* sKt = sK + 2 * TILE * 256;
+    if (k0 <= qw + WROWS - 1) {
+      const bool diag = k0 + TILE - 1 > qw;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      f32x16_t st = zero16(), dp = zero16();
+      for (int t = 0; t < 2; ++t) {
+        f32x16_t st = zero16(), dp = zero16();
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        st = mfma(rd_rm(sK, t, s, lane), qf[s], st);
-        dp = mfma(rd_rm(sV, t, s, lane), dof[s], dp);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = fexp2(st[r] * p.c2 - l2);
-        if (diag) {
-          const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key > qpos) pr = 0.f;
+        for (int s = 0; s < 8; ++s) {
+          st = mfma(rd_rm(sK, t, s, lane), qf[s], st);
+          dp = mfma(rd_rm(sV, t, s, lane), dof[s], dp);
         }
-        st[r] = pr * (dp[r] - dd);  // dS
-      }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bf16x8_t sb = to_operand(st, j);
+        for (int r = 0; r < 16; ++r) {
+          float pr = fexp2(st[r] * p.c2 - l2);
+          if (diag) {
+            const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (key > qpos) pr = 0.f;
+          }
+          st[r] = pr * (dp[r] - dd);  // dS
+        }
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(rd_tr(sKt, dt, t, j, lane), sb, acc[dt]);
+        for (int j = 0; j < 2; ++j) {
+          const bf16x8_t sb = to_operand(st, j);
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(rd_tr(sKt, dt, t, j, lane), sb, acc[dt]);
+        }
       }
     }
+    if (kt + 1 < ntile) {
+      put(smem + ((kt + 1) & 1) * STAGE);
+      if (kt + 2 < ntile) ts.load(gsrc, gld, gcol, k0 + 2 * TILE, p.seq, tid);
+    }
+    __syncthreads();
   }
   store_acc_rows(acc, p.scale, dqkv + (int64_t)b * p.seq * p.ld, p.ld, qpos, p.seq, head * D, h);
 }
 
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup = 128 keys of one kv head, streaming 64-query tiles of
-// every query head of the group; wave w owns 32 keys
+// every query head of the group (Q and dO row-major and transposed, with their
+// lse and D rows), double-buffered in LDS; wave w owns 32 keys
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf16* __restrict__ dout,
                                                         const float* __restrict__ lse, const float* __restrict__ Dr,
                                                         bf16* __restrict__ dqkv) {
-  __shared__ __align__(16) char smem[4 * TILE * 256 + 2 * TILE * 4];
-  char* sQ = smem;
-  char* sO = smem + TILE * 256;        // dO row-major
-  char* sQt = smem + 2 * TILE * 256;   // Q transposed
-  char* sOt = smem + 3 * TILE * 256;   // dO transposed
-  float* sL = reinterpret_cast<float*>(smem + 4 * TILE * 256);  // lse * log2(e)
-  float* sD = sL + TILE;
+  constexpr int STAGE = 4 * TILE * 256 + 2 * TILE * 4;
+  extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
   const int hk = blockIdx.x, b = blockIdx.z;
   const int kb = blockIdx.y;  // earliest keys (most queries) first
@@ -387,22 +440,48 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
 #pragma unroll
   for (int i = 0; i < 4; ++i) dk[i] = dv[i] = zero16();
 
-  for (int g = 0; g < G; ++g) {
-    const int head = hk * G + g;
-    for (int q0 = k0; q0 < p.seq; q0 += TILE) {
-      __syncthreads();
-      load_rm(sQ, base, p.ld, q0, p.seq, head * D, tid);
-      load_rm(sO, dob, ldo, q0, p.seq, head * D, tid);
-      load_tr(sQt, base, p.ld, q0, p.seq, head * D, tid);
-      load_tr(sOt, dob, ldo, q0, p.seq, head * D, tid);
-      if (tid < TILE) {
-        const int q = min(q0 + tid, p.seq - 1);
-        const int64_t si = (int64_t)head * T + (int64_t)b * p.seq + q;
-        sL[tid] = lse[si] * LOG2E;
-        sD[tid] = Dr[si];
-      }
-      __syncthreads();
-      if (q0 + TILE - 1 < kw) continue;  // every query of the tile is before every key of the wave
+  // the streamed tiles: query tile qt of head g covers queries [k0 + 64 qt, +64)
+  const int nqt = (p.seq - k0 + TILE - 1) / TILE;
+  const int ntile = G * nqt;
+  TileSet<2> ts;
+  float ls = 0.f, ds = 0.f;
+  auto fetch = [&](int i) {
+    const int g = i / nqt, q0 = k0 + (i % nqt) * TILE, head = hk * G + g;
+    const bf16* const gr[2] = {base, dob};
+    const int64_t ldr[2] = {p.ld, ldo};
+    const int colr[2] = {head * D, head * D};
+    ts.load(gr, ldr, colr, q0, p.seq, tid);
+    if (tid < TILE) {
+      const int q = min(q0 + tid, p.seq - 1);
+      const int64_t si = (int64_t)head * T + (int64_t)b * p.seq + q;
+      ls = lse[si] * LOG2E;
+      ds = Dr[si];
+    }
+  };
+  auto put = [&](char* st) {
+    ts.store_rm(0, st, tid);
+    ts.store_rm(1, st + TILE * 256, tid);
+    ts.store_tr(0, st + 2 * TILE * 256, tid);
+    ts.store_tr(1, st + 3 * TILE * 256, tid);
+    if (tid < TILE) {
+      float* sl = reinterpret_cast<float*>(st + 4 * TILE * 256);
+      sl[tid] = ls;
+      sl[TILE + tid] = ds;
+    }
+  };
+  fetch(0);
+  put(smem);
+  if (ntile > 1) fetch(1);
+  __syncthreads();
+  for (int it = 0; it < ntile; ++it) {
+    const int q0 = k0 + (it % nqt) * TILE;
+    const char* sQ = smem + (it & 1) * STAGE;
+    const char* sO = sQ + TILE * 256;
+    const char* sQt = sQ + 2 * TILE * 256;
+    const char* sOt = sQ + 3 * TILE * 256;
+    const float* sL = reinterpret_cast<const float*>(sQ + 4 * TILE * 256);
+    const float* sD = sL + TILE;
+    if (q0 + TILE - 1 >= kw) {  // else every query of the tile is before every key of the wave
       const bool diag = q0 < kw + WROWS - 1;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -412,7 +491,7 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
           st = mfma(rd_rm(sQ, u, s, lane), kf[s], st);
           dp = mfma(rd_rm(sO, u, s, lane), vf[s], dp);
         }
-        f32x16_t ds;
+        f32x16_t dsr;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qi = 32 * u + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -420,11 +499,11 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
           if (diag && kpos > q0 + qi) pr = 0.f;
           if (q0 + qi >= p.seq) pr = 0.f;
           st[r] = pr;
-          ds[r] = pr * (dp[r] - sD[qi]);
+          dsr[r] = pr * (dp[r] - sD[qi]);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const bf16x8_t pb = to_operand(st, j), sb = to_operand(ds, j);
+          const bf16x8_t pb = to_operand(st, j), sb = to_operand(dsr, j);
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt) {
             dv[dt] = mfma(rd_tr(sOt, dt, u, j, lane), pb, dv[dt]);
@@ -433,6 +512,11 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
         }
       }
     }
+    if (it + 1 < ntile) {
+      put(smem + ((it + 1) & 1) * STAGE);
+      if (it + 2 < ntile) fetch(it + 2);
+    }
+    __syncthreads();
   }
   bf16* dst = dqkv + (int64_t)b * p.seq * p.ld;
   store_acc_rows(dk, p.scale, dst, p.ld, kpos, p.seq, kcol, h);
@@ -453,6 +537,22 @@ FlashParams make_params(const AttnDesc& a, const void* qkv) {
 }
 
 double causal_pairs(const AttnDesc& a) { return (double)a.batch * a.seq * (a.seq + 1.0) / 2.0; }
+
+// double-buffered LDS stages of the backward kernels (above the 64 KB static limit)
+constexpr size_t DQ_LDS = 2 * 3 * TILE * 256;
+constexpr size_t DKDV_LDS = 2 * (4 * TILE * 256 + 2 * TILE * 4);
+
+rp_status set_lds_limits() {
+  static bool done = false;
+  if (!done) {
+    RP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&flash_dq_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)DQ_LDS));
+    RP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&flash_dkdv_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)DKDV_LDS));
+    done = true;
+  }
+  return RP_OK;
+}
 
 }  // namespace
 
@@ -476,6 +576,7 @@ rp_status flash_bwd(const AttnDesc& a, const void* qkv, const void* o, const voi
   RP_CHECK(((uintptr_t)qkv & 15) == 0 && ((uintptr_t)o & 15) == 0 && ((uintptr_t)dout & 15) == 0 &&
                ((uintptr_t)dqkv & 15) == 0,
            RP_ERR_INVALID, "flash attention: buffers must be 16-byte aligned");
+  RP_TRY(set_lds_limits());
   const FlashParams p = make_params(a, qkv);
   const int T = a.batch * a.seq;
   const int64_t rows = (int64_t)T * a.n_q;
@@ -487,13 +588,13 @@ rp_status flash_bwd(const AttnDesc& a, const void* qkv, const void* o, const voi
   {
     // dV = P^T dO and dK = dS^T Q: two of the four backward products
     TraceScope ts(s, "flash_dkdv_kernel", 4.0 * D * a.n_q * causal_pairs(a), 0.0);
-    RP_LAUNCH(flash_dkdv_kernel, dim3(a.n_kv, p.n_blocks, a.batch), dim3(NT), 0, s, p, (const bf16*)dout, lse,
+    RP_LAUNCH(flash_dkdv_kernel, dim3(a.n_kv, p.n_blocks, a.batch), dim3(NT), DKDV_LDS, s, p, (const bf16*)dout, lse,
               Dbuf, (bf16*)dqkv);
   }
   {
     // dQ = dS K and dP = dO V^T: the other two
     TraceScope ts(s, "flash_dq_kernel", 4.0 * D * a.n_q * causal_pairs(a), 0.0);
-    RP_LAUNCH(flash_dq_kernel, dim3(a.n_q, p.n_blocks, a.batch), dim3(NT), 0, s, p, (const bf16*)dout, lse, Dbuf,
+    RP_LAUNCH(flash_dq_kernel, dim3(a.n_q, p.n_blocks, a.batch), dim3(NT), DQ_LDS, s, p, (const bf16*)dout, lse, Dbuf,
               (bf16*)dqkv);
   }
   return RP_OK;
