@@ -224,7 +224,23 @@ __global__ void swiglu_bwd_kernel(const float* dm, const T* gu, T* dgu, int rows
 // cross-entropy
 // ---------------------------------------------------------------------------
 
-// one wave per row: online (max, sum-exp) over the shard's logits
+// merge (m, l) <- (m, l) + values v: l is the sum of exp(x - m) over the
+// values seen so far (m = -inf, l = 0 before the first)
+__device__ __forceinline__ void lse_merge4(float& m, float& l, float4 v) {
+  const float mn = fmaxf(fmaxf(m, fmaxf(v.x, v.y)), fmaxf(v.z, v.w));
+  l = l * __expf(m - mn) + __expf(v.x - mn) + __expf(v.y - mn) + __expf(v.z - mn) + __expf(v.w - mn);
+  m = mn;
+}
+__device__ __forceinline__ void lse_merge1(float& m, float& l, float v) {
+  const float mn = fmaxf(m, v);
+  l = l * __expf(m - mn) + __expf(v - mn);
+  m = mn;
+}
+
+// one wave per row: online (max, sum-exp) over the shard's logits. VEC: the
+// row is read as 16-byte vectors, four in flight per lane (row starts 16-byte
+// aligned), the ragged end one value per lane.
+template <bool VEC>
 __global__ __launch_bounds__(256) void ce_stats_kernel(const float* __restrict__ z, int64_t ld, int rows,
                                                        int Vs, int vlo, const int32_t* __restrict__ labels,
                                                        int vocab, float2* part, float* zlab) {
@@ -233,15 +249,22 @@ __global__ __launch_bounds__(256) void ce_stats_kernel(const float* __restrict__
   if (row >= rows) return;
   const float* zr = z + (int64_t)row * ld;
   float m = -INFINITY, l = 0.f;
-  for (int c = lane; c < Vs; c += 64) {
-    const float v = zr[c];
-    if (v > m) {
-      l = l * __expf(m - v) + 1.f;
-      m = v;
-    } else {
-      l += __expf(v - m);
+  int c0 = 0;
+  if constexpr (VEC) {
+    const float4* z4 = reinterpret_cast<const float4*>(zr);
+    const int n4 = Vs >> 2;
+    int c = lane;
+    for (; c + 192 < n4; c += 256) {
+      const float4 a = z4[c], b = z4[c + 64], d = z4[c + 128], e = z4[c + 192];
+      lse_merge4(m, l, a);
+      lse_merge4(m, l, b);
+      lse_merge4(m, l, d);
+      lse_merge4(m, l, e);
     }
+    for (; c < n4; c += 64) lse_merge4(m, l, z4[c]);
+    c0 = n4 << 2;
   }
+  for (int c = c0 + lane; c < Vs; c += 64) lse_merge1(m, l, zr[c]);
   // merge lanes in butterfly order
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -299,21 +322,56 @@ __global__ __launch_bounds__(1024) void ce_combine_kernel(int rows, int n_shards
   }
 }
 
+// one block per row: dz = (softmax(z) - onehot(label)) / n_valid for a
+// labelled row, 0 for an ignored one. VEC: 16-byte loads and 4-element stores
+// (row starts aligned), the ragged end one element per thread.
 template <class T>
-__global__ void ce_grad_kernel(const float* __restrict__ z, int64_t ld, int rows, int Vs, int vlo,
-                               const int32_t* __restrict__ labels, int vocab, const float* __restrict__ lse,
-                               const float* __restrict__ inv_n, T* __restrict__ dz, int64_t ldz) {
-  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)rows * Vs) return;
-  const int t = (int)(idx / Vs), v = (int)(idx % Vs);
+__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+template <>
+__device__ __forceinline__ void store4<bf16>(bf16* p, float a, float b, float c, float d) {
+  const uint32_t lo = uint32_t(to_bf16(a).u) | (uint32_t(to_bf16(b).u) << 16);
+  const uint32_t hi = uint32_t(to_bf16(c).u) | (uint32_t(to_bf16(d).u) << 16);
+  *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+}
+
+template <class T, bool VEC>
+__global__ __launch_bounds__(256) void ce_grad_kernel(const float* __restrict__ z, int64_t ld, int Vs, int vlo,
+                                                      const int32_t* __restrict__ labels, int vocab,
+                                                      const float* __restrict__ lse, const float* __restrict__ inv_n,
+                                                      T* __restrict__ dz, int64_t ldz) {
+  const int t = blockIdx.x;
   const int y = labels[t];
-  float out = 0.f;
-  if (y >= 0 && y < vocab) {
-    out = __expf(z[(int64_t)t * ld + v] - lse[t]);
-    if (vlo + v == y) out -= 1.f;
-    out *= inv_n[0];
+  const bool valid = y >= 0 && y < vocab;
+  const float lt = lse[t], sc = valid ? inv_n[0] : 0.f;
+  const int yl = valid ? y - vlo : -1;  // label column within the shard (may lie outside it)
+  const float* zr = z + (int64_t)t * ld;
+  T* dr = dz + (int64_t)t * ldz;
+  int c0 = 0;
+  if constexpr (VEC) {
+    const float4* z4 = reinterpret_cast<const float4*>(zr);
+    const int n4 = Vs >> 2;
+    for (int c = threadIdx.x; c < n4; c += 256) {
+      const float4 v = z4[c];
+      float o0 = __expf(v.x - lt) * sc, o1 = __expf(v.y - lt) * sc, o2 = __expf(v.z - lt) * sc,
+            o3 = __expf(v.w - lt) * sc;
+      const int j = yl - 4 * c;
+      if (j == 0) o0 -= sc;
+      if (j == 1) o1 -= sc;
+      if (j == 2) o2 -= sc;
+      if (j == 3) o3 -= sc;
+      store4<T>(dr + 4 * c, o0, o1, o2, o3);
+    }
+    c0 = n4 << 2;
   }
-  dz[(int64_t)t * ldz + v] = from_f<T>(out);
+  for (int c = c0 + threadIdx.x; c < Vs; c += 256) {
+    float o = __expf(zr[c] - lt) * sc;
+    if (c == yl) o -= sc;
+    dr[c] = from_f<T>(o);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -523,8 +581,12 @@ rp_status ce_shard_stats(const float* logits, int64_t ld, int T, int Vs, int vlo
                          int vocab, float2* part, float* zlab, hipStream_t s) {
   if (T == 0) return RP_OK;
   TraceScope ts(s, "ce_stats_kernel", 0.0, (double)T * Vs * 4 + 16.0 * T);
-  RP_LAUNCH(ce_stats_kernel, dim3(blocks_for(T, 4)), dim3(256), 0, s, logits, ld, T, Vs, vlo, labels,
-            vocab, part, zlab);
+  if (((uintptr_t)logits & 15) == 0 && ld % 4 == 0)
+    RP_LAUNCH(ce_stats_kernel<true>, dim3(blocks_for(T, 4)), dim3(256), 0, s, logits, ld, T, Vs, vlo, labels,
+              vocab, part, zlab);
+  else
+    RP_LAUNCH(ce_stats_kernel<false>, dim3(blocks_for(T, 4)), dim3(256), 0, s, logits, ld, T, Vs, vlo, labels,
+              vocab, part, zlab);
   return RP_OK;
 }
 
@@ -541,12 +603,20 @@ rp_status ce_grad(int dt, const float* logits, int64_t ld, int T, int Vs, int vl
   const int64_t n = (int64_t)T * Vs;
   if (n == 0) return RP_OK;
   TraceScope ts(s, "ce_grad_kernel", 0.0, (double)n * (4 + dtype_size(dt)) + 8.0 * T);
-  if (dt == RP_DTYPE_BF16)
-    RP_LAUNCH(ce_grad_kernel<bf16>, dim3(blocks_for(n)), dim3(256), 0, s, logits, ld, T, Vs, vlo, labels,
-              vocab, lse, inv_n, (bf16*)dz, ldz);
-  else
-    RP_LAUNCH(ce_grad_kernel<float>, dim3(blocks_for(n)), dim3(256), 0, s, logits, ld, T, Vs, vlo, labels,
-              vocab, lse, inv_n, (float*)dz, ldz);
+  const size_t es = dtype_size(dt);
+  const bool vec = ((uintptr_t)logits & 15) == 0 && ld % 4 == 0 && ((uintptr_t)dz & (4 * es - 1)) == 0 && ldz % 4 == 0;
+  const dim3 g((unsigned)T), b(256);
+  if (dt == RP_DTYPE_BF16) {
+    if (vec)
+      RP_LAUNCH((ce_grad_kernel<bf16, true>), g, b, 0, s, logits, ld, Vs, vlo, labels, vocab, lse, inv_n, (bf16*)dz, ldz);
+    else
+      RP_LAUNCH((ce_grad_kernel<bf16, false>), g, b, 0, s, logits, ld, Vs, vlo, labels, vocab, lse, inv_n, (bf16*)dz, ldz);
+  } else {
+    if (vec)
+      RP_LAUNCH((ce_grad_kernel<float, true>), g, b, 0, s, logits, ld, Vs, vlo, labels, vocab, lse, inv_n, (float*)dz, ldz);
+    else
+      RP_LAUNCH((ce_grad_kernel<float, false>), g, b, 0, s, logits, ld, Vs, vlo, labels, vocab, lse, inv_n, (float*)dz, ldz);
+  }
   return RP_OK;
 }
 

@@ -135,6 +135,34 @@ def test_bf16_lmhead_sharded_matches_oracle(W):
     assert max_rel(dw, dw_ref) < GRAD_TOL["bf16"]
 
 
+@pytest.mark.parametrize("vocab,shards", [(4093, 3), (1000, 1)])
+def test_f32_lmhead_ragged_shards_matches_oracle(W, vocab, shards):
+    """fp32 LM head + CE whose shard widths are not multiples of 4 (4093 rows
+    in shards of 1365/1364/1364, or one shard of 1000), so the cross-entropy
+    kernels run their unaligned paths next to the vector ones: loss, dx and
+    every shard's weight gradient against the oracle."""
+    say("f32 lm head ragged", vocab, shards)
+    cfg = synth.config("tiny", vocab=vocab, n_shards=shards, final_norm=False, embedding=False)
+    x = synth.activation(cfg, "x")
+    w = synth.lmhead_weights(cfg)["w"]
+    labels = synth.uniform_labels(cfg)
+    labels[3] = -1
+    labels[cfg.tokens - 1] = vocab - 1
+    wk = W(cfg)
+    wk.add_lmhead(w)
+    T, H = cfg.tokens, cfg.hidden
+    dx = torch.empty(T, H, dtype=torch.float32, device=DEV)
+    loss = torch.zeros(1, device=DEV)
+    ws = wk.ctx.workspace(B_OP_LMHEAD(), cfg.batch, cfg.seq)
+    wk.ctx.lmhead_ce_fwd_bwd(cfg.batch, cfg.seq, x.to(DEV), labels.to(DEV), loss, dx, ws)
+    wk.ctx.sync()
+    l_ref, dx_ref, dw_ref, _ = O.lmhead_fwd_bwd(x, w, labels, shards)
+    assert abs(loss.item() - l_ref.item()) / abs(l_ref.item()) < LOSS_TOL["f32"]
+    assert max_rel(dx, dx_ref) < GRAD_TOL["f32"]
+    dw = torch.cat([d.cpu() for d in wk.head["dw"]], dim=0)
+    assert max_rel(dw, dw_ref) < GRAD_TOL["f32"]
+
+
 def test_recompute_equals_kept_and_split_invariance_bf16(W):
     """Two bf16 layers: (a) backward from kept activations (fused B_1) and
     backward with recomputation from checkpoints give bit-identical dx and
