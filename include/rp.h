@@ -121,13 +121,17 @@ typedef struct rp_layer_cfg {
 } rp_layer_cfg;
 
 /* The streams a context issues on (hipStream_t values, passed as void*).
- * compute  -- all kernels
+ * compute  -- all kernels (NULL: the legacy default stream)
  * act_h2d  -- activation / checkpoint uploads (critical path)
  * act_d2h  -- activation / checkpoint downloads (critical path)
  * w_h2d    -- parameter uploads (low priority by scheduling)
  * g_d2h    -- gradient downloads (low priority by scheduling)
- * Any of them may be NULL (the legacy default stream); distinct streams are
- * needed for copies to overlap compute. */
+ * A transfer stream left NULL is created by the context (and destroyed with
+ * it) on a hardware queue of its own, at the default priority. Recommended:
+ * streams that share a hardware queue execute in one order, so a transfer
+ * stream waiting for a copy on the compute stream's queue would hold the
+ * compute kernels queued behind it. Caller-provided streams stay the
+ * caller's. */
 typedef struct rp_streams {
   void* compute;
   void* act_h2d;

@@ -170,15 +170,18 @@ def xfer_plan(sizes: Sequence[int], n_windows: int, max_chunk: int = 0, align: i
 
 
 class Context:
-    """Owns an rp_ctx plus its five default-priority torch streams."""
+    """Owns an rp_ctx. Kernels run on a default-priority torch stream (or
+    streams["compute"]); the transfer streams are the library's own, each on a
+    hardware queue of its own, unless `streams` names them."""
 
     def __init__(self, cfg, device: int = 0, streams: Optional[Dict[str, torch.cuda.Stream]] = None):
         self.cfg = cfg
         self.device = device
         dev = torch.device("cuda", device)
         names = ("compute", "act_h2d", "act_d2h", "w_h2d", "g_d2h")
-        self.streams = streams or {n: torch.cuda.Stream(device=dev) for n in names}
-        s = rp_streams(*[self.streams[n].cuda_stream for n in names])
+        self.streams = dict(streams or {})
+        self.streams.setdefault("compute", torch.cuda.Stream(device=dev))
+        s = rp_streams(*[self.streams[n].cuda_stream if n in self.streams else None for n in names])
         self._c = make_cfg(cfg)
         h = _P()
         check(lib().rp_ctx_create(device, C.byref(self._c), C.byref(s), C.byref(h)))

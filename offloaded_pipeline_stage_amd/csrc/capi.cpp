@@ -158,6 +158,19 @@ rp_status rp_ctx_create(int device, const rp_layer_cfg* cfg, const rp_streams* s
     x->w_h2d = (hipStream_t)streams->w_h2d;
     x->g_d2h = (hipStream_t)streams->g_d2h;
   }
+  // missing transfer streams: created here, each on its own hardware queue
+  // (a stream with a CU mask never shares its queue); all CUs enabled
+  x->own_d2h[0] = x->act_d2h == nullptr;
+  x->own_d2h[1] = x->g_d2h == nullptr;
+  for (hipStream_t* ps : {&x->act_h2d, &x->act_d2h, &x->w_h2d, &x->g_d2h}) {
+    if (*ps) continue;
+    rp_status st = new_queue_stream(device, ps);
+    if (st != RP_OK) {
+      (void)rp_ctx_destroy(x);
+      return st;
+    }
+    x->owned.push_back(*ps);
+  }
   x->layers.resize(kMaxLayers);  // fixed: deferred transfers keep pointers into it
   *out = x;
   return RP_OK;
@@ -181,6 +194,12 @@ rp_status rp_ctx_destroy(rp_ctx* c) {
     hipStream_t ss[5] = {c->compute, c->act_h2d, c->act_d2h, c->w_h2d, c->g_d2h};
     for (hipStream_t s : ss)
       if (hipStreamSynchronize(s) != hipSuccess) st = RP_ERR_HIP;
+    for (hipStream_t d : c->dl)
+      if (d) {
+        if (hipStreamSynchronize(d) != hipSuccess) st = RP_ERR_HIP;
+        (void)hipStreamDestroy(d);
+      }
+    for (hipStream_t d : c->owned) (void)hipStreamDestroy(d);
     for (hipEvent_t e : c->all_events) (void)hipEventDestroy(e);
   }
   delete c;

@@ -74,11 +74,19 @@ struct XWindow {
 
 }  // namespace rp
 
+namespace rp {
+// a default-priority stream on a hardware queue of its own (all CUs enabled)
+rp_status new_queue_stream(int device, hipStream_t* out);
+}  // namespace rp
+
 struct rp_ctx {
   int device = 0;
   rp_layer_cfg cfg{};
   rp::Shape sh{};
   hipStream_t compute = nullptr, act_h2d = nullptr, act_d2h = nullptr, w_h2d = nullptr, g_d2h = nullptr;
+  // transfer streams the context created (each on a hardware queue of its own)
+  std::vector<hipStream_t> owned;
+  bool own_d2h[2] = {false, false};  // act_d2h, g_d2h were created here
   std::vector<rp::LayerBinding> layers;   // indexed by layer id
   // LM head
   int vocab = 0, n_shards = 0;
@@ -94,6 +102,11 @@ struct rp_ctx {
   std::vector<hipEvent_t> all_events;    // every event created (destroyed with the context)
   std::vector<hipEvent_t> ev_free;       // recycled ticket events
   hipEvent_t ev_mark = nullptr;          // scratch: "compute reached this point"
+  // downloads into caller-provided streams run on private streams (one for
+  // activations, one for gradients, each with a hardware queue of its own),
+  // fenced into the caller's stream by two events
+  hipStream_t dl[2] = {nullptr, nullptr};
+  hipEvent_t dl_in[2] = {nullptr, nullptr}, dl_out[2] = {nullptr, nullptr};
   // kept-activation bookkeeping for RP_USE_KEPT_ACTS
   const void* kept_ws = nullptr;
   int kept_l0 = -1, kept_l1 = -1, kept_batch = 0, kept_seq = 0;

@@ -81,6 +81,9 @@ rp_status gemm_validate(const GemmDesc& d);
 // ---------------------------------------------------------------------------
 rp_status fill_zero(void* p, size_t bytes, hipStream_t s);
 rp_status copy16(void* dst, const void* src, size_t bytes, hipStream_t s);
+// device -> pinned host through a small copy kernel (host_dev: the host
+// buffer's device mapping); see download() in the transfer engine
+rp_status download_copy(void* host_dev, const void* src, size_t bytes, hipStream_t s);
 
 // y = x * rsqrt(mean(x^2) + eps) * gamma ; rstd[t] = rsqrt(...)
 rp_status rmsnorm_fwd(int dt, const void* x, const void* gamma, void* y, float* rstd, int T,

@@ -74,6 +74,34 @@ def test_streamed_weights_and_grad_download_bit_identical(env):
         assert torch.equal(gh[l], ref.layers[l]["g"].cpu())
 
 
+def test_grad_download_kernel_and_fallback_paths(env):
+    """Gradient downloads take the copy kernel when the pinned host buffer and
+    the chunk are 16-byte aligned, and a DMA copy otherwise (a host address 8
+    bytes past a boundary, a ragged size, small chunks): both must reproduce
+    the device bytes exactly, and leave the host bytes around them untouched."""
+    B, Worker = env
+    say("download paths")
+    cfg = _small_cfg()
+    wk = Worker(cfg)
+    wk.add_layer(0, synth.layer_weights(cfg, 0))
+    g = wk.layers[0]["g"].view(torch.uint8)
+    gb = wk.g_bytes
+    gen = torch.Generator().manual_seed(7)
+    g[:gb].copy_(torch.randint(0, 256, (gb,), dtype=torch.uint8, generator=gen).to(DEV))
+    torch.cuda.synchronize()
+    h_al = torch.zeros(gb, dtype=torch.uint8).pin_memory()
+    h_mis = torch.zeros(gb + 64, dtype=torch.uint8).pin_memory()
+    off, nb = 4096, 123457  # device offset and a size that is not a multiple of 16
+    wk.ctx.weight_stream_submit([(B.RP_GRAD_D2H, B.RP_TGT_LAYER, 0, 0, gb, h_al)], n_windows=3, max_chunk=1 << 16)
+    wk.ctx.weight_stream_submit([(B.RP_GRAD_D2H, B.RP_TGT_LAYER, 0, off, nb, h_mis.data_ptr() + 8)],
+                                n_windows=2, max_chunk=1 << 14)
+    wk.ctx.sync()
+    dev = g[:gb].cpu()
+    assert torch.equal(h_al, dev)
+    assert torch.equal(h_mis[8:8 + nb], dev[off:off + nb])
+    assert not h_mis[:8].any() and not h_mis[8 + nb:].any()
+
+
 def test_deferred_window_waits_for_its_ticket(env):
     B, Worker = env
     say("deferred window")
