@@ -16,7 +16,9 @@ gradients):
 HBM when the timed region starts). With --streamed the same step also uploads
 every weight from pinned host memory and downloads every gradient to it
 through rp_weight_stream_submit; that host-link-inclusive rate is reported
-under "streamed", never as `value`.
+under "streamed", never as `value`. It also reports, under "priority", the
+latency of an activation upload alone, behind an ungated weight upload, and
+with that upload gated on the activation copy's ticket.
 
 Each kernel launch in the timed region is timed by the library's own HIP
 event pairs on the compute stream (rp_trace_*); the dominant kernel is priced
@@ -205,6 +207,51 @@ def copy_calibration(ctx, mib: int):
     torch.cuda.empty_cache()
 
 
+def priority_probe(cfg, chunk_mib: int = 16, reps: int = 5):
+    """Copy priority (the pages' multi-stream transfer scheduling): latency of
+    one [T, H] activation upload as the compute stream sees it, alone, behind
+    an ungated weight upload of two layers (chunked), and with that upload
+    gated on the activation copy's ticket. Median over `reps` of each."""
+    from offloaded_pipeline_stage_amd import binding as B
+    from offloaded_pipeline_stage_amd.worker import Worker
+    wk = Worker(cfg)
+    lw = synth.layer_weights(cfg, 0)
+    host_w = wk.pack_layer(lw, pinned=True)
+    del lw
+    for l in (0, 1):
+        wk.add_layer(l, resident=False)
+    ctx = wk.ctx
+    comp = ctx.streams["compute"]
+    T, H = cfg.tokens, cfg.hidden
+    x_host = synth.activation(cfg, "x").pin_memory()
+    x_dev = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    items = [(B.RP_PARAM_H2D, B.RP_TGT_LAYER, l, 0, wk.w_bytes, host_w) for l in (0, 1)]
+    chunk = chunk_mib << 20
+
+    def once(mode):
+        ctx.sync()
+        t_mark = ctx.act_copy(B.RP_H2D, x_dev, x_host, 256)  # the ticket counter's current value
+        ctx.sync()
+        if mode == "ungated":
+            ctx.weight_stream_submit(items, n_windows=1, max_chunk=chunk)
+        elif mode == "gated":
+            ctx.weight_stream_submit(items, n_windows=1, max_chunk=chunk, gate_ticket=t_mark + 1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(comp)
+        ctx.act_copy(B.RP_H2D, x_dev, x_host)  # the compute stream waits for it
+        e1.record(comp)
+        ctx.sync()
+        return e0.elapsed_time(e1)
+
+    out = {"act_copy_MB": round(T * H * 2 / 1e6, 1), "weight_stream_GB": round(2 * wk.w_bytes / 1e9, 3),
+           "chunk_MiB": chunk_mib}
+    for mode in ("alone", "ungated", "gated"):
+        once(mode)
+        ts = sorted(once(mode) for _ in range(reps))
+        out[f"{mode}_ms"] = round(ts[len(ts) // 2], 3)
+    return out
+
+
 def cpu_baseline(cfg, seq: int):
     """The oracle, as it stands, on `seq` tokens of the same stage: layer
     forward, LM head + cross-entropy forward/backward, layer recompute +
@@ -314,6 +361,8 @@ def main():
                            "h2d_GBps_if_link_bound": round(h2d / 1e9 / (ms_s / 1e3), 1),
                            "d2h_GBps_if_link_bound": round(d2h / 1e9 / (ms_s / 1e3), 1)}
         del st
+        torch.cuda.empty_cache()
+        out["priority"] = priority_probe(cfg)
         torch.cuda.empty_cache()
 
     if not a.no_cpu_baseline:

@@ -6,15 +6,19 @@
 // Four copy streams (activation up/down, parameter up, gradient down) plus the
 // compute stream. Uploads go through the DMA engine (hipMemcpyAsync);
 // downloads are a small copy kernel writing into the device mapping of the
-// pinned host buffer, on private streams with their own hardware queues so
-// that it runs beside the stage's kernels. On this platform DMA copies in the two directions
-// share one engine and run one after the other (about 57 GB/s in total),
-// whereas a DMA upload next to a kernel download moves about 90 GB/s, so the
-// link's two directions work at once. Priority of activation copies is enforced by scheduling:
-// a window of parameter/gradient chunks is issued only behind the completion
-// event of the activation copy it is gated on, and no chunk exceeds the
-// window threshold, so an activation copy never queues behind more than one
-// chunk of the low-priority class on the shared link.
+// pinned host buffer, on streams with hardware queues of their own so that
+// they run beside the stage's kernels. On this platform DMA copies in the two
+// directions share one engine and run one after the other (about 57 GB/s in
+// total), whereas a DMA upload next to a kernel download moves about 90 GB/s:
+// the link's two directions work at once.
+//
+// Priority of activation copies is enforced by scheduling: a window of
+// parameter/gradient chunks is issued only behind the completion event of the
+// activation copy it is gated on. The gate is what matters: the copy engine
+// serves its streams first in, first out, so an upload issued ungated ahead
+// of an activation copy delays it by the whole upload, however it is chunked
+// (measured: a 67 MB activation copy takes 1.2 ms alone or gated, 17 ms
+// behind an ungated 0.87 GB upload in 16 MiB chunks).
 #include <algorithm>
 #include <numeric>
 
