@@ -32,7 +32,7 @@ profiles/<workload>_step_traffic.txt.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--streamed]
                        [--no-cpu-baseline] [--cpu-seq S] [--trace-json PATH]
-                       [--copy-calibration-mib M]
+                       [--copy-calibration-mib M] [--configs]
 """
 from __future__ import annotations
 
@@ -75,6 +75,23 @@ def layer_flops(cfg, recompute: bool) -> dict:
 
 def lmhead_flops(cfg) -> float:
     return 3 * 2.0 * cfg.tokens * cfg.hidden * cfg.vocab
+
+
+def layer_cost(cfg):
+    """(forward, backward) matrix-product FLOPs of one layer, dense or MoE
+    (active experts only), full fine-tuning or LoRA (frozen base: no weight
+    gradient products); causal attention counts the causal pairs, its
+    backward twice its forward."""
+    T, H, Q, KV = cfg.tokens, cfg.hidden, cfg.q_dim, cfg.kv_dim
+    attn_lin = 2.0 * T * H * (Q + 2 * KV) + 2.0 * T * Q * H
+    if cfg.n_experts > 0:
+        mlp = cfg.top_k * (2.0 * T * H * 2 * cfg.expert_ffn + 2.0 * T * cfg.expert_ffn * H)
+    else:
+        mlp = 2.0 * T * H * 2 * cfg.ffn + 2.0 * T * cfg.ffn * H
+    att = 4.0 * cfg.head_dim * cfg.n_q * cfg.batch * cfg.seq * (cfg.seq + 1) / 2.0
+    lin = attn_lin + mlp
+    bwd = (lin if cfg.lora_rank > 0 else 2 * lin) + 2 * att
+    return lin + att, bwd
 
 
 class Step:
@@ -252,6 +269,115 @@ def priority_probe(cfg, chunk_mib: int = 16, reps: int = 5):
     return out
 
 
+def config_sweep(reps: int = 3):
+    """Per-call and per-configuration throughput with resident weights, each
+    configuration's own call sequence: wall time with the context synced
+    (median of `reps` after one warm-up), tokens/s = T / time, and
+    matrix-product TFLOP/s."""
+    from offloaded_pipeline_stage_amd import binding as B
+    from offloaded_pipeline_stage_amd.worker import Worker
+
+    def timed(ctx, fn):
+        fn()
+        ctx.sync()
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ctx.sync()
+            ts.append((time.perf_counter() - t0) * 1e3)
+        return sorted(ts)[len(ts) // 2]
+
+    def entry(cfg, ms, flops):
+        return {"ms": round(ms, 3), "tokens_per_s": round(cfg.tokens / (ms / 1e3), 1),
+                "tflops": round(flops / (ms / 1e3) / 1e12, 1)}
+
+    out = {}
+    dev = torch.device("cuda", 0)
+    for name, n_fwd in (("tiny", 0), ("qwen3_1p7b", 4), ("llama3_8b", 1), ("qwen3_32b", 2), ("qwen3_235b_moe", 1)):
+        cfg = synth.config(name)
+        log(f"[bench] sweep {name}")
+        T, H, b, s = cfg.tokens, cfg.hidden, cfg.batch, cfg.seq
+        dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+        f_l, b_l = layer_cost(cfg)
+        wk = Worker(cfg)
+        ctx = wk.ctx
+        moe = cfg.n_experts > 0
+        n_layers = max(n_fwd, 1) + (1 if name in ("qwen3_1p7b", "qwen3_32b") else 0)
+        if name == "tiny":
+            n_layers = 2
+        for l in range(n_layers):
+            lw = synth.layer_weights(cfg, l)
+            wk.add_layer(l, lw, lora=synth.lora_weights(cfg, l, b_zero=False) if cfg.lora_rank > 0 else None)
+            del lw
+        router = [synth.router_logits(cfg, l).to(dev) for l in range(n_layers)] if moe else None
+        x = synth.activation(cfg, "x").to(dev)
+        dy = synth.activation(cfg, "dy").to(dev)
+        y, dx = torch.empty(T, H, dtype=dt, device=dev), torch.empty(T, H, dtype=dt, device=dev)
+        res = {"tokens": T}
+        if name == "tiny":
+            # fused stage over both layers with the final-norm LM head
+            head = synth.lmhead_weights(cfg)
+            wk.add_lmhead(head["w"], head["gamma_f"])
+            labels = synth.shifted_labels(synth.token_ids(cfg)).reshape(-1).to(dev)
+            loss = torch.zeros(1, device=dev)
+            ws = ctx.workspace(B.RP_OP_FUSED, b, s, 2)
+            ws_h = ctx.workspace(B.RP_OP_LMHEAD, b, s)
+
+            def fused():
+                ctx.stage_fwd(0, 2, b, s, x, y, ws, flags=B.RP_KEEP_ACTS)
+                ctx.lmhead_ce_fwd_bwd(b, s, y, labels, loss, dy, ws_h)
+                ctx.stage_bwd_recompute(0, 2, b, s, dy, dx, ws, flags=B.RP_USE_KEPT_ACTS)
+            res["fused_2_layers_with_lm_head"] = entry(cfg, timed(ctx, fused), 2 * (f_l + b_l) + lmhead_flops(cfg))
+            res["note"] = "fp32: the generic FMA GEMM path, not MFMA"
+        elif name == "llama3_8b":
+            head = synth.lmhead_weights(cfg)
+            wk.add_lmhead(head["w"])
+            del head
+            labels = synth.uniform_labels(cfg).to(dev)
+            loss = torch.zeros(1, device=dev)
+            ck = [torch.empty(T, H, dtype=dt).pin_memory()]
+            ws_f = ctx.workspace(B.RP_OP_STAGE_FWD, b, s, 1)
+            ws_b = ctx.workspace(B.RP_OP_STAGE_BWD, b, s, 1)
+            ws_h = ctx.workspace(B.RP_OP_LMHEAD, b, s)
+            t_f = timed(ctx, lambda: ctx.stage_fwd(0, 1, b, s, x, y, ws_f, ckpt_host=ck))
+            t_h = timed(ctx, lambda: ctx.lmhead_ce_fwd_bwd(b, s, y, labels, loss, dy, ws_h))
+            t_b = timed(ctx, lambda: ctx.stage_bwd_recompute(0, 1, b, s, dy, dx, ws_b, ckpt=ck))
+            res["fwd_1_layer"] = entry(cfg, t_f, f_l)
+            res["lm_head_4_shards"] = entry(cfg, t_h, lmhead_flops(cfg))
+            res["bwd_recompute_1_layer"] = entry(cfg, t_b, f_l + b_l)
+            res["fwd_plus_bwd_recompute_1_layer"] = entry(cfg, t_f + t_b, 2 * f_l + b_l)
+            del ws_f, ws_b
+            torch.cuda.empty_cache()
+            ws = ctx.workspace(B.RP_OP_FUSED, b, s, 1)
+
+            def fused():
+                ctx.stage_fwd(0, 1, b, s, x, y, ws, flags=B.RP_KEEP_ACTS)
+                ctx.lmhead_ce_fwd_bwd(b, s, y, labels, loss, dy, ws_h)
+                ctx.stage_bwd_recompute(0, 1, b, s, dy, dx, ws, flags=B.RP_USE_KEPT_ACTS)
+            res["fused_b1_layer_with_lm_head"] = entry(cfg, timed(ctx, fused), f_l + b_l + lmhead_flops(cfg))
+            t_model = 32 * (t_f + t_b) + t_h
+            res["extrapolated_full_8b_model"] = {
+                "ms": round(t_model, 1), "tokens_per_s": round(T / (t_model / 1e3), 1),
+                "note": "extrapolation: T / (32 (t_fwd + t_bwd_recompute) + t_lm_head), weights resident"}
+        else:
+            ws_f = ctx.workspace(B.RP_OP_STAGE_FWD, b, s, max(n_fwd, 1))
+            ws_b = ctx.workspace(B.RP_OP_STAGE_BWD, b, s, 1)
+            lb = n_layers - 1  # the backward layer
+            rf = router[:n_fwd] if moe else None
+            rb = [router[lb]] if moe else None
+            t_f = timed(ctx, lambda: ctx.stage_fwd(0, n_fwd, b, s, x, y, ws_f, router=rf))
+            t_b = timed(ctx, lambda: ctx.stage_bwd_recompute(lb, lb + 1, b, s, dy, dx, ws_b, ckpt=[x], router=rb,
+                                                              flags=B.RP_CKPT_DEVICE))
+            res[f"fwd_{n_fwd}_layers"] = entry(cfg, t_f, n_fwd * f_l)
+            res["bwd_recompute_1_layer"] = entry(cfg, t_b, f_l + b_l)
+            res["stage_total"] = entry(cfg, t_f + t_b, (n_fwd + 1) * f_l + b_l)
+        out[name] = res
+        del wk, ctx
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cfg, seq: int):
     """The oracle, as it stands, on `seq` tokens of the same stage: layer
     forward, LM head + cross-entropy forward/backward, layer recompute +
@@ -284,6 +410,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seq", type=int, default=1024)
     ap.add_argument("--trace-json", default=None, help="write the per-kernel table here")
+    ap.add_argument("--configs", action="store_true",
+                    help="also time every configuration's own call sequence (resident weights)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one device copy of this size (for the HBM counter runs)")
     a = ap.parse_args()
@@ -365,6 +493,8 @@ def main():
         out["priority"] = priority_probe(cfg)
         torch.cuda.empty_cache()
 
+    if a.configs:
+        out["configs"] = config_sweep()
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, a.cpu_seq)
     print(json.dumps(out), flush=True)
