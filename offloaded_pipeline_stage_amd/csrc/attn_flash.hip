@@ -380,12 +380,23 @@ __global__ __launch_bounds__(NT) void flash_dq_kernel(FlashParams p, const bf16*
       const bool diag = k0 + TILE - 1 > qw;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
+        // fragment reads issued ahead of the products (see flash_dkdv_kernel)
+        bf16x8_t fk[8], fv[8], tk[2][4];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          fk[s] = rd_rm(sK, t, s, lane);
+          fv[s] = rd_rm(sV, t, s, lane);
+        }
         f32x16_t st = zero16(), dp = zero16();
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-          st = mfma(rd_rm(sK, t, s, lane), qf[s], st);
-          dp = mfma(rd_rm(sV, t, s, lane), dof[s], dp);
+          st = mfma(fk[s], qf[s], st);
+          dp = mfma(fv[s], dof[s], dp);
         }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) tk[j][dt] = rd_tr(sKt, dt, t, j, lane);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float pr = fexp2(st[r] * p.c2 - l2);
@@ -399,7 +410,7 @@ __global__ __launch_bounds__(NT) void flash_dq_kernel(FlashParams p, const bf16*
         for (int j = 0; j < 2; ++j) {
           const bf16x8_t sb = to_operand(st, j);
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(rd_tr(sKt, dt, t, j, lane), sb, acc[dt]);
+          for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(tk[j][dt], sb, acc[dt]);
         }
       }
     }
@@ -483,31 +494,67 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
     const float* sD = sL + TILE;
     if (q0 + TILE - 1 >= kw) {  // else every query of the tile is before every key of the wave
       const bool diag = q0 < kw + WROWS - 1;
-#pragma unroll
+      // the two 32-query sub-tiles one after the other (kept rolled: their
+      // fragment registers would not fit side by side)
+#pragma unroll 1
       for (int u = 0; u < 2; ++u) {
+        // all fragment reads of the sub-tile are issued before the products
+        // that use them: one wave per SIMD, so nothing else would hide a
+        // read's latency in front of each MFMA
+        bf16x8_t fq[8], fo[8], tq[2][4], to[2][4];  // to/tq: j = 0, 1
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          fq[s] = rd_rm(sQ, u, s, lane);
+          fo[s] = rd_rm(sO, u, s, lane);
+        }
         f32x16_t st = zero16(), dp = zero16();
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-          st = mfma(rd_rm(sQ, u, s, lane), kf[s], st);
-          dp = mfma(rd_rm(sO, u, s, lane), vf[s], dp);
+          st = mfma(fq[s], kf[s], st);
+          dp = mfma(fo[s], vf[s], dp);
+        }
+        // the j = 0 transposed fragments load under the softmax arithmetic,
+        // the j = 1 ones under the j = 0 products
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          to[0][dt] = rd_tr(sOt, dt, u, 0, lane);
+          tq[0][dt] = rd_tr(sQt, dt, u, 0, lane);
         }
         f32x16_t dsr;
+        // registers 4g .. 4g + 3 hold queries 32u + 8g + 4h + 0..3: their
+        // lse and D values are one 16-byte read each
+        float4 lq[4], dq4[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          lq[g] = *reinterpret_cast<const float4*>(sL + 32 * u + 8 * g + 4 * h);
+          dq4[g] = *reinterpret_cast<const float4*>(sD + 32 * u + 8 * g + 4 * h);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qi = 32 * u + 8 * (r >> 2) + 4 * h + (r & 3);
-          float pr = fexp2(st[r] * p.c2 - sL[qi]);
+          const float4 l4 = lq[r >> 2], d4 = dq4[r >> 2];
+          const float lv = (r & 3) == 0 ? l4.x : (r & 3) == 1 ? l4.y : (r & 3) == 2 ? l4.z : l4.w;
+          const float dv_ = (r & 3) == 0 ? d4.x : (r & 3) == 1 ? d4.y : (r & 3) == 2 ? d4.z : d4.w;
+          float pr = fexp2(st[r] * p.c2 - lv);
           if (diag && kpos > q0 + qi) pr = 0.f;
           if (q0 + qi >= p.seq) pr = 0.f;
           st[r] = pr;
-          dsr[r] = pr * (dp[r] - sD[qi]);
+          dsr[r] = pr * (dp[r] - dv_);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const bf16x8_t pb = to_operand(st, j), sb = to_operand(dsr, j);
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt) {
-            dv[dt] = mfma(rd_tr(sOt, dt, u, j, lane), pb, dv[dt]);
-            dk[dt] = mfma(rd_tr(sQt, dt, u, j, lane), sb, dk[dt]);
+            dv[dt] = mfma(to[j][dt], pb, dv[dt]);
+            dk[dt] = mfma(tq[j][dt], sb, dk[dt]);
+          }
+          if (j == 0) {
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+              to[1][dt] = rd_tr(sOt, dt, u, 1, lane);
+              tq[1][dt] = rd_tr(sQt, dt, u, 1, lane);
+            }
           }
         }
       }
