@@ -26,13 +26,20 @@ __host__ __device__ inline float to_f(bf16 x) {
 }
 
 // fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+// fp32 -> bf16, round to nearest even. On the device the hardware
+// conversion (v_cvt_pk_bf16_f32 on gfx950) does it in one instruction; the
+// host spells out the same rounding.
 __host__ __device__ inline bf16 to_bf16(float f) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return bf16{__builtin_bit_cast(uint16_t, (__bf16)f)};
+#else
   union { uint32_t u; float f; } c;
   c.f = f;
   uint32_t u = c.u;
   if ((u & 0x7fffffffu) > 0x7f800000u) return bf16{uint16_t((u >> 16) | 0x40u)};
   u += 0x7fffu + ((u >> 16) & 1u);
   return bf16{uint16_t(u >> 16)};
+#endif
 }
 
 template <class T> __host__ __device__ inline T from_f(float f);

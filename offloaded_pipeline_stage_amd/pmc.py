@@ -9,8 +9,9 @@ its steps (`--copy-calibration-mib`): the scale factor is the copy's known bytes
 divided by what the counter reports for it.
 
 The summary records, for each kernel, a hash of the source file that
-defines it; `traffic_for` returns None when that file has changed since the
-counters were taken, so a stale figure is never reported for a new kernel.
+defines it and of the library's headers; `traffic_for` returns None when
+any of them has changed since the counters were taken, so a stale figure is
+never reported for a new kernel.
 """
 from __future__ import annotations
 
@@ -62,7 +63,12 @@ def kernel_source(base: str) -> str | None:
 
 
 def source_hash(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Hash of the file that defines a kernel together with every header of
+    the library (a kernel's code also comes from the helpers it includes)."""
+    h = hashlib.sha256(open(path, "rb").read())
+    for hp in sorted(glob.glob(os.path.join(CSRC, "*.h"))):
+        h.update(open(hp, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def _dispatches(path: str, counter: str):

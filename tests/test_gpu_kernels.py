@@ -146,3 +146,30 @@ def test_copy_is_bit_exact(B, nbytes):
     assert not out[nbytes:].any()  # nothing written past the end
     with pytest.raises(B.RPError):
         ctx.op_copy(dst[1:17], s[:16])  # misaligned destination
+
+
+def test_bf16_output_rounding_is_nearest_even(B):
+    """bf16 outputs round fp32 to nearest even exactly like torch: C = A B^T
+    with selector rows in A (ones at k = m and k = m + 8) makes every output an
+    fp32 sum of two bf16 values, many of them exact ties between two bf16
+    neighbours; the bf16 result must equal torch's rounding of that sum bit
+    for bit (finite values, including subnormal and huge magnitudes)."""
+    ctx = _ctx(B)
+    M, N, K = 64, 96, 80
+    g = torch.Generator().manual_seed(11)
+    A = torch.zeros(M, K, dtype=torch.bfloat16)
+    for m in range(M):
+        A[m, m] = 1.0
+        A[m, m + 8] = 1.0
+    # B entries: random magnitudes over a wide exponent range, pairs chosen so
+    # that sums need rounding (ties included: b2 = b1 * 2^-8 lands on a tie)
+    base = torch.randn(N, K, generator=g) * torch.exp2(torch.randint(-100, 100, (N, K), generator=g).float())
+    Bm = base.to(torch.bfloat16)
+    Bm[:, 8:16] = (Bm[:, 0:8].float() * 2.0 ** -8).to(torch.bfloat16)
+    ref = (Bm.float()[:, :M] + Bm.float()[:, 8:M + 8]).t().contiguous().to(torch.bfloat16)
+    C = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    say("bf16 rounding")
+    ctx.op_gemm_bf16(M, N, K, A.cuda(), K, True, Bm.cuda(), K, True, C, N, False)
+    ctx.sync()
+    got = C.cpu()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
