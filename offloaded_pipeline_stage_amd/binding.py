@@ -8,7 +8,9 @@ otherwise -- there is no fallback path.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes as C
+import weakref
 import os
 from typing import Dict, Optional, Sequence
 
@@ -169,6 +171,20 @@ def xfer_plan(sizes: Sequence[int], n_windows: int, max_chunk: int = 0, align: i
         return [(it[k], of[k], by[k], wi[k]) for k in range(nc.value)]
 
 
+# contexts still open at interpreter exit are destroyed before the HIP runtime
+# shuts down (their transfer streams belong to the library)
+_LIVE = weakref.WeakSet()
+
+
+@atexit.register
+def _close_live():
+    for c in list(_LIVE):
+        try:
+            c.close()
+        except Exception:
+            pass
+
+
 class Context:
     """Owns an rp_ctx. Kernels run on a default-priority torch stream (or
     streams["compute"]); the transfer streams are the library's own, each on a
@@ -186,6 +202,7 @@ class Context:
         h = _P()
         check(lib().rp_ctx_create(device, C.byref(self._c), C.byref(s), C.byref(h)))
         self.h = h
+        _LIVE.add(self)
         # every tensor handed to an enqueueing call stays referenced until
         # sync(): the library reads and writes them asynchronously on its own
         # streams, so torch must not recycle their memory before then
@@ -207,13 +224,16 @@ class Context:
 
     def close(self):
         if self.h:
+            _LIVE.discard(self)
             check(lib().rp_ctx_destroy(self.h))
             self.h = None
 
     def __del__(self):
         try:
             if getattr(self, "h", None):
+                _LIVE.discard(self)
                 lib().rp_ctx_destroy(self.h)
+                self.h = None
         except Exception:
             pass
 
