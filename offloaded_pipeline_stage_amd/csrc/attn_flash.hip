@@ -31,6 +31,8 @@
 // The backward is two deterministic kernels (no atomics): dK/dV per key block
 // (summing over the query heads of its kv group and all later queries), and
 // dQ per query block; both recompute the probabilities from lse.
+#include <type_traits>
+
 #include "attn_flash.h"
 #include "trace.h"
 
@@ -50,10 +52,17 @@ constexpr int BROWS = 128;    // rows owned by one workgroup
 constexpr int TILE = 64;      // streamed rows per LDS tile
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+constexpr float RESCALE_LOG2 = 8.f;  // forward: lazy rescale threshold (log2 units)
 
 bool g_flash_on = true;
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float lane_of(float4 v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
+
+// wave index held in a scalar register, so that branches on the wave's rows
+// (tile skipping, causal-mask tiles) are uniform branches, not masked code
+__device__ __forceinline__ int wave_id(int tid) { return __builtin_amdgcn_readfirstlane(tid >> 6); }
 
 __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -66,8 +75,12 @@ __device__ __forceinline__ f32x16_t zero16() {
   return z;
 }
 
+// two fp32 values -> packed bf16 pair (round to nearest even), one
+// v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return uint32_t(to_bf16(a).u) | (uint32_t(to_bf16(b).u) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 // registers 8j..8j+7 of a score tile as a bf16x8 B operand
@@ -207,7 +220,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     FlashParams p, bf16* __restrict__ o, float* __restrict__ lse) {
   constexpr int STAGE = 2 * TILE * 256;
   __shared__ __align__(16) char smem[2 * STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(tid), h = lane >> 5, n = lane & 31;
   const int head = blockIdx.x, b = blockIdx.z;
   const int qb = p.n_blocks - 1 - blockIdx.y;  // longest rows first
   const int hk = head / (p.nq / p.nkv);
@@ -236,11 +249,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   put(smem);
   if (ntile > 1) tp.load(gsrc, gld, gcol, TILE, p.seq, tid);
   __syncthreads();
-  for (int kt = 0; kt < ntile; ++kt) {
+  // one key tile; MASK: the tile reaches past the wave's first query (the
+  // last one or two tiles; keys past the sequence end fall in them too, since
+  // every query is before the end). The two variants are separate loops so
+  // that the interior tiles carry no masking code at all.
+  auto tile = [&](int kt, auto mask_c) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_c)::value;
     const int k0 = kt * TILE;
     char* sK = smem + (kt & 1) * STAGE;
     char* sV = sK + TILE * 256;
-    if (k0 <= qw + WROWS - 1) {  // else every key of the tile is after every query of the wave
+    if (!MASK || k0 <= qw + WROWS - 1) {  // else every key of the tile is after every query of the wave
       f32x16_t st[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -248,39 +266,54 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
         for (int s = 0; s < 8; ++s) st[t] = mfma(rd_rm(sK, t, s, lane), qf[s], st[t]);
       }
-      const bool diag = k0 + TILE - 1 > qw;
       float mx = -INFINITY;
+      if constexpr (MASK) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = st[t][r] * p.c2;
-          if (diag) {
+          for (int r = 0; r < 16; ++r) {
             const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (key > qpos) v = -INFINITY;
+            const float v = key > qpos ? -INFINITY : st[t][r] * p.c2;
+            st[t][r] = v;
+            mx = fmaxf(mx, v);
           }
-          st[t][r] = v;
-          mx = fmaxf(mx, v);
-        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            st[t][r] *= p.c2;
+            mx = fmaxf(mx, st[t][r]);
+          }
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(m, mx);
-      const float alpha = fexp2(m - mn);
+      // The running max moves only when some lane's tile max exceeds it by
+      // more than 2^RESCALE_LOG2: until then the probabilities are taken
+      // against the stale max (each at most 2^RESCALE_LOG2, exact in fp32 and
+      // as bf16 operands), which leaves l, acc and lse = m + log2(l)
+      // unchanged and skips the rescale of the accumulator on most tiles.
+      // Tile 0 holds key 0 <= every query, so m is finite after it.
+      if (__builtin_amdgcn_ballot_w64(mx > m + RESCALE_LOG2) != 0) {  // uniform over the wave
+        const float mn = fmaxf(m, mx);
+        const float alpha = fexp2(m - mn);
+        l *= alpha;
+        m = mn;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+      }
       float sum = 0.f;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = fexp2(st[t][r] - mn);
+          const float e = fexp2(st[t][r] - m);
           st[t][r] = e;
           sum += e;
         }
       sum += __shfl_xor(sum, 32, 64);
-      l = l * alpha + sum;
-      m = mn;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+      l += sum;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -296,7 +329,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       if (kt + 2 < ntile) tp.load(gsrc, gld, gcol, k0 + 2 * TILE, p.seq, tid);
     }
     __syncthreads();
-  }
+  };
+  // tiles wholly at or before the wave's first query: k0 + TILE - 1 <= qw
+  const int kfree = min(ntile, (qw + 1) / TILE);
+  int kt = 0;
+  for (; kt < kfree; ++kt) tile(kt, std::false_type{});
+  for (; kt < ntile; ++kt) tile(kt, std::true_type{});
   const float inv = 1.f / l;
   store_acc_rows(acc, inv, o + (int64_t)b * p.seq * p.nq * D, (int64_t)p.nq * D, qpos, p.seq, head * D, h);
   if (h == 0 && qpos < p.seq) lse[(int64_t)head * gridDim.z * p.seq + (int64_t)b * p.seq + qpos] = (m + __log2f(l)) * LN2;
@@ -337,7 +375,7 @@ __global__ __launch_bounds__(NT) void flash_dq_kernel(FlashParams p, const bf16*
                                                       bf16* __restrict__ dqkv) {
   constexpr int STAGE = 3 * TILE * 256;
   extern __shared__ __align__(16) char smem[];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(tid), h = lane >> 5, n = lane & 31;
   const int head = blockIdx.x, b = blockIdx.z;
   const int qb = p.n_blocks - 1 - blockIdx.y;
   const int hk = head / (p.nq / p.nkv);
@@ -371,13 +409,14 @@ __global__ __launch_bounds__(NT) void flash_dq_kernel(FlashParams p, const bf16*
   put(smem);
   if (ntile > 1) ts.load(gsrc, gld, gcol, TILE, p.seq, tid);
   __syncthreads();
-  for (int kt = 0; kt < ntile; ++kt) {
+  // one key tile; MASK as in the forward (separate loops, see there)
+  auto tile = [&](int kt, auto mask_c) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_c)::value;
     const int k0 = kt * TILE;
     const char* sK = smem + (kt & 1) * STAGE;
     const char* sV = sK + TILE * 256;
     const char* sKt = sK + 2 * TILE * 256;
-    if (k0 <= qw + WROWS - 1) {
-      const bool diag = k0 + TILE - 1 > qw;
+    if (!MASK || k0 <= qw + WROWS - 1) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         // fragment reads issued ahead of the products (see flash_dkdv_kernel)
@@ -397,14 +436,16 @@ __global__ __launch_bounds__(NT) void flash_dq_kernel(FlashParams p, const bf16*
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt) tk[j][dt] = rd_tr(sKt, dt, t, j, lane);
+        if constexpr (MASK) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pr = fexp2(st[r] * p.c2 - l2);
-          if (diag) {
+          for (int r = 0; r < 16; ++r) {
             const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (key > qpos) pr = 0.f;
+            const float pr = key > qpos ? 0.f : fexp2(st[r] * p.c2 - l2);
+            st[r] = pr * (dp[r] - dd);  // dS
           }
-          st[r] = pr * (dp[r] - dd);  // dS
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) st[r] = fexp2(st[r] * p.c2 - l2) * (dp[r] - dd);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -419,7 +460,11 @@ __global__ __launch_bounds__(NT) void flash_dq_kernel(FlashParams p, const bf16*
       if (kt + 2 < ntile) ts.load(gsrc, gld, gcol, k0 + 2 * TILE, p.seq, tid);
     }
     __syncthreads();
-  }
+  };
+  const int kfree = min(ntile, (qw + 1) / TILE);
+  int kt = 0;
+  for (; kt < kfree; ++kt) tile(kt, std::false_type{});
+  for (; kt < ntile; ++kt) tile(kt, std::true_type{});
   store_acc_rows(acc, p.scale, dqkv + (int64_t)b * p.seq * p.ld, p.ld, qpos, p.seq, head * D, h);
 }
 
@@ -433,7 +478,7 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
                                                         bf16* __restrict__ dqkv) {
   constexpr int STAGE = 4 * TILE * 256 + 2 * TILE * 4;
   extern __shared__ __align__(16) char smem[];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(tid), h = lane >> 5, n = lane & 31;
   const int hk = blockIdx.x, b = blockIdx.z;
   const int kb = blockIdx.y;  // earliest keys (most queries) first
   const int G = p.nq / p.nkv;
@@ -484,7 +529,11 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
   put(smem);
   if (ntile > 1) fetch(1);
   __syncthreads();
-  for (int it = 0; it < ntile; ++it) {
+  // one query tile; MASK: the tile holds queries before some key of the
+  // wave (the diagonal) or past the sequence end. Separate loops per variant
+  // keep the masking code out of the interior tiles.
+  auto tile = [&](int it, auto mask_c) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_c)::value;
     const int q0 = k0 + (it % nqt) * TILE;
     const char* sQ = smem + (it & 1) * STAGE;
     const char* sO = sQ + TILE * 256;
@@ -492,8 +541,7 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
     const char* sOt = sQ + 3 * TILE * 256;
     const float* sL = reinterpret_cast<const float*>(sQ + 4 * TILE * 256);
     const float* sD = sL + TILE;
-    if (q0 + TILE - 1 >= kw) {  // else every query of the tile is before every key of the wave
-      const bool diag = q0 < kw + WROWS - 1;
+    if (!MASK || q0 + TILE - 1 >= kw) {  // else every query of the tile is before every key of the wave
       // the two 32-query sub-tiles one after the other (kept rolled: their
       // fragment registers would not fit side by side)
 #pragma unroll 1
@@ -529,17 +577,21 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
           lq[g] = *reinterpret_cast<const float4*>(sL + 32 * u + 8 * g + 4 * h);
           dq4[g] = *reinterpret_cast<const float4*>(sD + 32 * u + 8 * g + 4 * h);
         }
+        if constexpr (MASK) {  // kpos > q only on the diagonal
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = 32 * u + 8 * (r >> 2) + 4 * h + (r & 3);
-          const float4 l4 = lq[r >> 2], d4 = dq4[r >> 2];
-          const float lv = (r & 3) == 0 ? l4.x : (r & 3) == 1 ? l4.y : (r & 3) == 2 ? l4.z : l4.w;
-          const float dv_ = (r & 3) == 0 ? d4.x : (r & 3) == 1 ? d4.y : (r & 3) == 2 ? d4.z : d4.w;
-          float pr = fexp2(st[r] * p.c2 - lv);
-          if (diag && kpos > q0 + qi) pr = 0.f;
-          if (q0 + qi >= p.seq) pr = 0.f;
-          st[r] = pr;
-          dsr[r] = pr * (dp[r] - dv_);
+          for (int r = 0; r < 16; ++r) {
+            const int q = q0 + 32 * u + 8 * (r >> 2) + 4 * h + (r & 3);
+            const float pr = (kpos > q || q >= p.seq) ? 0.f : fexp2(st[r] * p.c2 - lane_of(lq[r >> 2], r & 3));
+            st[r] = pr;
+            dsr[r] = pr * (dp[r] - lane_of(dq4[r >> 2], r & 3));
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float pr = fexp2(st[r] * p.c2 - lane_of(lq[r >> 2], r & 3));
+            st[r] = pr;
+            dsr[r] = pr * (dp[r] - lane_of(dq4[r >> 2], r & 3));
+          }
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -564,6 +616,16 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
       if (it + 2 < ntile) fetch(it + 2);
     }
     __syncthreads();
+  };
+  // per query head: tiles qt < qa reach the wave's diagonal (q0 < kw + WROWS
+  // - 1), tiles qt >= qb pass the sequence end (q0 + TILE > seq)
+  const int qa = min(nqt, (kw + WROWS - 1 - k0 + TILE - 1) / TILE);
+  const int qb = max(qa, (p.seq - k0) / TILE);
+  for (int g = 0; g < G; ++g) {
+    int qt = 0;
+    for (; qt < qa; ++qt) tile(g * nqt + qt, std::true_type{});
+    for (; qt < qb; ++qt) tile(g * nqt + qt, std::false_type{});
+    for (; qt < nqt; ++qt) tile(g * nqt + qt, std::true_type{});
   }
   bf16* dst = dqkv + (int64_t)b * p.seq * p.ld;
   store_acc_rows(dk, p.scale, dst, p.ld, kpos, p.seq, kcol, h);
