@@ -45,6 +45,18 @@ __device__ __forceinline__ void store_vec<bf16>(bf16* p, const float* in) {
   *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// V consecutive elements of type T as floats (16-byte loads where they fit)
+template <class T, int V>
+__device__ __forceinline__ void load_n(const T* p, float* out) {
+  if constexpr (Vec<T>::N <= V) {
+#pragma unroll
+    for (int q = 0; q < V; q += Vec<T>::N) load_vec<T>(p + q, out + q);
+  } else {
+#pragma unroll
+    for (int q = 0; q < V; ++q) out[q] = to_f(p[q]);
+  }
+}
+
 __global__ void fill_zero_kernel(uint4* p, size_t n16, uint8_t* tail, size_t ntail) {
   size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -109,7 +121,7 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const T* __restrict__ 
 // dx = r*(g*gamma) - x * r^3 * mean(g*gamma*x) + resid
 // Each block owns RB consecutive rows (one wave per row at a time) and writes
 // its dgamma partial row; a second kernel sums the partials in block order.
-constexpr int RMS_BWD_ROWS = 32;
+constexpr int RMS_BWD_ROWS = 16;
 
 template <class T, class TR>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
@@ -164,12 +176,108 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(
     part[(int64_t)blockIdx.x * H + c] = sm[c] + sm[H + c] + sm[2 * H + c] + sm[3 * H + c];
 }
 
-__global__ void sum_rows_kernel(const float* __restrict__ part, int nrow, int H, float* __restrict__ out) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= H) return;
+// RMSNorm backward with the row in registers (H = 64 V NC): lane l owns the
+// columns (64 j + l) V .. + V - 1 for j < NC; a row is loaded once, all its
+// loads issued together. Each wave sums its share of dgamma over its rows
+// (wave, wave + 4 gridDim, ...) in its own LDS row (16-byte read-modify-
+// writes of the lane's own columns); the block's four rows are then added
+// into one partial row. Same per-row arithmetic as rmsnorm_bwd_kernel.
+template <class T, class TR, int NC>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_rows_kernel(
+    const float* __restrict__ g, const T* __restrict__ x, const T* __restrict__ gamma,
+    const float* __restrict__ rstd, const TR* __restrict__ resid, float* __restrict__ out_f32,
+    T* __restrict__ out_dt, float* __restrict__ part, int rows) {
+  constexpr int V = Vec<T>::N, H = 64 * V * NC;
+  typedef typename Vec<T>::type VT;
+  extern __shared__ float sm[];  // [4][H]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* my = sm + wave * H;
+#pragma unroll
+  for (int j = 0; j < NC; ++j)
+#pragma unroll
+    for (int q = 0; q < V; q += 4)
+      *reinterpret_cast<float4*>(my + (64 * j + lane) * V + q) = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int row = blockIdx.x * 4 + wave; row < rows; row += gridDim.x * 4) {
+    const float r = rstd[row];
+    const int64_t ro = (int64_t)row * H;
+    VT xr[NC];  // x as loaded (16 bytes per chunk)
+    float gv[NC][V];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int c = (64 * j + lane) * V;
+      xr[j] = *reinterpret_cast<const VT*>(x + ro + c);
+#pragma unroll
+      for (int q = 0; q < V; q += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(g + ro + c + q);
+        gv[j][q] = v.x; gv[j][q + 1] = v.y; gv[j][q + 2] = v.z; gv[j][q + 3] = v.w;
+      }
+    }
+    float dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      float xv[V], gm[V];
+      load_vec<T>(reinterpret_cast<const T*>(&xr[j]), xv);
+      load_vec<T>(gamma + (64 * j + lane) * V, gm);
+#pragma unroll
+      for (int i = 0; i < V; ++i) dot = fmaf(gv[j][i] * gm[i], xv[i], dot);
+    }
+    dot = wave_sum(dot);
+    const float coef = r * r * r * dot / (float)H;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int c = (64 * j + lane) * V;
+      float xv[V], gm[V], o[V];
+      load_vec<T>(reinterpret_cast<const T*>(&xr[j]), xv);
+      load_vec<T>(gamma + c, gm);
+      float rv[V];
+      if (resid) load_n<TR, V>(resid + ro + c, rv);
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        float v = r * gv[j][i] * gm[i] - xv[i] * coef;
+        if (resid) v += rv[i];
+        o[i] = v;
+      }
+#pragma unroll
+      for (int q = 0; q < V; q += 4) {
+        float4* a = reinterpret_cast<float4*>(my + c + q);
+        float4 t = *a;
+        t.x += gv[j][q] * xv[q] * r;
+        t.y += gv[j][q + 1] * xv[q + 1] * r;
+        t.z += gv[j][q + 2] * xv[q + 2] * r;
+        t.w += gv[j][q + 3] * xv[q + 3] * r;
+        *a = t;
+      }
+      if (out_f32) {
+#pragma unroll
+        for (int q = 0; q < V; q += 4)
+          *reinterpret_cast<float4*>(out_f32 + ro + c + q) = make_float4(o[q], o[q + 1], o[q + 2], o[q + 3]);
+      }
+      if (out_dt) store_vec<T>(out_dt + ro + c, o);
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < H; c += 256)
+    part[(int64_t)blockIdx.x * H + c] = sm[c] + sm[H + c] + sm[2 * H + c] + sm[3 * H + c];
+}
+
+// column sums of a [nrow][H] matrix: 32 columns x 8 row slices per block,
+// each slice summed in row order, the slices in a fixed order
+__global__ __launch_bounds__(256) void sum_rows_kernel(const float* __restrict__ part, int nrow, int H,
+                                                       float* __restrict__ out) {
+  __shared__ float red[8][33];
+  const int cx = threadIdx.x & 31, sy = threadIdx.x >> 5;
+  const int c = blockIdx.x * 32 + cx;
   float s = 0.f;
-  for (int r = 0; r < nrow; ++r) s += part[(int64_t)r * H + c];
-  out[c] = s;
+  if (c < H)
+    for (int r = sy; r < nrow; r += 8) s += part[(int64_t)r * H + c];
+  red[sy][cx] = s;
+  __syncthreads();
+  if (sy == 0 && c < H) {
+    float t = red[0][cx];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) t += red[k][cx];
+    out[c] = t;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -511,12 +619,26 @@ size_t rmsnorm_bwd_part_bytes(int T, int H) {
   return (size_t)cdiv(T, RMS_BWD_ROWS) * H * sizeof(float);
 }
 
+template <class T, class TR, int NC>
+static rp_status rows_bwd(const float* g, const void* x, const void* gamma, const float* rstd, const void* resid,
+                          float* out_f32, void* out_dt, float* part, int rows, unsigned nb, size_t lds,
+                          hipStream_t s) {
+  if (lds > 32 * 1024)
+    RP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&rmsnorm_bwd_rows_kernel<T, TR, NC>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+  RP_LAUNCH((rmsnorm_bwd_rows_kernel<T, TR, NC>), dim3(nb), dim3(256), lds, s, g, (const T*)x, (const T*)gamma, rstd,
+            (const TR*)resid, out_f32, (T*)out_dt, part, rows);
+  return RP_OK;
+}
+
 template <class T>
 static rp_status rmsnorm_bwd_t(const float* g, const void* x, const void* gamma, const float* rstd,
                                const void* resid, int resid_dt, float* out_f32, void* out_dt,
                                float* dgamma, float* part, int rows, int H, hipStream_t s) {
   const unsigned nb = blocks_for(rows, RMS_BWD_ROWS);
   const size_t lds = 4 * (size_t)H * sizeof(float);
+  constexpr int V = Vec<T>::N;
+  const int nc = H % (64 * V) == 0 ? H / (64 * V) : 0;
   // g (fp32), x, out, resid read/written once; dgamma partials
   const double es = sizeof(T);
   TraceScope ts(s, "rmsnorm_bwd_kernel", 0.0,
@@ -531,13 +653,25 @@ static rp_status rmsnorm_bwd_t(const float* g, const void* x, const void* gamma,
       RP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&rmsnorm_bwd_kernel<T, bf16>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
   }
-  if (resid_dt == RP_DTYPE_F32 || resid == nullptr)
+  const bool rf32 = resid_dt == RP_DTYPE_F32 || resid == nullptr;
+  if (nc == 1 || nc == 2 || nc == 4 || nc == 8) {
+    // the row fits the registers of one wave (up to 4096 bf16 / 2048 fp32)
+    RP_TRY(nc == 1   ? (rf32 ? rows_bwd<T, float, 1>(g, x, gamma, rstd, resid, out_f32, out_dt, part, rows, nb, lds, s)
+                             : rows_bwd<T, bf16, 1>(g, x, gamma, rstd, resid, out_f32, out_dt, part, rows, nb, lds, s))
+           : nc == 2 ? (rf32 ? rows_bwd<T, float, 2>(g, x, gamma, rstd, resid, out_f32, out_dt, part, rows, nb, lds, s)
+                             : rows_bwd<T, bf16, 2>(g, x, gamma, rstd, resid, out_f32, out_dt, part, rows, nb, lds, s))
+           : nc == 4 ? (rf32 ? rows_bwd<T, float, 4>(g, x, gamma, rstd, resid, out_f32, out_dt, part, rows, nb, lds, s)
+                             : rows_bwd<T, bf16, 4>(g, x, gamma, rstd, resid, out_f32, out_dt, part, rows, nb, lds, s))
+                     : (rf32 ? rows_bwd<T, float, 8>(g, x, gamma, rstd, resid, out_f32, out_dt, part, rows, nb, lds, s)
+                             : rows_bwd<T, bf16, 8>(g, x, gamma, rstd, resid, out_f32, out_dt, part, rows, nb, lds, s)));
+  } else if (rf32) {
     RP_LAUNCH((rmsnorm_bwd_kernel<T, float>), dim3(nb), dim3(256), lds, s, g, (const T*)x,
               (const T*)gamma, rstd, (const float*)resid, out_f32, (T*)out_dt, part, rows, H);
-  else
+  } else {
     RP_LAUNCH((rmsnorm_bwd_kernel<T, bf16>), dim3(nb), dim3(256), lds, s, g, (const T*)x,
               (const T*)gamma, rstd, (const bf16*)resid, out_f32, (T*)out_dt, part, rows, H);
-  if (dgamma) RP_LAUNCH(sum_rows_kernel, dim3(blocks_for(H)), dim3(256), 0, s, part, (int)nb, H, dgamma);
+  }
+  if (dgamma) RP_LAUNCH(sum_rows_kernel, dim3((unsigned)cdiv(H, 32)), dim3(256), 0, s, part, (int)nb, H, dgamma);
   return RP_OK;
 }
 
