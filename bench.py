@@ -20,6 +20,13 @@ under "streamed", never as `value`. It also reports, under "priority", the
 latency of an activation upload alone, behind an ungated weight upload, and
 with that upload gated on the activation copy's ticket.
 
+With --ablation it also runs the pages' priority-aware transfer ablation on
+Llama-3.1-8B-shaped layers (section 5.8.2): a forward + backward pass over
+4 one-layer stages of 4 micro-batches each, every weight, activation and
+gradient through pinned host memory, for micro-batch sizes 1..8 sequences of
+2048 tokens, under the policies no_prefetch, prefetch and windowed
+(offloaded_pipeline_stage_amd/microbatch.py). Reported under "ablation".
+
 Each kernel launch in the timed region is timed by the library's own HIP
 event pairs on the compute stream (rp_trace_*); the dominant kernel is priced
 against the MI355X peak for its bound. The CPU oracle is timed on a bounded
@@ -32,7 +39,7 @@ profiles/<workload>_step_traffic.txt.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--streamed]
                        [--no-cpu-baseline] [--cpu-seq S] [--trace-json PATH]
-                       [--copy-calibration-mib M] [--configs]
+                       [--copy-calibration-mib M] [--configs] [--ablation]
 """
 from __future__ import annotations
 
@@ -269,6 +276,50 @@ def priority_probe(cfg, chunk_mib: int = 16, reps: int = 5):
     return out
 
 
+def transfer_ablation(mbs_list=(1, 2, 3, 4, 6, 8), n_layers: int = 4, n_micro: int = 4, seq: int = 2048,
+                      reps: int = 2):
+    """Throughput (tokens/s) of one forward + backward pass over `n_layers`
+    one-layer stages of `n_micro` micro-batches per transfer policy and
+    micro-batch size. Every stage streams a full layer's weights in and (for
+    the backward) its fp32 gradients out; all layers share one host weight
+    block, which moves the same bytes as distinct ones."""
+    from offloaded_pipeline_stage_amd.microbatch import POLICIES, MicrobatchPass
+    from offloaded_pipeline_stage_amd.worker import Worker
+    cfg = synth.config("llama3_8b", seq=seq)
+    packer = Worker(cfg)
+    host_w = packer.pack_layer(synth.layer_weights(cfg, 0), pinned=True)
+    packer.ctx.close()
+    max_mbs = max(mbs_list)
+    out = {"workload": f"Llama-3.1-8B-shaped layers, {n_layers} forward + {n_layers} backward one-layer stages, "
+                       f"{n_micro} micro-batches per stage, micro-batch = mbs sequences of {seq} tokens",
+           "weights_GB_per_stage": None, "grads_GB_per_bwd_stage": None, "mbs": list(mbs_list)}
+    for pol in POLICIES:
+        mp = MicrobatchPass(cfg, [host_w] * n_layers, n_micro=n_micro, max_mbs=max_mbs, policy=pol)
+        out["weights_GB_per_stage"] = round(mp.wk.w_bytes / 1e9, 3)
+        out["grads_GB_per_bwd_stage"] = round(mp.wk.g_bytes / 1e9, 3)
+        src = synth.normal(tuple(mp.act[0][0].shape), cfg.seed, "ablation_in").to(mp.act[0][0].dtype)
+        for buf in mp.act[0] + mp.grad[n_layers]:
+            buf.copy_(src)
+        vals = []
+        for mbs in mbs_list:
+            mp.run(mbs)  # warm-up
+            mp.sync()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                mp.run(mbs)
+            mp.sync()
+            dt = (time.perf_counter() - t0) / reps
+            vals.append(round(mp.tokens(mbs) / dt, 1))
+            log(f"[ablation] {pol} mbs={mbs}: {dt * 1e3:.1f} ms/pass, {vals[-1]:.0f} tokens/s")
+        out[pol] = vals
+        mp.close()
+        del mp
+        torch.cuda.empty_cache()
+    out["windowed_over_no_prefetch"] = [round(w / n, 3) for w, n in zip(out["windowed"], out["no_prefetch"])]
+    out["windowed_over_prefetch"] = [round(w / p, 3) for w, p in zip(out["windowed"], out["prefetch"])]
+    return out
+
+
 def config_sweep(reps: int = 3):
     """Per-call and per-configuration throughput with resident weights, each
     configuration's own call sequence: wall time with the context synced
@@ -412,6 +463,8 @@ def main():
     ap.add_argument("--trace-json", default=None, help="write the per-kernel table here")
     ap.add_argument("--configs", action="store_true",
                     help="also time every configuration's own call sequence (resident weights)")
+    ap.add_argument("--ablation", action="store_true",
+                    help="also run the transfer-policy ablation over micro-batch sizes")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one device copy of this size (for the HBM counter runs)")
     a = ap.parse_args()
@@ -495,6 +548,8 @@ def main():
 
     if a.configs:
         out["configs"] = config_sweep()
+    if a.ablation:
+        out["ablation"] = transfer_ablation()
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, a.cpu_seq)
     print(json.dumps(out), flush=True)

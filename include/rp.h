@@ -238,8 +238,13 @@ enum {
   RP_USE_KEPT_ACTS = 2, /* bwd: use the internals kept by the preceding
                            rp_stage_fwd(RP_KEEP_ACTS) on this ws, skip the
                            recomputation                                     */
-  RP_CKPT_DEVICE = 4    /* bwd: ckpt[] are device pointers (default: pinned
+  RP_CKPT_DEVICE = 4,   /* bwd: ckpt[] are device pointers (default: pinned
                            host pointers, uploaded on act_h2d one layer ahead) */
+  RP_ACCUM_GRADS = 8    /* bwd: add the weight gradients to the bound gradient
+                           blocks instead of overwriting them: a stage that
+                           runs several micro-batches passes it from the second
+                           on and downloads the sum once (section 4.2, one
+                           gradient download per stage)                      */
 };
 
 /* Forward of layers [l0, l1) (each bound) on `batch` rows of `seq` tokens.
@@ -263,9 +268,10 @@ rp_status rp_stage_fwd(rp_ctx* ctx, int l0, int l1, int batch, int seq,
  *   dy           device [T, H]: gradient w.r.t. the stage output
  *   dx           device [T, H]: gradient w.r.t. the stage input (written)
  *   router       as for rp_stage_fwd
- * Weight gradients of each layer are written (overwritten, not accumulated)
- * into its bound fp32 gradient block, or LoRA-gradient block for LoRA layers.
- * Gradient accumulation across micro-batches is the controller's business. */
+ * Weight gradients of each layer are written (overwritten, or with
+ * RP_ACCUM_GRADS added in fp32) into its bound fp32 gradient block, or
+ * LoRA-gradient block for LoRA layers. Host gradient buffers are always
+ * overwritten by downloads; accumulation there is the controller's business. */
 rp_status rp_stage_bwd_recompute(rp_ctx* ctx, int l0, int l1, int batch, int seq,
                                  const void* const* ckpt, const void* dy, void* dx,
                                  const float* const* router, int flags, void* ws,
@@ -308,6 +314,20 @@ enum { RP_H2D = 0, RP_D2H = 1 };
 rp_status rp_act_copy(rp_ctx* ctx, int dir, void* dst, const void* src, size_t bytes,
                       int64_t* ticket);
 
+/* Ordering on activation copies (section 4.2.1: the compute stream syncs with
+ * the activation streams per micro-batch through events). rp_act_wait makes
+ * later work on the chosen stream wait until activation copy `ticket` has
+ * completed: RP_ON_ACT_H2D orders an upload after the download that fills its
+ * host buffer (an activation that passes through host memory between two
+ * stages), RP_ON_COMPUTE orders kernels after a copy. RP_ERR_STATE for a
+ * ticket not yet issued, or one of more than 256 copies ago (its event has
+ * been recycled). rp_act_next_ticket gives the ticket the next rp_act_copy
+ * will get, so that a caller can gate transfer windows on copies it is about
+ * to issue. */
+enum { RP_ON_COMPUTE = 0, RP_ON_ACT_H2D = 1, RP_ON_ACT_D2H = 2 };
+rp_status rp_act_wait(rp_ctx* ctx, int where, int64_t ticket);
+rp_status rp_act_next_ticket(const rp_ctx* ctx, int64_t* next);
+
 typedef enum rp_xfer_kind { RP_PARAM_H2D = 0, RP_GRAD_D2H = 1 } rp_xfer_kind;
 typedef enum rp_xfer_target {
   RP_TGT_LAYER = 0,  /* id = layer; bytes of the weight / gradient block      */
@@ -343,6 +363,15 @@ typedef struct rp_xfer {
  * wrote the gradient; the next backward writing that buffer waits for it. */
 rp_status rp_weight_stream_submit(rp_ctx* ctx, const rp_xfer* items, int n_items,
                                   int n_windows, uint64_t max_chunk, int64_t gate_ticket);
+/* The same with one gate per window: window w waits for activation ticket
+ * gates[w] (n_windows entries; negative: not gated; a ticket not yet issued
+ * defers the window as above). A stage that runs M micro-batches gates window
+ * j on the activation copy of its micro-batch j, so that every window follows
+ * the critical-path copy it belongs to (section 4.2.2, one window per
+ * micro-batch), also when a micro-batch issues several copies. */
+rp_status rp_weight_stream_submit_gated(rp_ctx* ctx, const rp_xfer* items, int n_items,
+                                        int n_windows, uint64_t max_chunk,
+                                        const int64_t* gates);
 
 /* The planner alone (pure host function, for tests): split + LPT-assign
  * n_items sizes into n_windows windows with the rule above (`align`-byte

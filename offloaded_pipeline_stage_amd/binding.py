@@ -25,8 +25,9 @@ RP_T_GAMMA1, RP_T_WQKV, RP_T_WO, RP_T_GAMMA2, RP_T_WGU, RP_T_WD = 0, 1, 2, 3, 4,
 RP_T_AQ, RP_T_BQ, RP_T_AK, RP_T_BK, RP_T_AV, RP_T_BV, RP_T_AO, RP_T_BO = range(16, 24)
 RP_BLOCK_WEIGHT, RP_BLOCK_GRAD, RP_BLOCK_LORA = 0, 1, 2
 RP_OP_STAGE_FWD, RP_OP_STAGE_BWD, RP_OP_LMHEAD, RP_OP_FUSED = 0, 1, 2, 3
-RP_KEEP_ACTS, RP_USE_KEPT_ACTS, RP_CKPT_DEVICE = 1, 2, 4
+RP_KEEP_ACTS, RP_USE_KEPT_ACTS, RP_CKPT_DEVICE, RP_ACCUM_GRADS = 1, 2, 4, 8
 RP_H2D, RP_D2H = 0, 1
+RP_ON_COMPUTE, RP_ON_ACT_H2D, RP_ON_ACT_D2H = 0, 1, 2
 RP_PARAM_H2D, RP_GRAD_D2H = 0, 1
 RP_TGT_LAYER, RP_TGT_LMHEAD, RP_TGT_LORA, RP_TGT_FINAL_NORM = 0, 1, 2, 3
 
@@ -74,7 +75,11 @@ _SIGS = {
     "rp_embed_fwd": (C.c_int, [_P, C.c_int, C.c_int, _P, _P, _P]),
     "rp_embed_bwd": (C.c_int, [_P, C.c_int, C.c_int, _P, _P, _P]),
     "rp_act_copy": (C.c_int, [_P, C.c_int, _P, _P, C.c_size_t, C.POINTER(C.c_int64)]),
+    "rp_act_wait": (C.c_int, [_P, C.c_int, C.c_int64]),
+    "rp_act_next_ticket": (C.c_int, [_P, C.POINTER(C.c_int64)]),
     "rp_weight_stream_submit": (C.c_int, [_P, C.POINTER(rp_xfer), C.c_int, C.c_int, C.c_uint64, C.c_int64]),
+    "rp_weight_stream_submit_gated": (C.c_int, [_P, C.POINTER(rp_xfer), C.c_int, C.c_int, C.c_uint64,
+                                                C.POINTER(C.c_int64)]),
     "rp_xfer_plan": (C.c_int, [C.POINTER(C.c_uint64), C.c_int, C.c_int, C.c_uint64, C.c_uint64, C.c_int,
                                C.POINTER(C.c_int32), C.POINTER(C.c_uint64), C.POINTER(C.c_uint64),
                                C.POINTER(C.c_int32), C.POINTER(C.c_int)]),
@@ -308,13 +313,33 @@ class Context:
         self._hold(dst, src)
         return t.value
 
-    def weight_stream_submit(self, items, n_windows: int = 1, max_chunk: int = 0, gate_ticket: int = -1):
-        """items: (kind, target, id, offset, bytes, host tensor or address)."""
+    def act_wait(self, where: int, ticket: int):
+        check(lib().rp_act_wait(self.h, where, ticket))
+
+    def act_next_ticket(self) -> int:
+        t = C.c_int64()
+        check(lib().rp_act_next_ticket(self.h, C.byref(t)))
+        return t.value
+
+    @staticmethod
+    def _xfer_array(items):
         arr = (rp_xfer * max(len(items), 1))()
         for i, (kind, tgt, ident, off, nb, host) in enumerate(items):
             addr = host if isinstance(host, int) else host.data_ptr()
             arr[i] = rp_xfer(kind, tgt, ident, 0, off, nb, addr)
+        return arr
+
+    def weight_stream_submit(self, items, n_windows: int = 1, max_chunk: int = 0, gate_ticket: int = -1):
+        """items: (kind, target, id, offset, bytes, host tensor or address)."""
+        arr = self._xfer_array(items)
         check(lib().rp_weight_stream_submit(self.h, arr, len(items), n_windows, max_chunk, gate_ticket))
+        self._hold([it[5] for it in items])
+
+    def weight_stream_submit_gated(self, items, gates: Sequence[int], max_chunk: int = 0):
+        """One window per entry of `gates` (the activation ticket it waits for, -1 for none)."""
+        arr = self._xfer_array(items)
+        g = (C.c_int64 * len(gates))(*gates)
+        check(lib().rp_weight_stream_submit_gated(self.h, arr, len(items), len(gates), max_chunk, g))
         self._hold([it[5] for it in items])
 
     # -- kernel trace

@@ -320,8 +320,8 @@ rp_status rp_stage_bwd_recompute(rp_ctx* c, int l0, int l1, int batch, int seq, 
                                  const void* dy, void* dx, const float* const* router, int flags, void* ws,
                                  size_t ws_bytes) {
   CTX_ENTER(c);
-  RP_CHECK((flags & ~(RP_USE_KEPT_ACTS | RP_CKPT_DEVICE)) == 0, RP_ERR_INVALID, "stage_bwd: unknown flags 0x%x",
-           flags);
+  RP_CHECK((flags & ~(RP_USE_KEPT_ACTS | RP_CKPT_DEVICE | RP_ACCUM_GRADS)) == 0, RP_ERR_INVALID,
+           "stage_bwd: unknown flags 0x%x", flags);
   return stage_bwd(c, l0, l1, batch, seq, ckpt, dy, dx, router, flags, ws, ws_bytes, nullptr);
 }
 
@@ -346,6 +346,20 @@ rp_status rp_embed_bwd(rp_ctx* c, int n_tokens, int vocab, const int32_t* ids, c
 rp_status rp_act_copy(rp_ctx* c, int dir, void* dst, const void* src, size_t bytes, int64_t* ticket) {
   CTX_ENTER(c);
   return act_copy(c, dir, dst, src, bytes, ticket);
+}
+
+rp_status rp_act_wait(rp_ctx* c, int where, int64_t ticket) {
+  CTX_ENTER(c);
+  RP_CHECK(where == RP_ON_COMPUTE || where == RP_ON_ACT_H2D || where == RP_ON_ACT_D2H, RP_ERR_INVALID,
+           "act_wait: bad stream selector %d", where);
+  return act_wait(c, where, ticket);
+}
+
+rp_status rp_act_next_ticket(const rp_ctx* c, int64_t* next) {
+  CTX_CHECK(c);
+  RP_CHECK(next != nullptr, RP_ERR_INVALID, "act_next_ticket: null output");
+  *next = c->next_ticket;
+  return RP_OK;
 }
 
 rp_status rp_op_gemm_bf16(rp_ctx* c, int M, int N, int K, const void* A, int lda, int a_kmajor, const void* B,

@@ -129,6 +129,9 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
 
 // transfer engine (xfer.cpp)
 rp_status act_copy(rp_ctx* c, int dir, void* dst, const void* src, size_t bytes, int64_t* ticket);
+rp_status act_wait(rp_ctx* c, int where, int64_t ticket);
+rp_status weight_stream_submit(rp_ctx* c, const rp_xfer* items, int n_items, int n_windows, uint64_t max_chunk,
+                               const int64_t* gates, int64_t gate0);
 rp_status wait_weights(rp_ctx* c, Slot& s);       // compute waits for a pending upload
 rp_status mark_consumed(rp_ctx* c, Slot& s);      // after the last compute read
 rp_status wait_grad_drained(rp_ctx* c, Slot& s);  // before compute overwrites a gradient

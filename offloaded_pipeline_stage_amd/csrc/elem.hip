@@ -261,9 +261,10 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_rows_kernel(
 }
 
 // column sums of a [nrow][H] matrix: 32 columns x 8 row slices per block,
-// each slice summed in row order, the slices in a fixed order
+// each slice summed in row order, the slices in a fixed order; `accumulate`
+// adds the sums to out instead of overwriting it
 __global__ __launch_bounds__(256) void sum_rows_kernel(const float* __restrict__ part, int nrow, int H,
-                                                       float* __restrict__ out) {
+                                                       float* __restrict__ out, int accumulate) {
   __shared__ float red[8][33];
   const int cx = threadIdx.x & 31, sy = threadIdx.x >> 5;
   const int c = blockIdx.x * 32 + cx;
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(256) void sum_rows_kernel(const float* __restrict__
     float t = red[0][cx];
 #pragma unroll
     for (int k = 1; k < 8; ++k) t += red[k][cx];
-    out[c] = t;
+    out[c] = accumulate ? out[c] + t : t;
   }
 }
 
@@ -634,7 +635,7 @@ static rp_status rows_bwd(const float* g, const void* x, const void* gamma, cons
 template <class T>
 static rp_status rmsnorm_bwd_t(const float* g, const void* x, const void* gamma, const float* rstd,
                                const void* resid, int resid_dt, float* out_f32, void* out_dt,
-                               float* dgamma, float* part, int rows, int H, hipStream_t s) {
+                               float* dgamma, bool dgamma_acc, float* part, int rows, int H, hipStream_t s) {
   const unsigned nb = blocks_for(rows, RMS_BWD_ROWS);
   const size_t lds = 4 * (size_t)H * sizeof(float);
   constexpr int V = Vec<T>::N;
@@ -671,21 +672,24 @@ static rp_status rmsnorm_bwd_t(const float* g, const void* x, const void* gamma,
     RP_LAUNCH((rmsnorm_bwd_kernel<T, bf16>), dim3(nb), dim3(256), lds, s, g, (const T*)x,
               (const T*)gamma, rstd, (const bf16*)resid, out_f32, (T*)out_dt, part, rows, H);
   }
-  if (dgamma) RP_LAUNCH(sum_rows_kernel, dim3((unsigned)cdiv(H, 32)), dim3(256), 0, s, part, (int)nb, H, dgamma);
+  if (dgamma)
+    RP_LAUNCH(sum_rows_kernel, dim3((unsigned)cdiv(H, 32)), dim3(256), 0, s, part, (int)nb, H, dgamma, (int)dgamma_acc);
   return RP_OK;
 }
 
 rp_status rmsnorm_bwd(int dt, const float* g, const void* x, const void* gamma, const float* rstd,
                       const void* resid, int resid_dt, float* out_f32, void* out_dt, float* dgamma,
-                      float* part, int T, int H, hipStream_t s) {
+                      bool dgamma_acc, float* part, int T, int H, hipStream_t s) {
   if (T == 0) {
-    if (dgamma) return fill_zero(dgamma, (size_t)H * 4, s);
+    if (dgamma && !dgamma_acc) return fill_zero(dgamma, (size_t)H * 4, s);
     return RP_OK;
   }
   RP_CHECK(H % 8 == 0, RP_ERR_UNSUPPORTED, "rmsnorm: H %% 8 != 0");
   if (dt == RP_DTYPE_BF16)
-    return rmsnorm_bwd_t<bf16>(g, x, gamma, rstd, resid, resid_dt, out_f32, out_dt, dgamma, part, T, H, s);
-  return rmsnorm_bwd_t<float>(g, x, gamma, rstd, resid, resid_dt, out_f32, out_dt, dgamma, part, T, H, s);
+    return rmsnorm_bwd_t<bf16>(g, x, gamma, rstd, resid, resid_dt, out_f32, out_dt, dgamma, dgamma_acc, part, T, H,
+                               s);
+  return rmsnorm_bwd_t<float>(g, x, gamma, rstd, resid, resid_dt, out_f32, out_dt, dgamma, dgamma_acc, part, T, H,
+                              s);
 }
 
 rp_status rope_table(float2* tab, int seq, int d, float base, hipStream_t s) {

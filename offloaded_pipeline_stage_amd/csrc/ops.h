@@ -91,10 +91,12 @@ rp_status rmsnorm_fwd(int dt, const void* x, const void* gamma, void* y, float* 
 
 // dx = (r * g*gamma - x * r^3 * mean(g*gamma*x)) + resid;  g fp32 [T, H].
 // resid: nullptr, or [T, H] of dtype resid_dt. Writes out_f32 and/or out_dt.
-// dgamma[h] = sum_t g[t,h] x[t,h] r[t] through part [n_part, H] partials.
+// dgamma[h] = sum_t g[t,h] x[t,h] r[t] through part [n_part, H] partials
+// (added to dgamma when dgamma_acc).
 rp_status rmsnorm_bwd(int dt, const float* g, const void* x, const void* gamma,
                       const float* rstd, const void* resid, int resid_dt, float* out_f32,
-                      void* out_dt, float* dgamma, float* part, int T, int H, hipStream_t s);
+                      void* out_dt, float* dgamma, bool dgamma_acc, float* part, int T, int H,
+                      hipStream_t s);
 size_t rmsnorm_bwd_part_bytes(int T, int H);
 
 // cos/sin table [seq][d/2] (fp32 pairs) computed in fp64

@@ -299,10 +299,12 @@ rp_status layer_fwd(rp_ctx* c, const LayerBinding& lb, const LoraBf16& lw, void*
   return RP_OK;
 }
 
-// a weight-gradient product dW = X^T Y (both operands M-major, fp32 out)
+// a weight-gradient product dW = X^T Y (both operands M-major, fp32 out),
+// added to dW when accumulating over micro-batches
 rp_status wgrad(int M, int N, int K, const void* A, int64_t lda, const void* Bm, int64_t ldb, float* C, int64_t ldc,
-                int dt, const BwdTmp& B, float alpha, hipStream_t st) {
+                int dt, const BwdTmp& B, float alpha, bool accum, hipStream_t st) {
   GemmDesc g = mk(M, N, K, A, lda, false, Bm, ldb, false, C, ldc, dt, RP_DTYPE_F32);
+  g.accumulate = accum;
   g.tr = B.tr;
   g.tr_bytes = B.tr_bytes;
   g.alpha = alpha;
@@ -316,9 +318,10 @@ rp_status wgrad(int M, int N, int K, const void* A, int64_t lda, const void* Bm,
 
 // backward of one layer from its forward internals: dy -> dx and the weight
 // gradients (every weight and gain for a full fine-tune; with LoRA the base is
-// frozen and only the adapters get gradients)
+// frozen and only the adapters get gradients), written or, with accum, added
+// to the gradient block
 rp_status layer_bwd(rp_ctx* c, LayerBinding& lb, const LoraBf16& lw, int T, int seq, const void* x, const Acts& A,
-                    const BwdTmp& B, const void* dy, void* dx, const float2* rope, hipStream_t st) {
+                    const BwdTmp& B, const void* dy, void* dx, const float2* rope, bool accum, hipStream_t st) {
   const Shape& s = c->sh;
   const int dt = s.dt;
   const rp_layer_cfg& cfg = c->cfg;
@@ -362,19 +365,19 @@ rp_status layer_bwd(rp_ctx* c, LayerBinding& lb, const LoraBf16& lw, int T, int 
     g1.R = A.gu; g1.ldr = F2; g1.tmp = B.dm_tmp;
     RP_TRY(gemm(g1, st));
     // dWd = dy^T m
-    if (full) RP_TRY(wgrad(s.H, s.F, T, dy, s.H, A.m, s.F, gptr(w, cfg, RP_T_WD), s.F, dt, B, 1.f, st));
+    if (full) RP_TRY(wgrad(s.H, s.F, T, dy, s.H, A.m, s.F, gptr(w, cfg, RP_T_WD), s.F, dt, B, 1.f, accum, st));
     // db = dgu Wgu
     RP_TRY(gemm(mk(T, s.H, F2, B.dgu, F2, true, wptr(w, cfg, RP_T_WGU), s.H, false, B.gbuf, s.H, dt, RP_DTYPE_F32),
                 st));
     // dWgu = dgu^T b
-    if (full) RP_TRY(wgrad(F2, s.H, T, B.dgu, F2, A.b, s.H, gptr(w, cfg, RP_T_WGU), s.H, dt, B, 1.f, st));
+    if (full) RP_TRY(wgrad(F2, s.H, T, B.dgu, F2, A.b, s.H, gptr(w, cfg, RP_T_WGU), s.H, dt, B, 1.f, accum, st));
   }
   // dh1 = dy + RMSNorm2^T db ; dgamma2
   RP_TRY(rmsnorm_bwd(dt, B.gbuf, A.h1, wptr(w, cfg, RP_T_GAMMA2), A.rstd2, dy, dt, B.dh1f, B.dh1,
-                     full ? gptr(w, cfg, RP_T_GAMMA2) : nullptr, B.part, T, s.H, st));
+                     full ? gptr(w, cfg, RP_T_GAMMA2) : nullptr, accum, B.part, T, s.H, st));
   // attention output projection: dO = dh1 Wo ; dWo = dh1^T o
   RP_TRY(gemm(mk(T, s.Q, s.H, B.dh1, s.H, true, wptr(w, cfg, RP_T_WO), s.Q, false, B.dO, s.Q, dt, dt), st));
-  if (full) RP_TRY(wgrad(s.H, s.Q, T, B.dh1, s.H, A.o, s.Q, gptr(w, cfg, RP_T_WO), s.Q, dt, B, 1.f, st));
+  if (full) RP_TRY(wgrad(s.H, s.Q, T, B.dh1, s.H, A.o, s.Q, gptr(w, cfg, RP_T_WO), s.Q, dt, B, 1.f, accum, st));
   if (r > 0) {
     const Slot& L = lb.lora;
     // g_o = dh1 B_o ; dO += s g_o A_o ; dA_o = s g_o^T o ; dB_o = dh1^T us_o
@@ -382,8 +385,8 @@ rp_status layer_bwd(rp_ctx* c, LayerBinding& lb, const LoraBf16& lw, int T, int 
     GemmDesc g = mk(T, s.Q, r, B.g_o, r, true, lw.ao, s.Q, false, B.dO, s.Q, dt, dt, EPI_RESID);
     g.R = B.dO; g.ldr = s.Q; g.alpha = ls;
     RP_TRY(gemm(g, st));
-    RP_TRY(wgrad(r, s.Q, T, B.g_o, r, A.o, s.Q, lgptr(L, cfg, RP_T_AO), s.Q, dt, B, ls, st));
-    RP_TRY(wgrad(s.H, r, T, B.dh1, s.H, A.us_o, r, lgptr(L, cfg, RP_T_BO), r, dt, B, 1.f, st));
+    RP_TRY(wgrad(r, s.Q, T, B.g_o, r, A.o, s.Q, lgptr(L, cfg, RP_T_AO), s.Q, dt, B, ls, accum, st));
+    RP_TRY(wgrad(s.H, r, T, B.dh1, s.H, A.us_o, r, lgptr(L, cfg, RP_T_BO), r, dt, B, 1.f, accum, st));
   }
   AttnDesc ad;
   ad.dt = dt; ad.batch = T / seq; ad.seq = seq; ad.n_q = s.nq; ad.n_kv = s.nkv; ad.d = s.d;
@@ -392,7 +395,7 @@ rp_status layer_bwd(rp_ctx* c, LayerBinding& lb, const LoraBf16& lw, int T, int 
   // da = dqkv Wqkv ; dWqkv = dqkv^T a
   RP_TRY(gemm(mk(T, s.H, s.QKV, B.dqkv, s.QKV, true, wptr(w, cfg, RP_T_WQKV), s.H, false, B.gbuf, s.H, dt,
                  RP_DTYPE_F32), st));
-  if (full) RP_TRY(wgrad(s.QKV, s.H, T, B.dqkv, s.QKV, A.a, s.H, gptr(w, cfg, RP_T_WQKV), s.H, dt, B, 1.f, st));
+  if (full) RP_TRY(wgrad(s.QKV, s.H, T, B.dqkv, s.QKV, A.a, s.H, gptr(w, cfg, RP_T_WQKV), s.H, dt, B, 1.f, accum, st));
   if (r > 0) {
     const Slot& L = lb.lora;
     // g_x = d{q,k,v} B_x ; da += s [g_q g_k g_v] [A_q; A_k; A_v] ;
@@ -413,13 +416,13 @@ rp_status layer_bwd(rp_ctx* c, LayerBinding& lb, const LoraBf16& lw, int T, int 
       const char* dcol = (const char*)B.dqkv + (size_t)cx[xi] * s.es;
       const char* gcol = (const char*)B.g_qkv + (size_t)xi * r * s.es;
       const char* ucol = (const char*)A.us_qkv + (size_t)xi * r * s.es;
-      RP_TRY(wgrad(r, s.H, T, gcol, 3 * r, A.a, s.H, lgptr(L, cfg, ta[xi]), s.H, dt, B, ls, st));
-      RP_TRY(wgrad(nx[xi], r, T, dcol, s.QKV, ucol, 3 * r, lgptr(L, cfg, tb[xi]), r, dt, B, 1.f, st));
+      RP_TRY(wgrad(r, s.H, T, gcol, 3 * r, A.a, s.H, lgptr(L, cfg, ta[xi]), s.H, dt, B, ls, accum, st));
+      RP_TRY(wgrad(nx[xi], r, T, dcol, s.QKV, ucol, 3 * r, lgptr(L, cfg, tb[xi]), r, dt, B, 1.f, accum, st));
     }
   }
   // dx = dh1 + RMSNorm1^T da ; dgamma1
   RP_TRY(rmsnorm_bwd(dt, B.gbuf, x, wptr(w, cfg, RP_T_GAMMA1), A.rstd1, B.dh1f, RP_DTYPE_F32, nullptr, dx,
-                     full ? gptr(w, cfg, RP_T_GAMMA1) : nullptr, B.part, T, s.H, st));
+                     full ? gptr(w, cfg, RP_T_GAMMA1) : nullptr, accum, B.part, T, s.H, st));
   RP_TRY(mark_consumed(c, w));
   if (r > 0) RP_TRY(mark_consumed(c, lb.lora));
   RP_TRY(mark_grad_ready(c, gs));
@@ -509,6 +512,7 @@ rp_status stage_bwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* c
   const Shape& s = c->sh;
   const bool kept = flags & RP_USE_KEPT_ACTS;
   const bool ck_dev = flags & RP_CKPT_DEVICE;
+  const bool accum = flags & RP_ACCUM_GRADS;
   const int n = l1 - l0;
   const int64_t T = (int64_t)batch * seq;
   Layout L;
@@ -581,7 +585,7 @@ rp_status stage_bwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* c
     }
     // inter-layer gradients alternate gp[0], gp[1]; the stage input's goes to dx
     void* g_out = (i == 0) ? dx : L.bt.gp[(n - 1 - i) & 1];
-    RP_TRY(layer_bwd(c, lb, L.lw, (int)T, seq, x, A, L.bt, g_in, g_out, L.rope, st));
+    RP_TRY(layer_bwd(c, lb, L.lw, (int)T, seq, x, A, L.bt, g_in, g_out, L.rope, accum, st));
     if (!kept && !ck_dev) {
       if (!ck_free[i & 1]) ck_free[i & 1] = c->new_event();
       RP_HIP(hipEventRecord(ck_free[i & 1], st));
@@ -665,7 +669,7 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
     RP_CHECK(c->final_norm.g != nullptr, RP_ERR_INVALID, "lmhead: final norm has no gradient buffer");
     RP_TRY(wait_grad_drained(c, c->final_norm));
     RP_TRY(rmsnorm_bwd(dt, dxf, x, c->final_norm.w, rstd, nullptr, RP_DTYPE_F32, nullptr, dx, c->final_norm.g,
-                       part, (int)T, s.H, st));
+                       false, part, (int)T, s.H, st));
     RP_TRY(mark_consumed(c, c->final_norm));
     RP_TRY(mark_grad_ready(c, c->final_norm));
   } else {

@@ -299,8 +299,12 @@ extern "C" rp_status rp_xfer_plan(const uint64_t* sizes, int n_items, int n_wind
   return RP_OK;
 }
 
-extern "C" rp_status rp_weight_stream_submit(rp_ctx* c, const rp_xfer* items, int n_items, int n_windows,
-                                             uint64_t max_chunk, int64_t gate_ticket) {
+namespace rp {
+
+// Window w waits for ticket gates[w] (or, with gates null, gate0 + w when
+// gate0 >= 0); a negative gate means none.
+rp_status weight_stream_submit(rp_ctx* c, const rp_xfer* items, int n_items, int n_windows, uint64_t max_chunk,
+                               const int64_t* gates, int64_t gate0) {
   RP_CHECK(c, RP_ERR_INVALID, "null context");
   RP_CHECK(n_items >= 0 && (n_items == 0 || items), RP_ERR_INVALID, "submit: bad item list");
   RP_CHECK(n_windows >= 1 && n_windows <= 4096, RP_ERR_INVALID, "submit: n_windows out of range");
@@ -332,7 +336,7 @@ extern "C" rp_status rp_weight_stream_submit(rp_ctx* c, const rp_xfer* items, in
     std::vector<XWindow> wins(n_windows);
     for (int w = 0; w < n_windows; ++w) {
       wins[w].dir = dir;
-      wins[w].gate = gate_ticket < 0 ? -1 : gate_ticket + w;
+      wins[w].gate = gates ? (gates[w] < 0 ? -1 : gates[w]) : (gate0 < 0 ? -1 : gate0 + w);
     }
     for (int k : order) {
       const PlanChunk& pc = plan[k];
@@ -357,4 +361,28 @@ extern "C" rp_status rp_weight_stream_submit(rp_ctx* c, const rp_xfer* items, in
     }
   }
   return RP_OK;
+}
+
+rp_status act_wait(rp_ctx* c, int where, int64_t ticket) {
+  RP_CHECK(ticket >= 0 && ticket < c->next_ticket, RP_ERR_STATE, "act_wait: ticket %lld not issued yet",
+           (long long)ticket);
+  hipEvent_t ev = ticket_event(c, ticket);
+  RP_CHECK(ev != nullptr, RP_ERR_STATE, "act_wait: ticket %lld is too old (its event was recycled)",
+           (long long)ticket);
+  hipStream_t st = where == RP_ON_COMPUTE ? c->compute : where == RP_ON_ACT_H2D ? c->act_h2d : c->act_d2h;
+  RP_HIP(hipStreamWaitEvent(st, ev, 0));
+  return RP_OK;
+}
+
+}  // namespace rp
+
+extern "C" rp_status rp_weight_stream_submit(rp_ctx* c, const rp_xfer* items, int n_items, int n_windows,
+                                             uint64_t max_chunk, int64_t gate_ticket) {
+  return rp::weight_stream_submit(c, items, n_items, n_windows, max_chunk, nullptr, gate_ticket);
+}
+
+extern "C" rp_status rp_weight_stream_submit_gated(rp_ctx* c, const rp_xfer* items, int n_items, int n_windows,
+                                                   uint64_t max_chunk, const int64_t* gates) {
+  RP_CHECK(gates != nullptr, RP_ERR_INVALID, "submit_gated: null gate list");
+  return rp::weight_stream_submit(c, items, n_items, n_windows, max_chunk, gates, -1);
 }

@@ -111,3 +111,23 @@ def test_ctx_create_without_gpu_fails_cleanly(B):
     st = B.lib().rp_ctx_create(0, C.byref(cfg), None, C.byref(h))
     assert st in (B.RP_ERR_HIP, B.RP_ERR_INVALID)
     assert not h.value
+
+
+def test_microbatch_window_gates():
+    """Window j of a stage's transfers is gated on the last activation upload
+    of micro-batch j + 1 (the last micro-batch for the final window), with
+    tickets numbered in the order the stage issues its copies."""
+    from offloaded_pipeline_stage_amd.microbatch import MicrobatchPass
+    # forward stage, M = 3: up x0 (t0), [fwd 0], up x1 (t0+1), down y0 (t0+2),
+    # [fwd 1], up x2 (t0+3), down y1 (t0+4), [fwd 2], down y2 (t0+5)
+    fwd = [("h2d", 0), ("compute", 0), ("h2d", 1), ("d2h", 0), ("compute", 1), ("h2d", 2), ("d2h", 1),
+           ("compute", 2), ("d2h", 2)]
+    ops = [(k, None, None, j) if k != "compute" else (k, j) for k, j in fwd]
+    assert MicrobatchPass.window_gates(ops, 10, 3) == [11, 13, 13]
+    # backward stage, M = 2: two uploads (checkpoint, dy) per micro-batch
+    bwd = [("h2d", 0), ("h2d", 0), ("compute", 0), ("h2d", 1), ("h2d", 1), ("d2h", 0), ("compute", 1),
+           ("d2h", 1)]
+    ops = [(k, None, None, j) if k != "compute" else (k, j) for k, j in bwd]
+    assert MicrobatchPass.window_gates(ops, 0, 2) == [3, 3]
+    # one micro-batch: the single window follows its upload
+    assert MicrobatchPass.window_gates([("h2d", None, None, 0), ("compute", 0), ("d2h", None, None, 0)], 5, 1) == [5]
