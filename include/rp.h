@@ -300,6 +300,32 @@ rp_status rp_embed_bwd(rp_ctx* ctx, int n_tokens, int vocab, const int32_t* ids,
                        const void* dx0, float* dtable);
 
 /* ------------------------------------------------------------------------ */
+/* stage partition                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* Automatic stage partitioning (section 4.4). Host-only; no device work.
+ * Inputs, per layer l < L (front to back): f[l] forward time, b[l] backward
+ * time with the recomputation, mf[l] / mb[l] memory in a forward / backward
+ * stage; h and mh: the LM head's time and memory; mem_cap: the memory limit
+ * of one stage; n_micro (M) micro-batches per iteration on n_gpus (N) GPUs.
+ * The LM head always sits in the fused first backward stage B_1 = the last
+ * b1 layers, which costs h + their backward times (its forward doubles as
+ * the recomputation). Forward stages cover layers [0, L - b1) front to back,
+ * the remaining backward stages the same layers back to front. Minimises
+ * (M S + N (N - 1)) t_max over t_max candidates = every contiguous sum of f,
+ * of b, and h + every suffix sum of b: per candidate, B_1 takes as many
+ * layers as fit, then both layer ranges are packed greedily into the fewest
+ * stages (section 4.4.2, O(L^3)). Ties keep the smallest candidate.
+ * Outputs: fwd_sizes[0 .. *n_fwd) layer counts of F_1.., *b1_out, and
+ * bwd_sizes[0 .. *n_bwd) layer counts of B_2.. (B_2 covers the layers just
+ * below B_1); both arrays need room for L entries. *objective gets the
+ * minimised value. RP_ERR_UNSUPPORTED when nothing fits the memory cap. */
+rp_status rp_partition(int L, const double* f, const double* b, double h, const double* mf,
+                       const double* mb, double mh, double mem_cap, int n_micro, int n_gpus,
+                       int* fwd_sizes, int* n_fwd, int* b1_out, int* bwd_sizes, int* n_bwd,
+                       double* objective);
+
+/* ------------------------------------------------------------------------ */
 /* transfers                                                                 */
 /* ------------------------------------------------------------------------ */
 

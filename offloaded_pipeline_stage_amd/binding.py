@@ -75,6 +75,10 @@ _SIGS = {
     "rp_embed_fwd": (C.c_int, [_P, C.c_int, C.c_int, _P, _P, _P]),
     "rp_embed_bwd": (C.c_int, [_P, C.c_int, C.c_int, _P, _P, _P]),
     "rp_act_copy": (C.c_int, [_P, C.c_int, _P, _P, C.c_size_t, C.POINTER(C.c_int64)]),
+    "rp_partition": (C.c_int, [C.c_int, C.POINTER(C.c_double), C.POINTER(C.c_double), C.c_double,
+                               C.POINTER(C.c_double), C.POINTER(C.c_double), C.c_double, C.c_double, C.c_int,
+                               C.c_int, C.POINTER(C.c_int), C.POINTER(C.c_int), C.POINTER(C.c_int),
+                               C.POINTER(C.c_int), C.POINTER(C.c_int), C.POINTER(C.c_double)]),
     "rp_act_wait": (C.c_int, [_P, C.c_int, C.c_int64]),
     "rp_act_next_ticket": (C.c_int, [_P, C.POINTER(C.c_int64)]),
     "rp_weight_stream_submit": (C.c_int, [_P, C.POINTER(rp_xfer), C.c_int, C.c_int, C.c_uint64, C.c_int64]),
@@ -179,6 +183,22 @@ def xfer_plan(sizes: Sequence[int], n_windows: int, max_chunk: int = 0, align: i
 # contexts still open at interpreter exit are destroyed before the HIP runtime
 # shuts down (their transfer streams belong to the library)
 _LIVE = weakref.WeakSet()
+
+
+def partition(f: Sequence[float], b: Sequence[float], h: float, mf: Sequence[float], mb: Sequence[float],
+              mh: float, mem_cap: float, n_micro: int, n_gpus: int):
+    """Stage partition (rp_partition): returns (objective, forward stage sizes,
+    b1, backward stage sizes after B_1)."""
+    L = len(f)
+    if not (len(b) == len(mf) == len(mb) == L):
+        raise ValueError("per-layer arrays must have the same length")
+    D = C.c_double * max(L, 1)
+    I = C.c_int * max(L, 1)
+    fs, bs = I(), I()
+    nf, b1, nb, obj = C.c_int(), C.c_int(), C.c_int(), C.c_double()
+    check(lib().rp_partition(L, D(*f), D(*b), h, D(*mf), D(*mb), mh, mem_cap, n_micro, n_gpus, fs, C.byref(nf),
+                             C.byref(b1), bs, C.byref(nb), C.byref(obj)))
+    return obj.value, tuple(fs[:nf.value]), b1.value, tuple(bs[:nb.value])
 
 
 @atexit.register

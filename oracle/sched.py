@@ -180,7 +180,11 @@ def partition_greedy(f, b, h, mf, mb, mh, cap, n_micro, n_gpus):
         suf += b[j]
         cands.add(h + suf)
     best = None
-    for t in sorted(cands):
+    for t0 in sorted(cands):
+        # a stage fits when its time is at most t0 up to summation order: a
+        # group summed in another order than the candidate can exceed it by a
+        # few ulps, and exactly equal times fit
+        t = t0 * (1 + 1e-12)
         b1, tt, mm = 0, h, mh
         for j in reversed(range(L)):
             if tt + b[j] <= t and mm + mb[j] <= cap:

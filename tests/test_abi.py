@@ -131,3 +131,50 @@ def test_microbatch_window_gates():
     assert MicrobatchPass.window_gates(ops, 0, 2) == [3, 3]
     # one micro-batch: the single window follows its upload
     assert MicrobatchPass.window_gates([("h2d", None, None, 0), ("compute", 0), ("d2h", None, None, 0)], 5, 1) == [5]
+
+
+def test_partition_matches_oracle_greedy_and_exhaustive(B):
+    """rp_partition (section 4.4) against the oracle: the same partition as the
+    oracle's statement of the greedy, and the optimum of an exhaustive search
+    over every contiguous partition (integer and real-valued times)."""
+    rng = random.Random(4321)
+    n_ok = 0
+    for it in range(300):
+        L = rng.randint(1, 7)
+        if it % 2:
+            f = [rng.randint(1, 9) for _ in range(L)]
+            b = [max(1, 3 * x + rng.randint(-2, 2)) for x in f]
+            h = rng.randint(1, 25)
+        else:
+            f = [rng.uniform(0.5, 9.0) for _ in range(L)]
+            b = [3.0 * x + rng.uniform(-1.0, 1.0) for x in f]
+            h = rng.uniform(1.0, 25.0)
+        mf = [rng.randint(1, 5) for _ in range(L)]
+        mb = [rng.randint(1, 8) for _ in range(L)]
+        mh = rng.randint(1, 8)
+        cap = rng.randint(8, 30)
+        M, N = rng.randint(1, 16), rng.randint(1, 8)
+        e = S.partition_exhaustive(f, b, h, mf, mb, mh, cap, M, N)
+        g = S.partition_greedy(f, b, h, mf, mb, mh, cap, M, N)
+        if e is None:
+            with pytest.raises(B.RPError):
+                B.partition(f, b, h, mf, mb, mh, cap, M, N)
+            continue
+        n_ok += 1
+        got = B.partition(f, b, h, mf, mb, mh, cap, M, N)
+        assert got == (g[0], tuple(g[1]), g[2], tuple(g[3]))
+        assert abs(got[0] - e[0]) <= 1e-9 * e[0]
+    assert n_ok > 200
+
+
+def test_partition_fills_fused_stage_and_rejects_bad_input(B):
+    # eight equal layers, LM head = one backward: B_1 holds two layers
+    assert B.partition([1.0] * 8, [3.0] * 8, 3.0, [1.0] * 8, [1.0] * 8, 1.0, 100.0, 16, 4) == \
+        ((16 * 4 + 12) * 9.0, (6,), 2, (3, 3))
+    # one GPU and room for everything: a single fused stage (no recomputation)
+    assert B.partition([1.0] * 4, [3.0] * 4, 2.0, [1.0] * 4, [1.0] * 4, 1.0, 100.0, 4, 1) == \
+        (4 * 14.0, (), 4, ())
+    with pytest.raises(B.RPError):  # the LM head alone exceeds the memory cap
+        B.partition([1.0], [3.0], 2.0, [1.0], [1.0], 50.0, 10.0, 1, 1)
+    with pytest.raises(B.RPError):  # negative time
+        B.partition([-1.0], [3.0], 2.0, [1.0], [1.0], 1.0, 10.0, 1, 1)

@@ -84,6 +84,30 @@ def test_partitioner_greedy_equals_exhaustive():
     assert n > 300
 
 
+def test_partitioner_greedy_equals_exhaustive_real_times():
+    # measured stage times are real numbers: a backward group summed back to
+    # front may differ from the same candidate summed front to back by a few
+    # ulps, which must not turn an exactly fitting stage into two
+    rng = random.Random(99)
+    n = 0
+    for _ in range(300):
+        L = rng.randint(1, 7)
+        f = [rng.uniform(0.5, 9.0) for _ in range(L)]
+        b = [3.0 * x + rng.uniform(-1.0, 1.0) for x in f]
+        h = rng.uniform(1.0, 25.0)
+        mf = [rng.randint(1, 5) for _ in range(L)]
+        mb = [rng.randint(1, 8) for _ in range(L)]
+        mh, cap = rng.randint(1, 8), rng.randint(8, 30)
+        M, N = rng.randint(1, 16), rng.randint(1, 8)
+        e = S.partition_exhaustive(f, b, h, mf, mb, mh, cap, M, N)
+        g = S.partition_greedy(f, b, h, mf, mb, mh, cap, M, N)
+        assert (e is None) == (g is None)
+        if e is not None:
+            n += 1
+            assert abs(e[0] - g[0]) <= 1e-9 * e[0]
+    assert n > 200
+
+
 def test_partitioner_fills_fused_stage_first():
     # section 4.4.2: the greedy fills the first backward stage to capacity, so
     # one more layer in B_1 would exceed the partition's bottleneck time
