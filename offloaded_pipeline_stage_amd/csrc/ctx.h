@@ -102,6 +102,10 @@ struct rp_ctx {
   std::vector<hipEvent_t> all_events;    // every event created (destroyed with the context)
   std::vector<hipEvent_t> ev_free;       // recycled ticket events
   hipEvent_t ev_mark = nullptr;          // scratch: "compute reached this point"
+  // per workspace (by base pointer): the compute stream is done with it after
+  // this event -- uploads into a workspace's checkpoint buffers wait for it
+  std::map<const void*, hipEvent_t> ws_done;
+  hipEvent_t ck_free[2] = {nullptr, nullptr};  // backward: checkpoint buffer i & 1 read
   // downloads into caller-provided streams run on private streams (one for
   // activations, one for gradients, each with a hardware queue of its own),
   // fenced into the caller's stream by two events

@@ -429,6 +429,20 @@ rp_status layer_bwd(rp_ctx* c, LayerBinding& lb, const LoraBf16& lw, int T, int 
   return RP_OK;
 }
 
+// A call that used workspace ws records when the compute stream is done with
+// it. The table is bounded: past 64 workspaces it starts over, and a
+// workspace without an entry is treated as in use up to the current point.
+rp_status ws_mark(rp_ctx* c, const void* ws) {
+  if (c->ws_done.size() >= 64 && !c->ws_done.count(ws)) {
+    for (auto& kv : c->ws_done) c->ev_free.push_back(kv.second);
+    c->ws_done.clear();
+  }
+  hipEvent_t& e = c->ws_done[ws];
+  if (!e) e = c->new_event();
+  RP_HIP(hipEventRecord(e, c->compute));
+  return RP_OK;
+}
+
 rp_status check_range(rp_ctx* c, int l0, int l1, int batch, int seq) {
   RP_CHECK(l0 >= 0 && l1 > l0 && l1 <= (int)c->layers.size(), RP_ERR_INVALID,
            "layer range [%d, %d) invalid or not bound", l0, l1);
@@ -504,7 +518,7 @@ rp_status stage_fwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* x
   } else if (c->kept_ws == ws) {
     c->kept_ws = nullptr;
   }
-  return RP_OK;
+  return ws_mark(c, ws);
 }
 
 rp_status stage_bwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* const* ckpt, const void* dy,
@@ -555,16 +569,29 @@ rp_status stage_bwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* c
   RP_TRY(rope_table(L.rope, seq, s.d, c->cfg.rope_base, st));
   const size_t xbytes = (size_t)T * s.H * s.es;
   // checkpoint uploads: layer i's input into ck[i & 1], one layer ahead
-  hipEvent_t ck_free[2] = {nullptr, nullptr};
+  bool ck_read[2] = {false, false};  // buffer i & 1 has been read by this call
   auto upload = [&](int i) -> rp_status {
     if (kept || ck_dev) return RP_OK;
-    if (ck_free[i & 1]) RP_HIP(hipStreamWaitEvent(c->act_h2d, ck_free[i & 1], 0));
+    if (ck_read[i & 1]) RP_HIP(hipStreamWaitEvent(c->act_h2d, c->ck_free[i & 1], 0));
     int64_t tk;
     return act_copy(c, RP_H2D, L.bt.ck[i & 1], ckpt[i], xbytes, &tk);
   };
   // the checkpoints may have been written to host memory by this context's
   // earlier downloads (the forward stage): uploads start after those
   if (!kept && !ck_dev && c->last_act_d2h_valid) RP_HIP(hipStreamWaitEvent(c->act_h2d, c->last_act_d2h, 0));
+  // the upload buffers live in ws, which earlier work on the compute stream
+  // (the previous call on the same workspace) may still be reading: uploads
+  // into them start after that work
+  if (!kept && !ck_dev) {
+    auto it = c->ws_done.find(ws);
+    if (it != c->ws_done.end()) {
+      RP_HIP(hipStreamWaitEvent(c->act_h2d, it->second, 0));
+    } else {
+      if (!c->ev_mark) c->ev_mark = c->new_event();
+      RP_HIP(hipEventRecord(c->ev_mark, st));
+      RP_HIP(hipStreamWaitEvent(c->act_h2d, c->ev_mark, 0));
+    }
+  }
   // act_copy(H2D) makes the compute stream wait at issue time, so the
   // prefetch of layer i - 1 is issued after layer i's compute is enqueued.
   if (!kept && !ck_dev) RP_TRY(upload(n - 1));
@@ -587,13 +614,14 @@ rp_status stage_bwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* c
     void* g_out = (i == 0) ? dx : L.bt.gp[(n - 1 - i) & 1];
     RP_TRY(layer_bwd(c, lb, L.lw, (int)T, seq, x, A, L.bt, g_in, g_out, L.rope, accum, st));
     if (!kept && !ck_dev) {
-      if (!ck_free[i & 1]) ck_free[i & 1] = c->new_event();
-      RP_HIP(hipEventRecord(ck_free[i & 1], st));
+      if (!c->ck_free[i & 1]) c->ck_free[i & 1] = c->new_event();
+      RP_HIP(hipEventRecord(c->ck_free[i & 1], st));
+      ck_read[i & 1] = true;
       if (i >= 1) RP_TRY(upload(i - 1));
     }
     g_in = g_out;
   }
-  return RP_OK;
+  return ws_mark(c, ws);
 }
 
 // ---------------------------------------------------------------------------
@@ -675,7 +703,7 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
   } else {
     RP_TRY(cast_from_f32(dt, dxf, dx, (size_t)T * s.H, st));
   }
-  return RP_OK;
+  return ws_mark(c, ws);
 }
 
 }  // namespace rp
