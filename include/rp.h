@@ -326,6 +326,80 @@ rp_status rp_partition(int L, const double* f, const double* b, double h, const 
                        double* objective);
 
 /* ------------------------------------------------------------------------ */
+/* optimizer worker                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* The host-side optimizer of section 2.1.2 with the Layerwise Model
+ * Consistency Protocol of section 4.3. Host-only; no device work.
+ *
+ * Per layer there is a low-precision master copy in host memory (the bytes
+ * the GPU uploads; bf16 or fp32) with its fp32 master gradient buffer (the
+ * bytes the GPU downloads into), and an fp32 optimizer copy with the Adam
+ * moments held by the optimizer. One worker thread runs the queued steps in
+ * order (rule 5). Step t, layer by layer from layer 0:
+ *   wait GRADS_DOWNLOADED(l, t)         rule 3: g_t is in the master buffer
+ *   G-cp, signal GCP_DONE(l, t)         rule 4: the GPU may download g_{t+1}
+ *   Adam on the fp32 copy
+ *   wait PARAMS_UPLOADED(l, t + 1)      rule 1: iteration t + 1 has uploaded
+ *                                        the master weights of step t - 1
+ *   P-cp (round to the master dtype), signal PCP_DONE(l, t)
+ *                                        rule 2: iteration t + 2 may upload
+ * The GPU side (the caller) signals PARAMS_UPLOADED(l, i) once its upload of
+ * layer l for iteration i has completed and GRADS_DOWNLOADED(l, i) once g_i
+ * is in the master buffer; before uploading layer l for iteration i it waits
+ * PCP_DONE(l, i - 2), before downloading g_i it waits GCP_DONE(l, i - 1).
+ * Iteration i thus trains on the weights of step i - 2 (staleness 1). At the
+ * end of training the caller signals PARAMS_UPLOADED(-1, last + 1) (layer -1:
+ * every layer) so that the last step can write its weights.
+ *
+ * Adam with decoupled weight decay, each operation one fp32 rounding:
+ *   g = grad_scale G; m = b1 m + (1 - b1) g; v = b2 v + (1 - b2) g g;
+ *   w = w - lr ((m / (1 - b1^s)) / (sqrt(v / (1 - b2^s)) + eps) + wd w)
+ * s = steps applied to the layer so far (1-based); 1 - b^s formed in double.
+ * P-cp to bf16 rounds to nearest even. */
+typedef struct rp_opt rp_opt;
+typedef struct rp_opt_hparams {
+  float lr, beta1, beta2, eps, weight_decay, grad_scale;
+} rp_opt_hparams;
+/* One tensor of a layer: n elements of master weights (master dtype) and of
+ * master fp32 gradients, both host memory owned by the caller and kept alive
+ * while the optimizer exists; init: NULL (the optimizer copy starts from the
+ * master weights) or n fp32 starting values. */
+typedef struct rp_opt_seg {
+  void* master_w;
+  const float* master_g;
+  const float* init;
+  uint64_t n;
+} rp_opt_seg;
+enum {
+  RP_OPT_PARAMS_UPLOADED = 0,  /* signalled by the GPU side */
+  RP_OPT_GRADS_DOWNLOADED = 1, /* signalled by the GPU side */
+  RP_OPT_PCP_DONE = 2,         /* signalled by the optimizer, waited by the GPU side */
+  RP_OPT_GCP_DONE = 3          /* signalled by the optimizer, waited by the GPU side */
+};
+/* n_threads <= 0: all hardware threads. edge_timeout_ms > 0 bounds every
+ * wait (the worker's and rp_opt_wait's): a missing signal then fails the
+ * step with RP_ERR_STATE instead of blocking forever; 0 waits without limit. */
+rp_status rp_opt_create(int n_layers, int master_dtype, int n_threads, int64_t edge_timeout_ms,
+                        rp_opt** out);
+rp_status rp_opt_destroy(rp_opt* opt);
+/* Bind (or rebind, with no step running) layer `layer`'s tensors. */
+rp_status rp_opt_bind_layer(rp_opt* opt, int layer, const rp_opt_seg* segs, int n_segs);
+/* Queue the optimizer step of iteration `iteration` and return. */
+rp_status rp_opt_step(rp_opt* opt, int64_t iteration, const rp_opt_hparams* hp);
+/* GPU side of the protocol: signal PARAMS_UPLOADED / GRADS_DOWNLOADED for a
+ * layer (-1: all), and wait for PCP_DONE / GCP_DONE of a layer (returns at
+ * once for iteration < 0). A failed step's error is returned by later
+ * rp_opt_wait, rp_opt_step and rp_opt_sync calls. */
+rp_status rp_opt_signal(rp_opt* opt, int edge, int layer, int64_t iteration);
+rp_status rp_opt_wait(rp_opt* opt, int edge, int layer, int64_t iteration);
+/* Wait until every queued step has finished. */
+rp_status rp_opt_sync(rp_opt* opt);
+/* Copy a layer's optimizer state out, with no step running: which = 0
+ * fp32 weights, 1 first moment, 2 second moment; n = the layer's elements. */
+rp_status rp_opt_read(rp_opt* opt, int layer, int which, float* dst, uint64_t n);
+
+/* ------------------------------------------------------------------------ */
 /* transfers                                                                 */
 /* ------------------------------------------------------------------------ */
 

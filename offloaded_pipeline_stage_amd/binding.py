@@ -28,6 +28,7 @@ RP_OP_STAGE_FWD, RP_OP_STAGE_BWD, RP_OP_LMHEAD, RP_OP_FUSED = 0, 1, 2, 3
 RP_KEEP_ACTS, RP_USE_KEPT_ACTS, RP_CKPT_DEVICE, RP_ACCUM_GRADS = 1, 2, 4, 8
 RP_H2D, RP_D2H = 0, 1
 RP_ON_COMPUTE, RP_ON_ACT_H2D, RP_ON_ACT_D2H = 0, 1, 2
+RP_OPT_PARAMS_UPLOADED, RP_OPT_GRADS_DOWNLOADED, RP_OPT_PCP_DONE, RP_OPT_GCP_DONE = 0, 1, 2, 3
 RP_PARAM_H2D, RP_GRAD_D2H = 0, 1
 RP_TGT_LAYER, RP_TGT_LMHEAD, RP_TGT_LORA, RP_TGT_FINAL_NORM = 0, 1, 2, 3
 
@@ -47,6 +48,15 @@ class rp_streams(C.Structure):
 class rp_xfer(C.Structure):
     _fields_ = [("kind", C.c_int32), ("target", C.c_int32), ("id", C.c_int32), ("reserved", C.c_int32),
                 ("offset", C.c_uint64), ("bytes", C.c_uint64), ("host", C.c_void_p)]
+
+
+class rp_opt_hparams(C.Structure):
+    _fields_ = [("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float),
+                ("weight_decay", C.c_float), ("grad_scale", C.c_float)]
+
+
+class rp_opt_seg(C.Structure):
+    _fields_ = [("master_w", C.c_void_p), ("master_g", C.c_void_p), ("init", C.c_void_p), ("n", C.c_uint64)]
 
 
 class rp_trace_rec(C.Structure):
@@ -79,6 +89,14 @@ _SIGS = {
                                C.POINTER(C.c_double), C.POINTER(C.c_double), C.c_double, C.c_double, C.c_int,
                                C.c_int, C.POINTER(C.c_int), C.POINTER(C.c_int), C.POINTER(C.c_int),
                                C.POINTER(C.c_int), C.POINTER(C.c_int), C.POINTER(C.c_double)]),
+    "rp_opt_create": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int64, C.POINTER(_P)]),
+    "rp_opt_destroy": (C.c_int, [_P]),
+    "rp_opt_bind_layer": (C.c_int, [_P, C.c_int, C.POINTER(rp_opt_seg), C.c_int]),
+    "rp_opt_step": (C.c_int, [_P, C.c_int64, C.POINTER(rp_opt_hparams)]),
+    "rp_opt_signal": (C.c_int, [_P, C.c_int, C.c_int, C.c_int64]),
+    "rp_opt_wait": (C.c_int, [_P, C.c_int, C.c_int, C.c_int64]),
+    "rp_opt_sync": (C.c_int, [_P]),
+    "rp_opt_read": (C.c_int, [_P, C.c_int, C.c_int, _P, C.c_uint64]),
     "rp_act_wait": (C.c_int, [_P, C.c_int, C.c_int64]),
     "rp_act_next_ticket": (C.c_int, [_P, C.POINTER(C.c_int64)]),
     "rp_weight_stream_submit": (C.c_int, [_P, C.POINTER(rp_xfer), C.c_int, C.c_int, C.c_uint64, C.c_int64]),
