@@ -118,6 +118,8 @@ typedef struct rp_layer_cfg {
   float rms_eps;
   float rope_base;
   int32_t dtype;
+  int32_t qk_norm; /* 1: per-head RMSNorm of q and k before RoPE (Qwen3-style),
+                      gains gamma_q, gamma_k [head_dim]; 0: none */
 } rp_layer_cfg;
 
 /* The streams a context issues on (hipStream_t values, passed as void*).
@@ -161,6 +163,7 @@ typedef struct rp_streams {
  * and the base weights are frozen (no weight-gradient block is written). */
 typedef enum rp_tensor {
   RP_T_GAMMA1 = 0, RP_T_WQKV = 1, RP_T_WO = 2, RP_T_GAMMA2 = 3, RP_T_WGU = 4, RP_T_WD = 5,
+  RP_T_QNORM = 6, RP_T_KNORM = 7, /* qk_norm only: gamma_q, gamma_k [head_dim], after WD */
   RP_T_AQ = 16, RP_T_BQ = 17, RP_T_AK = 18, RP_T_BK = 19,
   RP_T_AV = 20, RP_T_BV = 21, RP_T_AO = 22, RP_T_BO = 23
 } rp_tensor;

@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "librp.so")
 RP_OK, RP_ERR_INVALID, RP_ERR_UNSUPPORTED, RP_ERR_WORKSPACE, RP_ERR_NOT_PINNED, RP_ERR_HIP, RP_ERR_STATE = range(7)
 RP_DTYPE_F32, RP_DTYPE_BF16 = 0, 1
 RP_T_GAMMA1, RP_T_WQKV, RP_T_WO, RP_T_GAMMA2, RP_T_WGU, RP_T_WD = 0, 1, 2, 3, 4, 5
+RP_T_QNORM, RP_T_KNORM = 6, 7
 RP_T_AQ, RP_T_BQ, RP_T_AK, RP_T_BK, RP_T_AV, RP_T_BV, RP_T_AO, RP_T_BO = range(16, 24)
 RP_BLOCK_WEIGHT, RP_BLOCK_GRAD, RP_BLOCK_LORA = 0, 1, 2
 RP_OP_STAGE_FWD, RP_OP_STAGE_BWD, RP_OP_LMHEAD, RP_OP_FUSED = 0, 1, 2, 3
@@ -37,7 +38,7 @@ class rp_layer_cfg(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("n_q", C.c_int32), ("n_kv", C.c_int32), ("head_dim", C.c_int32),
                 ("ffn", C.c_int32), ("n_experts", C.c_int32), ("top_k", C.c_int32), ("expert_ffn", C.c_int32),
                 ("lora_rank", C.c_int32), ("lora_alpha", C.c_float), ("rms_eps", C.c_float),
-                ("rope_base", C.c_float), ("dtype", C.c_int32)]
+                ("rope_base", C.c_float), ("dtype", C.c_int32), ("qk_norm", C.c_int32)]
 
 
 class rp_streams(C.Structure):
@@ -163,7 +164,8 @@ def make_cfg(cfg) -> rp_layer_cfg:
     """rp_layer_cfg from any object with the StageConfig attribute names."""
     return rp_layer_cfg(cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.ffn, cfg.n_experts, cfg.top_k,
                         cfg.expert_ffn, cfg.lora_rank, float(cfg.lora_alpha), float(cfg.rms_eps),
-                        float(cfg.rope_base), RP_DTYPE_BF16 if cfg.dtype == "bf16" else RP_DTYPE_F32)
+                        float(cfg.rope_base), RP_DTYPE_BF16 if cfg.dtype == "bf16" else RP_DTYPE_F32,
+                        1 if getattr(cfg, "qk_norm", False) else 0)
 
 
 def block_layout(cfg, block: int, tensor: int):

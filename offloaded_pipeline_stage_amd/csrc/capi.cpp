@@ -29,6 +29,7 @@ Shape make_shape(const rp_layer_cfg& c) {
   s.Q = c.n_q * c.head_dim; s.KV = c.n_kv * c.head_dim; s.QKV = s.Q + 2 * s.KV;
   s.dt = c.dtype;
   s.es = dtype_size(c.dtype);
+  s.qkn = c.qk_norm != 0;
   return s;
 }
 
@@ -45,6 +46,11 @@ rp_status block_layout(const rp_layer_cfg& cfg, int block, int tensor, size_t* o
     const size_t dn = s.E > 0 ? (size_t)s.E * H * s.Fe : H * (size_t)s.F;
     ts = {{RP_T_GAMMA1, H}, {RP_T_WQKV, (size_t)s.QKV * H}, {RP_T_WO, H * s.Q}, {RP_T_GAMMA2, H},
           {RP_T_WGU, gu}, {RP_T_WD, dn}};
+    // the QK-norm gains come last, so that the other offsets do not move
+    if (s.qkn) {
+      ts.push_back({RP_T_QNORM, (size_t)s.d});
+      ts.push_back({RP_T_KNORM, (size_t)s.d});
+    }
   } else if (block == RP_BLOCK_LORA) {
     RP_CHECK(s.r > 0, RP_ERR_INVALID, "layout: no LoRA block when lora_rank == 0");
     es = 4;

@@ -41,6 +41,7 @@ struct Shape {
   int Q, KV, QKV;  // q width, kv width, packed qkv width
   int dt;
   size_t es;       // element size
+  bool qkn;        // per-head RMSNorm of q and k before RoPE
 };
 
 // Bump allocator over the caller's workspace; a dry run (base == nullptr)

@@ -616,6 +616,12 @@ rp_status rmsnorm_fwd(int dt, const void* x, const void* gamma, void* y, float* 
   return RP_OK;
 }
 
+rp_status sum_rows(const float* part, int nrow, int H, float* out, bool accumulate, hipStream_t s) {
+  if (H == 0) return RP_OK;
+  RP_LAUNCH(sum_rows_kernel, dim3((unsigned)cdiv(H, 32)), dim3(256), 0, s, part, nrow, H, out, (int)accumulate);
+  return RP_OK;
+}
+
 size_t rmsnorm_bwd_part_bytes(int T, int H) {
   return (size_t)cdiv(T, RMS_BWD_ROWS) * H * sizeof(float);
 }

@@ -98,6 +98,20 @@ rp_status rmsnorm_bwd(int dt, const float* g, const void* x, const void* gamma,
                       void* out_dt, float* dgamma, bool dgamma_acc, float* part, int T, int H,
                       hipStream_t s);
 size_t rmsnorm_bwd_part_bytes(int T, int H);
+// column sums of part [nrow, H] into out[0 .. H) (added when accumulate)
+rp_status sum_rows(const float* part, int nrow, int H, float* out, bool accumulate, hipStream_t s);
+
+// QK-norm fused with RoPE on the q and k heads of qkv [T, ld] (in place):
+// raw [T * (nq + nkv), d] keeps the pre-norm values, rstd [T * (nq + nkv)].
+rp_status qknorm_rope_fwd(int dt, void* qkv, int64_t ld, void* raw, float* rstd, const void* gq, const void* gk,
+                          int T, int seq, int nq, int nkv, int d, const float2* tab, float eps, hipStream_t s);
+// Its backward, in place on the q and k heads of dqkv; dgamma (nullable) gets
+// [gamma_q grad | gamma_k grad] (2d floats, added when dgamma_acc) through
+// part (qknorm_part_bytes).
+rp_status qknorm_rope_bwd(int dt, void* dqkv, int64_t ld, const void* raw, const float* rstd, const void* gq,
+                          const void* gk, int T, int seq, int nq, int nkv, int d, const float2* tab, float* dgamma,
+                          bool dgamma_acc, float* part, hipStream_t s);
+size_t qknorm_part_bytes(int T, int n_heads, int d);
 
 // cos/sin table [seq][d/2] (fp32 pairs) computed in fp64
 rp_status rope_table(float2* tab, int seq, int d, float base, hipStream_t s);

@@ -18,6 +18,8 @@ struct Acts {
   float* rstd1 = nullptr; // [T]
   void* a = nullptr;      // RMSNorm1(x) [T, H]
   void* qkv = nullptr;    // [T, QKV], q and k rotated
+  void* qkraw = nullptr;  // QK-norm: pre-norm q and k heads [T * (nq + nkv), d]
+  float* qkrstd = nullptr; // QK-norm: [T * (nq + nkv)]
   void* o = nullptr;      // attention output [T, Q]
   float* lse = nullptr;   // [nq, T]
   void* h1 = nullptr;     // x + o Wo^T [T, H]
@@ -60,6 +62,7 @@ struct BwdTmp {
   void* dbe = nullptr;     // MoE: input gradients per grouped row [T k, H]
   void* gp[2] = {nullptr, nullptr};  // inter-layer gradients
   void* ck[2] = {nullptr, nullptr};  // uploaded checkpoints
+  float* qkpart = nullptr;           // QK-norm gain-gradient partials
 };
 
 struct Layout {
@@ -76,6 +79,10 @@ void carve_acts(Bump& bp, const Shape& s, int64_t T, Acts& A) {
   A.rstd1 = bp.take<float>(T * 4);
   A.a = bp.take(T * s.H * s.es);
   A.qkv = bp.take(T * s.QKV * s.es);
+  if (s.qkn) {
+    A.qkraw = bp.take(T * (s.Q + s.KV) * s.es);
+    A.qkrstd = bp.take<float>(T * (s.nq + s.nkv) * 4);
+  }
   A.o = bp.take(T * s.Q * s.es);
   A.lse = bp.take<float>((size_t)s.nq * T * 4);
   A.h1 = bp.take(T * s.H * s.es);
@@ -143,6 +150,7 @@ void carve(Bump& bp, const Shape& s, int64_t T, int seq, int n_layers, bool keep
     b.Dbuf = bp.take<float>((size_t)s.nq * T * 4);
     if (s.dt == RP_DTYPE_F32) b.dm_tmp = bp.take<float>(T * s.F * 4);
     b.part = bp.take<float>(rmsnorm_bwd_part_bytes((int)T, s.H));
+    if (s.qkn) b.qkpart = bp.take<float>(qknorm_part_bytes((int)T, s.nq + s.nkv, s.d));
     if (s.dt == RP_DTYPE_BF16) {
       // largest weight-gradient product: dW_gu [2F, H] over T tokens
       size_t need = 0;
@@ -244,7 +252,11 @@ rp_status layer_fwd(rp_ctx* c, const LayerBinding& lb, const LoraBf16& lw, void*
       RP_TRY(gemm(g, st));
     }
   }
-  RP_TRY(rope_apply(dt, A.qkv, s.QKV, T, seq, s.nq + s.nkv, s.d, rope, false, st));
+  if (s.qkn)
+    RP_TRY(qknorm_rope_fwd(dt, A.qkv, s.QKV, A.qkraw, A.qkrstd, wptr(w, cfg, RP_T_QNORM), wptr(w, cfg, RP_T_KNORM), T,
+                           seq, s.nq, s.nkv, s.d, rope, cfg.rms_eps, st));
+  else
+    RP_TRY(rope_apply(dt, A.qkv, s.QKV, T, seq, s.nq + s.nkv, s.d, rope, false, st));
   AttnDesc ad;
   ad.dt = dt; ad.batch = T / seq; ad.seq = seq; ad.n_q = s.nq; ad.n_kv = s.nkv; ad.d = s.d;
   RP_TRY(attn_fwd(ad, A.qkv, A.o, A.lse, st));
@@ -391,7 +403,16 @@ rp_status layer_bwd(rp_ctx* c, LayerBinding& lb, const LoraBf16& lw, int T, int 
   AttnDesc ad;
   ad.dt = dt; ad.batch = T / seq; ad.seq = seq; ad.n_q = s.nq; ad.n_kv = s.nkv; ad.d = s.d;
   RP_TRY(attn_bwd(ad, A.qkv, A.o, B.dO, A.lse, B.Dbuf, B.dqkv, st));
-  RP_TRY(rope_apply(dt, B.dqkv, s.QKV, T, seq, s.nq + s.nkv, s.d, rope, true, st));
+  if (s.qkn) {
+    // the gains are base weights: trained in a full fine-tune, frozen with LoRA;
+    // gamma_k's gradient directly follows gamma_q's in the gradient block
+    float* dg = full ? gptr(w, cfg, RP_T_QNORM) : nullptr;
+    RP_CHECK(!dg || gptr(w, cfg, RP_T_KNORM) == dg + s.d, RP_ERR_STATE, "qk-norm: gain gradients not adjacent");
+    RP_TRY(qknorm_rope_bwd(dt, B.dqkv, s.QKV, A.qkraw, A.qkrstd, wptr(w, cfg, RP_T_QNORM), wptr(w, cfg, RP_T_KNORM),
+                           T, seq, s.nq, s.nkv, s.d, rope, dg, accum, B.qkpart, st));
+  } else {
+    RP_TRY(rope_apply(dt, B.dqkv, s.QKV, T, seq, s.nq + s.nkv, s.d, rope, true, st));
+  }
   // da = dqkv Wqkv ; dWqkv = dqkv^T a
   RP_TRY(gemm(mk(T, s.H, s.QKV, B.dqkv, s.QKV, true, wptr(w, cfg, RP_T_WQKV), s.H, false, B.gbuf, s.H, dt,
                  RP_DTYPE_F32), st));

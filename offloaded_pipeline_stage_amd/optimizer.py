@@ -73,7 +73,8 @@ class OptimizerWorker:
         master dtype inside) and fp32 gradient block (uint8); init: optional
         fp32 values of the trainable tensors in block order, concatenated."""
         segs, pos = [], 0
-        for tid in LAYER_TENSORS:
+        tids = LAYER_TENSORS + ((B.RP_T_QNORM, B.RP_T_KNORM) if getattr(cfg, "qk_norm", False) else ())
+        for tid in tids:
             wo, wn, _ = B.block_layout(cfg, B.RP_BLOCK_WEIGHT, tid)
             go, gn, _ = B.block_layout(cfg, B.RP_BLOCK_GRAD, tid)
             w = w_block[wo:wo + wn].view(self.master_dtype)

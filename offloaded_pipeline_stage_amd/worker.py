@@ -38,10 +38,14 @@ class Worker:
             gu = torch.cat([w["wg"], w["wu"]], dim=1)  # [E, 2Fe, H]
         else:
             gu = torch.cat([w["wg"], w["wu"]], dim=0)  # [2F, H]
-        return {
+        t = {
             B.RP_T_GAMMA1: w["gamma1"], B.RP_T_WQKV: torch.cat([w["wq"], w["wk"], w["wv"]], dim=0),
             B.RP_T_WO: w["wo"], B.RP_T_GAMMA2: w["gamma2"], B.RP_T_WGU: gu, B.RP_T_WD: w["wd"],
         }
+        if getattr(cfg, "qk_norm", False):
+            t[B.RP_T_QNORM] = w["qnorm"]
+            t[B.RP_T_KNORM] = w["knorm"]
+        return t
 
     def pack_layer(self, w: Dict[str, torch.Tensor], pinned: bool = False) -> torch.Tensor:
         """Packed weight block, on the device or in pinned host memory."""
@@ -96,13 +100,18 @@ class Worker:
     def unpack_grads(self, gbuf: torch.Tensor) -> Dict[str, torch.Tensor]:
         cfg = self.cfg
         g = {}
-        for tid in (B.RP_T_GAMMA1, B.RP_T_WQKV, B.RP_T_WO, B.RP_T_GAMMA2, B.RP_T_WGU, B.RP_T_WD):
+        tids = [B.RP_T_GAMMA1, B.RP_T_WQKV, B.RP_T_WO, B.RP_T_GAMMA2, B.RP_T_WGU, B.RP_T_WD]
+        if getattr(cfg, "qk_norm", False):
+            tids += [B.RP_T_QNORM, B.RP_T_KNORM]
+        for tid in tids:
             off, nb = self.ctx.layout(B.RP_BLOCK_GRAD, tid)
             g[tid] = gbuf[off:off + nb].view(torch.float32)
         H, Q, KV = cfg.hidden, cfg.q_dim, cfg.kv_dim
         qkv = g[B.RP_T_WQKV].view(Q + 2 * KV, H)
         out = {"gamma1": g[B.RP_T_GAMMA1], "wq": qkv[:Q], "wk": qkv[Q:Q + KV], "wv": qkv[Q + KV:],
                "wo": g[B.RP_T_WO].view(H, Q), "gamma2": g[B.RP_T_GAMMA2]}
+        if getattr(cfg, "qk_norm", False):
+            out.update(qnorm=g[B.RP_T_QNORM], knorm=g[B.RP_T_KNORM])
         if cfg.n_experts > 0:
             E, Fe = cfg.n_experts, cfg.expert_ffn
             gu = g[B.RP_T_WGU].view(E, 2 * Fe, H)

@@ -168,8 +168,14 @@ def attention_block(x: Tensor, w: Dict[str, Tensor], cfg, lora: Optional[Dict[st
         q = q + lora_delta(a, lora["aq"], lora["bq"], scale)
         kk = kk + lora_delta(a, lora["ak"], lora["bk"], scale)
         v = v + lora_delta(a, lora["av"], lora["bv"], scale)
-    q = rope(q.reshape(T, nq, d), pos, cfg.rope_base)
-    kk = rope(kk.reshape(T, nkv, d), pos, cfg.rope_base)
+    q, kk = q.reshape(T, nq, d), kk.reshape(T, nkv, d)
+    if getattr(cfg, "qk_norm", False):
+        # Qwen3-style QK-norm: RMSNorm of every query and key head over its d
+        # dims, own gains per q and k, before the rotation
+        q = rmsnorm(q, w["qnorm"], cfg.rms_eps)
+        kk = rmsnorm(kk, w["knorm"], cfg.rms_eps)
+    q = rope(q, pos, cfg.rope_base)
+    kk = rope(kk, pos, cfg.rope_base)
     v = v.reshape(T, nkv, d)
     o = causal_attention(q, kk, v, cfg.batch, T // cfg.batch).reshape(T, nq * d)
     proj = o @ w["wo"].T
@@ -220,7 +226,11 @@ def layer_forward_rows(x: Tensor, w: Dict[str, Tensor], cfg, rows: Sequence[int]
     if lora is not None:
         kk = kk + lora_delta(a, lora["ak"], lora["bk"], scale)
         v = v + lora_delta(a, lora["av"], lora["bv"], scale)
-    kk = rope(kk.reshape(T, nkv, d), pos, cfg.rope_base)
+    kk = kk.reshape(T, nkv, d)
+    qkn = getattr(cfg, "qk_norm", False)
+    if qkn:
+        kk = rmsnorm(kk, w["knorm"], cfg.rms_eps)
+    kk = rope(kk, pos, cfg.rope_base)
     v = v.reshape(T, nkv, d)
     out = []
     for t in rows:
@@ -228,7 +238,10 @@ def layer_forward_rows(x: Tensor, w: Dict[str, Tensor], cfg, rows: Sequence[int]
         q = at @ w["wq"].T
         if lora is not None:
             q = q + lora_delta(at, lora["aq"], lora["bq"], scale)
-        q = rope(q.reshape(1, nq, d), pos[t:t + 1], cfg.rope_base)[0]
+        q = q.reshape(1, nq, d)
+        if qkn:
+            q = rmsnorm(q, w["qnorm"], cfg.rms_eps)
+        q = rope(q, pos[t:t + 1], cfg.rope_base)[0]
         r0 = (t // seq) * seq
         o = torch.empty(nq, d, dtype=x.dtype)
         for h in range(nq):
@@ -304,7 +317,10 @@ def trainable_names(cfg) -> List[str]:
     """Dense full fine-tune: every weight and gain. LoRA: the adapters only."""
     if cfg.lora_rank > 0:
         return ["aq", "bq", "ak", "bk", "av", "bv", "ao", "bo"]
-    return ["gamma1", "wq", "wk", "wv", "wo", "gamma2", "wg", "wu", "wd"]
+    names = ["gamma1", "wq", "wk", "wv", "wo", "gamma2", "wg", "wu", "wd"]
+    if getattr(cfg, "qk_norm", False):
+        names += ["qnorm", "knorm"]
+    return names
 
 
 def _cast(d: Optional[Dict[str, Tensor]], dtype) -> Optional[Dict[str, Tensor]]:

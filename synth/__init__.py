@@ -54,6 +54,7 @@ class StageConfig:
     fwd_layers: int = 1        # layers run by the forward stage call
     bwd_layers: int = 1        # layers run by the recompute+backward call
     final_norm: bool = False   # LM head preceded by a final RMSNorm
+    qk_norm: bool = False      # per-head RMSNorm of q and k before RoPE (Qwen3-style)
     embedding: bool = False    # full model: token embedding in front
     weight_std: float = 0.02
     seed: int = 1000
@@ -157,10 +158,10 @@ def layer_weights(cfg: StageConfig, layer: int, gamma: str = "ones",
     H, std = cfg.hidden, cfg.weight_std
     p = f"layer{layer}/"
 
-    def gam(n):
+    def gam(n, size=H):
         if gamma == "ones":
-            return torch.ones(H, dtype=torch.float32).to(dt)
-        return normal((H,), s, p + n, std=std, mean=1.0, dtype=dt)
+            return torch.ones(size, dtype=torch.float32).to(dt)
+        return normal((size,), s, p + n, std=std, mean=1.0, dtype=dt)
 
     w = {
         "gamma1": gam("gamma1"),
@@ -180,6 +181,9 @@ def layer_weights(cfg: StageConfig, layer: int, gamma: str = "ones",
         w["wg"] = normal((F, H), s, p + "wg", std, dtype=dt)
         w["wu"] = normal((F, H), s, p + "wu", std, dtype=dt)
         w["wd"] = normal((H, F), s, p + "wd", std, dtype=dt)
+    if cfg.qk_norm:
+        w["qnorm"] = gam("qnorm", cfg.head_dim)
+        w["knorm"] = gam("knorm", cfg.head_dim)
     return w
 
 

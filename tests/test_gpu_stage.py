@@ -83,13 +83,16 @@ def _layer_case(name, seq, n_layers, gamma="perturbed", **over):
     return cfg, layers, x, dy
 
 
-@pytest.mark.parametrize("name,seq,batch", [("qwen3_1p7b", 320, 1), ("llama3_8b", 200, 2)])
-def test_bf16_layer_fwd_bwd_matches_oracle(W, name, seq, batch):
+@pytest.mark.parametrize("name,seq,batch,qkn", [("qwen3_1p7b", 320, 1, False), ("llama3_8b", 200, 2, False),
+                                                ("qwen3_1p7b", 257, 2, True)])
+def test_bf16_layer_fwd_bwd_matches_oracle(W, name, seq, batch, qkn):
     """One bf16 decoder layer at the workload's real widths (Qwen3-1.7B or
     Llama-3.1-8B shapes) on a short ragged sequence: forward output, dx and
-    every weight gradient against the fp64 oracle on the same bf16 inputs."""
-    say("bf16 layer", name, seq, batch)
-    cfg, layers, x, dy = _layer_case(name, seq, 1, batch=batch)
+    every weight gradient against the fp64 oracle on the same bf16 inputs.
+    qkn: with Qwen3's per-head QK-norm (gains perturbed, so their gradients
+    carry signal)."""
+    say("bf16 layer", name, seq, batch, "qk-norm" if qkn else "")
+    cfg, layers, x, dy = _layer_case(name, seq, 1, batch=batch, qk_norm=qkn)
     wk = W(cfg)
     wk.add_layer(0, layers[0])
     T, H = cfg.tokens, cfg.hidden
@@ -163,13 +166,14 @@ def test_f32_lmhead_ragged_shards_matches_oracle(W, vocab, shards):
     assert max_rel(dw, dw_ref) < GRAD_TOL["f32"]
 
 
-def test_recompute_equals_kept_and_split_invariance_bf16(W):
+@pytest.mark.parametrize("qkn", [False, True])
+def test_recompute_equals_kept_and_split_invariance_bf16(W, qkn):
     """Two bf16 layers: (a) backward from kept activations (fused B_1) and
     backward with recomputation from checkpoints give bit-identical dx and
     gradients; (b) running [0,2) as one stage or as [0,1) + [1,2) gives
-    bit-identical outputs and gradients."""
-    say("recompute/split invariance")
-    cfg, layers, x, dy = _layer_case("qwen3_1p7b", 136, 2, hidden=1024, n_q=8, n_kv=4, ffn=2048)
+    bit-identical outputs and gradients. qkn: with QK-norm."""
+    say("recompute/split invariance", "qk-norm" if qkn else "")
+    cfg, layers, x, dy = _layer_case("qwen3_1p7b", 136, 2, hidden=1024, n_q=8, n_kv=4, ffn=2048, qk_norm=qkn)
     from offloaded_pipeline_stage_amd import binding as Bd
     wk = W(cfg)
     for l in range(2):

@@ -59,11 +59,13 @@ def _fd_check(fn, tensors, grads, n_elem=6, h=1e-6, tol=1e-6, seed=0):
         assert abs(fd - an) / max(abs(an), 1e-8) < tol, (fd, an)
 
 
-@pytest.mark.parametrize("variant", ["dense", "gqa", "lora", "moe"])
+@pytest.mark.parametrize("variant", ["dense", "gqa", "lora", "moe", "qknorm"])
 def test_layer_fd(variant):
     kw = {}
     if variant == "dense":
         kw = dict(n_q=2, n_kv=2)
+    if variant == "qknorm":
+        kw = dict(qk_norm=True)
     if variant == "lora":
         kw = dict(lora_rank=3, lora_alpha=6.0)
     if variant == "moe":
@@ -104,6 +106,43 @@ def test_lmhead_fd():
 # ---------------------------------------------------------------------------
 # closed forms
 # ---------------------------------------------------------------------------
+
+
+def test_qk_norm_scale_invariance_and_unit_heads():
+    """QK-norm (Qwen3-style): with eps = 0 the per-head RMSNorm removes any
+    positive scale of the q and k projections, so scaling W_q and W_k leaves
+    the layer unchanged, while without QK-norm the same scaling changes it;
+    with unit gains every rotated head has norm sqrt(d) (rotation keeps norms)."""
+    cfg = tiny_cfg(qk_norm=True, rms_eps=0.0)
+    w = f64(synth.layer_weights(cfg, 0, gamma="perturbed"))
+    for k in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"):
+        w[k] = w[k] * 10
+    x = synth.activation(cfg, "x").to(D64)
+    y = O.layer_forward(x, w, cfg)
+    w2 = dict(w, wq=w["wq"] * 3.7, wk=w["wk"] * 0.45)
+    assert torch.allclose(O.layer_forward(x, w2, cfg), y, rtol=1e-12, atol=1e-12)
+    plain = tiny_cfg(rms_eps=0.0)
+    assert not torch.allclose(O.layer_forward(x, w2, plain), O.layer_forward(x, w, plain), rtol=1e-6, atol=1e-6)
+    w1 = dict(w, qnorm=torch.ones_like(w["qnorm"]), knorm=torch.ones_like(w["knorm"]))
+    _, q, k, _, _, _, _ = O.attention_block(x, w1, cfg)
+    d = cfg.head_dim
+    assert torch.allclose(q.norm(dim=-1), torch.full(q.shape[:2], math.sqrt(d), dtype=D64), rtol=1e-12)
+    assert torch.allclose(k.norm(dim=-1), torch.full(k.shape[:2], math.sqrt(d), dtype=D64), rtol=1e-12)
+
+
+def test_qk_norm_matches_library_rms_norm():
+    """The per-head normalisation equals torch's rms_norm over each head's d
+    dims (the rotation undone with the RoPE at position 0 of every row: seq 1)."""
+    cfg = tiny_cfg(qk_norm=True, seq=1, batch=6)
+    w = f64(synth.layer_weights(cfg, 0, gamma="perturbed"))
+    x = synth.activation(cfg, "x").to(D64)
+    a, q, k, _, _, _, _ = O.attention_block(x, w, cfg)
+    T, d = x.shape[0], cfg.head_dim
+    ref_q = F.rms_norm((a @ w["wq"].T).reshape(T, cfg.n_q, d), (d,), w["qnorm"], cfg.rms_eps)
+    ref_k = F.rms_norm((a @ w["wk"].T).reshape(T, cfg.n_kv, d), (d,), w["knorm"], cfg.rms_eps)
+    assert torch.allclose(q, ref_q, rtol=1e-12, atol=1e-14)
+    assert torch.allclose(k, ref_k, rtol=1e-12, atol=1e-14)
+
 
 
 @pytest.mark.parametrize("vocab,expect", [(4096, 8.317766166719343), (128256, 11.761783545564427)])
