@@ -104,12 +104,15 @@ def layer_cost(cfg):
 class Step:
     """Buffers and calls of one worker step through the C ABI."""
 
-    def __init__(self, cfg, streamed: bool):
+    def __init__(self, cfg, streamed: bool, grad_bf16: bool = False):
         from offloaded_pipeline_stage_amd import binding as B
         from offloaded_pipeline_stage_amd.worker import Worker
         self.B = B
         self.cfg = cfg
         self.streamed = streamed
+        # gradients on the link in bf16 (the pages' precision) instead of fp32
+        self.grad_kind = B.RP_GRAD_D2H_BF16 if grad_bf16 else B.RP_GRAD_D2H
+        gdt = torch.bfloat16 if grad_bf16 else torch.float32
         dev = torch.device("cuda", 0)
         T, H = cfg.tokens, cfg.hidden
         t0 = time.time()
@@ -130,8 +133,9 @@ class Step:
             for r in rows:
                 self.host_shards.append(head["w"][lo:lo + r].contiguous().pin_memory())
                 lo += r
-            self.host_grad = [torch.empty(self.wk.g_bytes, dtype=torch.uint8).pin_memory() for _ in (0, 1)]
-            self.host_dshards = [torch.empty(r, H, dtype=torch.float32).pin_memory() for r in rows]
+            gb = self.wk.g_bytes // (2 if grad_bf16 else 1)
+            self.host_grad = [torch.empty(gb, dtype=torch.uint8).pin_memory() for _ in (0, 1)]
+            self.host_dshards = [torch.empty(r, H, dtype=gdt).pin_memory() for r in rows]
         else:
             self.wk.add_layer(0, lw)
             self.wk.add_lmhead(head["w"])
@@ -155,7 +159,8 @@ class Step:
         B, out = self.B, []
         hs = self.host_shards if kind == B.RP_PARAM_H2D else self.host_dshards
         for sh, h in enumerate(hs):
-            out.append((kind, B.RP_TGT_LMHEAD, sh, 0, h.numel() * h.element_size(), h))
+            nb = h.numel() * (4 if kind != B.RP_PARAM_H2D else h.element_size())  # device-side bytes
+            out.append((kind, B.RP_TGT_LMHEAD, sh, 0, nb, h))
         return out
 
     def run(self):
@@ -175,10 +180,10 @@ class Step:
         ctx.lmhead_ce_fwd_bwd(b, s, self.y, self.labels, self.loss, self.dy, self.ws_h)
         if self.streamed:
             # shard gradients down; the next step's shards up once read
-            sub(self._shard_items(B.RP_GRAD_D2H) + self._shard_items(B.RP_PARAM_H2D))
+            sub(self._shard_items(self.grad_kind) + self._shard_items(B.RP_PARAM_H2D))
         ctx.stage_bwd_recompute(layer, layer + 1, b, s, self.dy, self.dx, self.ws_b, ckpt=self.ckpt)
         if self.streamed:
-            sub([(B.RP_GRAD_D2H, B.RP_TGT_LAYER, layer, 0, wk.g_bytes, self.host_grad[layer])])
+            sub([(self.grad_kind, B.RP_TGT_LAYER, layer, 0, wk.g_bytes, self.host_grad[layer])])
         self.n += 1
 
     def sync(self):
@@ -583,6 +588,23 @@ def main():
                            "h2d_GB_per_step": round(h2d / 1e9, 3), "d2h_GB_per_step": round(d2h / 1e9, 3),
                            "h2d_GBps_if_link_bound": round(h2d / 1e9 / (ms_s / 1e3), 1),
                            "d2h_GBps_if_link_bound": round(d2h / 1e9 / (ms_s / 1e3), 1)}
+        del st
+        torch.cuda.empty_cache()
+        # the same step with the gradients on the link in bf16 (the pages'
+        # precision; the workload's own gradients are fp32)
+        st = Step(cfg, streamed=True, grad_bf16=True)
+        for _ in range(a.warmup):
+            st.run()
+        st.sync()
+        t0 = time.perf_counter()
+        for _ in range(a.steps):
+            st.run()
+        st.sync()
+        ms_b = (time.perf_counter() - t0) * 1e3 / a.steps
+        d2h_b = d2h / 2
+        out["streamed_bf16_grads"] = {"tokens_per_s": round(cfg.tokens / (ms_b / 1e3), 1), "ms_per_step": round(ms_b, 3),
+                                      "h2d_GB_per_step": round(h2d / 1e9, 3), "d2h_GB_per_step": round(d2h_b / 1e9, 3),
+                                      "over_resident": round(ms_b / ms_step, 3)}
         del st
         torch.cuda.empty_cache()
         out["priority"] = priority_probe(cfg)

@@ -431,7 +431,12 @@ enum { RP_ON_COMPUTE = 0, RP_ON_ACT_H2D = 1, RP_ON_ACT_D2H = 2 };
 rp_status rp_act_wait(rp_ctx* ctx, int where, int64_t ticket);
 rp_status rp_act_next_ticket(const rp_ctx* ctx, int64_t* next);
 
-typedef enum rp_xfer_kind { RP_PARAM_H2D = 0, RP_GRAD_D2H = 1 } rp_xfer_kind;
+/* RP_GRAD_D2H_BF16 downloads an fp32 gradient range rounded to bf16 (nearest
+ * even): the host buffer receives bytes / 2. This is the pages' low-precision
+ * gradient on the link (section 4.3.1, the low-precision master copy, whose
+ * G-cp casts it back); offset and bytes must be multiples of 32, and the
+ * host buffer 16-byte aligned, pinned and device-mapped. */
+typedef enum rp_xfer_kind { RP_PARAM_H2D = 0, RP_GRAD_D2H = 1, RP_GRAD_D2H_BF16 = 2 } rp_xfer_kind;
 typedef enum rp_xfer_target {
   RP_TGT_LAYER = 0,  /* id = layer; bytes of the weight / gradient block      */
   RP_TGT_LMHEAD = 1, /* id = shard; bytes of the shard's weight / gradient    */

@@ -30,7 +30,7 @@ RP_KEEP_ACTS, RP_USE_KEPT_ACTS, RP_CKPT_DEVICE, RP_ACCUM_GRADS = 1, 2, 4, 8
 RP_H2D, RP_D2H = 0, 1
 RP_ON_COMPUTE, RP_ON_ACT_H2D, RP_ON_ACT_D2H = 0, 1, 2
 RP_OPT_PARAMS_UPLOADED, RP_OPT_GRADS_DOWNLOADED, RP_OPT_PCP_DONE, RP_OPT_GCP_DONE = 0, 1, 2, 3
-RP_PARAM_H2D, RP_GRAD_D2H = 0, 1
+RP_PARAM_H2D, RP_GRAD_D2H, RP_GRAD_D2H_BF16 = 0, 1, 2
 RP_TGT_LAYER, RP_TGT_LMHEAD, RP_TGT_LORA, RP_TGT_FINAL_NORM = 0, 1, 2, 3
 
 

@@ -65,7 +65,8 @@ struct XChunk {
   Slot* slot;
   char* dev;
   char* host;
-  uint64_t bytes;
+  uint64_t bytes;     // device-side bytes
+  bool bf16 = false;  // download fp32 as bf16 (host gets bytes / 2)
 };
 struct XWindow {
   int dir;

@@ -82,6 +82,22 @@ __global__ __launch_bounds__(256) void download_kernel(uint4* __restrict__ dst, 
   for (; i < n16; i += stride) dst[i] = src[i];
 }
 
+// fp32 device data -> bf16 in the host buffer's device mapping, rounded to
+// nearest even: 8 values (32 bytes in, 16 out) per lane and step
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, to_bf16(lo)) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, to_bf16(hi)) << 16);
+}
+__global__ __launch_bounds__(256) void download_bf16_kernel(uint4* __restrict__ dst, const float4* __restrict__ src,
+                                                            size_t n8) {
+  size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (; i < n8; i += stride) {
+    const float4 a = src[2 * i], b = src[2 * i + 1];
+    dst[i] = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // RMSNorm
 // ---------------------------------------------------------------------------
@@ -598,6 +614,14 @@ rp_status download_copy(void* host_dev, const void* src, size_t bytes, hipStream
   // 16 workgroups (4 waves each) keep the host link saturated; more would
   // only take compute units from the stage's kernels
   RP_LAUNCH(download_kernel, dim3(16), dim3(256), 0, s, (uint4*)host_dev, (const uint4*)src, bytes / 16);
+  return RP_OK;
+}
+
+rp_status download_bf16(void* host_dev, const void* src, size_t src_bytes, hipStream_t s) {
+  if (src_bytes == 0) return RP_OK;
+  RP_CHECK((((uintptr_t)host_dev | (uintptr_t)src) & 15) == 0 && src_bytes % 32 == 0, RP_ERR_INVALID,
+           "bf16 download: 16-byte aligned ends and a multiple of 32 source bytes required");
+  RP_LAUNCH(download_bf16_kernel, dim3(16), dim3(256), 0, s, (uint4*)host_dev, (const float4*)src, src_bytes / 32);
   return RP_OK;
 }
 

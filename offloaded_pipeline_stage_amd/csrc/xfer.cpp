@@ -87,17 +87,20 @@ namespace {
 // download stream q: 0 activations, 1 gradients; ordered after everything already on st and before
 // everything enqueued on st later) when the host buffer has a device mapping
 // and both ends are 16-byte aligned, else a DMA copy on st
-rp_status download(rp_ctx* c, int q, void* host, const void* dev, size_t bytes, hipStream_t st) {
+rp_status download(rp_ctx* c, int q, void* host, const void* dev, size_t bytes, hipStream_t st, bool bf16 = false) {
   void* hd = nullptr;
   if ((((uintptr_t)host | (uintptr_t)dev | bytes) & 15) != 0 || hipHostGetDevicePointer(&hd, host, 0) != hipSuccess ||
       hd == nullptr) {
     (void)hipGetLastError();  // a failed lookup leaves an error behind
+    // the bf16 conversion happens in the copy kernel: no DMA fallback for it
+    RP_CHECK(!bf16, RP_ERR_UNSUPPORTED, "bf16 gradient download needs an aligned, device-mapped pinned host buffer");
     RP_HIP(hipMemcpyAsync(host, dev, bytes, hipMemcpyDeviceToHost, st));
     return RP_OK;
   }
+  auto copy = [&](hipStream_t on) { return bf16 ? download_bf16(hd, dev, bytes, on) : download_copy(hd, dev, bytes, on); };
   // a stream the context created has its own hardware queue: the kernel
   // goes straight onto it
-  if (c->own_d2h[q]) return download_copy(hd, dev, bytes, st);
+  if (c->own_d2h[q]) return copy(st);
   if (!c->dl[q]) {
     RP_TRY(new_queue_stream(c->device, &c->dl[q]));
     c->dl_in[q] = c->new_event();
@@ -105,7 +108,7 @@ rp_status download(rp_ctx* c, int q, void* host, const void* dev, size_t bytes, 
   }
   RP_HIP(hipEventRecord(c->dl_in[q], st));
   RP_HIP(hipStreamWaitEvent(c->dl[q], c->dl_in[q], 0));
-  RP_TRY(download_copy(hd, dev, bytes, c->dl[q]));
+  RP_TRY(copy(c->dl[q]));
   RP_HIP(hipEventRecord(c->dl_out[q], c->dl[q]));
   RP_HIP(hipStreamWaitEvent(st, c->dl_out[q], 0));
   return RP_OK;
@@ -136,7 +139,7 @@ rp_status issue_window(rp_ctx* c, XWindow& win) {
       }
     } else {
       if (&s != prev && s.g_ready_valid) RP_HIP(hipStreamWaitEvent(st, s.g_ready, 0));
-      RP_TRY(download(c, 1, ch.host, ch.dev, ch.bytes, st));
+      RP_TRY(download(c, 1, ch.host, ch.dev, ch.bytes, st, ch.bf16));
       if (--s.g_chunks_unissued == 0) {
         if (!s.g_drained) s.g_drained = c->new_event();
         RP_HIP(hipEventRecord(s.g_drained, st));
@@ -187,7 +190,7 @@ rp_status resolve(rp_ctx* c, const rp_xfer& it, Slot** slot, char** dev, uint64_
     RP_CHECK(s->w != nullptr, RP_ERR_INVALID, "transfer: target has no weight buffer");
     *dev = (char*)s->w;
     *cap = s->w_bytes;
-  } else if (it.kind == RP_GRAD_D2H) {
+  } else if (it.kind == RP_GRAD_D2H || it.kind == RP_GRAD_D2H_BF16) {
     RP_CHECK(s->g != nullptr, RP_ERR_INVALID, "transfer: target has no gradient buffer");
     *dev = (char*)s->g;
     *cap = s->g_bytes;
@@ -319,14 +322,18 @@ rp_status weight_stream_submit(rp_ctx* c, const rp_xfer* items, int n_items, int
              "submit: item %d [%llu, +%llu) exceeds its buffer (%llu bytes)", i, (unsigned long long)it.offset,
              (unsigned long long)it.bytes, (unsigned long long)cap);
     RP_CHECK(it.host && is_pinned_host(it.host), RP_ERR_NOT_PINNED, "submit: item %d host pointer not pinned", i);
+    if (it.kind == RP_GRAD_D2H_BF16)
+      RP_CHECK(it.offset % 32 == 0 && it.bytes % 32 == 0 && ((uintptr_t)it.host & 15) == 0, RP_ERR_INVALID,
+               "submit: item %d: a bf16 gradient download needs offset and bytes in multiples of 32 and a 16-byte "
+               "aligned host buffer", i);
     devs[i] += it.offset;
   }
   for (int dir = RP_H2D; dir <= RP_D2H; ++dir) {
-    const int kind = dir == RP_H2D ? RP_PARAM_H2D : RP_GRAD_D2H;
     std::vector<int> idx;
     std::vector<uint64_t> sizes;
     for (int i = 0; i < n_items; ++i)
-      if (items[i].kind == kind) {
+      if (dir == RP_H2D ? items[i].kind == RP_PARAM_H2D
+                        : (items[i].kind == RP_GRAD_D2H || items[i].kind == RP_GRAD_D2H_BF16)) {
         idx.push_back(i);
         sizes.push_back(items[i].bytes);
       }
@@ -345,7 +352,8 @@ rp_status weight_stream_submit(rp_ctx* c, const rp_xfer* items, int n_items, int
       ch.dir = dir;
       ch.slot = slots[i];
       ch.dev = devs[i] + pc.off;
-      ch.host = (char*)items[i].host + pc.off;
+      ch.bf16 = items[i].kind == RP_GRAD_D2H_BF16;
+      ch.host = (char*)items[i].host + (ch.bf16 ? pc.off / 2 : pc.off);
       ch.bytes = pc.bytes;
       if (dir == RP_H2D) ch.slot->w_chunks_unissued++;
       else ch.slot->g_chunks_unissued++;

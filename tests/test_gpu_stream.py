@@ -102,6 +102,49 @@ def test_grad_download_kernel_and_fallback_paths(env):
     assert not h_mis[:8].any() and not h_mis[8 + nb:].any()
 
 
+def test_bf16_grad_download_rounds_to_nearest_even(env):
+    """RP_GRAD_D2H_BF16 (the pages' low-precision gradients on the link): an
+    fp32 gradient block downloaded in chunks over three windows, and a range
+    inside it, arrive as the fp32 values rounded to nearest even (torch's
+    rounding) -- ties, tiny values, infinities and NaN included -- and the host
+    bytes around the range stay untouched. Misaligned ranges are rejected."""
+    B, Worker = env
+    say("bf16 gradient download")
+    cfg = _small_cfg()
+    wk = Worker(cfg)
+    wk.add_layer(0, synth.layer_weights(cfg, 0))
+    gb = wk.g_bytes
+    n = gb // 4
+    gen = torch.Generator().manual_seed(11)
+    vals = torch.randn(n, generator=gen) * 3
+    specials = torch.tensor([1.00390625, 1.01171875, -1.00390625, 1e-30, -3e-35, float("inf"), float("-inf"),
+                             65504.0, 3.3895314e38, 0.0, -0.0])
+    vals[:specials.numel()] = specials
+    g = wk.layers[0]["g"].view(torch.float32)
+    g[:n].copy_(vals.to(DEV))
+    torch.cuda.synchronize()
+    h = torch.zeros(n, dtype=torch.bfloat16).pin_memory()
+    off, nb = 4096, 32 * 1000
+    h2 = torch.zeros(nb // 4 + 64, dtype=torch.bfloat16).pin_memory()
+    wk.ctx.weight_stream_submit([(B.RP_GRAD_D2H_BF16, B.RP_TGT_LAYER, 0, 0, gb, h)], n_windows=3, max_chunk=1 << 16)
+    wk.ctx.weight_stream_submit([(B.RP_GRAD_D2H_BF16, B.RP_TGT_LAYER, 0, off, nb, h2.data_ptr() + 64)],
+                                n_windows=2, max_chunk=1 << 12)
+    wk.ctx.sync()
+    ref = vals.to(torch.bfloat16)
+    assert torch.equal(h.view(torch.int16), ref.view(torch.int16))
+    seg = h2[32:32 + nb // 4]
+    assert torch.equal(seg.view(torch.int16), ref[off // 4:off // 4 + nb // 4].view(torch.int16))
+    assert not h2[:32].view(torch.int16).any() and not h2[32 + nb // 4:].view(torch.int16).any()
+    nan = torch.tensor([float("nan")])
+    g[:1].copy_(nan.to(DEV))
+    torch.cuda.synchronize()
+    wk.ctx.weight_stream_submit([(B.RP_GRAD_D2H_BF16, B.RP_TGT_LAYER, 0, 0, 32, h)])
+    wk.ctx.sync()
+    assert torch.isnan(h[:1].float()).all()
+    with pytest.raises(B.RPError):
+        wk.ctx.weight_stream_submit([(B.RP_GRAD_D2H_BF16, B.RP_TGT_LAYER, 0, 16, 64, h)])
+
+
 def test_deferred_window_waits_for_its_ticket(env):
     B, Worker = env
     say("deferred window")
