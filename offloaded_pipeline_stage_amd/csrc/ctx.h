@@ -104,6 +104,7 @@ struct rp_ctx {
   std::vector<hipEvent_t> all_events;    // every event created (destroyed with the context)
   std::vector<hipEvent_t> ev_free;       // recycled ticket events
   hipEvent_t ev_mark = nullptr;          // scratch: "compute reached this point"
+  void* bf16_stage = nullptr;            // device staging of bf16 gradient downloads
   // per workspace (by base pointer): the compute stream is done with it after
   // this event -- uploads into a workspace's checkpoint buffers wait for it
   std::map<const void*, hipEvent_t> ws_done;

@@ -3,6 +3,8 @@
 // cross-entropy, token embedding. All HBM-bound: one wavefront per row with
 // 16-byte vector accesses, reductions by fixed-order butterflies so every
 // result is deterministic (recomputation must reproduce the forward exactly).
+#include <algorithm>
+
 #include "ops.h"
 #include "trace.h"
 
@@ -82,13 +84,13 @@ __global__ __launch_bounds__(256) void download_kernel(uint4* __restrict__ dst, 
   for (; i < n16; i += stride) dst[i] = src[i];
 }
 
-// fp32 device data -> bf16 in the host buffer's device mapping, rounded to
-// nearest even: 8 values (32 bytes in, 16 out) per lane and step
+// fp32 -> bf16, rounded to nearest even: 8 values (32 bytes in, 16 out) per
+// lane and step
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, to_bf16(lo)) |
          ((uint32_t)__builtin_bit_cast(uint16_t, to_bf16(hi)) << 16);
 }
-__global__ __launch_bounds__(256) void download_bf16_kernel(uint4* __restrict__ dst, const float4* __restrict__ src,
+__global__ __launch_bounds__(256) void convert_f32_bf16_kernel(uint4* __restrict__ dst, const float4* __restrict__ src,
                                                             size_t n8) {
   size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -617,11 +619,14 @@ rp_status download_copy(void* host_dev, const void* src, size_t bytes, hipStream
   return RP_OK;
 }
 
-rp_status download_bf16(void* host_dev, const void* src, size_t src_bytes, hipStream_t s) {
+rp_status convert_f32_bf16(void* dst, const void* src, size_t src_bytes, hipStream_t s) {
   if (src_bytes == 0) return RP_OK;
-  RP_CHECK((((uintptr_t)host_dev | (uintptr_t)src) & 15) == 0 && src_bytes % 32 == 0, RP_ERR_INVALID,
-           "bf16 download: 16-byte aligned ends and a multiple of 32 source bytes required");
-  RP_LAUNCH(download_bf16_kernel, dim3(16), dim3(256), 0, s, (uint4*)host_dev, (const float4*)src, src_bytes / 32);
+  RP_CHECK((((uintptr_t)dst | (uintptr_t)src) & 15) == 0 && src_bytes % 32 == 0, RP_ERR_INVALID,
+           "bf16 conversion: 16-byte aligned ends and a multiple of 32 source bytes required");
+  const size_t n8 = src_bytes / 32;
+  TraceScope ts(s, "convert_f32_bf16_kernel", 0.0, 1.5 * (double)src_bytes);
+  RP_LAUNCH(convert_f32_bf16_kernel, dim3((unsigned)std::min<size_t>((n8 + 255) / 256, 2048)), dim3(256), 0, s,
+            (uint4*)dst, (const float4*)src, n8);
   return RP_OK;
 }
 

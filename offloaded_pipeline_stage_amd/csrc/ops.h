@@ -84,8 +84,8 @@ rp_status copy16(void* dst, const void* src, size_t bytes, hipStream_t s);
 // device -> pinned host through a small copy kernel (host_dev: the host
 // buffer's device mapping); see download() in the transfer engine
 rp_status download_copy(void* host_dev, const void* src, size_t bytes, hipStream_t s);
-// fp32 src (src_bytes) -> bf16 at host_dev (src_bytes / 2), round to nearest even
-rp_status download_bf16(void* host_dev, const void* src, size_t src_bytes, hipStream_t s);
+// fp32 src (src_bytes) -> bf16 at dst (src_bytes / 2), round to nearest even
+rp_status convert_f32_bf16(void* dst, const void* src, size_t src_bytes, hipStream_t s);
 
 // y = x * rsqrt(mean(x^2) + eps) * gamma ; rstd[t] = rsqrt(...)
 rp_status rmsnorm_fwd(int dt, const void* x, const void* gamma, void* y, float* rstd, int T,

@@ -75,10 +75,10 @@ def test_streamed_weights_and_grad_download_bit_identical(env):
 
 
 def test_grad_download_kernel_and_fallback_paths(env):
-    """Gradient downloads take the copy kernel when the pinned host buffer and
-    the chunk are 16-byte aligned, and a DMA copy otherwise (a host address 8
-    bytes past a boundary, a ragged size, small chunks): both must reproduce
-    the device bytes exactly, and leave the host bytes around them untouched."""
+    """Gradient downloads (by DMA) of an aligned block in chunks over three
+    windows and of a range at a host address 8 bytes past a boundary with a
+    ragged size: both must reproduce the device bytes exactly, and leave the
+    host bytes around them untouched."""
     B, Worker = env
     say("download paths")
     cfg = _small_cfg()
