@@ -434,11 +434,14 @@ rp_status rp_act_next_ticket(const rp_ctx* ctx, int64_t* next);
 /* RP_GRAD_D2H_BF16 downloads an fp32 gradient range rounded to bf16 (nearest
  * even): the host buffer receives bytes / 2. This is the pages' low-precision
  * gradient on the link (section 4.3.1, the low-precision master copy, whose
- * G-cp casts it back); offset and bytes must be multiples of 32. The values
- * are rounded into a 32 MiB device staging buffer that the context allocates
- * on first use and frees with the context, then copied by DMA. Gradient
- * downloads go by DMA; activation downloads by a copy kernel into the pinned
- * buffer's device mapping (DMA when it has none or is unaligned). */
+ * G-cp casts it back); offset and bytes must be multiples of 32. At submit
+ * time the range is rounded on the compute stream, behind the work already
+ * enqueued there (so submit it after the call that writes the gradient),
+ * into a bf16 staging copy of the gradient buffer that the context
+ * allocates on first use (half the buffer's size) and frees with the
+ * context; the download window copies from that by DMA. Gradient downloads
+ * go by DMA; activation downloads by a copy kernel into the pinned buffer's
+ * device mapping (DMA when it has none or is unaligned). */
 typedef enum rp_xfer_kind { RP_PARAM_H2D = 0, RP_GRAD_D2H = 1, RP_GRAD_D2H_BF16 = 2 } rp_xfer_kind;
 typedef enum rp_xfer_target {
   RP_TGT_LAYER = 0,  /* id = layer; bytes of the weight / gradient block      */

@@ -207,7 +207,7 @@ rp_status rp_ctx_destroy(rp_ctx* c) {
       }
     for (hipStream_t d : c->owned) (void)hipStreamDestroy(d);
     for (hipEvent_t e : c->all_events) (void)hipEventDestroy(e);
-    if (c->bf16_stage) (void)hipFree(c->bf16_stage);
+    for (void* p : c->stages) (void)hipFree(p);
   }
   delete c;
   return st;

@@ -28,6 +28,7 @@ struct Slot {
   hipEvent_t g_drained = nullptr;   // recorded on g_d2h after the last download chunk
   bool g_drained_pending = false;
   int g_chunks_unissued = 0;
+  void* g_stage = nullptr;          // bf16 staging copy of g (bf16 downloads), owned by the context
 };
 
 struct LayerBinding {
@@ -65,8 +66,7 @@ struct XChunk {
   Slot* slot;
   char* dev;
   char* host;
-  uint64_t bytes;     // device-side bytes
-  bool bf16 = false;  // download fp32 as bf16 (host gets bytes / 2)
+  uint64_t bytes;
 };
 struct XWindow {
   int dir;
@@ -104,7 +104,7 @@ struct rp_ctx {
   std::vector<hipEvent_t> all_events;    // every event created (destroyed with the context)
   std::vector<hipEvent_t> ev_free;       // recycled ticket events
   hipEvent_t ev_mark = nullptr;          // scratch: "compute reached this point"
-  void* bf16_stage = nullptr;            // device staging of bf16 gradient downloads
+  std::vector<void*> stages;             // bf16 gradient staging copies (freed with the context)
   // per workspace (by base pointer): the compute stream is done with it after
   // this event -- uploads into a workspace's checkpoint buffers wait for it
   std::map<const void*, hipEvent_t> ws_done;

@@ -87,28 +87,13 @@ namespace {
 // download stream q: 0 activations, 1 gradients; ordered after everything already on st and before
 // everything enqueued on st later) when the host buffer has a device mapping
 // and both ends are 16-byte aligned, else a DMA copy on st
-// bytes of the device staging buffer of bf16 gradient downloads
-constexpr size_t kBf16StageBytes = 32u << 20;
-
-rp_status download(rp_ctx* c, int q, void* host, const void* dev, size_t bytes, hipStream_t st, bool bf16 = false) {
+rp_status download(rp_ctx* c, int q, void* host, const void* dev, size_t bytes, hipStream_t st) {
   if (q == 1) {
     // Gradients go by DMA. A copy kernel writing the pinned buffer's device
     // mapping does reach full duplex beside the DMA uploads, but its host
     // writes slowed every compute kernel of the step (the streamed 8B-shaped
-    // step: 83 ms with the kernel, 72 ms with DMA).
-    if (!bf16) {
-      RP_HIP(hipMemcpyAsync(host, dev, bytes, hipMemcpyDeviceToHost, st));
-      return RP_OK;
-    }
-    // bf16: round into the staging buffer, then DMA it, a piece at a time
-    // (stream order keeps a piece's conversion behind the previous DMA)
-    if (!c->bf16_stage) RP_HIP(hipMalloc(&c->bf16_stage, kBf16StageBytes));
-    const size_t piece = 2 * kBf16StageBytes;  // fp32 bytes per piece
-    for (size_t off = 0; off < bytes; off += piece) {
-      const size_t n = std::min(piece, bytes - off);
-      RP_TRY(convert_f32_bf16(c->bf16_stage, (const char*)dev + off, n, st));
-      RP_HIP(hipMemcpyAsync((char*)host + off / 2, c->bf16_stage, n / 2, hipMemcpyDeviceToHost, st));
-    }
+    // step: 83 ms with the kernel, 64 ms with DMA).
+    RP_HIP(hipMemcpyAsync(host, dev, bytes, hipMemcpyDeviceToHost, st));
     return RP_OK;
   }
   void* hd = nullptr;
@@ -160,7 +145,7 @@ rp_status issue_window(rp_ctx* c, XWindow& win) {
       }
     } else {
       if (&s != prev && s.g_ready_valid) RP_HIP(hipStreamWaitEvent(st, s.g_ready, 0));
-      RP_TRY(download(c, 1, ch.host, ch.dev, ch.bytes, st, ch.bf16));
+      RP_TRY(download(c, 1, ch.host, ch.dev, ch.bytes, st));
       if (--s.g_chunks_unissued == 0) {
         if (!s.g_drained) s.g_drained = c->new_event();
         RP_HIP(hipEventRecord(s.g_drained, st));
@@ -343,10 +328,31 @@ rp_status weight_stream_submit(rp_ctx* c, const rp_xfer* items, int n_items, int
              "submit: item %d [%llu, +%llu) exceeds its buffer (%llu bytes)", i, (unsigned long long)it.offset,
              (unsigned long long)it.bytes, (unsigned long long)cap);
     RP_CHECK(it.host && is_pinned_host(it.host), RP_ERR_NOT_PINNED, "submit: item %d host pointer not pinned", i);
-    if (it.kind == RP_GRAD_D2H_BF16)
+    if (it.kind == RP_GRAD_D2H_BF16) {
       RP_CHECK(it.offset % 32 == 0 && it.bytes % 32 == 0, RP_ERR_INVALID,
                "submit: item %d: a bf16 gradient download needs offset and bytes in multiples of 32", i);
+      RP_CHECK(slots[i]->g_chunks_unissued == 0, RP_ERR_STATE,
+               "submit: item %d: an earlier download of this gradient is still deferred", i);
+    }
     devs[i] += it.offset;
+  }
+  // bf16 gradients: round each range on the compute stream, right behind the
+  // work that wrote it (there it needs no compute units of its own and costs
+  // the stream a few tenths of a millisecond per GB), into the buffer's bf16
+  // staging copy; the DMA windows below copy from there. The staging copy is
+  // rewritten only after its previous download, and the buffer's ready event
+  // moves behind the conversion.
+  for (int i = 0; i < n_items; ++i) {
+    if (items[i].kind != RP_GRAD_D2H_BF16) continue;
+    Slot& sl = *slots[i];
+    if (!sl.g_stage) {
+      RP_HIP(hipMalloc(&sl.g_stage, sl.g_bytes / 2 + 256));
+      c->stages.push_back(sl.g_stage);
+    }
+    RP_TRY(wait_grad_drained(c, sl));
+    RP_TRY(convert_f32_bf16((char*)sl.g_stage + items[i].offset / 2, (const char*)sl.g + items[i].offset,
+                            items[i].bytes, c->compute));
+    RP_TRY(mark_grad_ready(c, sl));
   }
   for (int dir = RP_H2D; dir <= RP_D2H; ++dir) {
     std::vector<int> idx;
@@ -371,10 +377,16 @@ rp_status weight_stream_submit(rp_ctx* c, const rp_xfer* items, int n_items, int
       XChunk ch;
       ch.dir = dir;
       ch.slot = slots[i];
-      ch.dev = devs[i] + pc.off;
-      ch.bf16 = items[i].kind == RP_GRAD_D2H_BF16;
-      ch.host = (char*)items[i].host + (ch.bf16 ? pc.off / 2 : pc.off);
-      ch.bytes = pc.bytes;
+      if (items[i].kind == RP_GRAD_D2H_BF16) {
+        // the bf16 staging copy: half the offsets and bytes
+        ch.dev = (char*)slots[i]->g_stage + (items[i].offset + pc.off) / 2;
+        ch.host = (char*)items[i].host + pc.off / 2;
+        ch.bytes = pc.bytes / 2;
+      } else {
+        ch.dev = devs[i] + pc.off;
+        ch.host = (char*)items[i].host + pc.off;
+        ch.bytes = pc.bytes;
+      }
       if (dir == RP_H2D) ch.slot->w_chunks_unissued++;
       else ch.slot->g_chunks_unissued++;
       wins[pc.window].chunks.push_back(ch);
