@@ -177,10 +177,12 @@ class MicrobatchPass:
         for k, (kind, layer) in enumerate(stages):
             par = k & 1
             ops = self._stage_ops(kind, layer, par, rows)
-            if k >= 2:
+            if k >= 2 and last_d2h[k - 2] >= ctx.act_next_ticket() - _TICKET_HORIZON:
                 # this stage reuses the device buffers of stage k - 2: its uploads
                 # (and through them its compute) start after that stage's last
-                # download, which itself followed all of that stage's compute
+                # download, which itself followed all of that stage's compute. An
+                # older ticket needs no wait: stage k - 1's uploads already waited
+                # on stage k - 2's downloads, ahead of everything on the stream.
                 ctx.act_wait(B.RP_ON_ACT_H2D, last_d2h[k - 2])
             nxt = [self._upload_item(k + 1, stages[k + 1][1])] if k + 1 < len(stages) else []
             if self.policy == "windowed":
