@@ -178,3 +178,19 @@ def test_partition_fills_fused_stage_and_rejects_bad_input(B):
         B.partition([1.0], [3.0], 2.0, [1.0], [1.0], 50.0, 10.0, 1, 1)
     with pytest.raises(B.RPError):  # negative time
         B.partition([-1.0], [3.0], 2.0, [1.0], [1.0], 1.0, 10.0, 1, 1)
+
+
+def test_model_partition_stages_cover_every_layer_once():
+    """The whole-model driver's stage list (section 3.2): forward stages front
+    to back over [0, L - b1), the fused stage B_1 over the last b1 layers,
+    backward stages back to front over [0, L - b1); malformed partitions are
+    refused."""
+    from offloaded_pipeline_stage_amd.model import Partition
+    st = Partition((2, 1), 3, (1, 2)).stages(6)
+    assert st == [("F", 0, 2), ("F", 2, 3), ("B1", 3, 6), ("B", 2, 3), ("B", 0, 2)]
+    assert Partition.fused(4).stages(4) == [("B1", 0, 4)]
+    assert Partition.one_layer_per_stage(3).stages(3) == [("F", 0, 1), ("F", 1, 2), ("B1", 2, 3), ("B", 1, 2),
+                                                          ("B", 0, 1)]
+    for bad in (Partition((2,), 3, (1, 2)), Partition((3,), 3, (2,)), Partition((6,), 0, (6,))):
+        with pytest.raises(ValueError):
+            bad.stages(6)
