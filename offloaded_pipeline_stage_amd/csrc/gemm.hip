@@ -343,6 +343,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(GemmParams p)
   constexpr int NRD = TM + TN;  // fragment reads per k-substep
   static_assert(NKS == 4, "the barrier placement assumes four substeps");
   static_assert(NRD <= NMF, "fewer MFMAs than fragment reads per substep");
+  // With an M-major B operand in the eight-wave tile, the fragment reads are
+  // spread evenly over the substep's MFMA slots instead of issued one per
+  // slot from the first: it frees the registers that spilled there. The
+  // K-major layouts keep the front-loaded reads, which spilled when spread,
+  // and so does the four-wave tile.
+  constexpr bool SPREAD_RD = !BKM && WGM * WGN == 8;
   // the loaders' issue units (A's, then B's) are spread over the MFMA slots of
   // the substeps before the barrier: slot ts = ks * NMF + t stores units
   // [ts * NU / NSL, (ts + 1) * NU / NSL) into the other buffer and reissues
@@ -371,7 +377,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(GemmParams p)
       for (int t = 0; t < NMF; ++t) {
         const int i = t / TN, j = t % TN;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j], 0, 0, 0);
-        if (t < NRD) {
+        if constexpr (SPREAD_RD) {
+          // slot t reads fragments [t * NRD / NMF, (t + 1) * NRD / NMF)
+#pragma unroll
+          for (int q = t * NRD / NMF; q < (t + 1) * NRD / NMF; ++q) {
+            if (ks + 1 < NKS) read_one(a_s, b_s, ks + 1, q, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+            else read_one(a_n, b_n, 0, q, af[0], bfr[0]);
+          }
+        } else if (t < NRD) {
           if (ks + 1 < NKS) read_one(a_s, b_s, ks + 1, t, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
           else read_one(a_n, b_n, 0, t, af[0], bfr[0]);
         }
