@@ -157,6 +157,11 @@ rp_status ce_combine(int T, int n_shards, const float2* parts, const float* zlab
 rp_status ce_grad(int dt, const float* logits, int64_t ld, int T, int Vs, int vlo,
                   const int32_t* labels, int vocab, const float* lse, const float* inv_n,
                   void* dz, int64_t ldz, hipStream_t s);
+// bf16 only: ce_grad's dz (bit for bit) and its transpose dzt [Vs, ldt] in
+// one pass; T and Vs multiples of 8, 16-byte aligned rows
+rp_status ce_grad_tr(const float* logits, int64_t ld, int T, int Vs, int vlo, const int32_t* labels, int vocab,
+                     const float* lse, const float* inv_n, void* dz, int64_t ldz, void* dzt, int64_t ldt,
+                     hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // mixture of experts

@@ -697,20 +697,35 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
   }
   RP_TRY(ce_combine((int)T, ns, parts, zlab, labels, c->vocab, lse, loss, inv_n, st));
   RP_TRY(fill_zero(dxf, (size_t)T * s.H * 4, st));
+  // bf16 with sizes in multiples of 8: the weight-gradient products take
+  // K-major operands made here, x^T once for every shard and each shard's
+  // dz^T by the gradient kernel itself, in the transpose scratch
+  bool pre_tr = tr != nullptr && T % 8 == 0 && s.H % 8 == 0;
+  for (int i = 0; i < ns; ++i) pre_tr = pre_tr && (c->shard_lo[i + 1] - c->shard_lo[i]) % 8 == 0;
+  char* dzt = reinterpret_cast<char*>(tr);
+  char* zzt = pre_tr ? dzt + align_up((size_t)vs_max * T * 2, 256) : nullptr;
+  if (pre_tr) RP_TRY(transpose_bf16(zz, s.H, zzt, (int64_t)T, (int)T, s.H, st));
   for (int i = 0; i < ns; ++i) {
     const int lo = c->shard_lo[i], vs = c->shard_lo[i + 1] - lo;
     Slot& w = c->shards[i];
     RP_CHECK(w.g != nullptr, RP_ERR_INVALID, "lmhead: shard %d has no gradient buffer", i);
     RP_TRY(wait_grad_drained(c, w));
     const float* lg = logits + (size_t)i * T * vs_max;
-    RP_TRY(ce_grad(dt, lg, vs, (int)T, vs, lo, labels, c->vocab, lse, inv_n, dz, vs, st));
+    if (pre_tr)
+      RP_TRY(ce_grad_tr(lg, vs, (int)T, vs, lo, labels, c->vocab, lse, inv_n, dz, vs, dzt, (int64_t)T, st));
+    else
+      RP_TRY(ce_grad(dt, lg, vs, (int)T, vs, lo, labels, c->vocab, lse, inv_n, dz, vs, st));
     GemmDesc gx = mk((int)T, s.H, vs, dz, vs, true, w.w, s.H, false, dxf, s.H, dt, RP_DTYPE_F32);
     gx.accumulate = true;
     RP_TRY(gemm(gx, st));
-    GemmDesc gw = mk(vs, s.H, (int)T, dz, vs, false, zz, s.H, false, w.g, s.H, dt, RP_DTYPE_F32);
-    gw.tr = tr;
-    gw.tr_bytes = tr_bytes;
-    RP_TRY(gemm(gw, st));
+    if (pre_tr) {
+      RP_TRY(gemm(mk(vs, s.H, (int)T, dzt, (int)T, true, zzt, (int)T, true, w.g, s.H, dt, RP_DTYPE_F32), st));
+    } else {
+      GemmDesc gw = mk(vs, s.H, (int)T, dz, vs, false, zz, s.H, false, w.g, s.H, dt, RP_DTYPE_F32);
+      gw.tr = tr;
+      gw.tr_bytes = tr_bytes;
+      RP_TRY(gemm(gw, st));
+    }
     RP_TRY(mark_consumed(c, w));
     RP_TRY(mark_grad_ready(c, w));
   }

@@ -114,15 +114,21 @@ def test_bf16_layer_fwd_bwd_matches_oracle(W, name, seq, batch, qkn):
         assert e < tol, (n, e)
 
 
-def test_bf16_lmhead_sharded_matches_oracle(W):
-    """LM head + CE with 4 vocabulary shards at hidden 4096 (vocab reduced to
-    4 x 2048 rows), bf16: loss, dx and every shard's weight gradient."""
-    say("bf16 lm head")
-    cfg = synth.config("llama3_8b", seq=320, vocab=8192, n_shards=4)
+@pytest.mark.parametrize("seq,vocab,shards", [(320, 8192, 4), (200, 6176, 4), (100, 4096, 2)])
+def test_bf16_lmhead_sharded_matches_oracle(W, seq, vocab, shards):
+    """LM head + CE with vocabulary shards at hidden 4096 (vocab reduced),
+    bf16: loss, dx and every shard's weight gradient. Token counts and shard
+    widths in multiples of 8 (bf16 shards always are) take the path whose
+    gradient kernel also writes dz transposed (320 tokens: a ragged 128-row
+    tile; 1544-row shards: a ragged 64-column tile); 100 tokens take the path
+    that transposes inside the product."""
+    say("bf16 lm head", seq, vocab, shards)
+    cfg = synth.config("llama3_8b", seq=seq, vocab=vocab, n_shards=shards)
     x = synth.activation(cfg, "x")
     w = synth.lmhead_weights(cfg)["w"]
     labels = synth.uniform_labels(cfg)
     labels[7] = -1
+    labels[0] = vocab - 1  # the last column of the last shard
     wk = W(cfg)
     wk.add_lmhead(w)
     T, H = cfg.tokens, cfg.hidden
@@ -131,7 +137,7 @@ def test_bf16_lmhead_sharded_matches_oracle(W):
     ws = wk.ctx.workspace(B_OP_LMHEAD(), cfg.batch, cfg.seq)
     wk.ctx.lmhead_ce_fwd_bwd(cfg.batch, cfg.seq, x.to(DEV), labels.to(DEV), loss, dx, ws)
     wk.ctx.sync()
-    l_ref, dx_ref, dw_ref, _ = O.lmhead_fwd_bwd(x, w, labels, 4)
+    l_ref, dx_ref, dw_ref, _ = O.lmhead_fwd_bwd(x, w, labels, shards)
     assert abs(loss.item() - l_ref.item()) / abs(l_ref.item()) < LOSS_TOL["bf16"]
     assert max_rel(dx, dx_ref) < GRAD_TOL["bf16"]
     dw = torch.cat([d.cpu() for d in wk.head["dw"]], dim=0)
