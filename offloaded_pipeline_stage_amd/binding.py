@@ -264,6 +264,19 @@ class Context:
             elif isinstance(o, torch.Tensor):
                 self._keep.append(o)
 
+    def _order(self):
+        """Order the library's compute stream after torch's current stream,
+        so that tensors torch has just filled or produced are complete before
+        the library's kernels read or overwrite them: the compute stream is a
+        separate non-blocking stream. Activation downloads are ordered after
+        the compute stream, so they are covered too; uploads deliberately run
+        ahead of it, so a device buffer an upload overwrites must not be in
+        use on torch's stream."""
+        cur = torch.cuda.current_stream(self.device)
+        comp = self.streams["compute"]
+        if cur.cuda_stream != comp.cuda_stream:
+            comp.wait_stream(cur)
+
     def sync(self):
         check(lib().rp_ctx_sync(self.h))
         self._keep.clear()
@@ -324,30 +337,36 @@ class Context:
 
     # -- stage calls
     def stage_fwd(self, l0, l1, batch, seq, x, y, ws, ckpt_host=None, router=None, flags=0):
+        self._order()
         check(lib().rp_stage_fwd(self.h, l0, l1, batch, seq, ptr(x), ptr(y), ptr_array(ckpt_host),
                                  ptr_array(router), flags, ptr(ws), ws.numel()))
         self._hold(x, y, ws, ckpt_host, router)
 
     def stage_bwd_recompute(self, l0, l1, batch, seq, dy, dx, ws, ckpt=None, router=None, flags=0):
+        self._order()
         check(lib().rp_stage_bwd_recompute(self.h, l0, l1, batch, seq, ptr_array(ckpt), ptr(dy), ptr(dx),
                                            ptr_array(router), flags, ptr(ws), ws.numel()))
         self._hold(dy, dx, ws, ckpt, router)
 
     def lmhead_ce_fwd_bwd(self, batch, seq, x, labels, loss, dx, ws):
+        self._order()
         check(lib().rp_lmhead_ce_fwd_bwd(self.h, batch, seq, ptr(x), ptr(labels), ptr(loss), ptr(dx), ptr(ws),
                                          ws.numel()))
         self._hold(x, labels, loss, dx, ws)
 
     def embed_fwd(self, ids, table, x0):
+        self._order()
         check(lib().rp_embed_fwd(self.h, ids.numel(), table.shape[0], ptr(ids), ptr(table), ptr(x0)))
         self._hold(ids, table, x0)
 
     def embed_bwd(self, ids, dx0, dtable):
+        self._order()
         check(lib().rp_embed_bwd(self.h, ids.numel(), dtable.shape[0], ptr(ids), ptr(dx0), ptr(dtable)))
         self._hold(ids, dx0, dtable)
 
     # -- transfers
     def act_copy(self, direction: int, dst: torch.Tensor, src: torch.Tensor, nbytes: Optional[int] = None) -> int:
+        self._order()
         t = C.c_int64()
         nb = nbytes if nbytes is not None else src.numel() * src.element_size()
         check(lib().rp_act_copy(self.h, direction, ptr(dst), ptr(src), nb, C.byref(t)))
@@ -398,6 +417,7 @@ class Context:
 
     # -- single kernels
     def op_gemm_bf16(self, M, N, K, A, lda, a_kmajor, B, ldb, b_kmajor, Cm, ldc, out_f32, accumulate=False):
+        self._order()
         check(lib().rp_op_gemm_bf16(self.h, M, N, K, ptr(A), lda, int(a_kmajor), ptr(B), ldb, int(b_kmajor),
                                     ptr(Cm), ldc, int(out_f32), int(accumulate)))
         self._hold(A, B, Cm)
@@ -410,9 +430,12 @@ class Context:
             raise ValueError("op_transpose_bf16: bf16 tensors with unit column stride")
         if dst.shape[0] < cols or dst.shape[1] < rows:
             raise ValueError("op_transpose_bf16: dst too small")
+        self._order()
         check(lib().rp_op_transpose_bf16(self.h, rows, cols, ptr(src), src.stride(0), ptr(dst), dst.stride(0)))
+        self._hold(src, dst)
 
     def op_copy(self, dst, src):
+        self._order()
         n = src.numel() * src.element_size()
         if dst.numel() * dst.element_size() < n:
             raise ValueError("op_copy: dst smaller than src")
@@ -420,10 +443,12 @@ class Context:
         self._hold(dst, src)
 
     def op_attn_fwd(self, batch, seq, qkv, o, lse):
+        self._order()
         check(lib().rp_op_attn_fwd(self.h, batch, seq, ptr(qkv), ptr(o), ptr(lse)))
         self._hold(qkv, o, lse)
 
     def op_attn_bwd(self, batch, seq, qkv, o, dout, lse, dqkv, ws):
+        self._order()
         check(lib().rp_op_attn_bwd(self.h, batch, seq, ptr(qkv), ptr(o), ptr(dout), ptr(lse), ptr(dqkv), ptr(ws),
                                    ws.numel()))
         self._hold(qkv, o, dout, lse, dqkv, ws)

@@ -88,6 +88,23 @@ def test_transpose_bf16(B, rows, cols, pad):
     assert torch.all(got[:, rows:] == -7.0)
 
 
+@pytest.mark.parametrize("rows,cols", [(8192, 32064), (8192, 28672)])
+def test_transpose_bf16_full_size(B, rows, cols):
+    """The step's largest transposed operands (a 32064-row vocabulary shard's
+    dz, the gate/up product's output gradient), every element bit-exact,
+    compared on the device."""
+    say("transpose full size", rows, cols)
+    ctx = _ctx(B)
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev).manual_seed(rows + cols)
+    src = torch.randn(rows, cols, generator=g, device=dev).to(torch.bfloat16)
+    dst = torch.empty(cols, rows, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()  # src is written on torch's stream, read on the library's
+    ctx.op_transpose_bf16(src, dst)
+    ctx.sync()
+    assert torch.equal(dst, src.t())
+
+
 def test_gemm_accumulate_and_strided_output(B):
     say("gemm accumulate")
     ctx = _ctx(B)
