@@ -99,6 +99,8 @@ struct rp_ctx {
   int64_t next_ticket = 0;
   std::map<int64_t, hipEvent_t> ticket_ev;
   std::vector<rp::XWindow> deferred;
+  // a parameter or gradient transfer has been submitted on this context
+  bool xfer_used = false;
   hipEvent_t last_act_d2h = nullptr;      // every call starts after the previous downloads
   bool last_act_d2h_valid = false;
   std::vector<hipEvent_t> all_events;    // every event created (destroyed with the context)

@@ -96,16 +96,24 @@ rp_status download(rp_ctx* c, int q, void* host, const void* dev, size_t bytes, 
     RP_HIP(hipMemcpyAsync(host, dev, bytes, hipMemcpyDeviceToHost, st));
     return RP_OK;
   }
+  // Activations. A context that has never carried parameter or gradient
+  // transfers (weights resident) downloads by DMA: the copy kernel's host
+  // writes slow the compute kernels beside it (the forward GEMM next to a
+  // 67 MB checkpoint download took three times as long). A context that
+  // streams keeps the copy kernel, so that a critical-path download never
+  // queues behind parameter or gradient chunks on the copy engine; deciding
+  // per download from the windows pending at issue time measured worse (a
+  // window issued after the choice can still run ahead of the download).
+  const bool engine_free = !c->xfer_used;
   void* hd = nullptr;
-  if ((((uintptr_t)host | (uintptr_t)dev | bytes) & 15) != 0 || hipHostGetDevicePointer(&hd, host, 0) != hipSuccess ||
-      hd == nullptr) {
+  if (engine_free || (((uintptr_t)host | (uintptr_t)dev | bytes) & 15) != 0 ||
+      hipHostGetDevicePointer(&hd, host, 0) != hipSuccess || hd == nullptr) {
     (void)hipGetLastError();  // a failed lookup leaves an error behind
     RP_HIP(hipMemcpyAsync(host, dev, bytes, hipMemcpyDeviceToHost, st));
     return RP_OK;
   }
-  // activations: the copy kernel, so that a critical-path download never
-  // queues behind gradient chunks on the copy engine; a stream the context
-  // created has its own hardware queue, so the kernel goes straight onto it
+  // the copy kernel: a stream the context created has its own hardware
+  // queue, so the kernel goes straight onto it
   if (c->own_d2h[q]) return download_copy(hd, dev, bytes, st);
   if (!c->dl[q]) {
     RP_TRY(new_queue_stream(c->device, &c->dl[q]));
@@ -336,6 +344,7 @@ rp_status weight_stream_submit(rp_ctx* c, const rp_xfer* items, int n_items, int
     }
     devs[i] += it.offset;
   }
+  if (n_items > 0) c->xfer_used = true;  // activation downloads keep the copy kernel from here on
   // bf16 gradients: round each range on the compute stream, right behind the
   // work that wrote it (there it needs no compute units of its own and costs
   // the stream a few tenths of a millisecond per GB), into the buffer's bf16
