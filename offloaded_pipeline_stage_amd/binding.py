@@ -267,11 +267,14 @@ class Context:
     def _order(self):
         """Order the library's compute stream after torch's current stream,
         so that tensors torch has just filled or produced are complete before
-        the library's kernels read or overwrite them: the compute stream is a
-        separate non-blocking stream. Activation downloads are ordered after
-        the compute stream, so they are covered too; uploads deliberately run
-        ahead of it, so a device buffer an upload overwrites must not be in
-        use on torch's stream."""
+        a single-kernel call reads or overwrites them (the compute stream is a
+        separate non-blocking stream). Only the op_* calls do this. An event
+        on torch's legacy default stream also waits for the library's
+        transfer streams, which are blocking streams, so on the stage calls
+        it would serialise compute behind in-flight weight and gradient
+        copies. Callers of the stage calls make their inputs complete first
+        (a copy from host memory is; a fill on another stream needs a
+        synchronize or a stream wait)."""
         cur = torch.cuda.current_stream(self.device)
         comp = self.streams["compute"]
         if cur.cuda_stream != comp.cuda_stream:
@@ -337,36 +340,30 @@ class Context:
 
     # -- stage calls
     def stage_fwd(self, l0, l1, batch, seq, x, y, ws, ckpt_host=None, router=None, flags=0):
-        self._order()
         check(lib().rp_stage_fwd(self.h, l0, l1, batch, seq, ptr(x), ptr(y), ptr_array(ckpt_host),
                                  ptr_array(router), flags, ptr(ws), ws.numel()))
         self._hold(x, y, ws, ckpt_host, router)
 
     def stage_bwd_recompute(self, l0, l1, batch, seq, dy, dx, ws, ckpt=None, router=None, flags=0):
-        self._order()
         check(lib().rp_stage_bwd_recompute(self.h, l0, l1, batch, seq, ptr_array(ckpt), ptr(dy), ptr(dx),
                                            ptr_array(router), flags, ptr(ws), ws.numel()))
         self._hold(dy, dx, ws, ckpt, router)
 
     def lmhead_ce_fwd_bwd(self, batch, seq, x, labels, loss, dx, ws):
-        self._order()
         check(lib().rp_lmhead_ce_fwd_bwd(self.h, batch, seq, ptr(x), ptr(labels), ptr(loss), ptr(dx), ptr(ws),
                                          ws.numel()))
         self._hold(x, labels, loss, dx, ws)
 
     def embed_fwd(self, ids, table, x0):
-        self._order()
         check(lib().rp_embed_fwd(self.h, ids.numel(), table.shape[0], ptr(ids), ptr(table), ptr(x0)))
         self._hold(ids, table, x0)
 
     def embed_bwd(self, ids, dx0, dtable):
-        self._order()
         check(lib().rp_embed_bwd(self.h, ids.numel(), dtable.shape[0], ptr(ids), ptr(dx0), ptr(dtable)))
         self._hold(ids, dx0, dtable)
 
     # -- transfers
     def act_copy(self, direction: int, dst: torch.Tensor, src: torch.Tensor, nbytes: Optional[int] = None) -> int:
-        self._order()
         t = C.c_int64()
         nb = nbytes if nbytes is not None else src.numel() * src.element_size()
         check(lib().rp_act_copy(self.h, direction, ptr(dst), ptr(src), nb, C.byref(t)))
