@@ -439,9 +439,8 @@ rp_status rp_act_next_ticket(const rp_ctx* ctx, int64_t* next);
  * enqueued there (so submit it after the call that writes the gradient),
  * into a bf16 staging copy of the gradient buffer that the context
  * allocates on first use (half the buffer's size) and frees with the
- * context; the download window copies from that by DMA. Gradient downloads
- * go by DMA; activation downloads by a copy kernel into the pinned buffer's
- * device mapping (DMA when it has none or is unaligned). */
+ * context; the download window copies from that by DMA. All transfers,
+ * activation and checkpoint downloads included, go by DMA. */
 typedef enum rp_xfer_kind { RP_PARAM_H2D = 0, RP_GRAD_D2H = 1, RP_GRAD_D2H_BF16 = 2 } rp_xfer_kind;
 typedef enum rp_xfer_target {
   RP_TGT_LAYER = 0,  /* id = layer; bytes of the weight / gradient block      */

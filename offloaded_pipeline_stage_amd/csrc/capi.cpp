@@ -166,8 +166,6 @@ rp_status rp_ctx_create(int device, const rp_layer_cfg* cfg, const rp_streams* s
   }
   // missing transfer streams: created here, each on its own hardware queue
   // (a stream with a CU mask never shares its queue); all CUs enabled
-  x->own_d2h[0] = x->act_d2h == nullptr;
-  x->own_d2h[1] = x->g_d2h == nullptr;
   for (hipStream_t* ps : {&x->act_h2d, &x->act_d2h, &x->w_h2d, &x->g_d2h}) {
     if (*ps) continue;
     rp_status st = new_queue_stream(device, ps);
@@ -200,11 +198,6 @@ rp_status rp_ctx_destroy(rp_ctx* c) {
     hipStream_t ss[5] = {c->compute, c->act_h2d, c->act_d2h, c->w_h2d, c->g_d2h};
     for (hipStream_t s : ss)
       if (hipStreamSynchronize(s) != hipSuccess) st = RP_ERR_HIP;
-    for (hipStream_t d : c->dl)
-      if (d) {
-        if (hipStreamSynchronize(d) != hipSuccess) st = RP_ERR_HIP;
-        (void)hipStreamDestroy(d);
-      }
     for (hipStream_t d : c->owned) (void)hipStreamDestroy(d);
     for (hipEvent_t e : c->all_events) (void)hipEventDestroy(e);
     for (void* p : c->stages) (void)hipFree(p);

@@ -88,7 +88,6 @@ struct rp_ctx {
   hipStream_t compute = nullptr, act_h2d = nullptr, act_d2h = nullptr, w_h2d = nullptr, g_d2h = nullptr;
   // transfer streams the context created (each on a hardware queue of its own)
   std::vector<hipStream_t> owned;
-  bool own_d2h[2] = {false, false};  // act_d2h, g_d2h were created here
   std::vector<rp::LayerBinding> layers;   // indexed by layer id
   // LM head
   int vocab = 0, n_shards = 0;
@@ -99,8 +98,6 @@ struct rp_ctx {
   int64_t next_ticket = 0;
   std::map<int64_t, hipEvent_t> ticket_ev;
   std::vector<rp::XWindow> deferred;
-  // a parameter or gradient transfer has been submitted on this context
-  bool xfer_used = false;
   hipEvent_t last_act_d2h = nullptr;      // every call starts after the previous downloads
   bool last_act_d2h_valid = false;
   std::vector<hipEvent_t> all_events;    // every event created (destroyed with the context)
@@ -111,11 +108,6 @@ struct rp_ctx {
   // this event -- uploads into a workspace's checkpoint buffers wait for it
   std::map<const void*, hipEvent_t> ws_done;
   hipEvent_t ck_free[2] = {nullptr, nullptr};  // backward: checkpoint buffer i & 1 read
-  // downloads into caller-provided streams run on private streams (one for
-  // activations, one for gradients, each with a hardware queue of its own),
-  // fenced into the caller's stream by two events
-  hipStream_t dl[2] = {nullptr, nullptr};
-  hipEvent_t dl_in[2] = {nullptr, nullptr}, dl_out[2] = {nullptr, nullptr};
   // kept-activation bookkeeping for RP_USE_KEPT_ACTS
   const void* kept_ws = nullptr;
   int kept_l0 = -1, kept_l1 = -1, kept_batch = 0, kept_seq = 0;

@@ -74,16 +74,6 @@ __global__ void copy16_kernel(uint4* __restrict__ dst, const uint4* __restrict__
   for (; i < n16; i += stride) dst[i] = src[i];
 }
 
-// device -> host copy for downloads: dst is the device mapping of pinned host
-// memory, so the stores cross the host link while the DMA engine keeps the
-// other direction (uploads) busy
-__global__ __launch_bounds__(256) void download_kernel(uint4* __restrict__ dst, const uint4* __restrict__ src,
-                                                       size_t n16) {
-  size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (; i < n16; i += stride) dst[i] = src[i];
-}
-
 // fp32 -> bf16, rounded to nearest even: 8 values (32 bytes in, 16 out) per
 // lane and step
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -705,16 +695,6 @@ rp_status copy16(void* dst, const void* src, size_t bytes, hipStream_t s) {
   unsigned g = (unsigned)std::min<size_t>(std::max<size_t>(cdiv(n16, 256), 1), 8192);
   TraceScope ts(s, "copy16_kernel", 0.0, 2.0 * bytes);
   RP_LAUNCH(copy16_kernel, dim3(g), dim3(256), 0, s, (uint4*)dst, (const uint4*)src, n16);
-  return RP_OK;
-}
-
-rp_status download_copy(void* host_dev, const void* src, size_t bytes, hipStream_t s) {
-  if (bytes == 0) return RP_OK;
-  RP_CHECK((((uintptr_t)host_dev | (uintptr_t)src | bytes) & 15) == 0, RP_ERR_INVALID,
-           "download: pointers and size must be multiples of 16 bytes");
-  // 16 workgroups (4 waves each) keep the host link saturated; more would
-  // only take compute units from the stage's kernels
-  RP_LAUNCH(download_kernel, dim3(16), dim3(256), 0, s, (uint4*)host_dev, (const uint4*)src, bytes / 16);
   return RP_OK;
 }
 

@@ -81,9 +81,6 @@ rp_status gemm_validate(const GemmDesc& d);
 // ---------------------------------------------------------------------------
 rp_status fill_zero(void* p, size_t bytes, hipStream_t s);
 rp_status copy16(void* dst, const void* src, size_t bytes, hipStream_t s);
-// device -> pinned host through a small copy kernel (host_dev: the host
-// buffer's device mapping); see download() in the transfer engine
-rp_status download_copy(void* host_dev, const void* src, size_t bytes, hipStream_t s);
 // fp32 src (src_bytes) -> bf16 at dst (src_bytes / 2), round to nearest even
 rp_status convert_f32_bf16(void* dst, const void* src, size_t src_bytes, hipStream_t s);
 

@@ -4,13 +4,12 @@
 // section 4.2.2 "Scheduling Parameter Transfers").
 //
 // Four copy streams (activation up/down, parameter up, gradient down) plus the
-// compute stream. Uploads go through the DMA engine (hipMemcpyAsync);
-// downloads are a small copy kernel writing into the device mapping of the
-// pinned host buffer, on streams with hardware queues of their own so that
-// they run beside the stage's kernels. On this platform DMA copies in the two
-// directions share one engine and run one after the other (about 57 GB/s in
-// total), whereas a DMA upload next to a kernel download moves about 90 GB/s:
-// the link's two directions work at once.
+// compute stream, each copy stream on a hardware queue of its own. Every copy
+// goes by DMA (hipMemcpyAsync). A copy kernel writing downloads into the
+// device mapping of the pinned host buffer does use both directions of the
+// link at once next to a DMA upload (about 90 GB/s against about 57 GB/s for
+// DMA both ways), but its host writes slow the compute kernels beside it by
+// more than that gains (see download()).
 //
 // Priority of activation copies is enforced by scheduling: a window of
 // parameter/gradient chunks is issued only behind the completion event of the
@@ -83,48 +82,15 @@ rp_status new_queue_stream(int device, hipStream_t* out) {
 
 namespace {
 
-// device -> pinned host on stream st: the copy kernel (on the context's
-// download stream q: 0 activations, 1 gradients; ordered after everything already on st and before
-// everything enqueued on st later) when the host buffer has a device mapping
-// and both ends are 16-byte aligned, else a DMA copy on st
-rp_status download(rp_ctx* c, int q, void* host, const void* dev, size_t bytes, hipStream_t st) {
-  if (q == 1) {
-    // Gradients go by DMA. A copy kernel writing the pinned buffer's device
-    // mapping does reach full duplex beside the DMA uploads, but its host
-    // writes slowed every compute kernel of the step (the streamed 8B-shaped
-    // step: 83 ms with the kernel, 64 ms with DMA).
-    RP_HIP(hipMemcpyAsync(host, dev, bytes, hipMemcpyDeviceToHost, st));
-    return RP_OK;
-  }
-  // Activations. A context that has never carried parameter or gradient
-  // transfers (weights resident) downloads by DMA: the copy kernel's host
-  // writes slow the compute kernels beside it (the forward GEMM next to a
-  // 67 MB checkpoint download took three times as long). A context that
-  // streams keeps the copy kernel, so that a critical-path download never
-  // queues behind parameter or gradient chunks on the copy engine; deciding
-  // per download from the windows pending at issue time measured worse (a
-  // window issued after the choice can still run ahead of the download).
-  const bool engine_free = !c->xfer_used;
-  void* hd = nullptr;
-  if (engine_free || (((uintptr_t)host | (uintptr_t)dev | bytes) & 15) != 0 ||
-      hipHostGetDevicePointer(&hd, host, 0) != hipSuccess || hd == nullptr) {
-    (void)hipGetLastError();  // a failed lookup leaves an error behind
-    RP_HIP(hipMemcpyAsync(host, dev, bytes, hipMemcpyDeviceToHost, st));
-    return RP_OK;
-  }
-  // the copy kernel: a stream the context created has its own hardware
-  // queue, so the kernel goes straight onto it
-  if (c->own_d2h[q]) return download_copy(hd, dev, bytes, st);
-  if (!c->dl[q]) {
-    RP_TRY(new_queue_stream(c->device, &c->dl[q]));
-    c->dl_in[q] = c->new_event();
-    c->dl_out[q] = c->new_event();
-  }
-  RP_HIP(hipEventRecord(c->dl_in[q], st));
-  RP_HIP(hipStreamWaitEvent(c->dl[q], c->dl_in[q], 0));
-  RP_TRY(download_copy(hd, dev, bytes, c->dl[q]));
-  RP_HIP(hipEventRecord(c->dl_out[q], c->dl[q]));
-  RP_HIP(hipStreamWaitEvent(st, c->dl_out[q], 0));
+// device -> pinned host on stream st, by DMA: activations, checkpoints and
+// gradients alike. A copy kernel writing the pinned buffer's device mapping
+// was measured against it for both: its host writes slowed the compute
+// kernels beside it (the streamed 8B-shaped step took 83 ms with gradient
+// downloads by kernel, 64 ms by DMA; the resident step's forward QKV product
+// ran three times as long next to a checkpoint download by kernel), and the
+// windowed micro-batch schedule ran 13% faster with activations by DMA too.
+rp_status download(void* host, const void* dev, size_t bytes, hipStream_t st) {
+  RP_HIP(hipMemcpyAsync(host, dev, bytes, hipMemcpyDeviceToHost, st));
   return RP_OK;
 }
 
@@ -153,7 +119,7 @@ rp_status issue_window(rp_ctx* c, XWindow& win) {
       }
     } else {
       if (&s != prev && s.g_ready_valid) RP_HIP(hipStreamWaitEvent(st, s.g_ready, 0));
-      RP_TRY(download(c, 1, ch.host, ch.dev, ch.bytes, st));
+      RP_TRY(download(ch.host, ch.dev, ch.bytes, st));
       if (--s.g_chunks_unissued == 0) {
         if (!s.g_drained) s.g_drained = c->new_event();
         RP_HIP(hipEventRecord(s.g_drained, st));
@@ -245,7 +211,7 @@ rp_status act_copy(rp_ctx* c, int dir, void* dst, const void* src, size_t bytes,
     if (!c->ev_mark) c->ev_mark = c->new_event();
     RP_HIP(hipEventRecord(c->ev_mark, c->compute));
     RP_HIP(hipStreamWaitEvent(c->act_d2h, c->ev_mark, 0));
-    RP_TRY(download(c, 0, dst, src, bytes, c->act_d2h));
+    RP_TRY(download(dst, src, bytes, c->act_d2h));
     RP_HIP(hipEventRecord(ev, c->act_d2h));
   }
   c->next_ticket = t + 1;
@@ -344,7 +310,6 @@ rp_status weight_stream_submit(rp_ctx* c, const rp_xfer* items, int n_items, int
     }
     devs[i] += it.offset;
   }
-  if (n_items > 0) c->xfer_used = true;  // activation downloads keep the copy kernel from here on
   // bf16 gradients: round each range on the compute stream, right behind the
   // work that wrote it (there it needs no compute units of its own and costs
   // the stream a few tenths of a millisecond per GB), into the buffer's bf16

@@ -74,7 +74,7 @@ def test_streamed_weights_and_grad_download_bit_identical(env):
         assert torch.equal(gh[l], ref.layers[l]["g"].cpu())
 
 
-def test_grad_download_kernel_and_fallback_paths(env):
+def test_grad_download_chunked_and_unaligned_paths(env):
     """Gradient downloads (by DMA) of an aligned block in chunks over three
     windows and of a range at a host address 8 bytes past a boundary with a
     ragged size: both must reproduce the device bytes exactly, and leave the
