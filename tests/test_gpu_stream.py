@@ -171,6 +171,36 @@ def test_deferred_window_waits_for_its_ticket(env):
     assert torch.equal(wk.layers[0]["w"].cpu(), host)
 
 
+def test_activation_download_unaligned_and_ragged(env):
+    """Activation downloads (by DMA) into pinned host memory at an address 8
+    bytes past a boundary with a size that is not a multiple of 16, and into
+    an aligned buffer: the host bytes equal the device bytes, the bytes
+    around them stay untouched, and the download's ticket orders a later
+    upload of the same host bytes."""
+    B, Worker = env
+    say("activation download paths")
+    cfg = _small_cfg()
+    wk = Worker(cfg)
+    n = 200001
+    gen = torch.Generator().manual_seed(11)
+    src = torch.randint(0, 256, (n,), dtype=torch.uint8, generator=gen).to(DEV)
+    back = torch.empty(n, dtype=torch.uint8, device=DEV)
+    torch.cuda.synchronize()
+    host = torch.full((n + 64,), 0xA5, dtype=torch.uint8).pin_memory()
+    al = torch.zeros(n, dtype=torch.uint8).pin_memory()
+    t0 = wk.ctx.act_copy(B.RP_D2H, host[8:8 + n], src)
+    t1 = wk.ctx.act_copy(B.RP_D2H, al, src)
+    wk.ctx.act_wait(B.RP_ON_ACT_H2D, t1)
+    wk.ctx.act_copy(B.RP_H2D, back, al)
+    wk.ctx.sync()
+    ref = src.cpu()
+    assert t1 == t0 + 1
+    assert torch.equal(host[8:8 + n], ref)
+    assert torch.all(host[:8] == 0xA5) and torch.all(host[8 + n:] == 0xA5)
+    assert torch.equal(al, ref)
+    assert torch.equal(back.cpu(), ref)
+
+
 def test_error_paths(env):
     B, Worker = env
     say("error paths")
