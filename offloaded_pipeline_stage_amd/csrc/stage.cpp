@@ -6,6 +6,7 @@
 // section 4.2.1 compute synchronised with the activation streams by events).
 #include <algorithm>
 #include <cstring>
+#include <functional>
 
 #include "ctx.h"
 
@@ -227,7 +228,8 @@ GemmDesc mk(int M, int N, int K, const void* A, int64_t lda, bool ak, const void
 // internals, never its output. LoRA layers add s (x A^T) B^T to the q, k, v
 // and o projections (s = alpha / r), in place on the bf16 projection output.
 rp_status layer_fwd(rp_ctx* c, const LayerBinding& lb, const LoraBf16& lw, void* ye, const float* router, int T,
-                    int seq, const void* x, const Acts& A, void* y, const float2* rope, hipStream_t st) {
+                    int seq, const void* x, const Acts& A, void* y, const float2* rope, hipStream_t st,
+                    const std::function<rp_status()>& after_qkv = {}) {
   const Shape& s = c->sh;
   const int dt = s.dt;
   const rp_layer_cfg& cfg = c->cfg;
@@ -236,6 +238,7 @@ rp_status layer_fwd(rp_ctx* c, const LayerBinding& lb, const LoraBf16& lw, void*
   const float ls = r > 0 ? cfg.lora_alpha / (float)r : 0.f;
   RP_TRY(rmsnorm_fwd(dt, x, wptr(w, cfg, RP_T_GAMMA1), A.a, A.rstd1, T, s.H, cfg.rms_eps, st));
   RP_TRY(gemm(mk(T, s.QKV, s.H, A.a, s.H, true, wptr(w, cfg, RP_T_WQKV), s.H, true, A.qkv, s.QKV, dt, dt), st));
+  if (after_qkv) RP_TRY(after_qkv());
   if (r > 0) {
     RP_TRY(lora_cast(c, lb.lora, lw, st));
     // us = s a [A_q; A_k; A_v]^T, then q|k|v += us_x B_x^T
@@ -517,7 +520,13 @@ rp_status stage_fwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* x
     const Acts& A = keep ? L.acts[i] : L.acts[0];
     const void* x = keep ? A.x : (i == 0 ? x_in : L.xb[(i - 1) & 1]);
     void* y = (i == n - 1) ? y_out : (keep ? L.acts[i + 1].x : L.xb[i & 1]);
-    if (ckpt_host) {
+    // the checkpoint download of this layer's input, issued once the layer's
+    // QKV product is enqueued: the runtime copies device to host with a
+    // blit kernel that takes CUs while it runs, and started with the layer
+    // it starved the first RMSNorm; the input stays intact until the layer's
+    // residual add, after the download has been ordered
+    auto download_ckpt = [&]() -> rp_status {
+      if (!ckpt_host) return RP_OK;
       int64_t tk;
       RP_TRY(act_copy(c, RP_D2H, ckpt_host[i], x, xbytes, &tk));
       d2h_done[i] = c->ticket_ev[tk];
@@ -525,11 +534,13 @@ rp_status stage_fwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* x
       if (!c->last_act_d2h) c->last_act_d2h = c->new_event();
       RP_HIP(hipEventRecord(c->last_act_d2h, c->act_d2h));
       c->last_act_d2h_valid = true;
-    }
+      return RP_OK;
+    };
     // the ping-pong buffer written by this layer held the input of layer
     // i - 1, whose checkpoint download must have finished
     if (!keep && ckpt_host && i >= 1 && i != n - 1) RP_HIP(hipStreamWaitEvent(st, d2h_done[i - 1], 0));
-    RP_TRY(layer_fwd(c, lb, L.lw, L.ye, s.E > 0 ? router[i] : nullptr, (int)T, seq, x, A, y, L.rope, st));
+    RP_TRY(layer_fwd(c, lb, L.lw, L.ye, s.E > 0 ? router[i] : nullptr, (int)T, seq, x, A, y, L.rope, st,
+                     download_ckpt));
     RP_TRY(mark_consumed(c, w));
     if (s.r > 0) RP_TRY(mark_consumed(c, lb.lora));
   }
