@@ -232,6 +232,7 @@ def layer_forward_rows(x: Tensor, w: Dict[str, Tensor], cfg, rows: Sequence[int]
         kk = rmsnorm(kk, w["knorm"], cfg.rms_eps)
     kk = rope(kk, pos, cfg.rope_base)
     v = v.reshape(T, nkv, d)
+    group = nq // nkv
     out = []
     for t in rows:
         at = a[t:t + 1]
@@ -243,12 +244,13 @@ def layer_forward_rows(x: Tensor, w: Dict[str, Tensor], cfg, rows: Sequence[int]
             q = rmsnorm(q, w["qnorm"], cfg.rms_eps)
         q = rope(q, pos[t:t + 1], cfg.rope_base)[0]
         r0 = (t // seq) * seq
-        o = torch.empty(nq, d, dtype=x.dtype)
-        for h in range(nq):
-            hk = (h * nkv) // nq
-            s = (kk[r0:t + 1, hk, :] @ q[h]) / math.sqrt(d)
-            o[h] = torch.softmax(s, dim=0) @ v[r0:t + 1, hk, :]
-        o = o.reshape(1, nq * d)
+        # the query heads of kv head g are g*group .. (g+1)*group - 1, i.e.
+        # query head h reads kv head floor(h * n_kv / n_q)
+        qg = q.reshape(nkv, group, d)                       # [n_kv, group, d]
+        kt = kk[r0:t + 1].permute(1, 2, 0)                  # [n_kv, d, L]
+        vt = v[r0:t + 1].permute(1, 0, 2)                   # [n_kv, L, d]
+        p = torch.softmax((qg @ kt) / math.sqrt(d), dim=-1)  # [n_kv, group, L]
+        o = (p @ vt).reshape(1, nq * d)
         proj = o @ w["wo"].T
         if lora is not None:
             proj = proj + lora_delta(o, lora["ao"], lora["bo"], scale)
@@ -362,6 +364,32 @@ def layer_backward(x: Tensor, w: Dict[str, Tensor], dy: Tensor, cfg,
         y = layer_forward(xx, ww, cfg, ll, router)
         grads = torch.autograd.grad((y * dy.to(dtype)).sum(), [xx] + [src[n] for n in names])
     return grads[0], dict(zip(names, grads[1:])), y.detach()
+
+
+def layer_backward_rows(x: Tensor, w: Dict[str, Tensor], rows: Sequence[int], dy_rows: Tensor, cfg,
+                        lora: Optional[Dict[str, Tensor]] = None,
+                        router: Optional[Tensor] = None, dtype=torch.float64):
+    """The exact layer gradients for an upstream gradient that is zero outside
+    the token rows `rows` (dy[rows[i]] = dy_rows[i]): differentiates
+    sum_i y[rows[i]] * dy_rows[i], with y[rows] from layer_forward_rows.
+    Returns (dx for every row [T, H], {trainable name: full gradient}).
+
+    Only the listed rows receive an upstream gradient, yet dx is non-zero at
+    every row at or before a listed row of its batch row (keys and values feed
+    the later queries), and every weight gradient is complete. So a full-size
+    layer is checked element by element without the T x T forward."""
+    xx = x.to(dtype).detach().requires_grad_(True)
+    ww = {k: v.to(dtype).detach() for k, v in w.items()}
+    ll = {k: v.to(dtype).detach() for k, v in lora.items()} if lora is not None else None
+    names = trainable_names(cfg)
+    src = ll if cfg.lora_rank > 0 else ww
+    for n in names:
+        src[n].requires_grad_(True)
+    rr = router.to(dtype) if router is not None else None
+    with torch.enable_grad():
+        yr = layer_forward_rows(xx, ww, cfg, rows, ll, rr)
+        grads = torch.autograd.grad((yr * dy_rows.to(dtype)).sum(), [xx] + [src[n] for n in names])
+    return grads[0], dict(zip(names, grads[1:]))
 
 
 def stage_backward_recompute(ckpts: Sequence[Tensor], layers: Sequence[Dict[str, Tensor]],

@@ -494,3 +494,143 @@ def test_mlp_weight_grad_columns_equals_autograd():
     assert torch.allclose(dwd, gd[:, cols], rtol=1e-12, atol=1e-12)
     assert torch.allclose(dwg, gg[cols], rtol=1e-12, atol=1e-12)
     assert torch.allclose(dwu, gu[cols], rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# the layer's wiring: closed forms with some weights zero, and the layer
+# rebuilt from library routines (pre-norm residual layer of the paperlayer.ai
+# summary, appendix B.1; the residual sources and norm placement are a reading
+# of a component list, so they are fixed here against things the oracle does
+# not compute itself)
+# ---------------------------------------------------------------------------
+
+
+def _wiring_case(batch=2, seq=8):
+    cfg = tiny_cfg(n_q=4, n_kv=2, batch=batch, seq=seq)
+    w = f64(synth.layer_weights(cfg, 0, gamma="perturbed"))
+    for k in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"):
+        w[k] = w[k] * 10
+    x = synth.activation(cfg, "x").to(D64)
+    return cfg, w, x
+
+
+def _lib_swiglu(b, w):
+    """SwiGLU MLP from library routines: silu(b Wg^T) * (b Wu^T), then Wd."""
+    return F.linear(F.silu(F.linear(b, w["wg"])) * F.linear(b, w["wu"]), w["wd"])
+
+
+def _lib_norm(x, gamma, cfg):
+    return F.rms_norm(x, (x.shape[-1],), gamma, cfg.rms_eps)
+
+
+def test_layer_wiring_zero_projections_is_identity():
+    """Every projection zero: both residual branches vanish, y == x exactly."""
+    cfg, w, x = _wiring_case()
+    for k in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"):
+        w[k] = torch.zeros_like(w[k])
+    assert torch.equal(O.layer_forward(x, w, cfg), x)
+
+
+def test_layer_wiring_zero_wo_is_mlp_of_normed_input():
+    """W_o = 0: the attention branch adds nothing, h1 = x, so
+    y = x + SwiGLU(RMSNorm(x; gamma2)). Fixes that the MLP reads the second
+    norm of the residual stream and that its output is added to x (not to
+    the normed input)."""
+    cfg, w, x = _wiring_case()
+    w["wo"] = torch.zeros_like(w["wo"])
+    y, keep = O.layer_forward(x, w, cfg, keep=True)
+    assert torch.equal(keep["h1"], x)
+    ref = x + _lib_swiglu(_lib_norm(x, w["gamma2"], cfg), w)
+    assert torch.allclose(y, ref, rtol=0, atol=1e-13)
+
+
+def test_layer_wiring_zero_wq_is_running_mean_of_values():
+    """W_q = 0: every score is 0, so each query head's output is the running
+    mean of its kv head's values over the earlier tokens of its batch row,
+    whatever RoPE does to the keys. Then h1 = x + mean(v) W_o^T with v taken
+    from RMSNorm(x; gamma1), and y = h1 + SwiGLU(RMSNorm(h1; gamma2)).
+    Fixes the first norm's input, the value projection, the GQA head map, the
+    per-row restart and the first residual."""
+    cfg, w, x = _wiring_case()
+    w["wq"] = torch.zeros_like(w["wq"])
+    B, S, d = cfg.batch, cfg.seq, cfg.head_dim
+    v = F.linear(_lib_norm(x, w["gamma1"], cfg), w["wv"]).reshape(B, S, cfg.n_kv, d)
+    mean = torch.cumsum(v, dim=1) / torch.arange(1, S + 1, dtype=D64)[None, :, None, None]
+    o = mean.repeat_interleave(cfg.n_q // cfg.n_kv, dim=2).reshape(B * S, cfg.n_q * d)
+    h1 = x + F.linear(o, w["wo"])
+    y = O.layer_forward(x, w, cfg)
+    assert torch.allclose(y, h1 + _lib_swiglu(_lib_norm(h1, w["gamma2"], cfg), w), rtol=0, atol=1e-12)
+    w["wd"] = torch.zeros_like(w["wd"])
+    assert torch.allclose(O.layer_forward(x, w, cfg), h1, rtol=0, atol=1e-12)
+
+
+def test_layer_matches_library_composition():
+    """The whole layer rebuilt from library routines: torch's rms_norm, RoPE as
+    multiplication of the complex pairs (u_i + i u_{i+d/2}) by exp(i theta),
+    torch's causal scaled_dot_product_attention with the kv heads repeated per
+    query group, silu and linear. Two batch rows, so positions restart."""
+    cfg, w, x = _wiring_case()
+    B, S, d, nq, nkv = cfg.batch, cfg.seq, cfg.head_dim, cfg.n_q, cfg.n_kv
+    half = d // 2
+    a = _lib_norm(x, w["gamma1"], cfg)
+    th = torch.arange(S, dtype=D64)[:, None] * cfg.rope_base ** (-2.0 * torch.arange(half, dtype=D64) / d)
+    rot = torch.polar(torch.ones_like(th), th)                         # [S, d/2]
+
+    def rope_c(u, nh):
+        u = u.reshape(B, S, nh, d)
+        z = torch.complex(u[..., :half], u[..., half:]) * rot[None, :, None, :]
+        return torch.cat([z.real, z.imag], dim=-1).transpose(1, 2)   # [B, nh, S, d]
+
+    q = rope_c(F.linear(a, w["wq"]), nq)
+    k = rope_c(F.linear(a, w["wk"]), nkv).repeat_interleave(nq // nkv, dim=1)
+    v = F.linear(a, w["wv"]).reshape(B, S, nkv, d).transpose(1, 2).repeat_interleave(nq // nkv, dim=1)
+    o = F.scaled_dot_product_attention(q, k, v, is_causal=True).transpose(1, 2).reshape(B * S, nq * d)
+    h1 = x + F.linear(o, w["wo"])
+    ref = h1 + _lib_swiglu(_lib_norm(h1, w["gamma2"], cfg), w)
+    assert torch.allclose(O.layer_forward(x, w, cfg), ref, rtol=0, atol=1e-12)
+
+
+def test_moe_layer_with_one_expert_equals_dense_layer():
+    """A mixture of one expert, top-1 (weight exactly 1), is the dense layer
+    with that expert's weights: fixes the MoE layer's residual and norm wiring
+    to the dense one pinned above."""
+    cfg, w, x = _wiring_case()
+    moe = cfg.with_(ffn=0, n_experts=1, top_k=1, expert_ffn=cfg.ffn)
+    wm = dict(w)
+    for k in ("wg", "wu", "wd"):
+        wm[k] = w[k][None]
+    router = torch.randn(cfg.tokens, 1, dtype=D64)
+    assert torch.allclose(O.layer_forward(x, wm, moe, router=router), O.layer_forward(x, w, cfg),
+                          rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("variant", ["gqa", "qknorm", "lora_moe"])
+def test_layer_backward_rows_equals_masked_full_backward(variant):
+    """The sparse-upstream-gradient backward used at full size equals the
+    complete backward with dy zeroed outside the listed rows, for dx at every
+    row and for every trainable gradient; rows after the last listed row of a
+    batch row get dx exactly 0 (causality)."""
+    kw = dict(n_q=4, n_kv=2)
+    if variant == "qknorm":
+        kw.update(qk_norm=True)
+    if variant == "lora_moe":
+        kw.update(lora_rank=3, lora_alpha=6.0, ffn=0, n_experts=4, top_k=2, expert_ffn=12)
+    cfg = tiny_cfg(**kw)
+    w = f64(synth.layer_weights(cfg, 0, gamma="perturbed"))
+    for k in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"):
+        w[k] = w[k] * 10
+    lora = f64(synth.lora_weights(cfg, 0, b_zero=False)) if cfg.lora_rank else None
+    router = synth.router_logits(cfg, 0).to(D64) if cfg.is_moe else None
+    x = synth.activation(cfg, "x").to(D64)
+    rows = [1, 7, 8, 12]
+    dy_rows = synth.normal((len(rows), cfg.hidden), cfg.seed, "dy_rows", 1.0).to(D64)
+    dy = torch.zeros_like(x)
+    dy[rows] = dy_rows
+    dx_ref, g_ref, _ = O.layer_backward(x, w, dy, cfg, lora, router)
+    dx, g = O.layer_backward_rows(x, w, rows, dy_rows, cfg, lora, router)
+    assert torch.allclose(dx, dx_ref, rtol=1e-12, atol=1e-13)
+    assert set(g) == set(g_ref)
+    for n in g_ref:
+        assert torch.allclose(g[n], g_ref[n], rtol=1e-12, atol=1e-13), n
+    assert dx[13:].abs().max().item() == 0.0
+    assert dx[:8].abs().min().item() > 0.0
