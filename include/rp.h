@@ -220,8 +220,9 @@ typedef enum rp_op {
   RP_OP_STAGE_FWD = 0,
   RP_OP_STAGE_BWD = 1,
   RP_OP_LMHEAD = 2,
-  RP_OP_FUSED = 3 /* rp_stage_fwd(RP_KEEP_ACTS) followed by
-                     rp_stage_bwd_recompute(RP_USE_KEPT_ACTS) on one workspace */
+  RP_OP_FUSED = 3, /* rp_stage_fwd(RP_KEEP_ACTS) followed by
+                      rp_stage_bwd_recompute(RP_USE_KEPT_ACTS) on one workspace */
+  RP_OP_MOE_ROUTE = 4 /* rp_op_moe_route (MoE contexts; n_layers, flags ignored) */
 } rp_op;
 
 /* Bytes of device workspace the call needs for T = batch * seq tokens and
@@ -296,7 +297,9 @@ rp_status rp_lmhead_ce_fwd_bwd(rp_ctx* ctx, int batch, int seq, const void* x,
 
 /* Token embedding of the full-model case: x0[t] = table[ids[t]] and its
  * backward dtable = scatter-add of dx0 over ids (overwrites dtable, fp32).
- * table: device [vocab, H] context dtype; ids int32 [T] in [0, vocab). */
+ * table: device [vocab, H] context dtype; ids int32 [T]. An id outside
+ * [0, vocab) (a padding id) gives a zero row of x0 and adds nothing to
+ * dtable. */
 rp_status rp_embed_fwd(rp_ctx* ctx, int n_tokens, int vocab, const int32_t* ids,
                        const void* table, void* x0);
 rp_status rp_embed_bwd(rp_ctx* ctx, int n_tokens, int vocab, const int32_t* ids,
@@ -520,6 +523,30 @@ rp_status rp_op_attn_fwd(rp_ctx* ctx, int batch, int seq, const void* qkv, void*
 rp_status rp_op_attn_bwd(rp_ctx* ctx, int batch, int seq, const void* qkv, const void* o,
                          const void* dout, const float* lse, void* dqkv, void* ws,
                          size_t ws_bytes);
+
+/* MoE routing alone, for checking its integer outputs bit for bit (the
+ * top-k expert selection of the paperlayer.ai summary, appendix C.2, which
+ * activates E_act of E_total experts per token; the grouped order is the
+ * permutation that lets each expert's rows run as one product). For the
+ * context's E experts and top_k = k, T = batch * seq tokens:
+ *   logits    device fp32 [T, E] router logits (an input of the layer)
+ *   idx       device int32 [T, k]: the k largest logits of each token, by
+ *             value descending; equal logits are taken lower index first
+ *   wgt       device fp32 [T, k]: softmax over the k selected logits
+ *   cnt       device int32 [E]: (token, slot) pairs routed to each expert
+ *   off       device int32 [E + 1]: first grouped row of each expert
+ *             (off[0] = 0, off[E] = T k)
+ *   perm_row  device int32 [T k]: the token of each grouped row; expert e's
+ *             rows off[e] .. off[e+1]-1 list its pairs in increasing
+ *             (token, slot) order (a stable counting sort)
+ *   perm_w    device fp32 [T k]: the routing weight of each grouped row
+ *   inv       device int32 [T k]: the grouped row of pair (token, slot)
+ *   ws        rp_workspace_size(RP_OP_MOE_ROUTE, batch, seq) bytes: the tile
+ *             map of the grouped products
+ * RP_ERR_STATE for a dense context. Enqueued on the compute stream. */
+rp_status rp_op_moe_route(rp_ctx* ctx, int batch, int seq, const float* logits, int32_t* idx,
+                          float* wgt, int32_t* cnt, int32_t* off, int32_t* perm_row,
+                          float* perm_w, int32_t* inv, void* ws, size_t ws_bytes);
 
 /* Plain device-to-device copy of `bytes` (a multiple of 16; both pointers
  * 16-byte aligned, non-overlapping device memory), 16 bytes per lane. Its

@@ -25,7 +25,7 @@ RP_T_GAMMA1, RP_T_WQKV, RP_T_WO, RP_T_GAMMA2, RP_T_WGU, RP_T_WD = 0, 1, 2, 3, 4,
 RP_T_QNORM, RP_T_KNORM = 6, 7
 RP_T_AQ, RP_T_BQ, RP_T_AK, RP_T_BK, RP_T_AV, RP_T_BV, RP_T_AO, RP_T_BO = range(16, 24)
 RP_BLOCK_WEIGHT, RP_BLOCK_GRAD, RP_BLOCK_LORA = 0, 1, 2
-RP_OP_STAGE_FWD, RP_OP_STAGE_BWD, RP_OP_LMHEAD, RP_OP_FUSED = 0, 1, 2, 3
+RP_OP_STAGE_FWD, RP_OP_STAGE_BWD, RP_OP_LMHEAD, RP_OP_FUSED, RP_OP_MOE_ROUTE = 0, 1, 2, 3, 4
 RP_KEEP_ACTS, RP_USE_KEPT_ACTS, RP_CKPT_DEVICE, RP_ACCUM_GRADS = 1, 2, 4, 8
 RP_H2D, RP_D2H = 0, 1
 RP_ON_COMPUTE, RP_ON_ACT_H2D, RP_ON_ACT_D2H = 0, 1, 2
@@ -112,6 +112,7 @@ _SIGS = {
     "rp_op_copy": (C.c_int, [_P, _P, _P, C.c_size_t]),
     "rp_op_transpose_bf16": (C.c_int, [_P, C.c_int, C.c_int, _P, C.c_int64, _P, C.c_int64]),
     "rp_op_attn_bwd": (C.c_int, [_P, C.c_int, C.c_int, _P, _P, _P, _P, _P, _P, C.c_size_t]),
+    "rp_op_moe_route": (C.c_int, [_P, C.c_int, C.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t]),
     "rp_trace_begin": (C.c_int, [_P, C.c_int]),
     "rp_trace_end": (C.c_int, [_P]),
     "rp_trace_read": (C.c_int, [_P, C.POINTER(rp_trace_rec), C.c_int, C.POINTER(C.c_int)]),
@@ -443,6 +444,12 @@ class Context:
         self._order()
         check(lib().rp_op_attn_fwd(self.h, batch, seq, ptr(qkv), ptr(o), ptr(lse)))
         self._hold(qkv, o, lse)
+
+    def op_moe_route(self, batch, seq, logits, idx, wgt, cnt, off, perm_row, perm_w, inv, ws):
+        self._order()
+        check(lib().rp_op_moe_route(self.h, batch, seq, ptr(logits), ptr(idx), ptr(wgt), ptr(cnt), ptr(off),
+                                    ptr(perm_row), ptr(perm_w), ptr(inv), ptr(ws), ws.numel()))
+        self._hold(logits, idx, wgt, cnt, off, perm_row, perm_w, inv, ws)
 
     def op_attn_bwd(self, batch, seq, qkv, o, dout, lse, dqkv, ws):
         self._order()

@@ -296,6 +296,12 @@ rp_status rp_workspace_size(const rp_ctx* cc, int op, int batch, int seq, int n_
                        bytes);
     case RP_OP_LMHEAD:
       return lmhead(c, batch, seq, nullptr, nullptr, nullptr, nullptr, nullptr, 0, bytes);
+    case RP_OP_MOE_ROUTE: {
+      RP_CHECK(c->sh.E > 0, RP_ERR_STATE, "workspace_size: MoE routing in a dense context");
+      const int64_t T = (int64_t)batch * seq;
+      *bytes = 2 * align_up((size_t)moe_max_tiles(T, c->sh.topk, c->sh.E) * 4, 256);
+      return RP_OK;
+    }
   }
   set_error("workspace_size: unknown op %d", op);
   return RP_ERR_INVALID;
@@ -334,7 +340,7 @@ rp_status rp_lmhead_ce_fwd_bwd(rp_ctx* c, int batch, int seq, const void* x, con
 rp_status rp_embed_fwd(rp_ctx* c, int n_tokens, int vocab, const int32_t* ids, const void* table, void* x0) {
   CTX_ENTER(c);
   RP_CHECK(n_tokens >= 0 && vocab > 0 && ids && table && x0, RP_ERR_INVALID, "embed_fwd: bad arguments");
-  return embed_fwd(c->sh.dt, ids, table, x0, n_tokens, c->sh.H, c->compute);
+  return embed_fwd(c->sh.dt, ids, table, x0, n_tokens, vocab, c->sh.H, c->compute);
 }
 
 rp_status rp_embed_bwd(rp_ctx* c, int n_tokens, int vocab, const int32_t* ids, const void* dx0, float* dtable) {
@@ -407,6 +413,33 @@ rp_status rp_op_attn_bwd(rp_ctx* c, int batch, int seq, const void* qkv, const v
   a.dt = c->sh.dt; a.batch = batch; a.seq = seq; a.n_q = c->sh.nq; a.n_kv = c->sh.nkv; a.d = c->sh.d;
   RP_CHECK(ws_bytes >= attn_bwd_ws_bytes(a), RP_ERR_WORKSPACE, "op_attn_bwd: workspace too small");
   return attn_bwd(a, qkv, o, dout, lse, (float*)ws, dqkv, c->compute);
+}
+
+rp_status rp_op_moe_route(rp_ctx* c, int batch, int seq, const float* logits, int32_t* idx, float* wgt,
+                          int32_t* cnt, int32_t* off, int32_t* perm_row, float* perm_w, int32_t* inv, void* ws,
+                          size_t ws_bytes) {
+  CTX_ENTER(c);
+  RP_CHECK(c->sh.E > 0, RP_ERR_STATE, "op_moe_route: dense context");
+  RP_CHECK(batch >= 1 && seq >= 1, RP_ERR_INVALID, "op_moe_route: bad sizes");
+  const int64_t T = (int64_t)batch * seq;
+  RP_CHECK(T * c->sh.topk <= INT32_MAX, RP_ERR_UNSUPPORTED, "op_moe_route: too many tokens");
+  RP_CHECK(logits && idx && wgt && cnt && off && perm_row && perm_w && inv && ws, RP_ERR_INVALID,
+           "op_moe_route: null pointer");
+  size_t need = 0;
+  RP_TRY(rp_workspace_size(c, RP_OP_MOE_ROUTE, batch, seq, 1, 0, &need));
+  RP_CHECK(ws_bytes >= need, RP_ERR_WORKSPACE, "op_moe_route: workspace %zu < %zu bytes", ws_bytes, need);
+  MoeRouting m;
+  m.max_tiles = moe_max_tiles(T, c->sh.topk, c->sh.E);
+  m.idx = idx;
+  m.wgt = wgt;
+  m.cnt = cnt;
+  m.off = off;
+  m.tile_e = (int*)ws;
+  m.tile_m0 = (int*)((char*)ws + need / 2);
+  m.perm_row = perm_row;
+  m.perm_w = perm_w;
+  m.inv = inv;
+  return moe_route(m, logits, (int)T, c->sh.E, c->sh.topk, c->compute);
 }
 
 rp_status rp_trace_begin(rp_ctx* c, int max_launches) {

@@ -25,8 +25,7 @@ __host__ __device__ inline float to_f(bf16 x) {
   return c.f;
 }
 
-// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
-// fp32 -> bf16, round to nearest even. On the device the hardware
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN. On the device the hardware
 // conversion (v_cvt_pk_bf16_f32 on gfx950) does it in one instruction; the
 // host spells out the same rounding.
 __host__ __device__ inline bf16 to_bf16(float f) {

@@ -504,12 +504,15 @@ __global__ __launch_bounds__(256) void ce_grad_kernel(const float* __restrict__ 
 // ---------------------------------------------------------------------------
 // embedding
 // ---------------------------------------------------------------------------
+// an id outside [0, vocab) (e.g. a padding id of -100) gives a zero row, as
+// the backward ignores it
 template <class T>
-__global__ void embed_fwd_kernel(const int32_t* ids, const T* table, T* x0, int rows, int H) {
+__global__ void embed_fwd_kernel(const int32_t* ids, const T* table, T* x0, int rows, int vocab, int H) {
   const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (idx >= (int64_t)rows * H) return;
   const int t = (int)(idx / H), c = (int)(idx % H);
-  x0[idx] = table[(int64_t)ids[t] * H + c];
+  const int v = ids[t];
+  x0[idx] = (v >= 0 && v < vocab) ? table[(int64_t)v * H + c] : from_f<T>(0.f);
 }
 
 // one block per vocabulary row, one thread per column: tokens scanned in order
@@ -905,13 +908,16 @@ rp_status ce_grad_tr(const float* logits, int64_t ld, int T, int Vs, int vlo, co
   return RP_OK;
 }
 
-rp_status embed_fwd(int dt, const int32_t* ids, const void* table, void* x0, int T, int H, hipStream_t s) {
+rp_status embed_fwd(int dt, const int32_t* ids, const void* table, void* x0, int T, int V, int H,
+                    hipStream_t s) {
   const int64_t n = (int64_t)T * H;
   if (n == 0) return RP_OK;
   if (dt == RP_DTYPE_BF16)
-    RP_LAUNCH(embed_fwd_kernel<bf16>, dim3(blocks_for(n)), dim3(256), 0, s, ids, (const bf16*)table, (bf16*)x0, T, H);
+    RP_LAUNCH(embed_fwd_kernel<bf16>, dim3(blocks_for(n)), dim3(256), 0, s, ids, (const bf16*)table, (bf16*)x0, T, V,
+              H);
   else
-    RP_LAUNCH(embed_fwd_kernel<float>, dim3(blocks_for(n)), dim3(256), 0, s, ids, (const float*)table, (float*)x0, T, H);
+    RP_LAUNCH(embed_fwd_kernel<float>, dim3(blocks_for(n)), dim3(256), 0, s, ids, (const float*)table, (float*)x0, T,
+              V, H);
   return RP_OK;
 }
 

@@ -188,7 +188,7 @@ rp_status moe_uncombine(const void* dbe, const MoeRouting& m, int T, int k, int 
 // ---------------------------------------------------------------------------
 // misc
 // ---------------------------------------------------------------------------
-rp_status embed_fwd(int dt, const int32_t* ids, const void* table, void* x0, int T, int H,
+rp_status embed_fwd(int dt, const int32_t* ids, const void* table, void* x0, int T, int V, int H,
                     hipStream_t s);
 rp_status embed_bwd(int dt, const int32_t* ids, const void* dx0, float* dtable, int T, int V,
                     int H, hipStream_t s);

@@ -4,8 +4,11 @@ rows, sampled weight-gradient rows and columns, the exact LM-head loss) and on
 properties that hold at any size (recomputation reproduces the forward bit for
 bit, splitting a stage changes nothing, B = 0 adapters get exactly zero dA).
 
-The Qwen3-1.7B-shaped stage is small enough for the complete fp64 oracle:
-every output and gradient is compared element by element there."""
+The Qwen3-1.7B-shaped stage is small enough for the complete fp64 oracle, and
+the Llama-3.1-8B-shaped layer for the complete fp32 oracle: every output and
+gradient is compared element by element there. For the larger layers the
+upstream gradient is made zero outside sampled rows; the exact oracle of that
+case still gives dx at every row and every weight gradient in full."""
 import pytest
 import torch
 
@@ -104,9 +107,10 @@ def test_qwen3_1p7b_stage_full_streamed(env):
 def test_llama3_8b_layer_full(env):
     """Llama-3.1-8B-shaped layer at full size (1 x 8192 tokens), the calls the
     benchmark times: forward with a host checkpoint, then recompute + backward
-    from that checkpoint. Sampled output rows and sampled MLP weight-gradient
-    rows / columns against the oracle; the fused path (kept internals) gives
-    the same bits as the recompute path."""
+    from that checkpoint. Sampled output rows against the fp64 oracle; y, dx
+    and all nine weight gradients, every element, against the complete fp32
+    oracle; the fused path (kept internals) gives the same bits as the
+    recompute path."""
     B, Worker = env
     cfg = synth.config("llama3_8b")
     T, H, b, s = cfg.tokens, cfg.hidden, cfg.batch, cfg.seq
@@ -145,14 +149,22 @@ def test_llama3_8b_layer_full(env):
     rows = sample_rows(T)
     y_ref = O.layer_forward_rows(x64, w64, cfg, rows)
     assert rel_rows(y.cpu()[rows], y_ref) < TOL
-    say("llama3_8b layer full: oracle MLP gradients")
-    bmat = mlp_input(x64, w64, cfg)
-    cols = sample_rows(cfg.ffn, n=12, seed=1)
-    dwd, dwg, dwu = O.mlp_weight_grad_columns(bmat, dy.double(), w64, cols)
-    got = wk.unpack_grads(wk.layers[0]["g"])
-    assert max_rel(got["wd"][:, cols], dwd) < TOL
-    assert max_rel(got["wg"][cols], dwg) < TOL
-    assert max_rel(got["wu"][cols], dwu) < TOL
+    say("llama3_8b layer full: complete fp32 oracle")
+    got = {k: v.cpu() for k, v in wk.unpack_grads(wk.layers[0]["g"]).items()}
+    y, dx = y.cpu(), dx.cpu()
+    del wk, ctx
+    torch.cuda.empty_cache()
+    # the whole layer, fwd and bwd, in fp32 (the workload's gradient precision;
+    # fp64 would need twice the host memory for the 32 T x T score matrices)
+    dx_ref, g_ref, y_ref = O.layer_backward(x, lw, dy, cfg, dtype=torch.float32)
+    for what, a, r in (("y", y, y_ref), ("dx", dx, dx_ref)):
+        e = max_rel(a, r)
+        say(f"llama3_8b complete {what}: max rel {e:.2e}")
+        assert e < TOL, (what, e)
+    for n, r in g_ref.items():
+        e = max_rel(got[n], r)
+        say(f"llama3_8b complete {n}: max rel {e:.2e}")
+        assert e < TOL, (n, e)
 
 
 def test_llama3_8b_lmhead_full(env):
@@ -302,3 +314,138 @@ def test_qwen3_235b_moe_lora_stage_full(env):
     rows = sample_rows(T, n=6)
     ref = O.layer_forward_rows(x.double(), f64(lw), cfg, rows, f64(lora), router.double())
     assert rel_rows(y.cpu()[rows], ref) < TOL
+
+
+# ---------------------------------------------------------------------------
+# complete gradients at full size: an upstream gradient that is zero outside
+# a set of sampled token rows. Every kernel still runs over every row and
+# tile at the benchmark's launch configuration; the exact oracle
+# (layer_backward_rows) gives dx at every row and every weight gradient in
+# full, so both are compared element by element.
+# ---------------------------------------------------------------------------
+
+
+def sparse_dy(cfg, n=16, seed=7):
+    """dy with N(0, 1) rows at the sampled positions (tile edges, the first
+    and last rows, random rows) and zeros elsewhere."""
+    T, H = cfg.tokens, cfg.hidden
+    rows = set(sample_rows(T, n=n, seed=seed)) | {127, 128, 255, 256, T - 129, T - 128}
+    rows = sorted(r for r in rows if 0 <= r < T)
+    dy_rows = synth.normal((len(rows), H), cfg.seed, "dy_rows", 1.0, dtype=torch.bfloat16)
+    dy = torch.zeros(T, H, dtype=torch.bfloat16)
+    dy[rows] = dy_rows
+    return rows, dy_rows, dy
+
+
+def check_grads(got, ref, what):
+    for n, r in ref.items():
+        e = max_rel(got[n], r)
+        say(f"{what} {n}: max rel {e:.2e}")
+        assert e < TOL, (what, n, e)
+
+
+def test_llama3_8b_layer_full_grads_sparse_dy(env):
+    """Llama-3.1-8B-shaped layer at 1 x 8192 tokens, the benchmark's calls
+    (forward with a host checkpoint, recompute + backward from it): dx at all
+    8192 rows and all nine weight gradients against the exact oracle."""
+    B, Worker = env
+    cfg = synth.config("llama3_8b")
+    T, H, b, s = cfg.tokens, cfg.hidden, cfg.batch, cfg.seq
+    say("llama3_8b sparse-dy: run")
+    lw = synth.layer_weights(cfg, 0, gamma="perturbed")
+    x = synth.activation(cfg, "x")
+    rows, dy_rows, dy = sparse_dy(cfg)
+    wk = Worker(cfg)
+    wk.add_layer(0, lw)
+    ctx = wk.ctx
+    bf = dict(dtype=torch.bfloat16, device=DEV)
+    xd, dyd = x.to(DEV), dy.to(DEV)
+    ck = [torch.empty(T, H, dtype=torch.bfloat16).pin_memory()]
+    y, dx = torch.empty(T, H, **bf), torch.empty(T, H, **bf)
+    ws_f = ctx.workspace(B.RP_OP_STAGE_FWD, b, s, 1)
+    ws_b = ctx.workspace(B.RP_OP_STAGE_BWD, b, s, 1)
+    ctx.stage_fwd(0, 1, b, s, xd, y, ws_f, ckpt_host=ck)
+    ctx.stage_bwd_recompute(0, 1, b, s, dyd, dx, ws_b, ckpt=ck)
+    ctx.sync()
+    got = {k: v.cpu() for k, v in wk.unpack_grads(wk.layers[0]["g"]).items()}
+    dx = dx.cpu()
+    del ws_f, ws_b, wk, ctx
+    torch.cuda.empty_cache()
+    say("llama3_8b sparse-dy: oracle")
+    dx_ref, g_ref = O.layer_backward_rows(x.double(), f64(lw), rows, dy_rows.double(), cfg)
+    e = max_rel(dx, dx_ref)
+    say(f"llama3_8b sparse-dy dx: max rel {e:.2e}")
+    assert e < TOL
+    check_grads(got, g_ref, "llama3_8b sparse-dy")
+
+
+def test_qwen3_32b_layer_full_grads_sparse_dy(env):
+    """Qwen3-32B-shaped fused stage at 1 x 16384 tokens (64/8 heads, FFN
+    25600): forward keeping its internals, then backward. dx at all 16384 rows
+    and all nine weight gradients against the exact oracle."""
+    B, Worker = env
+    cfg = synth.config("qwen3_32b")
+    T, H, b, s = cfg.tokens, cfg.hidden, cfg.batch, cfg.seq
+    say("qwen3_32b sparse-dy: run")
+    lw = synth.layer_weights(cfg, 2, gamma="perturbed")
+    x = synth.activation(cfg, "x2")
+    rows, dy_rows, dy = sparse_dy(cfg)
+    wk = Worker(cfg)
+    wk.add_layer(2, lw)
+    ctx = wk.ctx
+    bf = dict(dtype=torch.bfloat16, device=DEV)
+    xd, dyd = x.to(DEV), dy.to(DEV)
+    y, dx = torch.empty(T, H, **bf), torch.empty(T, H, **bf)
+    ws = ctx.workspace(B.RP_OP_FUSED, b, s, 1)
+    ctx.stage_fwd(2, 3, b, s, xd, y, ws, flags=B.RP_KEEP_ACTS)
+    ctx.stage_bwd_recompute(2, 3, b, s, dyd, dx, ws, flags=B.RP_USE_KEPT_ACTS)
+    ctx.sync()
+    got = {k: v.cpu() for k, v in wk.unpack_grads(wk.layers[2]["g"]).items()}
+    dx = dx.cpu()
+    del ws, wk, ctx
+    torch.cuda.empty_cache()
+    say("qwen3_32b sparse-dy: oracle")
+    dx_ref, g_ref = O.layer_backward_rows(x.double(), f64(lw), rows, dy_rows.double(), cfg)
+    e = max_rel(dx, dx_ref)
+    say(f"qwen3_32b sparse-dy dx: max rel {e:.2e}")
+    assert e < TOL
+    check_grads(got, g_ref, "qwen3_32b sparse-dy")
+
+
+def test_qwen3_235b_moe_lora_full_grads_sparse_dy(env):
+    """Qwen3-235B-A22B-shaped MoE LoRA stage at 1 x 32768 tokens with
+    adapters B ~ N(0, 0.02) (so every adapter gradient carries signal):
+    fused forward + backward, dx at all 32768 rows and all eight adapter
+    gradients against the exact oracle (routing on the same fp32 logits)."""
+    B, Worker = env
+    cfg = synth.config("qwen3_235b_moe")
+    T, H, b, s = cfg.tokens, cfg.hidden, cfg.batch, cfg.seq
+    say("qwen3_235b sparse-dy: run")
+    lw = synth.layer_weights(cfg, 0, gamma="perturbed")
+    lora = synth.lora_weights(cfg, 0, b_zero=False)
+    router = synth.router_logits(cfg, 0)
+    x = synth.activation(cfg, "x")
+    rows, dy_rows, dy = sparse_dy(cfg)
+    wk = Worker(cfg)
+    wk.add_layer(0, lw, lora=lora)
+    ctx = wk.ctx
+    bf = dict(dtype=torch.bfloat16, device=DEV)
+    xd, dyd, rd = x.to(DEV), dy.to(DEV), router.to(DEV)
+    y, dx = torch.empty(T, H, **bf), torch.empty(T, H, **bf)
+    ws = ctx.workspace(B.RP_OP_FUSED, b, s, 1)
+    ctx.stage_fwd(0, 1, b, s, xd, y, ws, router=[rd], flags=B.RP_KEEP_ACTS)
+    ctx.stage_bwd_recompute(0, 1, b, s, dyd, dx, ws, flags=B.RP_USE_KEPT_ACTS)
+    ctx.sync()
+    got = {k: v.cpu() for k, v in wk.unpack_lora_grads(wk.layers[0]["lora_g"]).items()}
+    dx = dx.cpu()
+    del ws, wk, ctx
+    torch.cuda.empty_cache()
+    say("qwen3_235b sparse-dy: oracle")
+    # the kernels take the adapters rounded to bf16 once per call; so does the oracle
+    lora_b = {k: v.to(torch.bfloat16).double() for k, v in lora.items()}
+    dx_ref, g_ref = O.layer_backward_rows(x.double(), f64(lw), rows, dy_rows.double(), cfg, lora_b,
+                                          router.double())
+    e = max_rel(dx, dx_ref)
+    say(f"qwen3_235b sparse-dy dx: max rel {e:.2e}")
+    assert e < TOL
+    check_grads(got, g_ref, "qwen3_235b sparse-dy")

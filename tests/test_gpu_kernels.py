@@ -215,3 +215,32 @@ def test_bf16_output_rounding_is_nearest_even(B):
     ctx.sync()
     got = C.cpu()
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
+def test_embed_out_of_range_ids_give_zero_rows(B):
+    """Token embedding with ids outside [0, vocab) (a padding id of -100, vocab
+    itself, a large id): those rows of x0 are zero and the backward ignores
+    them; the valid rows gather and scatter-add as the oracle does."""
+    say("embedding with out-of-range ids")
+    cfg = synth.config("tiny")
+    ctx = B.Context(cfg)
+    V, H = cfg.vocab, cfg.hidden
+    table = synth.normal((V, H), 5, "embed_table", 0.02)
+    ids = synth.uniform_int((300,), V, 5, "embed_ids")
+    ids[[0, 7, 150, 299]] = torch.tensor([-100, V, 1 << 30, -1], dtype=torch.int32)
+    ids[10:20] = 3  # repeated id: its gradient row sums ten token rows
+    dx0 = synth.normal((300, H), 5, "embed_dx0")
+    dev = torch.device("cuda")
+    x0 = torch.full((300, H), float("nan"), device=dev)
+    dtable = torch.full((V, H), float("nan"), device=dev)
+    ids_d, table_d, dx0_d = ids.to(dev), table.to(dev), dx0.to(dev)
+    torch.cuda.synchronize()
+    ctx.embed_fwd(ids_d, table_d, x0)
+    ctx.embed_bwd(ids_d, dx0_d, dtable)
+    ctx.sync()
+    ok = (ids >= 0) & (ids < V)
+    x0 = x0.cpu()
+    assert torch.equal(x0[~ok], torch.zeros(int((~ok).sum()), H))
+    assert torch.equal(x0[ok], O.embed(ids[ok], table))
+    ref = O.embed_backward(ids[ok], dx0[ok].double(), V)
+    assert max_rel(dtable, ref) < 1e-6
