@@ -13,32 +13,37 @@ gradients):
                           backward -> dx and the fp32 weight gradients
 
 `value` is trained tokens per second with weights resident in HBM (inputs in
-HBM when the timed region starts). With --streamed the same step also uploads
-every weight from pinned host memory and downloads every gradient to it
-through rp_weight_stream_submit; that host-link-inclusive rate is reported
-under "streamed", never as `value`. It also reports, under "priority", the
-latency of an activation upload alone, behind an ungated weight upload, and
-with that upload gated on the activation copy's ticket.
+HBM when the timed region starts): the compute of the step. By default the
+same step also runs as the workload states it, every weight uploaded from
+pinned host memory and every fp32 gradient downloaded to it through
+rp_weight_stream_submit, reported under "streamed" (never as `value`) with
+the transfers alone, the overlap efficiency
+(t_compute + t_transfers - t_step) / min(t_compute, t_transfers) and the link
+rates against the box's measured pinned-copy peak ("link_peak"); then with
+the gradients on the link in bf16 ("streamed_bf16_grads"), and, under
+"priority", the latency of an activation upload alone, behind an ungated
+weight upload, and with that upload gated on the activation copy's ticket.
 
 With --ablation it also runs the pages' priority-aware transfer ablation on
 Llama-3.1-8B-shaped layers (section 5.8.2): a forward + backward pass over
 4 one-layer stages of 4 micro-batches each, every weight, activation and
-gradient through pinned host memory, for micro-batch sizes 1..8 sequences of
+gradient through pinned host memory, for micro-batch sizes 1..10 sequences of
 2048 tokens, under the policies no_prefetch, prefetch and windowed
 (offloaded_pipeline_stage_amd/microbatch.py). Reported under "ablation".
 
 Each kernel launch in the timed region is timed by the library's own HIP
 event pairs on the compute stream (rp_trace_*); the dominant kernel is priced
-against the MI355X peak for its bound. The CPU oracle is timed on a bounded
-sample of the same step for the cpu_baseline field.
+against the MI355X peak for its bound. The CPU oracle is timed in fp32 on the
+full layer at the workload's length and on a row sample of the LM head for
+the cpu_baseline field.
 
 `roofline.traffic` comes from two rocprofv3 counter runs of this script
 (FETCH_SIZE, then WRITE_SIZE, with --copy-calibration-mib for the scale),
 reduced by offloaded_pipeline_stage_amd/pmc.py into
 profiles/<workload>_step_traffic.txt.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--streamed]
-                       [--no-cpu-baseline] [--cpu-seq S] [--trace-json PATH]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-streamed]
+                       [--no-cpu-baseline] [--cpu-head-rows R] [--trace-json PATH]
                        [--copy-calibration-mib M] [--configs] [--ablation] [--optimizer]
 """
 from __future__ import annotations
@@ -186,6 +191,15 @@ class Step:
             sub([(self.grad_kind, B.RP_TGT_LAYER, layer, 0, wk.g_bytes, self.host_grad[layer])])
         self.n += 1
 
+    def run_transfers_only(self):
+        """The streamed step's uploads and downloads alone (the same items and
+        chunking, no kernels): the time the host link needs for one step."""
+        B, wk = self.B, self.wk
+        items = ([(B.RP_PARAM_H2D, B.RP_TGT_LAYER, 0, 0, wk.w_bytes, self.host_layer)]
+                 + self._shard_items(B.RP_PARAM_H2D) + self._shard_items(self.grad_kind)
+                 + [(self.grad_kind, B.RP_TGT_LAYER, 1, 0, wk.g_bytes, self.host_grad[1])])
+        wk.ctx.weight_stream_submit(items, n_windows=1, max_chunk=64 << 20)
+
     def sync(self):
         self.wk.ctx.sync()
         torch.cuda.synchronize()
@@ -281,7 +295,7 @@ def priority_probe(cfg, chunk_mib: int = 16, reps: int = 5):
     return out
 
 
-def transfer_ablation(mbs_list=(1, 2, 3, 4, 6, 8), n_layers: int = 4, n_micro: int = 4, seq: int = 2048,
+def transfer_ablation(mbs_list=tuple(range(1, 11)), n_layers: int = 4, n_micro: int = 4, seq: int = 2048,
                       reps: int = 2):
     """Throughput (tokens/s) of one forward + backward pass over `n_layers`
     one-layer stages of `n_micro` micro-batches per transfer policy and
@@ -474,26 +488,128 @@ def config_sweep(reps: int = 3):
     return out
 
 
-def cpu_baseline(cfg, seq: int):
-    """The oracle, as it stands, on `seq` tokens of the same stage: layer
-    forward, LM head + cross-entropy forward/backward, layer recompute +
-    backward, all in fp64 on the host cores."""
+def link_peak(nbytes: int = 1 << 30, chunk: int = 64 << 20, reps: int = 3):
+    """The host link's pinned-copy rate on this machine through the library's own
+    copy path (rp_act_copy, DMA), in chunks of the size the streamed step
+    uses: one direction at a time, then both directions at once. Best of
+    `reps`, GB/s."""
+    from offloaded_pipeline_stage_amd import binding as B
+    ctx = B.Context(synth.config("llama3_8b"))
+    host_up = torch.ones(nbytes, dtype=torch.uint8).pin_memory()
+    host_dn = torch.empty(nbytes, dtype=torch.uint8).pin_memory()
+    dev_up = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dev_dn = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def up():
+        for o in range(0, nbytes, chunk):
+            ctx.act_copy(B.RP_H2D, dev_up[o:o + chunk], host_up[o:o + chunk])
+
+    def down():
+        for o in range(0, nbytes, chunk):
+            ctx.act_copy(B.RP_D2H, host_dn[o:o + chunk], dev_dn[o:o + chunk])
+
+    def timed(fn):
+        best = float("inf")
+        for _ in range(reps + 1):
+            ctx.sync()
+            t0 = time.perf_counter()
+            fn()
+            ctx.sync()
+            best = min(best, time.perf_counter() - t0)
+        return best
+
+    t_up, t_dn = timed(up), timed(down)
+    t_both = timed(lambda: (up(), down()))
+    ctx.close()
+    return {"h2d_GBps": round(nbytes / t_up / 1e9, 1), "d2h_GBps": round(nbytes / t_dn / 1e9, 1),
+            "both_directions_GBps": round(2 * nbytes / t_both / 1e9, 1), "bytes_per_direction": nbytes,
+            "chunk_bytes": chunk}
+
+
+def time_steps(st, steps: int, warmup: int) -> float:
+    """ms per step of a Step over `steps` after `warmup`."""
+    for _ in range(warmup):
+        st.run()
+    st.sync()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        st.run()
+    st.sync()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def streamed_figures(cfg, steps: int, warmup: int, ms_resident: float, peak: dict, grad_bf16: bool = False):
+    """The step with every weight uploaded from pinned host memory and every
+    gradient downloaded to it (the workload as stated: bf16 weights streamed
+    in, fp32 gradients out), against the resident step (compute alone) and
+    the same transfers alone (link alone). link_bound_ms is the busier
+    direction at its measured peak (the directions overlapping fully),
+    link_serial_ms both directions one after the other."""
+    st = Step(cfg, streamed=True, grad_bf16=grad_bf16)
+    ms_s = time_steps(st, steps, warmup)
+    st.sync()
+    xs = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        st.run_transfers_only()
+        st.sync()
+        xs.append((time.perf_counter() - t0) * 1e3)
+    ms_x = sorted(xs)[1]
+    h2d = st.wk.w_bytes + sum(h.numel() * h.element_size() for h in st.host_shards)
+    d2h = (st.wk.g_bytes + sum(h.numel() * 4 for h in st.host_dshards)) // (2 if grad_bf16 else 1)
+    del st
+    torch.cuda.empty_cache()
+    t_up, t_dn = h2d / (peak["h2d_GBps"] * 1e9), d2h / (peak["d2h_GBps"] * 1e9)
+    return {"tokens_per_s": round(cfg.tokens / (ms_s / 1e3), 1), "ms_per_step": round(ms_s, 3),
+            "over_resident": round(ms_s / ms_resident, 3),
+            "h2d_GB_per_step": round(h2d / 1e9, 3), "d2h_GB_per_step": round(d2h / 1e9, 3),
+            "transfers_alone_ms": round(ms_x, 3),
+            "link_bound_ms": round(max(t_up, t_dn) * 1e3, 3),
+            "link_serial_ms": round((t_up + t_dn) * 1e3, 3),
+            "overlap_efficiency": round((ms_resident + ms_x - ms_s) / min(ms_resident, ms_x), 3),
+            "h2d_GBps": round(h2d / 1e9 / (ms_s / 1e3), 1), "d2h_GBps": round(d2h / 1e9 / (ms_s / 1e3), 1),
+            "h2d_frac_of_peak": round(h2d / 1e9 / (ms_s / 1e3) / peak["h2d_GBps"], 3),
+            "d2h_frac_of_peak": round(d2h / 1e9 / (ms_s / 1e3) / peak["d2h_GBps"], 3),
+            "link_GBps": round((h2d + d2h) / 1e9 / (ms_s / 1e3), 1)}
+
+
+def cpu_baseline(cfg, head_rows: int):
+    """The oracle, as it stands, on the host cores in fp32 (the workload's
+    gradient precision): the full layer at the workload's sequence length
+    (forward, then recompute + backward), and the LM head + cross-entropy on
+    `head_rows` of its token rows. The LM head's work per token does not
+    depend on the sequence length, so its time is scaled by tokens /
+    head_rows; tokens/s = tokens / (layer time + scaled LM-head time)."""
     from oracle import stage as O
-    c = cfg.with_(seq=seq)
-    lw = synth.layer_weights(c, 0)
-    w = synth.lmhead_weights(c)["w"]
-    x = synth.activation(c, "x")
-    labels = synth.uniform_labels(c)
+    f32 = torch.float32
+    lw = synth.layer_weights(cfg, 0)
+    x = synth.activation(cfg, "x")
+    dy = synth.activation(cfg, "dy")
     t0 = time.time()
-    y, ck = O.stage_forward(x, [lw], c)
-    _, dy, _, _ = O.lmhead_fwd_bwd(y, w, labels, c.n_shards)
-    O.stage_backward_recompute(ck, [lw], dy, c)
-    dt = time.time() - t0
-    return {"value": round(c.tokens / dt, 2), "unit": "tokens/s", "cores": torch.get_num_threads(),
+    y, ck = O.stage_forward(x, [lw], cfg, dtype=f32)
+    O.stage_backward_recompute(ck, [lw], dy, cfg, dtype=f32)
+    t_layer = time.time() - t0
+    del y, ck
+    w = synth.lmhead_weights(cfg)["w"]
+    labels = synth.uniform_labels(cfg)[:head_rows]
+    t0 = time.time()
+    O.lmhead_fwd_bwd(x[:head_rows], w, labels, cfg.n_shards, dtype=f32)
+    t_head = time.time() - t0
+    t_step = t_layer + t_head * cfg.tokens / head_rows
+    import platform
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    return {"value": round(cfg.tokens / t_step, 2), "unit": "tokens/s", "cores": torch.get_num_threads(),
             "kind": "oracle",
-            "sample": f"one step of the same stage at 1 x {seq} tokens (full layer and LM-head widths), "
-                      f"fp64 torch on the host, {dt:.1f} s; attention cost grows with sequence length, "
-                      f"so the full 8192-token step would run slower per token"}
+            "sample": f"fp32 torch on the host ({cpu}): the full layer at 1 x {cfg.seq} tokens, forward then "
+                      f"recompute + backward, {t_layer:.1f} s; the {cfg.n_shards}-shard LM head + CE forward/backward "
+                      f"on {head_rows} of the {cfg.tokens} token rows, {t_head:.1f} s, scaled by "
+                      f"{cfg.tokens // head_rows} (its work per token does not depend on the sequence length)"}
 
 
 def main():
@@ -502,9 +618,11 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3_8b")
-    ap.add_argument("--streamed", action="store_true", help="also time the weight-streaming variant")
+    ap.add_argument("--no-streamed", action="store_true",
+                    help="skip the weight-streaming step (run by default, reported under 'streamed')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seq", type=int, default=1024)
+    ap.add_argument("--cpu-head-rows", type=int, default=1024,
+                    help="token rows of the LM head in the CPU oracle's timed sample")
     ap.add_argument("--trace-json", default=None, help="write the per-kernel table here")
     ap.add_argument("--configs", action="store_true",
                     help="also time every configuration's own call sequence (resident weights)")
@@ -572,41 +690,14 @@ def main():
     del step
     torch.cuda.empty_cache()
 
-    if a.streamed:
-        st = Step(cfg, streamed=True)
-        for _ in range(a.warmup):
-            st.run()
-        st.sync()
-        t0 = time.perf_counter()
-        for _ in range(a.steps):
-            st.run()
-        st.sync()
-        ms_s = (time.perf_counter() - t0) * 1e3 / a.steps
-        h2d = st.wk.w_bytes + sum(h.numel() * h.element_size() for h in st.host_shards)
-        d2h = st.wk.g_bytes + sum(h.numel() * 4 for h in st.host_dshards)
-        out["streamed"] = {"tokens_per_s": round(cfg.tokens / (ms_s / 1e3), 1), "ms_per_step": round(ms_s, 3),
-                           "h2d_GB_per_step": round(h2d / 1e9, 3), "d2h_GB_per_step": round(d2h / 1e9, 3),
-                           "h2d_GBps_if_link_bound": round(h2d / 1e9 / (ms_s / 1e3), 1),
-                           "d2h_GBps_if_link_bound": round(d2h / 1e9 / (ms_s / 1e3), 1)}
-        del st
-        torch.cuda.empty_cache()
+    if not a.no_streamed:
+        peak = link_peak()
+        out["link_peak"] = peak
+        out["streamed"] = streamed_figures(cfg, a.steps, a.warmup, ms_step, peak)
+        log(f"[bench] streamed {out['streamed']}")
         # the same step with the gradients on the link in bf16 (the pages'
         # precision; the workload's own gradients are fp32)
-        st = Step(cfg, streamed=True, grad_bf16=True)
-        for _ in range(a.warmup):
-            st.run()
-        st.sync()
-        t0 = time.perf_counter()
-        for _ in range(a.steps):
-            st.run()
-        st.sync()
-        ms_b = (time.perf_counter() - t0) * 1e3 / a.steps
-        d2h_b = d2h / 2
-        out["streamed_bf16_grads"] = {"tokens_per_s": round(cfg.tokens / (ms_b / 1e3), 1), "ms_per_step": round(ms_b, 3),
-                                      "h2d_GB_per_step": round(h2d / 1e9, 3), "d2h_GB_per_step": round(d2h_b / 1e9, 3),
-                                      "over_resident": round(ms_b / ms_step, 3)}
-        del st
-        torch.cuda.empty_cache()
+        out["streamed_bf16_grads"] = streamed_figures(cfg, a.steps, a.warmup, ms_step, peak, grad_bf16=True)
         out["priority"] = priority_probe(cfg)
         torch.cuda.empty_cache()
 
@@ -617,7 +708,7 @@ def main():
     if a.optimizer:
         out["optimizer"] = optimizer_step_time()
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, a.cpu_seq)
+        out["cpu_baseline"] = cpu_baseline(cfg, a.cpu_head_rows)
     print(json.dumps(out), flush=True)
 
 

@@ -123,17 +123,21 @@ typedef struct rp_layer_cfg {
 } rp_layer_cfg;
 
 /* The streams a context issues on (hipStream_t values, passed as void*).
- * compute  -- all kernels (NULL: the legacy default stream)
+ * compute  -- all kernels
  * act_h2d  -- activation / checkpoint uploads (critical path)
  * act_d2h  -- activation / checkpoint downloads (critical path)
  * w_h2d    -- parameter uploads (low priority by scheduling)
  * g_d2h    -- gradient downloads (low priority by scheduling)
- * A transfer stream left NULL is created by the context (and destroyed with
- * it) on a hardware queue of its own, at the default priority. Recommended:
- * streams that share a hardware queue execute in one order, so a transfer
- * stream waiting for a copy on the compute stream's queue would hold the
- * compute kernels queued behind it. Caller-provided streams stay the
- * caller's. */
+ * A stream left NULL is created by the context (and destroyed with it) on a
+ * hardware queue of its own, at the default priority. Recommended: streams
+ * that share a hardware queue execute in one order, so a transfer stream
+ * waiting for a copy on the compute stream's queue would hold the compute
+ * kernels queued behind it. The streams the context creates are blocking
+ * streams: work on the legacy default stream enqueued before a call runs
+ * before the call's kernels, and default-stream work enqueued after a call
+ * waits for them, with no event from the caller. A caller working on another
+ * stream orders it with an event (rp_ctx_streams gives the compute stream).
+ * Caller-provided streams stay the caller's. */
 typedef struct rp_streams {
   void* compute;
   void* act_h2d;
@@ -186,6 +190,8 @@ typedef struct rp_ctx rp_ctx;
  * RP_ERR_UNSUPPORTED for shapes the kernels do not implement. */
 rp_status rp_ctx_create(int device, const rp_layer_cfg* cfg, const rp_streams* streams,
                         rp_ctx** out);
+/* The streams the context issues on (its own where the caller passed NULL). */
+rp_status rp_ctx_streams(const rp_ctx* ctx, rp_streams* out);
 /* Waits for the context's outstanding work, then frees it (NULL is a no-op). */
 rp_status rp_ctx_destroy(rp_ctx* ctx);
 /* Blocks until every stream of the context is idle; reports device errors. */

@@ -74,6 +74,7 @@ _SIGS = {
                                   C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
     "rp_ctx_create": (C.c_int, [C.c_int, C.POINTER(rp_layer_cfg), C.POINTER(rp_streams), C.POINTER(_P)]),
     "rp_ctx_destroy": (C.c_int, [_P]),
+    "rp_ctx_streams": (C.c_int, [_P, C.POINTER(rp_streams)]),
     "rp_ctx_sync": (C.c_int, [_P]),
     "rp_bind_layer": (C.c_int, [_P, C.c_int, _P, _P, _P, _P]),
     "rp_bind_lmhead": (C.c_int, [_P, C.c_int, C.c_int, C.POINTER(_P), C.POINTER(_P), _P, _P]),
@@ -233,23 +234,28 @@ def _close_live():
 
 
 class Context:
-    """Owns an rp_ctx. Kernels run on a default-priority torch stream (or
-    streams["compute"]); the transfer streams are the library's own, each on a
-    hardware queue of its own, unless `streams` names them."""
+    """Owns an rp_ctx. Unless `streams` names them, every stream is the
+    library's own, each on a hardware queue of its own: kernels run on its
+    compute stream, copies on its transfer streams. Those are blocking
+    streams, so torch work on the default stream is ordered against the
+    library's kernels by the runtime; a call made while torch's current stream
+    is another stream first makes the compute stream wait for it."""
 
     def __init__(self, cfg, device: int = 0, streams: Optional[Dict[str, torch.cuda.Stream]] = None):
         self.cfg = cfg
         self.device = device
-        dev = torch.device("cuda", device)
         names = ("compute", "act_h2d", "act_d2h", "w_h2d", "g_d2h")
-        self.streams = dict(streams or {})
-        self.streams.setdefault("compute", torch.cuda.Stream(device=dev))
-        s = rp_streams(*[self.streams[n].cuda_stream if n in self.streams else None for n in names])
+        given = dict(streams or {})
+        s = rp_streams(*[given[n].cuda_stream if n in given else None for n in names])
         self._c = make_cfg(cfg)
         h = _P()
         check(lib().rp_ctx_create(device, C.byref(self._c), C.byref(s), C.byref(h)))
         self.h = h
         _LIVE.add(self)
+        used = rp_streams()
+        check(lib().rp_ctx_streams(h, C.byref(used)))
+        self.streams = {n: given.get(n) or torch.cuda.ExternalStream(getattr(used, n), device=device)
+                        for n in names}
         # every tensor handed to an enqueueing call stays referenced until
         # sync(): the library reads and writes them asynchronously on its own
         # streams, so torch must not recycle their memory before then
@@ -266,19 +272,15 @@ class Context:
                 self._keep.append(o)
 
     def _order(self):
-        """Order the library's compute stream after torch's current stream,
-        so that tensors torch has just filled or produced are complete before
-        a single-kernel call reads or overwrites them (the compute stream is a
-        separate non-blocking stream). Only the op_* calls do this. An event
-        on torch's legacy default stream also waits for the library's
-        transfer streams, which are blocking streams, so on the stage calls
-        it would serialise compute behind in-flight weight and gradient
-        copies. Callers of the stage calls make their inputs complete first
-        (a copy from host memory is; a fill on another stream needs a
-        synchronize or a stream wait)."""
+        """Order the library's compute stream after torch's current stream
+        when that is neither the default stream nor the compute stream, so
+        that tensors torch has just filled or produced there are complete
+        before a call reads or overwrites them. Default-stream work needs no
+        event: the library's streams are blocking streams. (An event on the
+        default stream would also wait for the library's in-flight transfers.)"""
         cur = torch.cuda.current_stream(self.device)
         comp = self.streams["compute"]
-        if cur.cuda_stream != comp.cuda_stream:
+        if cur.cuda_stream not in (0, comp.cuda_stream):
             comp.wait_stream(cur)
 
     def sync(self):
@@ -341,25 +343,30 @@ class Context:
 
     # -- stage calls
     def stage_fwd(self, l0, l1, batch, seq, x, y, ws, ckpt_host=None, router=None, flags=0):
+        self._order()
         check(lib().rp_stage_fwd(self.h, l0, l1, batch, seq, ptr(x), ptr(y), ptr_array(ckpt_host),
                                  ptr_array(router), flags, ptr(ws), ws.numel()))
         self._hold(x, y, ws, ckpt_host, router)
 
     def stage_bwd_recompute(self, l0, l1, batch, seq, dy, dx, ws, ckpt=None, router=None, flags=0):
+        self._order()
         check(lib().rp_stage_bwd_recompute(self.h, l0, l1, batch, seq, ptr_array(ckpt), ptr(dy), ptr(dx),
                                            ptr_array(router), flags, ptr(ws), ws.numel()))
         self._hold(dy, dx, ws, ckpt, router)
 
     def lmhead_ce_fwd_bwd(self, batch, seq, x, labels, loss, dx, ws):
+        self._order()
         check(lib().rp_lmhead_ce_fwd_bwd(self.h, batch, seq, ptr(x), ptr(labels), ptr(loss), ptr(dx), ptr(ws),
                                          ws.numel()))
         self._hold(x, labels, loss, dx, ws)
 
     def embed_fwd(self, ids, table, x0):
+        self._order()
         check(lib().rp_embed_fwd(self.h, ids.numel(), table.shape[0], ptr(ids), ptr(table), ptr(x0)))
         self._hold(ids, table, x0)
 
     def embed_bwd(self, ids, dx0, dtable):
+        self._order()
         check(lib().rp_embed_bwd(self.h, ids.numel(), dtable.shape[0], ptr(ids), ptr(dx0), ptr(dtable)))
         self._hold(ids, dx0, dtable)
 
@@ -367,6 +374,7 @@ class Context:
     def act_copy(self, direction: int, dst: torch.Tensor, src: torch.Tensor, nbytes: Optional[int] = None) -> int:
         t = C.c_int64()
         nb = nbytes if nbytes is not None else src.numel() * src.element_size()
+        self._order()
         check(lib().rp_act_copy(self.h, direction, ptr(dst), ptr(src), nb, C.byref(t)))
         self._hold(dst, src)
         return t.value
@@ -390,6 +398,7 @@ class Context:
     def weight_stream_submit(self, items, n_windows: int = 1, max_chunk: int = 0, gate_ticket: int = -1):
         """items: (kind, target, id, offset, bytes, host tensor or address)."""
         arr = self._xfer_array(items)
+        self._order()
         check(lib().rp_weight_stream_submit(self.h, arr, len(items), n_windows, max_chunk, gate_ticket))
         self._hold([it[5] for it in items])
 
@@ -397,6 +406,7 @@ class Context:
         """One window per entry of `gates` (the activation ticket it waits for, -1 for none)."""
         arr = self._xfer_array(items)
         g = (C.c_int64 * len(gates))(*gates)
+        self._order()
         check(lib().rp_weight_stream_submit_gated(self.h, arr, len(items), len(gates), max_chunk, g))
         self._hold([it[5] for it in items])
 

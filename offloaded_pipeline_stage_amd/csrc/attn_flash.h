@@ -5,12 +5,9 @@
 
 namespace rp {
 
-// whether the flash kernels cover this shape (and are enabled)
+// whether the flash kernels cover this shape
 bool flash_supported(const AttnDesc& a);
 rp_status flash_fwd(const AttnDesc& a, const void* qkv, void* o, float* lse, hipStream_t s);
 rp_status flash_bwd(const AttnDesc& a, const void* qkv, const void* o, const void* dout,
                     const float* lse, float* Dbuf, void* dqkv, hipStream_t s);
-// process-wide switch (tests compare both paths); default on
-void flash_enable(bool on);
-
 }  // namespace rp

@@ -54,8 +54,6 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_LOG2 = 8.f;  // forward: lazy rescale threshold (log2 units)
 
-bool g_flash_on = true;
-
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float lane_of(float4 v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
@@ -665,10 +663,8 @@ rp_status set_lds_limits() {
 
 }  // namespace
 
-void flash_enable(bool on) { g_flash_on = on; }
-
 bool flash_supported(const AttnDesc& a) {
-  return g_flash_on && a.dt == RP_DTYPE_BF16 && a.d == D && a.n_kv > 0 && a.n_q % a.n_kv == 0 && a.seq >= 1;
+  return a.dt == RP_DTYPE_BF16 && a.d == D && a.n_kv > 0 && a.n_q % a.n_kv == 0 && a.seq >= 1;
 }
 
 rp_status flash_fwd(const AttnDesc& a, const void* qkv, void* o, float* lse, hipStream_t s) {

@@ -164,9 +164,12 @@ rp_status rp_ctx_create(int device, const rp_layer_cfg* cfg, const rp_streams* s
     x->w_h2d = (hipStream_t)streams->w_h2d;
     x->g_d2h = (hipStream_t)streams->g_d2h;
   }
-  // missing transfer streams: created here, each on its own hardware queue
-  // (a stream with a CU mask never shares its queue); all CUs enabled
-  for (hipStream_t* ps : {&x->act_h2d, &x->act_d2h, &x->w_h2d, &x->g_d2h}) {
+  // missing streams: created here, each on its own hardware queue (a stream
+  // with a CU mask never shares its queue; all CUs enabled). Such a stream is
+  // a blocking stream: work enqueued on the legacy default stream before a
+  // call runs before the call's kernels, and default-stream work enqueued
+  // after it waits for them.
+  for (hipStream_t* ps : {&x->compute, &x->act_h2d, &x->act_d2h, &x->w_h2d, &x->g_d2h}) {
     if (*ps) continue;
     rp_status st = new_queue_stream(device, ps);
     if (st != RP_OK) {
@@ -177,6 +180,17 @@ rp_status rp_ctx_create(int device, const rp_layer_cfg* cfg, const rp_streams* s
   }
   x->layers.resize(kMaxLayers);  // fixed: deferred transfers keep pointers into it
   *out = x;
+  return RP_OK;
+}
+
+rp_status rp_ctx_streams(const rp_ctx* c, rp_streams* out) {
+  CTX_CHECK(c);
+  RP_CHECK(out != nullptr, RP_ERR_INVALID, "ctx_streams: null output");
+  out->compute = c->compute;
+  out->act_h2d = c->act_h2d;
+  out->act_d2h = c->act_d2h;
+  out->w_h2d = c->w_h2d;
+  out->g_d2h = c->g_d2h;
   return RP_OK;
 }
 

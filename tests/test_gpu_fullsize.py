@@ -183,7 +183,6 @@ def test_llama3_8b_lmhead_full(env):
     wk.add_lmhead(w)
     dx = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
     loss = torch.zeros(1, dtype=torch.float32, device=DEV)
-    torch.cuda.synchronize()  # torch's fill is on another stream than the library's
     ws = wk.ctx.workspace(B.RP_OP_LMHEAD, cfg.batch, cfg.seq)
     wk.ctx.lmhead_ce_fwd_bwd(cfg.batch, cfg.seq, x.to(DEV), labels.to(DEV), loss, dx, ws)
     wk.ctx.sync()

@@ -46,7 +46,6 @@ def test_tiny_full_model_fp32_matches_oracle(W):
     dy = torch.empty(T, H, device=DEV)
     dx0 = torch.empty(T, H, device=DEV)
     loss = torch.zeros(1, device=DEV)
-    torch.cuda.synchronize()  # torch's fill is on another stream than the library's
     dtable = torch.empty(cfg.vocab, H, device=DEV)
     ws = wk.ctx.workspace(B_OP_FUSED(), cfg.batch, cfg.seq, 2)
     wsh = wk.ctx.workspace(B_OP_LMHEAD(), cfg.batch, cfg.seq)
@@ -135,7 +134,6 @@ def test_bf16_lmhead_sharded_matches_oracle(W, seq, vocab, shards):
     T, H = cfg.tokens, cfg.hidden
     dx = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
     loss = torch.zeros(1, device=DEV)
-    torch.cuda.synchronize()  # torch's fill is on another stream than the library's
     ws = wk.ctx.workspace(B_OP_LMHEAD(), cfg.batch, cfg.seq)
     wk.ctx.lmhead_ce_fwd_bwd(cfg.batch, cfg.seq, x.to(DEV), labels.to(DEV), loss, dx, ws)
     wk.ctx.sync()
@@ -164,7 +162,6 @@ def test_f32_lmhead_ragged_shards_matches_oracle(W, vocab, shards):
     T, H = cfg.tokens, cfg.hidden
     dx = torch.empty(T, H, dtype=torch.float32, device=DEV)
     loss = torch.zeros(1, device=DEV)
-    torch.cuda.synchronize()  # torch's fill is on another stream than the library's
     ws = wk.ctx.workspace(B_OP_LMHEAD(), cfg.batch, cfg.seq)
     wk.ctx.lmhead_ce_fwd_bwd(cfg.batch, cfg.seq, x.to(DEV), labels.to(DEV), loss, dx, ws)
     wk.ctx.sync()

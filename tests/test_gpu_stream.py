@@ -229,3 +229,39 @@ def test_error_paths(env):
         wk.ctx.stage_fwd(0, 1, b, s, x, x, ws)  # output aliases input
     assert e.value.status == B.RP_ERR_INVALID
     wk.ctx.sync()
+
+
+@pytest.mark.parametrize("side", [False, True])
+def test_calls_ordered_after_torch_stream(env, side):
+    """torch writes a stage call's input late on its current stream (a bounded
+    sleep kernel ahead of the write), and the call follows with no
+    synchronisation in between: it must read the written values. On the
+    default stream the library's blocking streams give the order (and torch's
+    next default-stream write waits for the call's reads); on another stream
+    the binding's event does."""
+    B, Worker = env
+    say("stream order", "side stream" if side else "default stream")
+    cfg = _small_cfg()
+    wk = Worker(cfg)
+    wk.add_layer(0, synth.layer_weights(cfg, 0, gamma="perturbed"))
+    ctx = wk.ctx
+    T, H, b, s = cfg.tokens, cfg.hidden, cfg.batch, cfg.seq
+    x_val = synth.activation(cfg, "x").to(DEV)
+    ws = ctx.workspace(B.RP_OP_STAGE_FWD, b, s, 1)
+    y_ref = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+    torch.cuda.synchronize()
+    ctx.stage_fwd(0, 1, b, s, x_val, y_ref, ws)
+    ctx.sync()
+    x = torch.zeros_like(x_val)
+    y = torch.zeros_like(y_ref)
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream() if side else torch.cuda.default_stream()
+    with torch.cuda.stream(st):
+        torch.cuda._sleep(50_000_000)  # tens of milliseconds
+        x.copy_(x_val)
+        ctx.stage_fwd(0, 1, b, s, x, y, ws)
+        if not side:
+            x.zero_()  # waits for the call's reads of x
+    ctx.sync()
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
