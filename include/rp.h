@@ -530,6 +530,19 @@ rp_status rp_op_attn_bwd(rp_ctx* ctx, int batch, int seq, const void* qkv, const
                          const void* dout, const float* lse, void* dqkv, void* ws,
                          size_t ws_bytes);
 
+/* rp_op_attn_bwd without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). The per-row terms D = rowsum(dO * O) that the
+ * workspace holds go to a fixed device array of the library instead:
+ * 2^21 fp32 (8 MiB) on each GPU the library runs on, held until the process
+ * ends, so n_q * batch * seq <= 2^21 (RP_ERR_UNSUPPORTED above that). Nothing
+ * is allocated. The array is shared by every call on the GPU and keeps the
+ * last call's contents; each call writes every entry it reads, so it needs no
+ * clearing, but calls that overlap on one GPU (other streams or contexts)
+ * race on it. Arguments and results otherwise as rp_op_attn_bwd. */
+rp_status rp_op_attn_bwd_noalloc(rp_ctx* ctx, int batch, int seq, const void* qkv, const void* o,
+                                 const void* dout, const float* lse, void* dqkv);
+
 /* MoE routing alone, for checking its integer outputs bit for bit (the
  * top-k expert selection of the paperlayer.ai summary, appendix C.2, which
  * activates E_act of E_total experts per token; the grouped order is the

@@ -113,6 +113,7 @@ _SIGS = {
     "rp_op_copy": (C.c_int, [_P, _P, _P, C.c_size_t]),
     "rp_op_transpose_bf16": (C.c_int, [_P, C.c_int, C.c_int, _P, C.c_int64, _P, C.c_int64]),
     "rp_op_attn_bwd": (C.c_int, [_P, C.c_int, C.c_int, _P, _P, _P, _P, _P, _P, C.c_size_t]),
+    "rp_op_attn_bwd_noalloc": (C.c_int, [_P, C.c_int, C.c_int, _P, _P, _P, _P, _P]),
     "rp_op_moe_route": (C.c_int, [_P, C.c_int, C.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t]),
     "rp_trace_begin": (C.c_int, [_P, C.c_int]),
     "rp_trace_end": (C.c_int, [_P]),
@@ -454,6 +455,11 @@ class Context:
         self._order()
         check(lib().rp_op_attn_fwd(self.h, batch, seq, ptr(qkv), ptr(o), ptr(lse)))
         self._hold(qkv, o, lse)
+
+    def op_attn_bwd_noalloc(self, batch, seq, qkv, o, dout, lse, dqkv):
+        self._order()
+        check(lib().rp_op_attn_bwd_noalloc(self.h, batch, seq, ptr(qkv), ptr(o), ptr(dout), ptr(lse), ptr(dqkv)))
+        self._hold(qkv, o, dout, lse, dqkv)
 
     def op_moe_route(self, batch, seq, logits, idx, wgt, cnt, off, perm_row, perm_w, inv, ws):
         self._order()

@@ -10,12 +10,21 @@
 // This file holds the reference-grade kernels (one wavefront per query row,
 // lanes over the head dimension), used for fp32 and for head_dim 64, and the
 // MFMA flash kernels for bf16 with head_dim 128 (attn_flash.hip).
+#include <mutex>
+#include <vector>
+
 #include "ops.h"
 #include "attn_flash.h"
 #include "trace.h"
 
 namespace rp {
 namespace {
+
+// The allocation-free backward's per-row softmax terms D = rowsum(dO * O):
+// one fixed array per GPU, held until the process ends. In host code this
+// name is a host-side stand-in, never a device address: kernels get the
+// address that attn_scratch() looked up for the device.
+static __device__ __align__(256) float scratch[kAttnScratchFloats];
 
 // causal (query, key) pairs of all batch rows
 double causal_pairs(const AttnDesc& a) { return (double)a.batch * a.seq * (a.seq + 1.0) / 2.0; }
@@ -215,5 +224,27 @@ rp_status attn_bwd(const AttnDesc& a, const void* qkv, const void* o, const void
 }
 
 size_t attn_bwd_ws_bytes(const AttnDesc& a) { return (size_t)a.n_q * a.batch * a.seq * sizeof(float); }
+
+rp_status attn_scratch(int device, float** out) {
+  static std::mutex mu;
+  static std::vector<float*> addr;  // per device, looked up once with that device current
+  std::lock_guard<std::mutex> lock(mu);
+  if (device < 0) {
+    set_error("attention scratch: bad device %d", device);
+    return RP_ERR_INVALID;
+  }
+  if ((size_t)device >= addr.size()) addr.resize(device + 1, nullptr);
+  if (!addr[device]) {
+    int cur = 0;
+    RP_HIP(hipGetDevice(&cur));
+    RP_CHECK(cur == device, RP_ERR_STATE, "attention scratch: device %d is not current (%d is)", device, cur);
+    void* p = nullptr;
+    RP_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    RP_CHECK(p != nullptr, RP_ERR_HIP, "attention scratch: no device address");
+    addr[device] = (float*)p;
+  }
+  *out = addr[device];
+  return RP_OK;
+}
 
 }  // namespace rp

@@ -178,6 +178,15 @@ rp_status rp_ctx_create(int device, const rp_layer_cfg* cfg, const rp_streams* s
     }
     x->owned.push_back(*ps);
   }
+  {
+    // the allocation-free attention backward's scratch: its address on this
+    // device, with the device current
+    rp_status st = attn_scratch(device, &x->attn_scratch);
+    if (st != RP_OK) {
+      (void)rp_ctx_destroy(x);
+      return st;
+    }
+  }
   x->layers.resize(kMaxLayers);  // fixed: deferred transfers keep pointers into it
   *out = x;
   return RP_OK;
@@ -427,6 +436,20 @@ rp_status rp_op_attn_bwd(rp_ctx* c, int batch, int seq, const void* qkv, const v
   a.dt = c->sh.dt; a.batch = batch; a.seq = seq; a.n_q = c->sh.nq; a.n_kv = c->sh.nkv; a.d = c->sh.d;
   RP_CHECK(ws_bytes >= attn_bwd_ws_bytes(a), RP_ERR_WORKSPACE, "op_attn_bwd: workspace too small");
   return attn_bwd(a, qkv, o, dout, lse, (float*)ws, dqkv, c->compute);
+}
+
+rp_status rp_op_attn_bwd_noalloc(rp_ctx* c, int batch, int seq, const void* qkv, const void* o, const void* dout,
+                                 const float* lse, void* dqkv) {
+  CTX_ENTER(c);
+  RP_CHECK(batch >= 1 && seq >= 1 && qkv && o && dout && lse && dqkv, RP_ERR_INVALID,
+           "op_attn_bwd_noalloc: bad arguments");
+  AttnDesc a;
+  a.dt = c->sh.dt; a.batch = batch; a.seq = seq; a.n_q = c->sh.nq; a.n_kv = c->sh.nkv; a.d = c->sh.d;
+  RP_CHECK(attn_bwd_ws_bytes(a) <= kAttnScratchFloats * sizeof(float), RP_ERR_UNSUPPORTED,
+           "op_attn_bwd_noalloc: n_q * batch * seq = %lld exceeds the fixed scratch of %zu rows",
+           (long long)a.n_q * batch * seq, kAttnScratchFloats);
+  RP_CHECK(c->attn_scratch != nullptr, RP_ERR_STATE, "op_attn_bwd_noalloc: no scratch address");
+  return attn_bwd(a, qkv, o, dout, lse, c->attn_scratch, dqkv, c->compute);
 }
 
 rp_status rp_op_moe_route(rp_ctx* c, int batch, int seq, const float* logits, int32_t* idx, float* wgt,

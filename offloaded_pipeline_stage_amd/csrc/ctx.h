@@ -86,6 +86,8 @@ struct rp_ctx {
   rp_layer_cfg cfg{};
   rp::Shape sh{};
   hipStream_t compute = nullptr, act_h2d = nullptr, act_d2h = nullptr, w_h2d = nullptr, g_d2h = nullptr;
+  // the device's fixed scratch of rp_op_attn_bwd_noalloc (looked up at creation)
+  float* attn_scratch = nullptr;
   // transfer streams the context created (each on a hardware queue of its own)
   std::vector<hipStream_t> owned;
   std::vector<rp::LayerBinding> layers;   // indexed by layer id

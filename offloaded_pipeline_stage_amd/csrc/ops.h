@@ -137,6 +137,11 @@ rp_status attn_fwd(const AttnDesc& a, const void* qkv, void* o, float* lse, hipS
 rp_status attn_bwd(const AttnDesc& a, const void* qkv, const void* o, const void* dout,
                    const float* lse, float* Dbuf, void* dqkv, hipStream_t s);
 size_t attn_bwd_ws_bytes(const AttnDesc& a);
+// the allocation-free backward's fixed scratch: kAttnScratchFloats fp32 per
+// GPU (8 MiB: n_q * batch * seq <= 2^21); its device address for `device`,
+// which must be current on the first call for that device
+constexpr size_t kAttnScratchFloats = size_t(1) << 21;
+rp_status attn_scratch(int device, float** out);
 
 // ---------------------------------------------------------------------------
 // cross-entropy over vocabulary shards
