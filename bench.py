@@ -620,6 +620,8 @@ def main():
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--no-streamed", action="store_true",
                     help="skip the weight-streaming step (run by default, reported under 'streamed')")
+    ap.add_argument("--streamed-only", action="store_true",
+                    help="run only the streamed step with fp32 gradients (for copy traces); prints its figures")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-head-rows", type=int, default=1024,
                     help="token rows of the LM head in the CPU oracle's timed sample")
@@ -645,6 +647,12 @@ def main():
 
     cfg = synth.config(a.workload)
     traffic_file = os.path.join(ROOT, "profiles", f"{a.workload}_step_traffic.txt")
+    if a.streamed_only:
+        st = Step(cfg, streamed=True)
+        ms_s = time_steps(st, a.steps, a.warmup)
+        print(json.dumps({"streamed_only": {"ms_per_step": round(ms_s, 3), "steps": a.steps, "warmup": a.warmup,
+                                            "tokens_per_s": round(cfg.tokens / (ms_s / 1e3), 1)}}), flush=True)
+        return
     step = Step(cfg, streamed=False)
     if a.copy_calibration_mib > 0:
         copy_calibration(step.wk.ctx, a.copy_calibration_mib)

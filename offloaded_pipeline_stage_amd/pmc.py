@@ -164,7 +164,105 @@ def traffic_for(path: str, kernel: str) -> float | None:
     return t["fetch_bytes"] + t["write_bytes"]
 
 
+# ---------------------------------------------------------------------------
+# utilisation counters (MFMA, LDS, waits, L2) per kernel and launch shape
+# ---------------------------------------------------------------------------
+
+SIMDS = 1024  # MI355X: 256 CUs x 4 SIMDs
+XCDS = 8      # GRBM_GUI_ACTIVE comes summed over the 8 XCDs' instances
+
+
+def _counter_rows(dirs):
+    """{(kernel, grid size): {counter: [value per dispatch]}} and durations (ns)
+    over every counter_collection.csv under `dirs` (one pass each)."""
+    vals = defaultdict(lambda: defaultdict(list))
+    durs = defaultdict(dict)
+    meta = {}
+    for d in dirs:
+        with open(_find_csv(d)) as f:
+            for r in csv.DictReader(f):
+                key = (norm_name(r["Kernel_Name"]), int(r["Grid_Size"]))
+                vals[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                durs[key][(d, r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                meta[key] = (int(r["VGPR_Count"]), int(r["Accum_VGPR_Count"]), int(r["LDS_Block_Size"]))
+    return vals, durs, meta
+
+
+def derived(c: dict, dur_ns: float) -> dict:
+    """Ratios from one kernel's mean counter values per dispatch."""
+    g = lambda n: c.get(n)  # noqa: E731
+    out = {}
+    if g("SQ_VALU_MFMA_BUSY_CYCLES") is not None and g("GRBM_GUI_ACTIVE"):
+        out["mfma_busy"] = g("SQ_VALU_MFMA_BUSY_CYCLES") / (g("GRBM_GUI_ACTIVE") / XCDS * SIMDS)
+    if g("SQ_INSTS_VALU_MFMA_MOPS_BF16") is not None and dur_ns > 0:
+        out["mfma_bf16_tflops"] = g("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512 / dur_ns / 1e3
+    if g("SQ_WAVE_CYCLES"):
+        for n, k in (("SQ_WAIT_INST_ANY", "wait_inst_frac"), ("SQ_WAIT_ANY", "wait_any_frac"),
+                     ("SQ_ACTIVE_INST_ANY", "active_inst_frac"), ("SQ_ACTIVE_INST_VALU", "valu_frac"),
+                     ("SQ_ACTIVE_INST_LDS", "lds_frac"), ("SQ_ACTIVE_INST_VMEM", "vmem_frac"),
+                     ("SQ_WAIT_INST_LDS", "wait_lds_frac")):
+            if g(n) is not None:
+                out[k] = g(n) / g("SQ_WAVE_CYCLES")
+    if g("SQ_LDS_BANK_CONFLICT") is not None and g("SQ_LDS_IDX_ACTIVE"):
+        out["lds_bank_conflict_frac"] = g("SQ_LDS_BANK_CONFLICT") / g("SQ_LDS_IDX_ACTIVE")
+    if g("SQ_LDS_IDX_ACTIVE") is not None and g("GRBM_GUI_ACTIVE"):
+        out["lds_busy"] = g("SQ_LDS_IDX_ACTIVE") / (g("GRBM_GUI_ACTIVE") / XCDS * 256)
+    h, m = g("TCC_HIT_sum"), g("TCC_MISS_sum")
+    if h is not None and m is not None and h + m > 0:
+        out["l2_hit"] = h / (h + m)
+    return out
+
+
+def summarize_counters(dirs, title: str, commands, min_us: float = 20.0) -> str:
+    """Text summary: per (kernel, grid size) with a mean duration of at least
+    min_us, the mean of every counter per dispatch and the derived ratios."""
+    vals, durs, meta = _counter_rows(dirs)
+    table = {}
+    for key, cs in vals.items():
+        dur = sum(durs[key].values()) / len(durs[key])
+        if dur < min_us * 1e3:
+            continue
+        mean = {n: sum(v) / len(v) for n, v in cs.items()}
+        name, grid = key
+        src = kernel_source(base_name(name))
+        table[f"{name} grid={grid}"] = {
+            "launches": max(len(v) for v in cs.values()), "mean_us": dur / 1e3, "vgpr": meta[key][0],
+            "agpr": meta[key][1], "lds_bytes": meta[key][2], "counters": mean, "derived": derived(mean, dur),
+            "source": os.path.basename(src) if src else None, "source_sha": source_hash(src) if src else None}
+    lines = [f"# {title}", ""]
+    lines += [f"command: {c}" for c in commands]
+    cols = ("mfma_busy", "mfma_bf16_tflops", "wait_inst_frac", "valu_frac", "lds_frac", "vmem_frac",
+            "lds_bank_conflict_frac", "lds_busy", "l2_hit")
+    lines += ["", "mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); mfma_bf16_tflops = "
+              "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / duration; *_frac of SQ_WAVE_CYCLES; lds_bank_conflict_frac = "
+              "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; lds_busy = SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE / 8 x 256 CUs); "
+              "l2_hit = TCC_HIT / (TCC_HIT + TCC_MISS). Durations are from the counter runs (dispatches serialised).",
+              "", f"{'launch':>6} {'us':>8} {'vgpr':>4} {'agpr':>4} " + " ".join(f"{c[:11]:>11}" for c in cols)
+              + "  kernel"]
+    for n, t in sorted(table.items(), key=lambda kv: -kv[1]["mean_us"] * kv[1]["launches"]):
+        dv = t["derived"]
+        cells = " ".join(f"{dv[c]:11.3f}" if c in dv else f"{'-':>11}" for c in cols)
+        lines.append(f"{t['launches']:6d} {t['mean_us']:8.1f} {t['vgpr']:4d} {t['agpr']:4d} {cells}  {n}")
+    lines += ["", "counters_json: " + json.dumps(table, sort_keys=True)]
+    return "\n".join(lines) + "\n"
+
+
 if __name__ == "__main__":
+    import sys
+    if len(sys.argv) > 1 and sys.argv[1] == "counters":
+        import argparse
+        ap = argparse.ArgumentParser(description="summarise utilisation counter runs")
+        ap.add_argument("mode")
+        ap.add_argument("dirs", nargs="+")
+        ap.add_argument("--title", required=True)
+        ap.add_argument("--command", action="append", default=[])
+        ap.add_argument("--out", required=True)
+        a = ap.parse_args()
+        txt = summarize_counters(a.dirs, a.title, a.command)
+        with open(a.out, "w") as f:
+            f.write(txt)
+        print(txt)
+        sys.exit(0)
     import argparse
     ap = argparse.ArgumentParser(description="summarise FETCH_SIZE / WRITE_SIZE counter runs")
     ap.add_argument("fetch_dir")
