@@ -9,7 +9,7 @@
 #include <cstdio>
 #include <string>
 
-#include "../../include/rp.h"
+#include "rp.h"
 
 namespace rp {
 

@@ -2,7 +2,11 @@
 section 3.2 stage structure, section 4.4 profiling and partitioning): every
 partition -- one fused stage, one layer per stage, hand-picked splits and the
 partitioner's own choice from profiled layer times -- gives bit-identical loss
-and gradients, and they match the oracle's end-to-end fp64 model."""
+and gradients, and they match the oracle's end-to-end fp64 model. Two
+models: the tiny fp32 decoder, and a bf16 Qwen3-1.7B-shaped decoder (hidden
+2048, 16 / 8 heads of 128, FFN 6144, 4 layers, embedding, final norm and a
+2-shard LM head over 16384 tokens of vocabulary, 2 x 1024 tokens) whose
+checkpoints go through pinned host memory between its stages."""
 import pytest
 import torch
 
@@ -11,6 +15,7 @@ from _helpers import GRAD_TOL, LOSS_TOL, ensure_built, max_rel, say
 from oracle import stage as O
 
 pytestmark = pytest.mark.gpu
+MODEL_GRAD_TOL = {"f32": GRAD_TOL["f32"], "bf16": 3e-2}
 DEV = torch.device("cuda")
 N_LAYERS = 6
 
@@ -31,11 +36,21 @@ def _same(a, b):
     return len(a) == len(b) and all(_same(x, y) for x, y in zip(a, b))
 
 
-def test_partitions_bit_identical_and_match_oracle():
+MODELS = {
+    "tiny_f32": (lambda: synth.config("tiny"), 6, "f32"),
+    "qwen3_1p7b_bf16": (lambda: synth.config("qwen3_1p7b", batch=2, seq=1024, vocab=16384, n_shards=2,
+                                             final_norm=True, embedding=True), 4, "bf16"),
+}
+
+
+@pytest.mark.parametrize("model", list(MODELS))
+def test_partitions_bit_identical_and_match_oracle(model):
     ensure_built()
     from offloaded_pipeline_stage_amd.model import Partition, RoundPipeModel
-    cfg = synth.config("tiny")
-    layers = [synth.layer_weights(cfg, l, gamma="perturbed") for l in range(N_LAYERS)]
+    make, n_layers, prec = MODELS[model]
+    cfg = make()
+    say("model", model)
+    layers = [synth.layer_weights(cfg, l, gamma="perturbed") for l in range(n_layers)]
     head = synth.lmhead_weights(cfg)
     ids = synth.token_ids(cfg)
     labels = synth.shifted_labels(ids).reshape(-1)
@@ -48,8 +63,12 @@ def test_partitions_bit_identical_and_match_oracle():
     assert all(x > 0 for x in f + bw) and h >= 0
     _, planned = m.plan(f, bw, h, n_micro=8, n_gpus=4, mem_cap=1e15)
     say("planned", planned)
-    parts = [Partition.fused(N_LAYERS), Partition.one_layer_per_stage(N_LAYERS),
-             Partition((2, 2), 2, (3, 1)), Partition((1, 3), 2, (1, 1, 2)), planned]
+    parts = [Partition.fused(n_layers), Partition.one_layer_per_stage(n_layers)]
+    if n_layers == 6:
+        parts += [Partition((2, 2), 2, (3, 1)), Partition((1, 3), 2, (1, 1, 2))]
+    else:
+        parts += [Partition((2,), 2, (1, 1)), Partition((1, 2), 1, (2, 1))]
+    parts.append(planned)
     results = []
     for p in parts:
         say("partition", p)
@@ -61,15 +80,26 @@ def test_partitions_bit_identical_and_match_oracle():
     for p, rep, r in results[1:]:
         for k in ref:
             assert _same(r[k], ref[k]), f"partition {p} pass {rep}: {k} differs from the fused stage"
-
-    loss_ref, g_ref = O.full_model_fwd_bwd(ids, labels, layers, head, cfg)
-    tol = GRAD_TOL["f32"]
-    assert abs(ref["loss"].item() - loss_ref.item()) / abs(loss_ref.item()) < LOSS_TOL["f32"]
-    assert max_rel(ref["dtable"], g_ref["embed"]) < tol
-    assert max_rel(ref["dw"][0], g_ref["w"]) < tol
-    assert max_rel(ref["dgamma_f"], g_ref["gamma_f"]) < tol
-    for l in range(N_LAYERS):
-        for n, r in g_ref["layers"][l].items():
-            e = max_rel(ref[f"layer{l}"][n], r)
-            assert e < tol, (l, n, e)
     m.close()
+
+    say("oracle")
+    loss_ref, g_ref = O.full_model_fwd_bwd(ids, labels, layers, head, cfg)
+    # the per-stage bar holds for each stage against the oracle on the same
+    # inputs; end to end the bf16 path stores every activation between stages
+    # (and between kernels) in bf16 while the oracle carries one fp64 forward
+    # through all layers, and the weight gradients of the layers above drift
+    # with those inputs (about 1-2.2e-2 on this 4-layer model, uniformly over
+    # layers and tensors), so the whole-model comparison allows 3e-2
+    tol = MODEL_GRAD_TOL[prec]
+    e = abs(ref["loss"].item() - loss_ref.item()) / abs(loss_ref.item())
+    say(f"loss rel {e:.2e}")
+    assert e < LOSS_TOL[prec]
+    assert max_rel(ref["dtable"], g_ref["embed"]) < tol
+    dw = torch.cat([t.cpu() for t in ref["dw"]], dim=0)
+    assert max_rel(dw, g_ref["w"]) < tol
+    assert max_rel(ref["dgamma_f"], g_ref["gamma_f"]) < tol
+    errs = {(l, n): max_rel(ref[f"layer{l}"][n], r) for l in range(n_layers) for n, r in g_ref["layers"][l].items()}
+    for l in range(n_layers):
+        say(f"layer {l}:", " ".join(f"{n} {errs[(l, n)]:.2e}" for n in g_ref["layers"][l]))
+    for (l, n), e in errs.items():
+        assert e < tol, (l, n, e)
