@@ -58,6 +58,8 @@ struct GemmParams {
   const int* g_rows;      // gathered A: operand row of each grouped row
   const float* row_scale; // [rows] per-row factor of the epilogue (or null)
   int64_t b_stride;       // elements between consecutive experts' B
+  const float2* rope_tab; // EPI_ROPE: (cos, sin) of position p, pair i at [p * 64 + i]
+  int rope_seq, rope_heads;
 };
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 7); }
@@ -105,13 +107,18 @@ template <> struct Lay<false> {
 enum RowMode {
   ROWS_CONTIG = 0,  // tile row r is operand row row0 + r
   ROWS_SWIGLU = 1,  // gate/up interleave (see LoaderK)
-  ROWS_GATHER = 2   // tile row r is operand row rows[row0 + r] (rows past nrows read as zeros)
+  ROWS_GATHER = 2,  // tile row r is operand row rows[row0 + r] (rows past nrows read as zeros)
+  ROWS_ROPE = 3     // rotation pairs: see LoaderK
 };
 
 // K-major operand: element (r, k) at g[r * ld + k]; R rows per tile, NT
 // threads. ROWS_SWIGLU: tile row r of wave column w = r / wn_span holds gate
 // row f (first half of the span) or up row F + f (second half), so one lane
 // ends up with the gate and up pre-activations of the same output column.
+// ROWS_ROPE (64-row wave spans, heads of 128 rows): wave column w covers dims
+// 32 (w % 2) + [0, 32) of head w / 2 of the tile in the first half of its
+// span and the same dims + 64 in the second, so one lane holds both members
+// of every rotation pair; rows at or past F (the product's N) read as zeros.
 template <int R, int MODE, int NT>
 struct LoaderK {
   static_assert(R * 8 % NT == 0, "tile rows x 8 chunks must split evenly over the threads");
@@ -125,7 +132,15 @@ struct LoaderK {
                                        int nrows = 0) {
     kcol = (tid & 7) * 8;
     rstride = (uint32_t)((NT / 8) * ld * 2);
-    if constexpr (MODE == ROWS_SWIGLU) {
+    if constexpr (MODE == ROWS_ROPE) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int r = (tid >> 3) + i * (NT / 8);
+        const int w = r / wn_span, j = r % wn_span;
+        const int grow = row0 + (w >> 1) * 128 + (w & 1) * 32 + (j & 31) + (j >> 5) * 64;
+        voff[i] = grow < F ? (uint32_t)(((int64_t)grow * ld + (tid & 7) * 8) * 2) : OOB_SHIFT;
+      }
+    } else if constexpr (MODE == ROWS_SWIGLU) {
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
         const int r = (tid >> 3) + i * (NT / 8);
@@ -287,11 +302,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(GemmParams p)
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B, p.b_bytes);
   constexpr int AMODE = GRP == 2 ? ROWS_GATHER : ROWS_CONTIG;
   std::conditional_t<AK, LoaderK<BM, AMODE, NT>, LoaderM<BM, NT>> la;
-  std::conditional_t<BKM, LoaderK<BN, SW ? ROWS_SWIGLU : ROWS_CONTIG, NT>, LoaderM<BN, NT>> lb;
+  constexpr bool RO = (EPI == EPI_ROPE);
+  static_assert(!RO || (BKM && WN == 64 && !OUT_F32 && GRP == 0), "RoPE epilogue: K-major B, 64-column waves");
+  std::conditional_t<BKM, LoaderK<BN, SW ? ROWS_SWIGLU : (RO ? ROWS_ROPE : ROWS_CONTIG), NT>, LoaderM<BN, NT>> lb;
   static_assert(GRP != 2 || AK, "gathered rows need a K-major A");
   if constexpr (AK) la.init(p.lda, m0, tid, 0, 1, p.g_rows, p.M);
   else la.init(p.lda, m0, tid);
-  if constexpr (BKM) lb.init(p.ldb, n0, tid, p.F, WN);
+  if constexpr (BKM) lb.init(p.ldb, n0, tid, RO ? p.N : p.F, WN);
   else lb.init(p.ldb, n0, tid);
 
   // k range of this split (the whole K unless the product is split along K)
@@ -410,7 +427,37 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(GemmParams p)
   // --- epilogue: lane holds column (lane & 31) of each 32x32 tile, rows
   // 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15
   const int lc = lane & 31, lr = (lane >> 5) * 4;
-  if constexpr (EPI == EPI_SWIGLU) {
+  if constexpr (EPI == EPI_ROPE) {
+    // lane column lc: dim dl of head `head` in acc[i][0], dim dl + 64 in acc[i][1]
+    bf16* c = reinterpret_cast<bf16*>(p.C);
+    const int head = (n0 >> 7) + (wn >> 1);
+    const int dl = (wn & 1) * 32 + lc;
+    const int col = head * 128 + dl;
+    if (col < p.N) {
+      const bool rot = head < p.rope_heads;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + lr + (r & 3);
+          if (m >= p.M) continue;
+          float lo = acc[i][0][r], hi = acc[i][1][r];
+          if (p.R) {  // an addend of the same layout (the LoRA deltas), before the rotation
+            const bf16* rr = reinterpret_cast<const bf16*>(p.R) + (int64_t)m * p.ldr + col;
+            lo += to_f(rr[0]);
+            hi += to_f(rr[64]);
+          }
+          if (rot) {
+            const float2 cs = p.rope_tab[(m % p.rope_seq) * 64 + dl];
+            const float l2 = lo * cs.x - hi * cs.y;
+            hi = hi * cs.x + lo * cs.y;
+            lo = l2;
+          }
+          c[(int64_t)m * p.ldc + col] = to_bf16(lo);
+          c[(int64_t)m * p.ldc + col + 64] = to_bf16(hi);
+        }
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
     bf16* gu = reinterpret_cast<bf16*>(p.C);
     bf16* mo = reinterpret_cast<bf16*>(p.C2);
 #pragma unroll
@@ -600,6 +647,9 @@ rp_status launch_mfma(const GemmDesc& d, hipStream_t s) {
   p.tiles_m = (int)cdiv(d.M, BM);
   p.tiles_n = EPI == EPI_SWIGLU ? (int)cdiv(d.N / 2, BN / 2) : (int)cdiv(d.N, BN);
   p.row_scale = d.row_scale;
+  p.rope_tab = d.rope_tab;
+  p.rope_seq = d.rope_seq;
+  p.rope_heads = d.rope_heads;
   uint64_t ab = operand_bytes(AK, d.M, d.K, d.lda), bb = operand_bytes(BKM, d.N, d.K, d.ldb);
   if constexpr (GRP != 0) {
     const GemmGroup& g = *d.group;
@@ -660,6 +710,11 @@ rp_status dispatch_epi(const GemmDesc& d, hipStream_t s) {
     case EPI_SWIGLU_BWD:
       RP_CHECK(!of32, RP_ERR_UNSUPPORTED, "swiglu bwd epilogue: bf16 only");
       return dispatch_layout<BM, BN, WGM, WGN, EPI_SWIGLU_BWD, false>(d, s);
+    case EPI_ROPE:
+      RP_CHECK(!of32 && d.a_kmajor && d.b_kmajor, RP_ERR_UNSUPPORTED, "rope epilogue: K-major bf16 only");
+      if constexpr (BN / WGN == 64) return launch_mfma<BM, BN, WGM, WGN, true, true, EPI_ROPE, false>(d, s);
+      set_error("rope epilogue: needs 64-column wave tiles");
+      return RP_ERR_UNSUPPORTED;
   }
   set_error("gemm: unknown epilogue %d", d.epi);
   return RP_ERR_INVALID;
@@ -686,6 +741,11 @@ rp_status gemm_validate(const GemmDesc& d) {
   }
   if (d.epi == EPI_RESID || d.epi == EPI_SWIGLU_BWD) RP_CHECK(d.R, RP_ERR_INVALID, "gemm: missing R");
   if (d.epi == EPI_SWIGLU) RP_CHECK(d.C2, RP_ERR_INVALID, "gemm: missing C2");
+  if (d.epi == EPI_ROPE)
+    RP_CHECK(d.in_dtype == RP_DTYPE_BF16 && d.out_dtype == RP_DTYPE_BF16 && !d.force_simple && d.a_kmajor &&
+                 d.b_kmajor && d.rope_tab && d.rope_seq > 0 && d.N % 128 == 0 && d.rope_heads >= 0 &&
+                 d.split_k <= 1 && !d.accumulate && d.alpha == 1.f,
+             RP_ERR_UNSUPPORTED, "gemm: the RoPE epilogue needs bf16 K-major operands, heads of 128 and the table");
   RP_CHECK(!d.accumulate || d.out_dtype == RP_DTYPE_F32, RP_ERR_INVALID,
            "gemm: accumulation needs an fp32 output");
   if (d.split_k > 1)

@@ -13,7 +13,12 @@ enum Epi {
   EPI_RESID = 1,      // C = acc + R (out dtype; R same dtype as C)
   EPI_SWIGLU = 2,     // B rows [0,F) gate, [F,2F) up: C = gu [M, 2F] pre-activations,
                       // C2 = silu(g) * u [M, F]; N passed = 2F
-  EPI_SWIGLU_BWD = 3  // acc = dm [M, F]; R = gu [M, 2F]; C = dgu [M, 2F]
+  EPI_SWIGLU_BWD = 3, // acc = dm [M, F]; R = gu [M, 2F]; C = dgu [M, 2F]
+  EPI_ROPE = 4        // the packed q|k|v product with RoPE: columns are heads of
+                      // 128; an optional R (same layout, bf16) is added, then
+                      // heads < rope_heads are rotated (pairs i, i + 64 by the
+                      // angle of position m % rope_seq) before the one bf16
+                      // rounding; the others are stored as they are
 };
 
 // Grouped product: one GEMM per expert over that expert's rows, in one launch.
@@ -56,6 +61,8 @@ struct GemmDesc {
   int split_k = 1;
   float* partial = nullptr; size_t partial_bytes = 0;
   const float* row_scale = nullptr;  // per-row factor applied in the epilogue (grouped rows)
+  const float2* rope_tab = nullptr;  // EPI_ROPE: (cos, sin) [rope_seq][64]
+  int rope_seq = 0, rope_heads = 0;
   const GemmGroup* group = nullptr;  // gemm_grouped only
 };
 

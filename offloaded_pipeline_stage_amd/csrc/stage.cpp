@@ -70,10 +70,15 @@ struct Layout {
   float2* rope = nullptr;
   LoraBf16 lw;
   void* ye = nullptr;     // MoE: expert outputs [T k, H] (grouped rows)
+  void* lora_d = nullptr; // LoRA with the rotation fused: us_x B_x^T for q|k|v [T, QKV]
   std::vector<Acts> acts;
   void* xb[2] = {nullptr, nullptr};
   BwdTmp bt;
 };
+
+// whether the QKV product applies RoPE in its epilogue: bf16 heads of 128 and
+// no QK-norm between the product and the rotation
+bool fused_rope(const Shape& s) { return s.dt == RP_DTYPE_BF16 && s.d == 128 && !s.qkn; }
 
 void carve_acts(Bump& bp, const Shape& s, int64_t T, Acts& A) {
   A.x = bp.take(T * s.H * s.es);
@@ -131,6 +136,7 @@ void carve(Bump& bp, const Shape& s, int64_t T, int seq, int n_layers, bool keep
   L.acts.assign(keep ? n_layers : 1, Acts{});
   for (auto& a : L.acts) carve_acts(bp, s, T, a);
   if (s.E > 0) L.ye = bp.take(T * s.topk * s.H * s.es);
+  if (s.r > 0 && fused_rope(s)) L.lora_d = bp.take(T * s.QKV * s.es);
   if (fwd_pp) {
     L.xb[0] = bp.take(T * s.H * s.es);
     L.xb[1] = bp.take(T * s.H * s.es);
@@ -227,7 +233,8 @@ GemmDesc mk(int M, int N, int K, const void* A, int64_t lda, bool ak, const void
 // backward) the down projection is skipped: the backward reads the layer's
 // internals, never its output. LoRA layers add s (x A^T) B^T to the q, k, v
 // and o projections (s = alpha / r), in place on the bf16 projection output.
-rp_status layer_fwd(rp_ctx* c, const LayerBinding& lb, const LoraBf16& lw, void* ye, const float* router, int T,
+rp_status layer_fwd(rp_ctx* c, const LayerBinding& lb, const LoraBf16& lw, void* ye, void* lora_d,
+                     const float* router, int T,
                     int seq, const void* x, const Acts& A, void* y, const float2* rope, hipStream_t st,
                     const std::function<rp_status()>& after_qkv = {}) {
   const Shape& s = c->sh;
@@ -237,14 +244,40 @@ rp_status layer_fwd(rp_ctx* c, const LayerBinding& lb, const LoraBf16& lw, void*
   const int r = s.r;
   const float ls = r > 0 ? cfg.lora_alpha / (float)r : 0.f;
   RP_TRY(rmsnorm_fwd(dt, x, wptr(w, cfg, RP_T_GAMMA1), A.a, A.rstd1, T, s.H, cfg.rms_eps, st));
-  RP_TRY(gemm(mk(T, s.QKV, s.H, A.a, s.H, true, wptr(w, cfg, RP_T_WQKV), s.H, true, A.qkv, s.QKV, dt, dt), st));
-  if (after_qkv) RP_TRY(after_qkv());
+  // the rotation of q and k rides in the product's epilogue unless the
+  // QK-norm must come between the product and the rotation. LoRA deltas
+  // (us_x = s a A_x^T, then us_x B_x^T per part) are computed first and added
+  // in that epilogue before the rotation; unfused they are added in place.
+  const bool rope_fused = fused_rope(s);
   if (r > 0) {
     RP_TRY(lora_cast(c, lb.lora, lw, st));
-    // us = s a [A_q; A_k; A_v]^T, then q|k|v += us_x B_x^T
     GemmDesc gu = mk(T, 3 * r, s.H, A.a, s.H, true, lw.aqkv, s.H, true, A.us_qkv, 3 * r, dt, dt);
     gu.alpha = ls;
     RP_TRY(gemm(gu, st));
+    if (rope_fused) {
+      const void* bx[3] = {lw.bq, lw.bk, lw.bv};
+      const int nx[3] = {s.Q, s.KV, s.KV}, cx[3] = {0, s.Q, s.Q + s.KV};
+      for (int xi = 0; xi < 3; ++xi)
+        RP_TRY(gemm(mk(T, nx[xi], r, (const char*)A.us_qkv + (size_t)xi * r * s.es, 3 * r, true, bx[xi], r, true,
+                       (char*)lora_d + (size_t)cx[xi] * s.es, s.QKV, dt, dt),
+                    st));
+    }
+  }
+  GemmDesc gqkv = mk(T, s.QKV, s.H, A.a, s.H, true, wptr(w, cfg, RP_T_WQKV), s.H, true, A.qkv, s.QKV, dt, dt,
+                     rope_fused ? EPI_ROPE : EPI_STORE);
+  if (rope_fused) {
+    gqkv.rope_tab = rope;
+    gqkv.rope_seq = seq;
+    gqkv.rope_heads = s.nq + s.nkv;
+    if (r > 0) {
+      gqkv.R = lora_d;
+      gqkv.ldr = s.QKV;
+    }
+  }
+  RP_TRY(gemm(gqkv, st));
+  if (after_qkv) RP_TRY(after_qkv());
+  if (r > 0 && !rope_fused) {
+    // q|k|v += us_x B_x^T in place
     const void* bx[3] = {lw.bq, lw.bk, lw.bv};
     const int nx[3] = {s.Q, s.KV, s.KV}, cx[3] = {0, s.Q, s.Q + s.KV};
     for (int xi = 0; xi < 3; ++xi) {
@@ -258,7 +291,7 @@ rp_status layer_fwd(rp_ctx* c, const LayerBinding& lb, const LoraBf16& lw, void*
   if (s.qkn)
     RP_TRY(qknorm_rope_fwd(dt, A.qkv, s.QKV, A.qkraw, A.qkrstd, wptr(w, cfg, RP_T_QNORM), wptr(w, cfg, RP_T_KNORM), T,
                            seq, s.nq, s.nkv, s.d, rope, cfg.rms_eps, st));
-  else
+  else if (!rope_fused)
     RP_TRY(rope_apply(dt, A.qkv, s.QKV, T, seq, s.nq + s.nkv, s.d, rope, false, st));
   AttnDesc ad;
   ad.dt = dt; ad.batch = T / seq; ad.seq = seq; ad.n_q = s.nq; ad.n_kv = s.nkv; ad.d = s.d;
@@ -539,7 +572,7 @@ rp_status stage_fwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* x
     // the ping-pong buffer written by this layer held the input of layer
     // i - 1, whose checkpoint download must have finished
     if (!keep && ckpt_host && i >= 1 && i != n - 1) RP_HIP(hipStreamWaitEvent(st, d2h_done[i - 1], 0));
-    RP_TRY(layer_fwd(c, lb, L.lw, L.ye, s.E > 0 ? router[i] : nullptr, (int)T, seq, x, A, y, L.rope, st,
+    RP_TRY(layer_fwd(c, lb, L.lw, L.ye, L.lora_d, s.E > 0 ? router[i] : nullptr, (int)T, seq, x, A, y, L.rope, st,
                      download_ckpt));
     RP_TRY(mark_consumed(c, w));
     if (s.r > 0) RP_TRY(mark_consumed(c, lb.lora));
@@ -640,7 +673,8 @@ rp_status stage_bwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* c
     } else {
       x = ck_dev ? ckpt[i] : L.bt.ck[i & 1];
       // recompute the forward from the checkpoint (same kernels as the forward)
-      RP_TRY(layer_fwd(c, lb, L.lw, L.ye, s.E > 0 ? router[i] : nullptr, (int)T, seq, x, A, nullptr, L.rope, st));
+      RP_TRY(layer_fwd(c, lb, L.lw, L.ye, L.lora_d, s.E > 0 ? router[i] : nullptr, (int)T, seq, x, A, nullptr, L.rope,
+                       st));
     }
     // inter-layer gradients alternate gp[0], gp[1]; the stage input's goes to dx
     void* g_out = (i == 0) ? dx : L.bt.gp[(n - 1 - i) & 1];

@@ -322,3 +322,35 @@ def test_bf16_moe_lora_layer_matches_oracle(W, experts, top_k, seq):
     for n, r in g_ref.items():
         e = max_rel(got[n], r)
         assert e < tol, (n, e)
+
+
+def test_bf16_layer_odd_head_count_fused_rope(W):
+    """The RoPE epilogue of the QKV product on a packed width that 256-column
+    tiles do not divide (3 query heads + 1 kv head: 5 heads of 128, the last
+    tile half past the end) at a token count that takes the 256 x 256 tiles:
+    sampled output rows against the oracle, and the recomputed backward of
+    the fused stage equal to the kept one."""
+    cfg = synth.StageConfig(name="odd", hidden=384, n_q=3, n_kv=1, head_dim=128, ffn=512, batch=2, seq=10240,
+                            dtype="bf16", seed=1234)
+    say("bf16 odd head count", cfg.tokens)
+    lw = synth.layer_weights(cfg, 0, gamma="perturbed")
+    x = synth.activation(cfg, "x")
+    dy = synth.activation(cfg, "dy")
+    wk = W(cfg)
+    wk.add_layer(0, lw)
+    ctx = wk.ctx
+    T, H, b, s = cfg.tokens, cfg.hidden, cfg.batch, cfg.seq
+    xd, dyd = x.to(DEV), dy.to(DEV)
+    y, dx, dx2 = (torch.empty(T, H, dtype=torch.bfloat16, device=DEV) for _ in range(3))
+    ws = ctx.workspace(B_OP_FUSED(), b, s, 1)
+    ctx.stage_fwd(0, 1, b, s, xd, y, ws, flags=1)
+    ctx.stage_bwd_recompute(0, 1, b, s, dyd, dx, ws, flags=2)
+    ctx.sync()
+    g_kept = wk.layers[0]["g"].clone()
+    ws_b = ctx.workspace(1, b, s, 1)
+    ctx.stage_bwd_recompute(0, 1, b, s, dyd, dx2, ws_b, ckpt=[xd], flags=4)
+    ctx.sync()
+    assert torch.equal(dx, dx2) and torch.equal(g_kept, wk.layers[0]["g"])
+    rows = [0, 1, 255, 256, s - 1, s, s + 300, T - 1]
+    ref = O.layer_forward_rows(x.double(), {k: v.double() for k, v in lw.items()}, cfg, rows)
+    assert max_rel(y.cpu()[rows], ref) < GRAD_TOL["bf16"]
