@@ -489,39 +489,44 @@ def config_sweep(reps: int = 3):
 
 
 def link_peak(nbytes: int = 1 << 30, chunk: int = 64 << 20, reps: int = 3):
-    """The host link's pinned-copy rate on this machine through the library's own
-    copy path (rp_act_copy, DMA), in chunks of the size the streamed step
-    uses: one direction at a time, then both directions at once. Best of
-    `reps`, GB/s."""
-    from offloaded_pipeline_stage_amd import binding as B
-    ctx = B.Context(synth.config("llama3_8b"))
+    """The host link's pinned-copy rate on this machine: plain asynchronous copies
+    between pinned host memory and the device, in chunks of the size the
+    streamed step uses, on two independent non-blocking streams: one
+    direction at a time, then both directions at once. Best of `reps`, GB/s.
+    (A measurement of the link itself, outside the library's ordering rules:
+    its activation downloads follow the compute stream, which waits for its
+    activation uploads.)"""
     host_up = torch.ones(nbytes, dtype=torch.uint8).pin_memory()
     host_dn = torch.empty(nbytes, dtype=torch.uint8).pin_memory()
     dev_up = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     dev_dn = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    s_up, s_dn = torch.cuda.Stream(), torch.cuda.Stream()
     torch.cuda.synchronize()
 
     def up():
-        for o in range(0, nbytes, chunk):
-            ctx.act_copy(B.RP_H2D, dev_up[o:o + chunk], host_up[o:o + chunk])
+        with torch.cuda.stream(s_up):
+            for o in range(0, nbytes, chunk):
+                dev_up[o:o + chunk].copy_(host_up[o:o + chunk], non_blocking=True)
 
     def down():
-        for o in range(0, nbytes, chunk):
-            ctx.act_copy(B.RP_D2H, host_dn[o:o + chunk], dev_dn[o:o + chunk])
+        with torch.cuda.stream(s_dn):
+            for o in range(0, nbytes, chunk):
+                host_dn[o:o + chunk].copy_(dev_dn[o:o + chunk], non_blocking=True)
 
     def timed(fn):
         best = float("inf")
         for _ in range(reps + 1):
-            ctx.sync()
+            torch.cuda.synchronize()
             t0 = time.perf_counter()
             fn()
-            ctx.sync()
+            torch.cuda.synchronize()
             best = min(best, time.perf_counter() - t0)
         return best
 
     t_up, t_dn = timed(up), timed(down)
     t_both = timed(lambda: (up(), down()))
-    ctx.close()
+    del host_up, host_dn, dev_up, dev_dn
+    torch.cuda.empty_cache()
     return {"h2d_GBps": round(nbytes / t_up / 1e9, 1), "d2h_GBps": round(nbytes / t_dn / 1e9, 1),
             "both_directions_GBps": round(2 * nbytes / t_both / 1e9, 1), "bytes_per_direction": nbytes,
             "chunk_bytes": chunk}

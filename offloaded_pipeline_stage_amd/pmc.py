@@ -247,8 +247,101 @@ def summarize_counters(dirs, title: str, commands, min_us: float = 20.0) -> str:
     return "\n".join(lines) + "\n"
 
 
+# ---------------------------------------------------------------------------
+# kernel + memory-copy timeline (rocprofv3 --kernel-trace --memory-copy-trace)
+# ---------------------------------------------------------------------------
+
+BLIT = "__amd_rocclr_copyBuffer"
+
+
+def _union_ns(ivs):
+    total, end = 0, None
+    for a, b in sorted(ivs):
+        if end is None or a > end:
+            total += b - a
+            end = b
+        elif b > end:
+            total += b - end
+            end = b
+    return total
+
+
+def _overlap_ns(xs, ys):
+    """Time covered by both interval sets."""
+    def merged(v):
+        out = []
+        for a, b in sorted(v):
+            if out and a <= out[-1][1]:
+                out[-1][1] = max(out[-1][1], b)
+            else:
+                out.append([a, b])
+        return out
+    xs, ys = merged(xs), merged(ys)
+    i = j = 0
+    tot = 0
+    while i < len(xs) and j < len(ys):
+        a, b = max(xs[i][0], ys[j][0]), min(xs[i][1], ys[j][1])
+        if a < b:
+            tot += b - a
+        if xs[i][1] < ys[j][1]:
+            i += 1
+        else:
+            j += 1
+    return tot
+
+
+def summarize_copies(d: str, title: str, commands, window_ms: float) -> str:
+    """Busy time of the compute kernels, the runtime's device-to-host blit
+    kernels and the DMA copies per direction over the last `window_ms` of
+    the trace (the timed steps), and how much of each overlaps the compute."""
+    ks = list(csv.DictReader(open(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)[0])))
+    ms = list(csv.DictReader(open(glob.glob(os.path.join(d, "**", "*memory_copy_trace.csv"), recursive=True)[0])))
+    iv = lambda r: (int(r["Start_Timestamp"]), int(r["End_Timestamp"]))  # noqa: E731
+    end = max(iv(r)[1] for r in ks + ms)
+    lo = end - int(window_ms * 1e6)
+    inwin = lambda v: [x for x in v if x[0] >= lo]  # noqa: E731
+    comp = inwin([iv(r) for r in ks if BLIT not in r["Kernel_Name"]])
+    blit = inwin([iv(r) for r in ks if BLIT in r["Kernel_Name"]])
+    up = inwin([iv(r) for r in ms if "HOST_TO_DEVICE" in r["Direction"]])
+    dn = inwin([iv(r) for r in ms if "DEVICE_TO_HOST" in r["Direction"]])
+    c_busy = _union_ns(comp)
+    rows = [("compute kernels", comp), ("device-to-host blit kernels", blit), ("DMA copies host to device", up),
+            ("DMA copies device to host", dn)]
+    lines = [f"# {title}", ""] + [f"command: {c}" for c in commands]
+    lines += ["", f"window: the last {window_ms:.0f} ms of the trace", "",
+              f"{'count':>6} {'busy_ms':>9} {'mean_ms':>8} {'with_compute_ms':>15}  what"]
+    for name, v in rows:
+        if not v:
+            lines.append(f"{0:6d} {0.0:9.2f} {0.0:8.3f} {0.0:15.2f}  {name}")
+            continue
+        busy = _union_ns(v)
+        mean = sum(b - a for a, b in v) / len(v)
+        ov = _overlap_ns(v, comp) if name != "compute kernels" else busy
+        lines.append(f"{len(v):6d} {busy / 1e6:9.2f} {mean / 1e6:8.3f} {ov / 1e6:15.2f}  {name}")
+    lines += ["", f"compute busy {c_busy / 1e6:.2f} ms of the {window_ms:.0f} ms window"]
+    return "\n".join(lines) + "\n"
+
+
 if __name__ == "__main__":
     import sys
+    if len(sys.argv) > 1 and sys.argv[1] == "copies":
+        import argparse
+        ap = argparse.ArgumentParser(description="summarise a kernel + memory-copy trace")
+        ap.add_argument("mode")
+        ap.add_argument("dir")
+        ap.add_argument("--title", required=True)
+        ap.add_argument("--window-ms", type=float, required=True)
+        ap.add_argument("--command", action="append", default=[])
+        ap.add_argument("--note", action="append", default=[])
+        ap.add_argument("--out", required=True)
+        a = ap.parse_args()
+        txt = summarize_copies(a.dir, a.title, a.command, a.window_ms)
+        if a.note:
+            txt += "\n" + "\n".join(a.note) + "\n"
+        with open(a.out, "w") as f:
+            f.write(txt)
+        print(txt)
+        sys.exit(0)
     if len(sys.argv) > 1 and sys.argv[1] == "counters":
         import argparse
         ap = argparse.ArgumentParser(description="summarise utilisation counter runs")
