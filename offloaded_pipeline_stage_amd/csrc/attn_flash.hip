@@ -468,13 +468,70 @@ __global__ __launch_bounds__(NT) void flash_dq_kernel(FlashParams p, const bf16*
 
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup = 128 keys of one kv head, streaming 64-query tiles of
-// every query head of the group (Q and dO row-major and transposed, with their
-// lse and D rows), double-buffered in LDS; wave w owns 32 keys
+// every query head of the group; wave w owns 32 keys, whose K and V rows it
+// holds in registers and whose dK and dV it accumulates.
+//
+// The query tiles (Q and dO rows, their lse and D values) go from global
+// memory straight into a ring of three LDS stages (buffer loads with the LDS
+// as destination, no registers on the way), two tiles ahead of the one being
+// computed. Only the row-major image is stored: the transposed operands of
+// the dV and dK products are read from it with the transposing LDS read
+// (ds_read_b64_tr_b16), so no wave spends vector instructions on transposes.
+// A manual barrier (wait for this wave's loads of the next tile, then
+// s_barrier) replaces __syncthreads, whose fence would also wait for the
+// loads two tiles ahead.
 // ---------------------------------------------------------------------------
+
+// row-major [64 rows][128] bf16 stage tile: 256-byte rows of 16 chunks of 16
+// bytes, chunk c of row r stored at position c ^ g(r), with g a bijection of
+// r % 16 such that (a) 16 consecutive rows (a fragment read of 16 lanes with
+// one chunk each) hit 16 distinct positions and (b) the four rows 4a .. 4a + 3
+// together with chunks {c, c ^ 1} (a transposing read of 16 lanes) hit 8
+// distinct positions
+__device__ __forceinline__ int dr_swz(int row) {
+  const int a = (row >> 2) & 3, b = row & 3;
+  return 8 * (a >> 1) + 2 * b + (a & 1);
+}
+__device__ __forceinline__ int dr_off(int row, int c16) { return row * 256 + ((c16 ^ dr_swz(row)) << 4); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t* lds_bf16x4_t;
+
+// s_waitcnt: at most n vector-memory operations outstanding and no LDS
+// operation (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+// A operand of a dV / dK product from a row-major stage tile: d-row
+// 32 dt + (lane % 32), k-step j of 32-row sub-tile u (rows 32u + 16j +
+// {4h .. 4h + 3, 8 + 4h .. 8 + 4h + 3}), as two transposing reads. In a read,
+// lane c of each 16-lane group addresses 4 consecutive d of one row and
+// receives, in slot k, element c % 4 of the chunk addressed by lane
+// 4k + c / 4: so lane c of the group addresses row r0 + c / 4, d
+// d0 + 4 (c % 4), and every lane receives its own d for rows r0 .. r0 + 3.
+__device__ __forceinline__ bf16x8_t rd_trl(const char* t, int dt, int u, int j, int lane) {
+  const int grp = lane >> 4, c = lane & 15, h = lane >> 5;
+  const int d = 32 * dt + 16 * (grp & 1) + 4 * (c & 3);
+  const int r = 32 * u + 16 * j + 4 * h + (c >> 2);
+  const int off0 = r * 256 + (((d >> 3) ^ dr_swz(r)) << 4) + (d & 4) * 2;
+  const int off1 = (r + 8) * 256 + (((d >> 3) ^ dr_swz(r + 8)) << 4) + (d & 4) * 2;
+  const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t)(t + off0));
+  const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t)(t + off1));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// A operand of a score product: rows 32u + (lane % 32), d-step s
+__device__ __forceinline__ bf16x8_t rd_rml(const char* t, int u, int s, int lane) {
+  const int row = 32 * u + (lane & 31);
+  return *reinterpret_cast<const bf16x8_t*>(t + dr_off(row, 2 * s + (lane >> 5)));
+}
+
 __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf16* __restrict__ dout,
                                                         const float* __restrict__ lse, const float* __restrict__ Dr,
                                                         bf16* __restrict__ dqkv) {
-  constexpr int STAGE = 4 * TILE * 256 + 2 * TILE * 4;
+  constexpr int NST = 3;                                   // LDS stages
+  constexpr int STAGE = 2 * TILE * 256 + 2 * TILE * 4;     // Q, dO, lse, D
+  constexpr int NDMA = 10;                                 // loads per wave per tile
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(tid), h = lane >> 5, n = lane & 31;
   const int hk = blockIdx.x, b = blockIdx.z;
@@ -482,8 +539,8 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
   const int G = p.nq / p.nkv;
   const int T = gridDim.z * p.seq;
   const bf16* base = p.qkv + (int64_t)b * p.seq * p.ld;
-  const bf16* dob = dout + (int64_t)b * p.seq * p.nq * D;
   const int64_t ldo = (int64_t)p.nq * D;
+  const bf16* dob = dout + (int64_t)b * p.seq * ldo;
   const int k0 = kb * BROWS, kw = k0 + w * WROWS, kpos = kw + n;
   const int kcol = (p.nq + hk) * D, vcol = (p.nq + p.nkv + hk) * D;
 
@@ -497,123 +554,188 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
   // the streamed tiles: query tile qt of head g covers queries [k0 + 64 qt, +64)
   const int nqt = (p.seq - k0 + TILE - 1) / TILE;
   const int ntile = G * nqt;
-  TileSet<2> ts;
-  float ls = 0.f, ds = 0.f;
-  auto fetch = [&](int i) {
-    const int g = i / nqt, q0 = k0 + (i % nqt) * TILE, head = hk * G + g;
-    const bf16* const gr[2] = {base, dob};
-    const int64_t ldr[2] = {p.ld, ldo};
-    const int colr[2] = {head * D, head * D};
-    ts.load(gr, ldr, colr, q0, p.seq, tid);
-    if (tid < TILE) {
-      const int q = min(q0 + tid, p.seq - 1);
-      const int64_t si = (int64_t)head * T + (int64_t)b * p.seq + q;
-      ls = lse[si] * LOG2E;
-      ds = Dr[si];
+  // tile i (clamped to the last one: the loads past the end repeat it into a
+  // stage nobody reads, which keeps every wave's count of loads uniform)
+  // into stage i % NST. Wave w loads rows 16w .. 16w + 15 of Q and dO (four
+  // 1 KB instructions each: lane L writes 16 bytes at row 4j + L / 16,
+  // position L % 16, so it loads chunk (L % 16) ^ g(row)) and lse / D rows
+  // 16w .. 16w + 15 (lanes 0..15). Rows at or past the sequence end read as
+  // zeros (each tile's buffer resources end at its last valid row).
+  auto issue = [&](int i) __attribute__((always_inline)) {
+    const int ic = min(i, ntile - 1);
+    const int g = ic / nqt, q0 = k0 + (ic % nqt) * TILE, head = hk * G + g;
+    const int nvalid = min(TILE, p.seq - q0);
+    char* st = smem + (i % NST) * STAGE;
+    const auto rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base + (int64_t)q0 * p.ld + head * D), (short)0,
+                                                      (int)((nvalid - 1) * p.ld * 2 + 256), 0x00020000);
+    const auto ro = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(dob + (int64_t)q0 * ldo + head * D), (short)0,
+                                                      (int)((nvalid - 1) * ldo * 2 + 256), 0x00020000);
+    const int64_t si = (int64_t)head * T + (int64_t)b * p.seq + q0;
+    const auto rl = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(lse + si), (short)0, nvalid * 4, 0x00020000);
+    const auto rd = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(Dr + si), (short)0, nvalid * 4, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * w + 4 * j + (lane >> 4);
+      const int c = (lane & 15) ^ dr_swz(row);
+      // a row past the end gets an offset past every buffer's range: zeros
+      const uint32_t oq = row < nvalid ? (uint32_t)(row * p.ld * 2 + c * 16) : 0x80000000u;
+      const uint32_t oo = row < nvalid ? (uint32_t)(row * ldo * 2 + c * 16) : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_ptr_t)(st + (16 * w + 4 * j) * 256), 16, (int)oq, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (lds_ptr_t)(st + TILE * 256 + (16 * w + 4 * j) * 256), 16, (int)oo,
+                                               0, 0, 0);
+    }
+    float* sl = reinterpret_cast<float*>(st + 2 * TILE * 256);
+    if (lane < 16) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_ptr_t)(sl + 16 * w), 4, (16 * w + lane) * 4, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_ptr_t)(sl + TILE + 16 * w), 4, (16 * w + lane) * 4, 0, 0, 0);
     }
   };
-  auto put = [&](char* st) {
-    ts.store_rm(0, st, tid);
-    ts.store_rm(1, st + TILE * 256, tid);
-    ts.store_tr(0, st + 2 * TILE * 256, tid);
-    ts.store_tr(1, st + 3 * TILE * 256, tid);
-    if (tid < TILE) {
-      float* sl = reinterpret_cast<float*>(st + 4 * TILE * 256);
-      sl[tid] = ls;
-      sl[TILE + tid] = ds;
+  // this wave's loads of the next tile landed (the NDMA loads of the tile
+  // after it may still be in flight), its LDS reads done, then all waves
+  auto sync_next = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(NDMA));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  issue(0);
+  issue(1);
+  sync_next();
+
+  // lse (in log2 units) and D of the 16 queries of sub-tile u that a lane's
+  // score registers hold: registers 4g .. 4g + 3 are queries
+  // 32u + 8g + 4h + 0..3, one 16-byte read each
+  auto stats = [&](float4 (&lq)[4], float4 (&dq)[4], int u, const float* sL) __attribute__((always_inline)) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 l = *reinterpret_cast<const float4*>(sL + 32 * u + 8 * g + 4 * h);
+      lq[g] = make_float4(l.x * LOG2E, l.y * LOG2E, l.z * LOG2E, l.w * LOG2E);
+      dq[g] = *reinterpret_cast<const float4*>(sL + TILE + 32 * u + 8 * g + 4 * h);
     }
   };
-  fetch(0);
-  put(smem);
-  if (ntile > 1) fetch(1);
-  __syncthreads();
+  // probabilities P and dS = P (dP - D) of sub-tile u of the query tile at
+  // q0 from its scores st and dp, packed as the bf16 operands of the dV and
+  // dK products (k-steps j = 0, 1)
+  auto probs = [&](const f32x16_t& st, const f32x16_t& dp, bf16x8_t (&pb)[2], bf16x8_t (&sb)[2],
+                   const float4 (&lq)[4], const float4 (&dq)[4], int u, int q0, auto mask_c)
+                   __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_c)::value;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float pr[8], ds[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * j + i;
+        pr[i] = fexp2(st[r] * p.c2 - lane_of(lq[r >> 2], r & 3));
+        if constexpr (MASK) {  // kpos > q only on the diagonal
+          const int q = q0 + 32 * u + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (kpos > q || q >= p.seq) pr[i] = 0.f;
+        }
+        ds[i] = pr[i] * (dp[r] - lane_of(dq[r >> 2], r & 3));
+      }
+      u32x4_t a, c;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = pack_bf16x2(pr[2 * i], pr[2 * i + 1]);
+        c[i] = pack_bf16x2(ds[2 * i], ds[2 * i + 1]);
+      }
+      pb[j] = __builtin_bit_cast(bf16x8_t, a);
+      sb[j] = __builtin_bit_cast(bf16x8_t, c);
+    }
+  };
+
   // one query tile; MASK: the tile holds queries before some key of the
   // wave (the diagonal) or past the sequence end. Separate loops per variant
   // keep the masking code out of the interior tiles.
   auto tile = [&](int it, auto mask_c) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_c)::value;
     const int q0 = k0 + (it % nqt) * TILE;
-    const char* sQ = smem + (it & 1) * STAGE;
+    const char* sQ = smem + (it % NST) * STAGE;
     const char* sO = sQ + TILE * 256;
-    const char* sQt = sQ + 2 * TILE * 256;
-    const char* sOt = sQ + 3 * TILE * 256;
-    const float* sL = reinterpret_cast<const float*>(sQ + 4 * TILE * 256);
-    const float* sD = sL + TILE;
-    if (!MASK || q0 + TILE - 1 >= kw) {  // else every query of the tile is before every key of the wave
-      // the two 32-query sub-tiles one after the other (kept rolled: their
-      // fragment registers would not fit side by side)
-#pragma unroll 1
-      for (int u = 0; u < 2; ++u) {
-        // all fragment reads of the sub-tile are issued before the products
-        // that use them: one wave per SIMD, so nothing else would hide a
-        // read's latency in front of each MFMA
-        bf16x8_t fq[8], fo[8], tq[2][4], to[2][4];  // to/tq: j = 0, 1
+    const float* sL = reinterpret_cast<const float*>(sQ + 2 * TILE * 256);
+    if (!decltype(mask_c)::value || q0 + TILE - 1 >= kw) {  // else every query of the tile is before every key of the wave
+      // The two 32-query sub-tiles u = 0, 1, each in three phases: P(u) the
+      // score products S = Q K^T and dP = dO V^T (16 MFMAs), E(u) the
+      // probabilities and dS on the vector ALU, D(u) the dV and dK products
+      // (16 MFMAs). With one wave per SIMD the vector work hides only under
+      // MFMAs of the same wave, so the phases run as P(0); P(1) with E(0);
+      // D(0) with E(1); D(1); LDS reads are issued a phase ahead.
+      bf16x8_t fq[8], fo[8], tq[2][4], to[2][4];
+      f32x16_t st0 = zero16(), dp0 = zero16(), st1 = zero16(), dp1 = zero16();
+      bf16x8_t pb0[2], sb0[2], pb1[2], sb1[2];
+      float4 lq0[4], dq0[4], lq1[4], dq1[4];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          fq[s] = rd_rm(sQ, u, s, lane);
-          fo[s] = rd_rm(sO, u, s, lane);
-        }
-        f32x16_t st = zero16(), dp = zero16();
+      for (int s = 0; s < 8; ++s) {
+        fq[s] = rd_rml(sQ, 0, s, lane);
+        fo[s] = rd_rml(sO, 0, s, lane);
+      }
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          st = mfma(fq[s], kf[s], st);
-          dp = mfma(fo[s], vf[s], dp);
-        }
-        // the j = 0 transposed fragments load under the softmax arithmetic,
-        // the j = 1 ones under the j = 0 products
+      for (int s = 0; s < 8; ++s) {
+        st0 = mfma(fq[s], kf[s], st0);
+        dp0 = mfma(fo[s], vf[s], dp0);
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        fq[s] = rd_rml(sQ, 1, s, lane);
+        fo[s] = rd_rml(sO, 1, s, lane);
+      }
+      stats(lq0, dq0, 0, sL);
+      __builtin_amdgcn_sched_barrier(0);
+      // P(1) with E(0); sub-tile 0's transposed operands load meanwhile
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        st1 = mfma(fq[s], kf[s], st1);
+        dp1 = mfma(fo[s], vf[s], dp1);
+      }
+      probs(st0, dp0, pb0, sb0, lq0, dq0, 0, q0, mask_c);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          to[0][dt] = rd_tr(sOt, dt, u, 0, lane);
-          tq[0][dt] = rd_tr(sQt, dt, u, 0, lane);
+          to[j][dt] = rd_trl(sO, dt, 0, j, lane);
+          tq[j][dt] = rd_trl(sQ, dt, 0, j, lane);
         }
-        f32x16_t dsr;
-        // registers 4g .. 4g + 3 hold queries 32u + 8g + 4h + 0..3: their
-        // lse and D values are one 16-byte read each
-        float4 lq[4], dq4[4];
+      stats(lq1, dq1, 1, sL);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          lq[g] = *reinterpret_cast<const float4*>(sL + 32 * u + 8 * g + 4 * h);
-          dq4[g] = *reinterpret_cast<const float4*>(sD + 32 * u + 8 * g + 4 * h);
-        }
-        if constexpr (MASK) {  // kpos > q only on the diagonal
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int q = q0 + 32 * u + 8 * (r >> 2) + 4 * h + (r & 3);
-            const float pr = (kpos > q || q >= p.seq) ? 0.f : fexp2(st[r] * p.c2 - lane_of(lq[r >> 2], r & 3));
-            st[r] = pr;
-            dsr[r] = pr * (dp[r] - lane_of(dq4[r >> 2], r & 3));
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float pr = fexp2(st[r] * p.c2 - lane_of(lq[r >> 2], r & 3));
-            st[r] = pr;
-            dsr[r] = pr * (dp[r] - lane_of(dq4[r >> 2], r & 3));
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const bf16x8_t pb = to_operand(st, j), sb = to_operand(dsr, j);
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            dv[dt] = mfma(to[j][dt], pb, dv[dt]);
-            dk[dt] = mfma(tq[j][dt], sb, dk[dt]);
-          }
-          if (j == 0) {
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-              to[1][dt] = rd_tr(sOt, dt, u, 1, lane);
-              tq[1][dt] = rd_tr(sQt, dt, u, 1, lane);
-            }
-          }
-        }
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA,
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // up to five vector ops,
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
       }
+      __builtin_amdgcn_sched_barrier(0);
+      // D(0) with E(1); sub-tile 1's transposed operands load meanwhile
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          dv[dt] = mfma(to[j][dt], pb0[j], dv[dt]);
+          dk[dt] = mfma(tq[j][dt], sb0[j], dk[dt]);
+        }
+      probs(st1, dp1, pb1, sb1, lq1, dq1, 1, q0, mask_c);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          to[j][dt] = rd_trl(sO, dt, 1, j, lane);
+          tq[j][dt] = rd_trl(sQ, dt, 1, j, lane);
+        }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // D(1), then the loads of the tile two ahead
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          dv[dt] = mfma(to[j][dt], pb1[j], dv[dt]);
+          dk[dt] = mfma(tq[j][dt], sb1[j], dk[dt]);
+        }
     }
-    if (it + 1 < ntile) {
-      put(smem + ((it + 1) & 1) * STAGE);
-      if (it + 2 < ntile) fetch(it + 2);
-    }
-    __syncthreads();
+    issue(it + 2);  // into the stage of tile it - 1, which every wave left before the last barrier
+    sync_next();
   };
   // per query head: tiles qt < qa reach the wave's diagonal (q0 < kw + WROWS
   // - 1), tiles qt >= qb pass the sequence end (q0 + TILE > seq)
@@ -625,6 +747,8 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
     for (; qt < qb; ++qt) tile(g * nqt + qt, std::false_type{});
     for (; qt < nqt; ++qt) tile(g * nqt + qt, std::true_type{});
   }
+  // drain the loads past the end before the workgroup exits
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
   bf16* dst = dqkv + (int64_t)b * p.seq * p.ld;
   store_acc_rows(dk, p.scale, dst, p.ld, kpos, p.seq, kcol, h);
   store_acc_rows(dv, 1.f, dst, p.ld, kpos, p.seq, vcol, h);
@@ -647,7 +771,7 @@ double causal_pairs(const AttnDesc& a) { return (double)a.batch * a.seq * (a.seq
 
 // double-buffered LDS stages of the backward kernels (above the 64 KB static limit)
 constexpr size_t DQ_LDS = 2 * 3 * TILE * 256;
-constexpr size_t DKDV_LDS = 2 * (4 * TILE * 256 + 2 * TILE * 4);
+constexpr size_t DKDV_LDS = 3 * (2 * TILE * 256 + 2 * TILE * 4);
 
 rp_status set_lds_limits() {
   static bool done = false;
