@@ -365,108 +365,6 @@ __global__ __launch_bounds__(NT) void flash_bwd_dot_kernel(const bf16* __restric
 }
 
 // ---------------------------------------------------------------------------
-// dQ: one workgroup = 128 queries of one head, streaming 64-key tiles (K and V
-// row-major, K transposed) double-buffered in LDS like the forward
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(NT) void flash_dq_kernel(FlashParams p, const bf16* __restrict__ dout,
-                                                      const float* __restrict__ lse, const float* __restrict__ Dr,
-                                                      bf16* __restrict__ dqkv) {
-  constexpr int STAGE = 3 * TILE * 256;
-  extern __shared__ __align__(16) char smem[];
-  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(tid), h = lane >> 5, n = lane & 31;
-  const int head = blockIdx.x, b = blockIdx.z;
-  const int qb = p.n_blocks - 1 - blockIdx.y;
-  const int hk = head / (p.nq / p.nkv);
-  const int T = gridDim.z * p.seq;
-  const bf16* base = p.qkv + (int64_t)b * p.seq * p.ld;
-  const int q0 = qb * BROWS, qw = q0 + w * WROWS, qpos = qw + n;
-  const int kcol = (p.nq + hk) * D, vcol = (p.nq + p.nkv + hk) * D;
-  const int64_t ldo = (int64_t)p.nq * D;
-
-  bf16x8_t qf[8], dof[8];
-  load_rows_b(qf, base, p.ld, qpos, p.seq, head * D, h);
-  load_rows_b(dof, dout + (int64_t)b * p.seq * ldo, ldo, qpos, p.seq, head * D, h);
-  const int64_t si = (int64_t)head * T + (int64_t)b * p.seq + min(qpos, p.seq - 1);
-  const float l2 = lse[si] * LOG2E, dd = Dr[si];
-  f32x16_t acc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = zero16();
-
-  const bf16* const gsrc[2] = {base, base};
-  const int64_t gld[2] = {p.ld, p.ld};
-  const int gcol[2] = {kcol, vcol};
-  const int klast = min(q0 + BROWS, p.seq) - 1;
-  const int ntile = klast / TILE + 1;
-  TileSet<2> ts;
-  auto put = [&](char* st) {
-    ts.store_rm(0, st, tid);
-    ts.store_rm(1, st + TILE * 256, tid);
-    ts.store_tr(0, st + 2 * TILE * 256, tid);
-  };
-  ts.load(gsrc, gld, gcol, 0, p.seq, tid);
-  put(smem);
-  if (ntile > 1) ts.load(gsrc, gld, gcol, TILE, p.seq, tid);
-  __syncthreads();
-  // one key tile; MASK as in the forward (separate loops, see there)
-  auto tile = [&](int kt, auto mask_c) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_c)::value;
-    const int k0 = kt * TILE;
-    const char* sK = smem + (kt & 1) * STAGE;
-    const char* sV = sK + TILE * 256;
-    const char* sKt = sK + 2 * TILE * 256;
-    if (!MASK || k0 <= qw + WROWS - 1) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        // fragment reads issued ahead of the products (see flash_dkdv_kernel)
-        bf16x8_t fk[8], fv[8], tk[2][4];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          fk[s] = rd_rm(sK, t, s, lane);
-          fv[s] = rd_rm(sV, t, s, lane);
-        }
-        f32x16_t st = zero16(), dp = zero16();
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          st = mfma(fk[s], qf[s], st);
-          dp = mfma(fv[s], dof[s], dp);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) tk[j][dt] = rd_tr(sKt, dt, t, j, lane);
-        if constexpr (MASK) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-            const float pr = key > qpos ? 0.f : fexp2(st[r] * p.c2 - l2);
-            st[r] = pr * (dp[r] - dd);  // dS
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) st[r] = fexp2(st[r] * p.c2 - l2) * (dp[r] - dd);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const bf16x8_t sb = to_operand(st, j);
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(tk[j][dt], sb, acc[dt]);
-        }
-      }
-    }
-    if (kt + 1 < ntile) {
-      put(smem + ((kt + 1) & 1) * STAGE);
-      if (kt + 2 < ntile) ts.load(gsrc, gld, gcol, k0 + 2 * TILE, p.seq, tid);
-    }
-    __syncthreads();
-  };
-  const int kfree = min(ntile, (qw + 1) / TILE);
-  int kt = 0;
-  for (; kt < kfree; ++kt) tile(kt, std::false_type{});
-  for (; kt < ntile; ++kt) tile(kt, std::true_type{});
-  store_acc_rows(acc, p.scale, dqkv + (int64_t)b * p.seq * p.ld, p.ld, qpos, p.seq, head * D, h);
-}
-
-// ---------------------------------------------------------------------------
 // dK, dV: one workgroup = 128 keys of one kv head, streaming 64-query tiles of
 // every query head of the group; wave w owns 32 keys, whose K and V rows it
 // holds in registers and whose dK and dV it accumulates.
@@ -483,24 +381,43 @@ __global__ __launch_bounds__(NT) void flash_dq_kernel(FlashParams p, const bf16*
 // ---------------------------------------------------------------------------
 
 // row-major [64 rows][128] bf16 stage tile: 256-byte rows of 16 chunks of 16
-// bytes, chunk c of row r stored at position c ^ g(r), with g a bijection of
-// r % 16 such that (a) 16 consecutive rows (a fragment read of 16 lanes with
-// one chunk each) hit 16 distinct positions and (b) the four rows 4a .. 4a + 3
-// together with chunks {c, c ^ 1} (a transposing read of 16 lanes) hit 8
-// distinct positions
-__device__ __forceinline__ int dr_swz(int row) {
-  const int a = (row >> 2) & 3, b = row & 3;
-  return 8 * (a >> 1) + 2 * b + (a & 1);
-}
+// bytes, chunk c of row r stored at position c ^ g(r), where g swaps the two
+// 2-bit halves of r % 16. It is a bijection of r % 16, so 16 consecutive rows
+// with one chunk each (a 16-byte fragment read of 16 lanes) hit 16 distinct
+// positions; and the four rows 4a .. 4a + 3 get distinct high bits, so those
+// rows together with chunks 4m .. 4m + 3 (a transposing 8-byte read of 32
+// lanes) hit 16 distinct positions too.
+__device__ __forceinline__ int dr_swz(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
 __device__ __forceinline__ int dr_off(int row, int c16) { return row * 256 + ((c16 ^ dr_swz(row)) << 4); }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t* lds_bf16x4_t;
 
 // s_waitcnt: at most n vector-memory operations outstanding and no LDS
 // operation (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+// Buffer resource over `bytes` bytes at base (raw buffer: offsets at or past
+// `bytes` read as zeros).
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t rsrc4(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return i32x4_t{(int)(uint32_t)a, (int)(uint32_t)(a >> 32) & 0xffff, (int)bytes, 0x00020000};
+}
+// One 16-byte-per-lane load from global memory straight into LDS: lane L's
+// 16 bytes (at voff of the buffer) land at lds + 16 L. Written as inline
+// assembly on purpose: for the builtin form the compiler makes every later
+// LDS read it cannot tell apart from the destination wait for all loads in
+// flight, which would drain the loads issued two tiles ahead. The kernels
+// therefore count these loads themselves (s_waitcnt before each barrier) and
+// wait for all their own register loads before issuing the first one, so no
+// wait the compiler places for a register load can fall inside the loop.
+__device__ __forceinline__ void dma16(i32x4_t r, const void* lds, uint32_t voff) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)lds;
+  // an SALU write of M0 needs one wait state before a load that writes LDS
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
 
 // A operand of a dV / dK product from a row-major stage tile: d-row
 // 32 dt + (lane % 32), k-step j of 32-row sub-tile u (rows 32u + 16j +
@@ -530,9 +447,10 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
                                                         const float* __restrict__ lse, const float* __restrict__ Dr,
                                                         bf16* __restrict__ dqkv) {
   constexpr int NST = 3;                                   // LDS stages
-  constexpr int STAGE = 2 * TILE * 256 + 2 * TILE * 4;     // Q, dO, lse, D
-  constexpr int NDMA = 10;                                 // loads per wave per tile
+  constexpr int STAGE = 2 * TILE * 256;                    // Q, dO
+  constexpr int NDMA = 10;                                 // loads per wave per tile (8 rows, 2 statistics)
   extern __shared__ __align__(16) char smem[];
+  __shared__ __align__(16) float sstat[NST][2 * TILE];   // lse and D of each stage's queries
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(tid), h = lane >> 5, n = lane & 31;
   const int hk = blockIdx.x, b = blockIdx.z;
   const int kb = blockIdx.y;  // earliest keys (most queries) first
@@ -550,29 +468,32 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
   f32x16_t dk[4], dv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) dk[i] = dv[i] = zero16();
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));  // K and V landed (see dma16)
 
   // the streamed tiles: query tile qt of head g covers queries [k0 + 64 qt, +64)
   const int nqt = (p.seq - k0 + TILE - 1) / TILE;
   const int ntile = G * nqt;
-  // tile i (clamped to the last one: the loads past the end repeat it into a
-  // stage nobody reads, which keeps every wave's count of loads uniform)
+  // Tile i (clamped to the last one: the loads past the end repeat it into a
+  // stage nobody reads, which keeps every wave's count of loads uniform) goes
   // into stage i % NST. Wave w loads rows 16w .. 16w + 15 of Q and dO (four
   // 1 KB instructions each: lane L writes 16 bytes at row 4j + L / 16,
-  // position L % 16, so it loads chunk (L % 16) ^ g(row)) and lse / D rows
-  // 16w .. 16w + 15 (lanes 0..15). Rows at or past the sequence end read as
-  // zeros (each tile's buffer resources end at its last valid row).
-  auto issue = [&](int i) __attribute__((always_inline)) {
+  // position L % 16, so it loads chunk (L % 16) ^ g(row)). Rows at or past
+  // the sequence end read as zeros (each tile's buffer resources end at its
+  // last valid row). The lse and D rows 16w .. 16w + 15 go through registers
+  // of lanes 0..15, loaded one tile before they are stored.
+  auto tile_rows = [&](int i, int& q0, int& head, int& nvalid) __attribute__((always_inline)) {
     const int ic = min(i, ntile - 1);
-    const int g = ic / nqt, q0 = k0 + (ic % nqt) * TILE, head = hk * G + g;
-    const int nvalid = min(TILE, p.seq - q0);
+    const int g = ic / nqt;
+    q0 = k0 + (ic % nqt) * TILE;
+    head = hk * G + g;
+    nvalid = min(TILE, p.seq - q0);
+  };
+  auto issue = [&](int i) __attribute__((always_inline)) {
+    int q0, head, nvalid;
+    tile_rows(i, q0, head, nvalid);
     char* st = smem + (i % NST) * STAGE;
-    const auto rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base + (int64_t)q0 * p.ld + head * D), (short)0,
-                                                      (int)((nvalid - 1) * p.ld * 2 + 256), 0x00020000);
-    const auto ro = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(dob + (int64_t)q0 * ldo + head * D), (short)0,
-                                                      (int)((nvalid - 1) * ldo * 2 + 256), 0x00020000);
-    const int64_t si = (int64_t)head * T + (int64_t)b * p.seq + q0;
-    const auto rl = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(lse + si), (short)0, nvalid * 4, 0x00020000);
-    const auto rd = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(Dr + si), (short)0, nvalid * 4, 0x00020000);
+    const i32x4_t rq = rsrc4(base + (int64_t)q0 * p.ld + head * D, (uint32_t)((nvalid - 1) * p.ld * 2 + 256));
+    const i32x4_t ro = rsrc4(dob + (int64_t)q0 * ldo + head * D, (uint32_t)((nvalid - 1) * ldo * 2 + 256));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = 16 * w + 4 * j + (lane >> 4);
@@ -580,26 +501,43 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
       // a row past the end gets an offset past every buffer's range: zeros
       const uint32_t oq = row < nvalid ? (uint32_t)(row * p.ld * 2 + c * 16) : 0x80000000u;
       const uint32_t oo = row < nvalid ? (uint32_t)(row * ldo * 2 + c * 16) : 0x80000000u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_ptr_t)(st + (16 * w + 4 * j) * 256), 16, (int)oq, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (lds_ptr_t)(st + TILE * 256 + (16 * w + 4 * j) * 256), 16, (int)oo,
-                                               0, 0, 0);
-    }
-    float* sl = reinterpret_cast<float*>(st + 2 * TILE * 256);
-    if (lane < 16) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_ptr_t)(sl + 16 * w), 4, (16 * w + lane) * 4, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_ptr_t)(sl + TILE + 16 * w), 4, (16 * w + lane) * 4, 0, 0, 0);
+      dma16(rq, st + (16 * w + 4 * j) * 256, oq);
+      dma16(ro, st + TILE * 256 + (16 * w + 4 * j) * 256, oo);
     }
   };
-  // this wave's loads of the next tile landed (the NDMA loads of the tile
-  // after it may still be in flight), its LDS reads done, then all waves
+  float ls = 0.f, dsv = 0.f;  // lanes 0..15: lse and D of row 16w + lane of the tile being staged
+  auto fetch_stats = [&](int i) __attribute__((always_inline)) {
+    int q0, head, nvalid;
+    tile_rows(i, q0, head, nvalid);
+    if (lane < 16) {
+      const int r = min(16 * w + lane, nvalid - 1);  // rows past the end: any finite value (masked)
+      const int64_t si = (int64_t)head * T + (int64_t)b * p.seq + q0 + r;
+      ls = lse[si];
+      dsv = Dr[si];
+    }
+  };
+  auto put_stats = [&](int i) __attribute__((always_inline)) {
+    float* sl = sstat[i % NST];
+    if (lane < 16) {
+      sl[16 * w + lane] = ls;
+      sl[TILE + 16 * w + lane] = dsv;
+    }
+  };
+  // this wave's loads of the next tile landed (the NDMA loads issued since
+  // may still be in flight), its LDS operations done, then all waves
   auto sync_next = [&]() __attribute__((always_inline)) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(NDMA));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
+  fetch_stats(0);
+  put_stats(0);
+  fetch_stats(1);
+  put_stats(1);
   issue(0);
   issue(1);
+  fetch_stats(2);
   sync_next();
 
   // lse (in log2 units) and D of the 16 queries of sub-tile u that a lane's
@@ -651,7 +589,7 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
     const int q0 = k0 + (it % nqt) * TILE;
     const char* sQ = smem + (it % NST) * STAGE;
     const char* sO = sQ + TILE * 256;
-    const float* sL = reinterpret_cast<const float*>(sQ + 2 * TILE * 256);
+    const float* sL = sstat[it % NST];
     if (!decltype(mask_c)::value || q0 + TILE - 1 >= kw) {  // else every query of the tile is before every key of the wave
       // The two 32-query sub-tiles u = 0, 1, each in three phases: P(u) the
       // score products S = Q K^T and dP = dO V^T (16 MFMAs), E(u) the
@@ -698,7 +636,7 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA,
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // up to five vector ops,
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // up to eight vector ops,
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -721,7 +659,7 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -734,7 +672,12 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
           dk[dt] = mfma(tq[j][dt], sb1[j], dk[dt]);
         }
     }
-    issue(it + 2);  // into the stage of tile it - 1, which every wave left before the last barrier
+    // tile it + 2 into the stage of tile it - 1, which every wave left before
+    // the last barrier: its statistics (loaded a tile ago), its rows, then
+    // the statistics of the tile after it
+    put_stats(it + 2);
+    issue(it + 2);
+    fetch_stats(it + 3);
     sync_next();
   };
   // per query head: tiles qt < qa reach the wave's diagonal (q0 < kw + WROWS
@@ -754,6 +697,169 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
   store_acc_rows(dv, 1.f, dst, p.ld, kpos, p.seq, vcol, h);
 }
 
+// ---------------------------------------------------------------------------
+// dQ: one workgroup = 128 queries of one head, streaming 64-key tiles of its
+// kv head (K and V rows) through the same three-stage LDS ring as the dK/dV
+// kernel (direct loads, row-major image only, K^T operands by transposing
+// reads); wave w owns 32 queries, whose Q and dO rows it holds in registers
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT) void flash_dq_kernel(FlashParams p, const bf16* __restrict__ dout,
+                                                      const float* __restrict__ lse, const float* __restrict__ Dr,
+                                                      bf16* __restrict__ dqkv) {
+  constexpr int NST = 3;
+  constexpr int STAGE = 2 * TILE * 256;  // K, V
+  constexpr int NDMA = 8;                // loads per wave per tile
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(tid), h = lane >> 5, n = lane & 31;
+  const int head = blockIdx.x, b = blockIdx.z;
+  const int qb = p.n_blocks - 1 - blockIdx.y;  // longest rows first
+  const int hk = head / (p.nq / p.nkv);
+  const int T = gridDim.z * p.seq;
+  const bf16* base = p.qkv + (int64_t)b * p.seq * p.ld;
+  const int q0 = qb * BROWS, qw = q0 + w * WROWS, qpos = qw + n;
+  const int kcol = (p.nq + hk) * D, vcol = (p.nq + p.nkv + hk) * D;
+  const int64_t ldo = (int64_t)p.nq * D;
+
+  bf16x8_t qf[8], dof[8];
+  load_rows_b(qf, base, p.ld, qpos, p.seq, head * D, h);
+  load_rows_b(dof, dout + (int64_t)b * p.seq * ldo, ldo, qpos, p.seq, head * D, h);
+  const int64_t si = (int64_t)head * T + (int64_t)b * p.seq + min(qpos, p.seq - 1);
+  const float l2 = lse[si] * LOG2E, dd = Dr[si];
+  f32x16_t acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = zero16();
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));  // Q, dO, lse and D landed (see dma16)
+
+  const int klast = min(q0 + BROWS, p.seq) - 1;
+  const int ntile = klast / TILE + 1;
+  // key tile i (clamped as in the dK/dV kernel) into stage i % NST: wave w
+  // loads rows 16w .. 16w + 15 of K and V
+  auto issue = [&](int i) __attribute__((always_inline)) {
+    const int k0 = min(i, ntile - 1) * TILE;
+    const int nvalid = min(TILE, p.seq - k0);
+    char* st = smem + (i % NST) * STAGE;
+    const i32x4_t rk = rsrc4(base + (int64_t)k0 * p.ld + kcol, (uint32_t)((nvalid - 1) * p.ld * 2 + 256));
+    const i32x4_t rv = rsrc4(base + (int64_t)k0 * p.ld + vcol, (uint32_t)((nvalid - 1) * p.ld * 2 + 256));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * w + 4 * j + (lane >> 4);
+      const int c = (lane & 15) ^ dr_swz(row);
+      const uint32_t off = row < nvalid ? (uint32_t)(row * p.ld * 2 + c * 16) : 0x80000000u;
+      dma16(rk, st + (16 * w + 4 * j) * 256, off);
+      dma16(rv, st + TILE * 256 + (16 * w + 4 * j) * 256, off);
+    }
+  };
+  auto sync_next = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(NDMA));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  issue(0);
+  issue(1);
+  sync_next();
+
+  // dS of 32-key sub-tile t of the key tile at k0 from its scores, packed as
+  // the bf16 B operands of the dQ product (k-steps j = 0, 1)
+  auto dscore = [&](const f32x16_t& st, const f32x16_t& dp, bf16x8_t (&sb)[2], int t, int k0, auto mask_c)
+                    __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_c)::value;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float ds[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * j + i;
+        float pr = fexp2(st[r] * p.c2 - l2);
+        if constexpr (MASK) {
+          const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (key > qpos) pr = 0.f;
+        }
+        ds[i] = pr * (dp[r] - dd);
+      }
+      u32x4_t c;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] = pack_bf16x2(ds[2 * i], ds[2 * i + 1]);
+      sb[j] = __builtin_bit_cast(bf16x8_t, c);
+    }
+  };
+  // one key tile; MASK as in the forward (separate loops, see there). The two
+  // 32-key sub-tiles run as P(0); P(1) with E(0); D(0) with E(1); D(1), where
+  // P is the score products S = K Q^T and dP = V dO^T (16 MFMAs), E the dS
+  // arithmetic and D the dQ product (8 MFMAs).
+  auto tile = [&](int kt, auto mask_c) __attribute__((always_inline)) {
+    const int k0 = kt * TILE;
+    const char* sK = smem + (kt % NST) * STAGE;
+    const char* sV = sK + TILE * 256;
+    if (!decltype(mask_c)::value || k0 <= qw + WROWS - 1) {
+      bf16x8_t fk[8], fv[8], tk[2][4];
+      f32x16_t st0 = zero16(), dp0 = zero16(), st1 = zero16(), dp1 = zero16();
+      bf16x8_t sb0[2], sb1[2];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        fk[s] = rd_rml(sK, 0, s, lane);
+        fv[s] = rd_rml(sV, 0, s, lane);
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        st0 = mfma(fk[s], qf[s], st0);
+        dp0 = mfma(fv[s], dof[s], dp0);
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        fk[s] = rd_rml(sK, 1, s, lane);
+        fv[s] = rd_rml(sV, 1, s, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        st1 = mfma(fk[s], qf[s], st1);
+        dp1 = mfma(fv[s], dof[s], dp1);
+      }
+      dscore(st0, dp0, sb0, 0, k0, mask_c);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) tk[j][dt] = rd_trl(sK, dt, 0, j, lane);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA,
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // up to three vector ops,
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // an LDS read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(tk[j][dt], sb0[j], acc[dt]);
+      dscore(st1, dp1, sb1, 1, k0, mask_c);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) tk[j][dt] = rd_trl(sK, dt, 1, j, lane);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(tk[j][dt], sb1[j], acc[dt]);
+    }
+    issue(kt + 2);
+    sync_next();
+  };
+  const int kfree = min(ntile, (qw + 1) / TILE);
+  int kt = 0;
+  for (; kt < kfree; ++kt) tile(kt, std::false_type{});
+  for (; kt < ntile; ++kt) tile(kt, std::true_type{});
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+  store_acc_rows(acc, p.scale, dqkv + (int64_t)b * p.seq * p.ld, p.ld, qpos, p.seq, head * D, h);
+}
+
 FlashParams make_params(const AttnDesc& a, const void* qkv) {
   FlashParams p;
   p.qkv = reinterpret_cast<const bf16*>(qkv);
@@ -770,8 +876,8 @@ FlashParams make_params(const AttnDesc& a, const void* qkv) {
 double causal_pairs(const AttnDesc& a) { return (double)a.batch * a.seq * (a.seq + 1.0) / 2.0; }
 
 // double-buffered LDS stages of the backward kernels (above the 64 KB static limit)
-constexpr size_t DQ_LDS = 2 * 3 * TILE * 256;
-constexpr size_t DKDV_LDS = 3 * (2 * TILE * 256 + 2 * TILE * 4);
+constexpr size_t DQ_LDS = 3 * 2 * TILE * 256;
+constexpr size_t DKDV_LDS = 3 * 2 * TILE * 256;  // plus the kernel's static statistics array
 
 rp_status set_lds_limits() {
   static bool done = false;
