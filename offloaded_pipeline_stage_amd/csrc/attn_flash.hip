@@ -22,11 +22,13 @@
 //     32-row tile is registers 8j..8j+7, which hold rows 16j + {4h..4h+3,
 //     8+4h..8+4h+3} for lane half h. The A operand read from LDS uses the same
 //     row permutation, so the sum over k is unchanged.
-// Streamed tiles live in LDS in two layouts: row-major [rows][128] with the
-// 16-byte chunk index XOR-swizzled by row%16 (A operand of QK^T-type products,
-// 16-byte reads), and transposed [128][64 rows] with the 8-byte chunk index
-// XOR-swizzled by d%16 (A operand of PV-type products, 8-byte reads). Both
-// read patterns and the store patterns are free of bank conflicts.
+// Streamed tiles (64 rows of K and V, or of Q and dO) go from global memory
+// straight into LDS stages with buffer loads that target LDS, and are kept
+// row-major only ([rows][128], 16-byte chunks XOR-swizzled by the row): the
+// A operands of QK^T-type products are 16-byte fragment reads of it, those of
+// PV-type products (the transposed tile) come from gfx950's transposing LDS
+// read. No register staging and no in-register transposes; both read
+// patterns are free of bank conflicts.
 //
 // The backward is two deterministic kernels (no atomics): dK/dV per key block
 // (summing over the query heads of its kv group and all later queries), and
@@ -91,42 +93,6 @@ __device__ __forceinline__ bf16x8_t to_operand(const f32x16_t& c, int j) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
-// --- LDS layouts -------------------------------------------------------------
-
-// row-major tile [rows][128] bf16: 256-byte rows of 16 chunks of 16 bytes,
-// chunk index XOR (row%16 ^ (row/16)%4): 16 consecutive rows (a fragment read)
-// and rows {4i + j : i < 16} (a store of the 4-row loads below) both spread
-// over all 16 chunk positions
-__device__ __forceinline__ int rm_off(int row, int c16) {
-  return row * 256 + ((c16 ^ ((row & 15) ^ ((row >> 4) & 3))) << 4);
-}
-// transposed tile [128][64] bf16: 128-byte rows (one per d) of 8 chunks of 16
-// bytes, chunk index XOR (d/2)%8, so that 16 consecutive d rows (a fragment
-// read) hit 16 distinct bank groups. Within each 16-key block the four 4-key
-// groups are stored in the order 0, 2, 1, 3: the 8 keys that one lane needs
-// for an operand (groups h and 2 + h of the block) then form one 16-byte chunk.
-__device__ __forceinline__ int tr_off(int d, int c16) { return d * 128 + ((c16 ^ ((d >> 1) & 7)) << 4); }
-// byte offset of the 8-byte slot of key group kg (keys 4kg .. 4kg + 3) in row d
-__device__ __forceinline__ int tr_slot(int d, int kg) {
-  const int kp = (kg & ~3) | ((kg & 1) << 1) | ((kg >> 1) & 1);
-  return tr_off(d, kp >> 1) + ((kp & 1) << 3);
-}
-
-// A operand of a QK^T-type product: rows 32t + (lane%32) of a row-major tile,
-// d-step s
-__device__ __forceinline__ bf16x8_t rd_rm(const char* lds, int t, int s, int lane) {
-  const int row = 32 * t + (lane & 31);
-  return *reinterpret_cast<const bf16x8_t*>(lds + rm_off(row, 2 * s + (lane >> 5)));
-}
-
-// A operand of a PV-type product: d-row 32dt + (lane%32) of a transposed tile,
-// k-step j of 32-row subtile t (rows 32t + 16j + {4h..4h+3, 8+4h..8+4h+3}):
-// key groups 8t + 4j + h and 8t + 4j + 2 + h, one 16-byte chunk
-__device__ __forceinline__ bf16x8_t rd_tr(const char* lds, int dt, int t, int j, int lane) {
-  const int d = 32 * dt + (lane & 31), h = lane >> 5;
-  return *reinterpret_cast<const bf16x8_t*>(lds + tr_off(d, 2 * (2 * t + j) + h));
-}
-
 // B operand held in registers: row `row` (< rmax, else zero) of a strided
 // matrix, columns [col, col + 128), d-step s for lane half h
 __device__ __forceinline__ void load_rows_b(bf16x8_t (&f)[8], const bf16* g, int64_t ld, int row, int rmax, int col,
@@ -165,178 +131,6 @@ struct FlashParams {
   float scale;
   int n_blocks;      // row blocks of 128 per sequence
 };
-
-// Streamed 64-row tiles of NM matrices in flight between global memory and
-// LDS. Each thread loads 4 consecutive rows x 8 columns of every matrix; the
-// same registers then fill a row-major tile (four 16-byte stores) and/or a
-// transposed tile (transposed in registers, eight 8-byte stores). Loads and
-// stores are separate calls so that a later tile's loads can be issued a whole
-// tile of compute before their stores.
-template <int NM>
-struct TileSet {
-  u32x4_t v[NM][4];
-  __device__ __forceinline__ void load(const bf16* const (&g)[NM], const int64_t (&ld)[NM], const int (&col)[NM],
-                                       int r0, int rmax, int tid) {
-    const int kg = tid & 15, db = tid >> 4;
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = r0 + 4 * kg + j;
-        v[m][j] = u32x4_t{0u, 0u, 0u, 0u};
-        if (row < rmax) v[m][j] = *reinterpret_cast<const u32x4_t*>(g[m] + (int64_t)row * ld[m] + col[m] + 8 * db);
-      }
-  }
-  __device__ __forceinline__ void store_rm(int m, char* t, int tid) const {
-    const int kg = tid & 15, db = tid >> 4;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4_t*>(t + rm_off(4 * kg + j, db)) = v[m][j];
-  }
-  __device__ __forceinline__ void store_tr(int m, char* t, int tid) const {
-    const int kg = tid & 15, db = tid >> 4;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t a0 = v[m][0][q], a1 = v[m][1][q], a2 = v[m][2][q], a3 = v[m][3][q];
-      const u32x2_t lo = u32x2_t{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-      const u32x2_t hi = u32x2_t{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-      const int d0 = 8 * db + 2 * q;
-      *reinterpret_cast<u32x2_t*>(t + tr_slot(d0, kg)) = lo;
-      *reinterpret_cast<u32x2_t*>(t + tr_slot(d0 + 1, kg)) = hi;
-    }
-  }
-};
-
-// ---------------------------------------------------------------------------
-// forward: one workgroup = 128 queries of one head; wave w owns 32 of them.
-// K (row-major) and V (transposed) tiles are double-buffered in LDS: while
-// tile kt is computed, tile kt + 1 (loaded during tile kt - 1) is written to
-// the other buffer and tile kt + 2's global loads are issued; one barrier per
-// tile. Registers are capped for two waves per SIMD, so two workgroups share
-// a CU and one's softmax overlaps the other's MFMAs.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_fwd_kernel(
-    FlashParams p, bf16* __restrict__ o, float* __restrict__ lse) {
-  constexpr int STAGE = 2 * TILE * 256;
-  __shared__ __align__(16) char smem[2 * STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(tid), h = lane >> 5, n = lane & 31;
-  const int head = blockIdx.x, b = blockIdx.z;
-  const int qb = p.n_blocks - 1 - blockIdx.y;  // longest rows first
-  const int hk = head / (p.nq / p.nkv);
-  const bf16* base = p.qkv + (int64_t)b * p.seq * p.ld;
-  const int q0 = qb * BROWS, qw = q0 + w * WROWS, qpos = qw + n;
-  const int kcol = (p.nq + hk) * D, vcol = (p.nq + p.nkv + hk) * D;
-
-  bf16x8_t qf[8];
-  load_rows_b(qf, base, p.ld, qpos, p.seq, head * D, h);
-  f32x16_t acc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = zero16();
-  float m = -INFINITY, l = 0.f;
-
-  const int klast = min(q0 + BROWS, p.seq) - 1;
-  const int ntile = klast / TILE + 1;
-  const bf16* const gsrc[2] = {base, base};
-  const int64_t gld[2] = {p.ld, p.ld};
-  const int gcol[2] = {kcol, vcol};
-  TileSet<2> tp;
-  auto put = [&](char* st) {
-    tp.store_rm(0, st, tid);
-    tp.store_tr(1, st + TILE * 256, tid);
-  };
-  tp.load(gsrc, gld, gcol, 0, p.seq, tid);
-  put(smem);
-  if (ntile > 1) tp.load(gsrc, gld, gcol, TILE, p.seq, tid);
-  __syncthreads();
-  // one key tile; MASK: the tile reaches past the wave's first query (the
-  // last one or two tiles; keys past the sequence end fall in them too, since
-  // every query is before the end). The two variants are separate loops so
-  // that the interior tiles carry no masking code at all.
-  auto tile = [&](int kt, auto mask_c) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_c)::value;
-    const int k0 = kt * TILE;
-    char* sK = smem + (kt & 1) * STAGE;
-    char* sV = sK + TILE * 256;
-    if (!MASK || k0 <= qw + WROWS - 1) {  // else every key of the tile is after every query of the wave
-      f32x16_t st[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        st[t] = zero16();
-#pragma unroll
-        for (int s = 0; s < 8; ++s) st[t] = mfma(rd_rm(sK, t, s, lane), qf[s], st[t]);
-      }
-      float mx = -INFINITY;
-      if constexpr (MASK) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-            const float v = key > qpos ? -INFINITY : st[t][r] * p.c2;
-            st[t][r] = v;
-            mx = fmaxf(mx, v);
-          }
-      } else {
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            st[t][r] *= p.c2;
-            mx = fmaxf(mx, st[t][r]);
-          }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // The running max moves only when some lane's tile max exceeds it by
-      // more than 2^RESCALE_LOG2: until then the probabilities are taken
-      // against the stale max (each at most 2^RESCALE_LOG2, exact in fp32 and
-      // as bf16 operands), which leaves l, acc and lse = m + log2(l)
-      // unchanged and skips the rescale of the accumulator on most tiles.
-      // Tile 0 holds key 0 <= every query, so m is finite after it.
-      if (__builtin_amdgcn_ballot_w64(mx > m + RESCALE_LOG2) != 0) {  // uniform over the wave
-        const float mn = fmaxf(m, mx);
-        const float alpha = fexp2(m - mn);
-        l *= alpha;
-        m = mn;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-      }
-      float sum = 0.f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fexp2(st[t][r] - m);
-          st[t][r] = e;
-          sum += e;
-        }
-      sum += __shfl_xor(sum, 32, 64);
-      l += sum;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const bf16x8_t pb = to_operand(st[t], j);
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(rd_tr(sV, dt, t, j, lane), pb, acc[dt]);
-        }
-    }
-    if (kt + 1 < ntile) {
-      // the other buffer was last read before the previous barrier
-      put(smem + ((kt + 1) & 1) * STAGE);
-      if (kt + 2 < ntile) tp.load(gsrc, gld, gcol, k0 + 2 * TILE, p.seq, tid);
-    }
-    __syncthreads();
-  };
-  // tiles wholly at or before the wave's first query: k0 + TILE - 1 <= qw
-  const int kfree = min(ntile, (qw + 1) / TILE);
-  int kt = 0;
-  for (; kt < kfree; ++kt) tile(kt, std::false_type{});
-  for (; kt < ntile; ++kt) tile(kt, std::true_type{});
-  const float inv = 1.f / l;
-  store_acc_rows(acc, inv, o + (int64_t)b * p.seq * p.nq * D, (int64_t)p.nq * D, qpos, p.seq, head * D, h);
-  if (h == 0 && qpos < p.seq) lse[(int64_t)head * gridDim.z * p.seq + (int64_t)b * p.seq + qpos] = (m + __log2f(l)) * LN2;
-}
 
 // ---------------------------------------------------------------------------
 // backward preprocessing: Dr[h][t] = sum_d dO[t, h, d] * O[t, h, d]
@@ -414,9 +208,12 @@ __device__ __forceinline__ i32x4_t rsrc4(const void* base, uint32_t bytes) {
 // wait the compiler places for a register load can fall inside the loop.
 __device__ __forceinline__ void dma16(i32x4_t r, const void* lds, uint32_t voff) {
   const uint32_t m0 = (uint32_t)(uintptr_t)lds;
-  // an SALU write of M0 needs one wait state before a load that writes LDS
+  // An SALU write of M0 needs one wait state before a load that writes LDS.
+  // M0 cannot be declared clobbered (the compiler reserves it and ignores
+  // the clobber); the kernels that call this use M0 nowhere else (their
+  // code has no other M0 access), and each call sets it afresh.
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(r)
-               : "memory", "m0");
+               : "memory");
 }
 
 // A operand of a dV / dK product from a row-major stage tile: d-row
@@ -858,6 +655,150 @@ __global__ __launch_bounds__(NT) void flash_dq_kernel(FlashParams p, const bf16*
   for (; kt < ntile; ++kt) tile(kt, std::true_type{});
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
   store_acc_rows(acc, p.scale, dqkv + (int64_t)b * p.seq * p.ld, p.ld, qpos, p.seq, head * D, h);
+}
+
+// ---------------------------------------------------------------------------
+// forward: one workgroup = 128 queries of one head; wave w owns 32 of them.
+// The key tiles (K and V rows) go from global memory straight into two LDS
+// stages (the backward kernels' direct loads and row-major layout; V^T
+// operands by transposing reads): tile kt + 1 is loaded while tile kt is
+// computed, one barrier per tile. Registers are capped for two waves per
+// SIMD, so two workgroups share a CU and one's softmax overlaps the other's
+// MFMAs.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_fwd_kernel(
+    FlashParams p, bf16* __restrict__ o, float* __restrict__ lse) {
+  constexpr int STAGE = 2 * TILE * 256;  // K, V
+  __shared__ __align__(16) char smem[2 * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(tid), h = lane >> 5, n = lane & 31;
+  const int head = blockIdx.x, b = blockIdx.z;
+  const int qb = p.n_blocks - 1 - blockIdx.y;  // longest rows first
+  const int hk = head / (p.nq / p.nkv);
+  const bf16* base = p.qkv + (int64_t)b * p.seq * p.ld;
+  const int q0 = qb * BROWS, qw = q0 + w * WROWS, qpos = qw + n;
+  const int kcol = (p.nq + hk) * D, vcol = (p.nq + p.nkv + hk) * D;
+
+  bf16x8_t qf[8];
+  load_rows_b(qf, base, p.ld, qpos, p.seq, head * D, h);
+  f32x16_t acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = zero16();
+  float m = -INFINITY, l = 0.f;
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));  // Q landed (see dma16)
+
+  const int klast = min(q0 + BROWS, p.seq) - 1;
+  const int ntile = klast / TILE + 1;
+  // key tile i (clamped to the last one) into stage i & 1: wave w loads
+  // rows 16w .. 16w + 15 of K and V
+  auto issue = [&](int i) __attribute__((always_inline)) {
+    const int k0 = min(i, ntile - 1) * TILE;
+    const int nvalid = min(TILE, p.seq - k0);
+    char* st = smem + (i & 1) * STAGE;
+    const i32x4_t rk = rsrc4(base + (int64_t)k0 * p.ld + kcol, (uint32_t)((nvalid - 1) * p.ld * 2 + 256));
+    const i32x4_t rv = rsrc4(base + (int64_t)k0 * p.ld + vcol, (uint32_t)((nvalid - 1) * p.ld * 2 + 256));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * w + 4 * j + (lane >> 4);
+      const int c = (lane & 15) ^ dr_swz(row);
+      const uint32_t off = row < nvalid ? (uint32_t)(row * p.ld * 2 + c * 16) : 0x80000000u;
+      dma16(rk, st + (16 * w + 4 * j) * 256, off);
+      dma16(rv, st + TILE * 256 + (16 * w + 4 * j) * 256, off);
+    }
+  };
+  // this wave's loads of the next tile landed, its LDS reads done, then all
+  auto sync_next = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  issue(0);
+  sync_next();
+  // one key tile; MASK: the tile reaches past the wave's first query (the
+  // last one or two tiles; keys past the sequence end fall in them too, since
+  // every query is before the end). The two variants are separate loops so
+  // that the interior tiles carry no masking code at all.
+  auto tile = [&](int kt, auto mask_c) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    const int k0 = kt * TILE;
+    const char* sK = smem + (kt & 1) * STAGE;
+    const char* sV = sK + TILE * 256;
+    issue(kt + 1);  // into the other stage, which every wave left before the last barrier
+    if (!MASK || k0 <= qw + WROWS - 1) {  // else every key of the tile is after every query of the wave
+      f32x16_t st[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        st[t] = zero16();
+#pragma unroll
+        for (int s = 0; s < 8; ++s) st[t] = mfma(rd_rml(sK, t, s, lane), qf[s], st[t]);
+      }
+      float mx = -INFINITY;
+      if constexpr (MASK) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+            const float v = key > qpos ? -INFINITY : st[t][r] * p.c2;
+            st[t][r] = v;
+            mx = fmaxf(mx, v);
+          }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            st[t][r] *= p.c2;
+            mx = fmaxf(mx, st[t][r]);
+          }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // The running max moves only when some lane's tile max exceeds it by
+      // more than 2^RESCALE_LOG2: until then the probabilities are taken
+      // against the stale max (each at most 2^RESCALE_LOG2, exact in fp32 and
+      // as bf16 operands), which leaves l, acc and lse = m + log2(l)
+      // unchanged and skips the rescale of the accumulator on most tiles.
+      // Tile 0 holds key 0 <= every query, so m is finite after it.
+      if (__builtin_amdgcn_ballot_w64(mx > m + RESCALE_LOG2) != 0) {  // uniform over the wave
+        const float mn = fmaxf(m, mx);
+        const float alpha = fexp2(m - mn);
+        l *= alpha;
+        m = mn;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+      }
+      float sum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = fexp2(st[t][r] - m);
+          st[t][r] = e;
+          sum += e;
+        }
+      sum += __shfl_xor(sum, 32, 64);
+      l += sum;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const bf16x8_t pb = to_operand(st[t], j);
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(rd_trl(sV, dt, t, j, lane), pb, acc[dt]);
+        }
+    }
+    sync_next();
+  };
+  // tiles wholly at or before the wave's first query: k0 + TILE - 1 <= qw
+  const int kfree = min(ntile, (qw + 1) / TILE);
+  int kt = 0;
+  for (; kt < kfree; ++kt) tile(kt, std::false_type{});
+  for (; kt < ntile; ++kt) tile(kt, std::true_type{});
+  const float inv = 1.f / l;
+  store_acc_rows(acc, inv, o + (int64_t)b * p.seq * p.nq * D, (int64_t)p.nq * D, qpos, p.seq, head * D, h);
+  if (h == 0 && qpos < p.seq) lse[(int64_t)head * gridDim.z * p.seq + (int64_t)b * p.seq + qpos] = (m + __log2f(l)) * LN2;
 }
 
 FlashParams make_params(const AttnDesc& a, const void* qkv) {

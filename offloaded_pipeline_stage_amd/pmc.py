@@ -322,8 +322,52 @@ def summarize_copies(d: str, title: str, commands, window_ms: float) -> str:
     return "\n".join(lines) + "\n"
 
 
+def summarize_kernels(d: str, title: str, commands, bench_line: str | None = None) -> str:
+    """Text summary of a `rocprofv3 --kernel-trace --stats` run: per kernel
+    (the library's name form) calls, total, average, minimum and maximum
+    duration and share of kernel time; optionally the bench line's own
+    figures for the dominant kernel (its event timing, measured in a run of
+    its own) for comparison."""
+    path = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not path:
+        raise FileNotFoundError(f"no kernel_stats.csv under {d}")
+    rows = list(csv.DictReader(open(path[0])))
+    lines = [f"# {title}", ""] + [f"command: {c}" for c in commands] + [
+        "", "calls  total_ms    avg_us    min_us    max_us   pct  kernel"]
+    for r in rows:
+        lines.append(f"{int(r['Calls']):5d} {int(r['TotalDurationNs']) / 1e6:9.2f} {float(r['AverageNs']) / 1e3:9.1f} "
+                     f"{int(r['MinNs']) / 1e3:9.1f} {int(r['MaxNs']) / 1e3:9.1f} {float(r['Percentage']):5.1f}  "
+                     f"{norm_name(r['Name'])}")
+    if bench_line:
+        b = json.loads(bench_line)
+        rf = b["roofline"]
+        lines += ["", f"bench line of the same build (its own run): the dominant kernel {rf['kernel']} averages "
+                      f"{rf['avg_launch_ms']:.4f} ms per launch by the library's event timing, {rf['achieved']:.1f} "
+                      f"{rf['unit']} = {rf['frac']:.3f} of the {rf['peak']:.0f} {rf['unit']} peak; step "
+                      f"{b['ms_per_step']} ms, {b['value']} {b['unit']}."]
+    return "\n".join(lines) + "\n"
+
+
 if __name__ == "__main__":
     import sys
+    if len(sys.argv) > 1 and sys.argv[1] == "kernels":
+        import argparse
+        ap = argparse.ArgumentParser(description="summarise a kernel trace")
+        ap.add_argument("mode")
+        ap.add_argument("dir")
+        ap.add_argument("--title", required=True)
+        ap.add_argument("--command", action="append", default=[])
+        ap.add_argument("--bench-log", default=None, help="a bench.py output whose last JSON line to quote")
+        ap.add_argument("--out", required=True)
+        a = ap.parse_args()
+        bl = None
+        if a.bench_log:
+            bl = [l for l in open(a.bench_log) if l.startswith("{")][-1]
+        txt = summarize_kernels(a.dir, a.title, a.command, bl)
+        with open(a.out, "w") as f:
+            f.write(txt)
+        print(txt)
+        sys.exit(0)
     if len(sys.argv) > 1 and sys.argv[1] == "copies":
         import argparse
         ap = argparse.ArgumentParser(description="summarise a kernel + memory-copy trace")

@@ -56,3 +56,22 @@ def test_stale_source_gives_none(tmp_path):
     out.write_text(txt.replace('"source_sha": "', '"source_sha": "0'))
     assert pmc.traffic_for(str(out), name) is None
     assert pmc.traffic_for(str(tmp_path / "missing.txt"), name) is None
+
+
+def test_kernel_trace_summary(tmp_path):
+    """The kernel-trace summary: one line per kernel in the library's name
+    form, durations in microseconds, and the bench line's roofline quoted."""
+    d = tmp_path / "kt"
+    d.mkdir()
+    with open(d / "run_kernel_stats.csv", "w") as f:
+        f.write('"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n')
+        f.write('"void rp::(anonymous namespace)::gemm_mfma_kernel<256, 256, 2, 4, true, true, 0, true, 0>'
+                '(rp::(anonymous namespace)::GemmParams)",4,6000000,1500000.0,60.0,1400000,1600000,1.0\n')
+        f.write('"rp::(anonymous namespace)::flash_dkdv_kernel(rp::(anonymous namespace)::FlashParams)",'
+                '2,2000000,1000000.0,20.0,990000,1010000,1.0\n')
+    bench = ('{"ms_per_step": 40.0, "value": 204800.0, "unit": "tokens/s", "roofline": {"kernel": "k", '
+             '"avg_launch_ms": 1.5, "achieved": 1154.7, "unit": "TFLOP/s", "frac": 0.462, "peak": 2500}}')
+    txt = pmc.summarize_kernels(str(tmp_path), "t", ["cmd"], bench)
+    assert "    4      6.00    1500.0    1400.0    1600.0  60.0  gemm_mfma_kernel<256, 256, 2, 4, 1, 1, 0, 1, 0>" in txt
+    assert "flash_dkdv_kernel" in txt and "1000.0" in txt
+    assert "0.462 of the 2500 TFLOP/s peak" in txt
