@@ -60,11 +60,55 @@ struct GemmParams {
   int64_t b_stride;       // elements between consecutive experts' B
   const float2* rope_tab; // EPI_ROPE: (cos, sin) of position p, pair i at [p * 64 + i]
   int rope_seq, rope_heads;
+  int vec;  // row strides of C, R and C2 (and F) multiples of 4 elements, bases aligned to 4 elements
 };
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 7); }
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
+
+// Four consecutive elements of one row, as fp32 values: one 16-byte (fp32)
+// or 8-byte (bf16) access when `vec` (the caller guarantees the alignment),
+// else `cnt` (<= 4) single-element accesses.
+__device__ __forceinline__ void ld4(const float* q, int cnt, bool vec, float (&v)[4]) {
+  if (vec && cnt == 4) {
+    const float4 t = *reinterpret_cast<const float4*>(q);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = e < cnt ? q[e] : 0.f;
+  }
+}
+__device__ __forceinline__ void ld4(const bf16* q, int cnt, bool vec, float (&v)[4]) {
+  if (vec && cnt == 4) {
+    const u32x2_t t = *reinterpret_cast<const u32x2_t*>(q);
+    v[0] = __builtin_bit_cast(float, t[0] << 16); v[1] = __builtin_bit_cast(float, t[0] & 0xffff0000u);
+    v[2] = __builtin_bit_cast(float, t[1] << 16); v[3] = __builtin_bit_cast(float, t[1] & 0xffff0000u);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = e < cnt ? to_f(q[e]) : 0.f;
+  }
+}
+__device__ __forceinline__ void st4(float* q, int cnt, bool vec, const float (&v)[4]) {
+  if (vec && cnt == 4) {
+    *reinterpret_cast<float4*>(q) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e < cnt) q[e] = v[e];
+  }
+}
+__device__ __forceinline__ void st4(bf16* q, int cnt, bool vec, const float (&v)[4]) {
+  if (vec && cnt == 4) {
+    const uint32_t w0 = (uint32_t)to_bf16(v[0]).u | ((uint32_t)to_bf16(v[1]).u << 16);
+    const uint32_t w1 = (uint32_t)to_bf16(v[2]).u | ((uint32_t)to_bf16(v[3]).u << 16);
+    *reinterpret_cast<u32x2_t*>(q) = u32x2_t{w0, w1};
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e < cnt) q[e] = to_bf16(v[e]);
+  }
+}
 
 // Buffer resource over `bytes` bytes at p: loads at offsets >= bytes return 0
 // (the hardware range check), so tile rows past the matrix edge read as zeros
@@ -424,89 +468,161 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(GemmParams p)
     }
   }
 
-  // --- epilogue: lane holds column (lane & 31) of each 32x32 tile, rows
-  // 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15
+  // --- epilogue. The MFMA result gives a lane one column of each 32x32 tile
+  // (rows 8 (r / 4) + 4 (lane / 32) + r % 4 in register r), so storing it
+  // directly takes one 2- or 4-byte access per element and lane. Instead each
+  // wave passes its block through LDS, 32 rows at a time, in a region of its
+  // own: it writes the 32 x WN accumulators and reads them back as rows of 4
+  // consecutive columns per lane, so every global load and store of the
+  // epilogue moves 4 elements (one 8- or 16-byte access when p.vec allows).
+  // Rows of the staging block are WN + 8 floats apart, so the two halves of a
+  // wave's writes (rows 4 apart) fall in different banks.
   const int lc = lane & 31, lr = (lane >> 5) * 4;
-  if constexpr (EPI == EPI_ROPE) {
-    // lane column lc: dim dl of head `head` in acc[i][0], dim dl + 64 in acc[i][1]
-    bf16* c = reinterpret_cast<bf16*>(p.C);
-    const int head = (n0 >> 7) + (wn >> 1);
-    const int dl = (wn & 1) * 32 + lc;
-    const int col = head * 128 + dl;
-    if (col < p.N) {
-      const bool rot = head < p.rope_heads;
+  if constexpr (OUT_F32 && EPI == EPI_STORE) {
+    // Plain fp32 stores go out directly: each half-wave writes a whole
+    // 128-byte row segment per instruction, and the store burst is bound by
+    // HBM writes either way; the staging pass measured 1-3% slower here.
+    if (!p.accumulate) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + lr + (r & 3);
-          if (m >= p.M) continue;
-          float lo = acc[i][0][r], hi = acc[i][1][r];
+        for (int j = 0; j < TN; ++j) {
+          const int n = n0 + wn * WN + j * 32 + lc;
+          if (n >= p.N) continue;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + lr + (r & 3);
+            if (m >= p.M) continue;
+            float v = acc[i][j][r] * p.alpha;
+            if (p.row_scale) v *= p.row_scale[m];
+            reinterpret_cast<float*>(p.C)[blockIdx.y * p.c_split + (int64_t)m * p.ldc + n] = v;
+          }
+        }
+      return;
+    }
+  }
+  __syncthreads();  // the k loop's last LDS reads are done in every wave
+  constexpr int CS = WN + 8;
+  static_assert(WGM * WGN * 32 * CS * 4 <= 2 * (A_BUF + B_BUF), "the staging blocks must fit in the k loop's LDS");
+  float* const stg = reinterpret_cast<float*>(smem) + wave * 32 * CS;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) stg[(8 * (r >> 2) + lr + (r & 3)) * CS + j * 32 + lc] = acc[i][j][r];
+    const int mb = m0 + wm * WM + i * 32;  // first row of this block
+    if constexpr (EPI == EPI_ROPE || EPI == EPI_SWIGLU) {
+      // two halves of WN / 2 columns each: RoPE's first and second members of
+      // the rotation pairs (dims dl and dl + 64 of one head), SwiGLU's gate
+      // and up pre-activations of the same output column
+      constexpr int HW = WN / 2, LPR = HW / 4, RPI = 64 / LPR;
+      const int c4 = 4 * (lane % LPR);
+#pragma unroll
+      for (int q = 0; q < 32 / RPI; ++q) {
+        const int row = lane / LPR + q * RPI, m = mb + row;
+        const float4 a4 = *reinterpret_cast<const float4*>(stg + row * CS + c4);
+        const float4 b4 = *reinterpret_cast<const float4*>(stg + row * CS + HW + c4);
+        float a[4] = {a4.x, a4.y, a4.z, a4.w}, bb[4] = {b4.x, b4.y, b4.z, b4.w};
+        if (m >= p.M) continue;
+        if constexpr (EPI == EPI_ROPE) {
+          bf16* c = reinterpret_cast<bf16*>(p.C);
+          const int head = (n0 >> 7) + (wn >> 1);
+          const int dl = (wn & 1) * 32 + c4;
+          const int col = head * 128 + dl;
+          if (col >= p.N) continue;  // whole heads: the four dims are in range together
           if (p.R) {  // an addend of the same layout (the LoRA deltas), before the rotation
             const bf16* rr = reinterpret_cast<const bf16*>(p.R) + (int64_t)m * p.ldr + col;
-            lo += to_f(rr[0]);
-            hi += to_f(rr[64]);
+            float x[4], y[4];
+            ld4(rr, 4, p.vec, x);
+            ld4(rr + 64, 4, p.vec, y);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              a[e] += x[e];
+              bb[e] += y[e];
+            }
           }
-          if (rot) {
-            const float2 cs = p.rope_tab[(m % p.rope_seq) * 64 + dl];
-            const float l2 = lo * cs.x - hi * cs.y;
-            hi = hi * cs.x + lo * cs.y;
-            lo = l2;
+          if (head < p.rope_heads) {
+            const float2* tab = p.rope_tab + (m % p.rope_seq) * 64 + dl;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float2 cs = tab[e];
+              const float l2 = a[e] * cs.x - bb[e] * cs.y;
+              bb[e] = bb[e] * cs.x + a[e] * cs.y;
+              a[e] = l2;
+            }
           }
-          c[(int64_t)m * p.ldc + col] = to_bf16(lo);
-          c[(int64_t)m * p.ldc + col + 64] = to_bf16(hi);
+          st4(c + (int64_t)m * p.ldc + col, 4, p.vec, a);
+          st4(c + (int64_t)m * p.ldc + col + 64, 4, p.vec, bb);
+        } else {
+          const int f = n0 + wn * HW + c4;
+          if (f >= p.F) continue;
+          const int cnt = min(4, p.F - f);
+          float mo[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mo[e] = silu_f(a[e]) * bb[e];
+          bf16* gu = reinterpret_cast<bf16*>(p.C) + (int64_t)m * p.ldc;
+          st4(gu + f, cnt, p.vec, a);
+          st4(gu + p.F + f, cnt, p.vec, bb);
+          st4(reinterpret_cast<bf16*>(p.C2) + (int64_t)m * p.ldc2 + f, cnt, p.vec, mo);
         }
+      }
+    } else {
+      constexpr int LPR = WN / 4, RPI = 64 / LPR;
+      const int c4 = 4 * (lane % LPR);
+      const int n = n0 + wn * WN + c4;
+#pragma unroll
+      for (int q = 0; q < 32 / RPI; ++q) {
+        const int row = lane / LPR + q * RPI, m = mb + row;
+        const float4 a4 = *reinterpret_cast<const float4*>(stg + row * CS + c4);
+        if (m >= p.M || n >= p.N) continue;
+        const int cnt = min(4, p.N - n);
+        float v[4] = {a4.x * p.alpha, a4.y * p.alpha, a4.z * p.alpha, a4.w * p.alpha};
+        if (p.row_scale) {
+          const float rs = p.row_scale[m];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] *= rs;
+        }
+        if constexpr (EPI == EPI_SWIGLU_BWD) {
+          const bf16* gu = reinterpret_cast<const bf16*>(p.R) + (int64_t)m * p.ldr;
+          float g[4], u[4], dg[4], du[4];
+          ld4(gu + n, cnt, p.vec, g);
+          ld4(gu + p.F + n, cnt, p.vec, u);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float sg = 1.f / (1.f + __expf(-g[e]));
+            dg[e] = v[e] * u[e] * sg * (1.f + g[e] * (1.f - sg));
+            du[e] = v[e] * g[e] * sg;
+          }
+          bf16* dgu = reinterpret_cast<bf16*>(p.C) + (int64_t)m * p.ldc;
+          st4(dgu + n, cnt, p.vec, dg);
+          st4(dgu + p.F + n, cnt, p.vec, du);
+        } else if constexpr (OUT_F32) {
+          float* c = reinterpret_cast<float*>(p.C) + blockIdx.y * p.c_split + (int64_t)m * p.ldc + n;
+          if (EPI == EPI_RESID) {
+            float x[4];
+            ld4(reinterpret_cast<const float*>(p.R) + (int64_t)m * p.ldr + n, cnt, p.vec, x);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += x[e];
+          }
+          if (p.accumulate) {
+            float o[4];
+            ld4(c, cnt, p.vec, o);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = o[e] + v[e];
+          }
+          st4(c, cnt, p.vec, v);
+        } else {
+          if (EPI == EPI_RESID) {
+            float x[4];
+            ld4(reinterpret_cast<const bf16*>(p.R) + (int64_t)m * p.ldr + n, cnt, p.vec, x);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += x[e];
+          }
+          st4(reinterpret_cast<bf16*>(p.C) + (int64_t)m * p.ldc + n, cnt, p.vec, v);
+        }
+      }
     }
-  } else if constexpr (EPI == EPI_SWIGLU) {
-    bf16* gu = reinterpret_cast<bf16*>(p.C);
-    bf16* mo = reinterpret_cast<bf16*>(p.C2);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN / 2; ++j) {
-        const int f = n0 + wn * (WN / 2) + j * 32 + lc;
-        if (f >= p.F) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + lr + (r & 3);
-          if (m >= p.M) continue;
-          const float g = acc[i][j][r], u = acc[i][j + TN / 2][r];
-          gu[(int64_t)m * p.ldc + f] = to_bf16(g);
-          gu[(int64_t)m * p.ldc + p.F + f] = to_bf16(u);
-          mo[(int64_t)m * p.ldc2 + f] = to_bf16(silu_f(g) * u);
-        }
-      }
-  } else {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WN + j * 32 + lc;
-        if (n >= p.N) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + lr + (r & 3);
-          if (m >= p.M) continue;
-          float v = acc[i][j][r] * p.alpha;
-          if (p.row_scale) v *= p.row_scale[m];
-          if constexpr (EPI == EPI_SWIGLU_BWD) {
-            const bf16* gu = reinterpret_cast<const bf16*>(p.R);
-            const float g = to_f(gu[(int64_t)m * p.ldr + n]);
-            const float u = to_f(gu[(int64_t)m * p.ldr + p.F + n]);
-            const float sg = 1.f / (1.f + __expf(-g));
-            bf16* dgu = reinterpret_cast<bf16*>(p.C);
-            dgu[(int64_t)m * p.ldc + n] = to_bf16(v * u * sg * (1.f + g * (1.f - sg)));
-            dgu[(int64_t)m * p.ldc + p.F + n] = to_bf16(v * g * sg);
-          } else if constexpr (OUT_F32) {
-            float* c = reinterpret_cast<float*>(p.C) + blockIdx.y * p.c_split + (int64_t)m * p.ldc + n;
-            if (EPI == EPI_RESID) v += reinterpret_cast<const float*>(p.R)[(int64_t)m * p.ldr + n];
-            *c = p.accumulate ? *c + v : v;
-          } else {
-            if (EPI == EPI_RESID) v += to_f(reinterpret_cast<const bf16*>(p.R)[(int64_t)m * p.ldr + n]);
-            reinterpret_cast<bf16*>(p.C)[(int64_t)m * p.ldc + n] = to_bf16(v);
-          }
-        }
-      }
   }
 }
 
@@ -667,6 +783,17 @@ rp_status launch_mfma(const GemmDesc& d, hipStream_t s) {
            "gemm(bf16): each operand must span less than 2 GiB");
   p.a_bytes = (uint32_t)ab;
   p.b_bytes = (uint32_t)bb;
+  {
+    // the epilogue's four-element accesses: row strides and the column offset
+    // F in multiples of 4 elements, bases aligned to 4 elements
+    const size_t ce = OF32 ? 4 : 2;
+    const size_t re = EPI == EPI_RESID ? ce : 2;
+    auto al = [](const void* q, size_t b) { return reinterpret_cast<uintptr_t>(q) % b == 0; };
+    bool v = p.ldc % 4 == 0 && al(p.C, 4 * ce) && p.c_split % 4 == 0 && p.F % 4 == 0;
+    if (p.R) v = v && p.ldr % 4 == 0 && al(p.R, 4 * re);
+    if (p.C2) v = v && p.ldc2 % 4 == 0 && al(p.C2, 8);
+    p.vec = v ? 1 : 0;
+  }
   const size_t lds = 2 * ((size_t)BM * (AK ? 144 : 128) + (size_t)BN * (BKM ? 144 : 128));
   static bool attr_set = false;  // one instantiation per template: set once
   if (!attr_set) {

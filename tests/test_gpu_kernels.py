@@ -243,3 +243,32 @@ def test_embed_out_of_range_ids_give_zero_rows(B):
     assert torch.equal(x0[ok], O.embed(ids[ok], table))
     ref = O.embed_backward(ids[ok], dx0[ok].double(), V)
     assert max_rel(dtable, ref) < 1e-6
+
+
+@pytest.mark.parametrize("M,N,K,ldc,out_f32,accumulate", [
+    (70, 131, 80, 131, True, False),    # row stride not a multiple of 4: element-wise epilogue
+    (70, 131, 80, 131, False, False),
+    (300, 1002, 136, 1002, False, False),  # N = 2 mod 4: a partial last group of four columns
+    (300, 94, 128, 100, True, True),    # aligned stride, partial last group, accumulation
+    (257, 520, 64, 520, False, False),  # ragged rows, whole groups
+])
+def test_gemm_epilogue_edges(B, M, N, K, ldc, out_f32, accumulate):
+    """The epilogue's four-column accesses: vector accesses only where the row
+    stride and base allow, element-wise otherwise, columns past N untouched."""
+    say("gemm epilogue", M, N, K, ldc, out_f32, accumulate)
+    ctx = _ctx(B)
+    a_s, a = _operand(M, K, True, 31, f"ea{M}{K}")
+    b_s, b = _operand(N, K, True, 32, f"eb{N}{K}")
+    dev = torch.device("cuda")
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    base = synth.normal((M, ldc), 33, f"ec{M}{ldc}").to(dt)
+    C = base.clone().to(dev)
+    ctx.op_gemm_bf16(M, N, K, a_s.to(dev), K, True, b_s.to(dev), K, True, C, ldc, out_f32=out_f32,
+                     accumulate=accumulate)
+    ctx.sync()
+    ref = a @ b.T
+    if accumulate:
+        ref = ref + base[:, :N].double()
+    tol = 1e-5 if out_f32 else 2 ** -8
+    assert max_rel(C[:, :N], ref) < tol
+    assert torch.equal(C[:, N:].cpu(), base[:, N:])  # columns past N untouched
