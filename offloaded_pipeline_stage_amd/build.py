@@ -39,9 +39,16 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
+# Per-file flags. The GEMM's k-tile body (its MFMA, fragment-read and loader
+# slots) is unrolled in full by pragma; with the transposing reads of M-major
+# operands it exceeds the default threshold for such pragmas, and a loop left
+# partly rolled keeps the tile loaders in scratch memory.
+EXTRA = {"gemm.hip": ["-mllvm", "-pragma-unroll-threshold=1000000"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + COMMON + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + COMMON + EXTRA.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -3,18 +3,18 @@
 // LM-head shard products. These are the dense contractions that carry almost
 // all of a layer's FLOPs (the paper's appendix C counts matrix multiplies only).
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16 on gfx950. 256 threads = 4 waves in a
-// 2 x 2 grid, each wave owns a (BM/2) x (BN/2) block of 32x32 MFMA tiles.
+// bf16 path: v_mfma_f32_32x32x16_bf16 on gfx950. WGM x WGN waves per
+// workgroup (2 x 4 for the 256 x 256 tiles of the large products), each
+// owning a (BM/WGM) x (BN/WGN) block of 32x32 MFMA tiles.
 // K advances 64 at a time through double-buffered LDS (one barrier per step):
 // the next step's global loads are issued before the current step's MFMAs.
-// LDS rows are 128 bytes (64 bf16 of K) with the 16-byte chunk index XOR-
-// swizzled by row bits 0-2 and 3-5, so the MFMA fragment reads (32 rows, same
-// chunk) and both store patterns below are free of bank conflicts.
-// Operands whose K is the contiguous dimension are copied 16 bytes at a time;
-// operands whose M/N is contiguous (the transposed operands of the backward
-// products) are loaded as 4 K-rows x 8 elements and transposed in registers
-// before the LDS store, so every layout reaches the same LDS image and the
-// same MFMA loop.
+// Both kinds of operand are copied 16 bytes at a time and stored into LDS as
+// they lie in memory: operands whose K is the contiguous dimension as rows of
+// 64 k (padded to 144 bytes), operands whose M/N is contiguous (the
+// transposed operands of the backward products) as 64 k rows of the tile's
+// M/N extent, whose fragments come from gfx950's transposing LDS read. The
+// MFMA loop is the same for every layout, and the kernel transposes nothing,
+// in registers or otherwise.
 // Epilogues fuse the residual add, the SwiGLU activation (gate and up columns
 // of one output column are held by the same lane) and its backward, and fp32
 // accumulation.
@@ -62,8 +62,6 @@ struct GemmParams {
   int rope_seq, rope_heads;
   int vec;  // row strides of C, R and C2 (and F) multiples of 4 elements, bases aligned to 4 elements
 };
-
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 7); }
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
 
@@ -128,18 +126,43 @@ __device__ __forceinline__ u32x4_t bload(__amdgpu_buffer_rsrc_t r, uint32_t voff
 // K-major operands: rows padded to 144 bytes (16-byte chunk kc at row*144 +
 // 16*kc); the 8 lanes of a read phase hit 8 distinct 16-byte bank groups and
 // fragment addresses step by immediates.
-// M-major operands (written after an in-register transpose): 128-byte rows,
-// chunk index XOR-swizzled by row bits, which keeps the 8-byte transposed
-// stores and the 16-byte fragment reads conflict-free.
+// M-major operands are kept as they lie in memory: 64 k rows of R elements
+// (2R bytes each, so the tile takes R x 128 bytes like a K-major one without
+// padding), 16-byte chunk c of k row k at position c ^ 4 (k % 4). Fragments
+// come from transposing LDS reads (read_mm); the stores of whole rows and
+// the reads of four k rows x four chunks are both free of bank conflicts.
 template <bool KM> struct Lay;
 template <> struct Lay<true> {
   static constexpr int RS = 144;
   __device__ __forceinline__ static int off(int row, int kc) { return row * 144 + kc * 16; }
 };
 template <> struct Lay<false> {
-  static constexpr int RS = 128;
-  __device__ __forceinline__ static int off(int row, int kc) { return row * 128 + ((kc ^ swz(row)) << 4); }
+  static constexpr int RS = 128;  // bytes per operand row (index m or n) of the tile
+  template <int R>
+  __device__ __forceinline__ static int off(int k, int m) {  // element (m, k), m a multiple of 4
+    return k * (2 * R) + (((m >> 3) ^ (4 * (k & 3))) << 4) + (m & 4) * 2;
+  }
 };
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t* lds_bf16x4_t;
+
+// Fragment of an M-major operand tile of R rows: operand rows rb + (lane %
+// 32), k-substep ks (k = 16 ks + 8 (lane / 32) + 0..7, the order of the
+// K-major fragments), as two transposing reads (ds_read_b64_tr_b16). In such
+// a read, lane c of each 16-lane group addresses 4 consecutive elements of
+// one k row and receives, in slot j, element c % 4 of the 4 addressed by lane
+// 4j + c / 4; so lane c addresses k row k0 + c / 4 at m0 + 4 (c % 4), and
+// every lane receives its own m for k rows k0 .. k0 + 3.
+template <int R>
+__device__ __forceinline__ bf16x8_t read_mm(const char* t, int rb, int ks, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  const int m = rb + 16 * (g & 1) + 4 * (c & 3);
+  const int k = 16 * ks + 8 * (lane >> 5) + (c >> 2);
+  const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t)(t + Lay<false>::off<R>(k, m)));
+  const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t)(t + Lay<false>::off<R>(k + 4, m)));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 // --- global -> register -> LDS copies --------------------------------------
 
@@ -226,58 +249,41 @@ struct LoaderK {
   }
 };
 
-// M-major operand: element (r, k) at g[k * ld + r]; loaded as blocks of
-// 4 K-rows x 8 r, transposed in registers into 8 rows x 4 k. Rows k >= K lie
-// past the end of the buffer and read as zeros.
+// M-major operand: element (r, k) at g[k * ld + r]; 16-byte chunks (8
+// consecutive r of one k row) copied unchanged into the tile (see Lay<false>).
+// Rows k >= kend read as zeros.
 template <int R, int NT>
 struct LoaderM {
-  static constexpr int NRB = R / 8;
-  static_assert((BK / 4) * NRB % NT == 0, "4x8 blocks must split evenly over the threads");
-  static constexpr int NBLK = (BK / 4) * NRB / NT;
-  u32x4_t reg[NBLK][4];
-  uint32_t voff[NBLK];
-  int krow[NBLK];  // first k row of each block
+  static constexpr int CPR = R / 8;  // chunks per k row
+  static_assert(NT % CPR == 0 && BK * CPR % NT == 0, "k rows of chunks must split evenly over the threads");
+  static constexpr int NCH = BK * CPR / NT;
+  static constexpr int KSTEP = NT / CPR;  // k rows between a thread's chunks
+  u32x4_t reg[NCH];
+  uint32_t voff;  // this thread's chunk in k row krow (at k0 = 0)
+  int krow, ch;
   __device__ __forceinline__ void init(int64_t ld, int row0, int tid) {
-#pragma unroll
-    for (int i = 0; i < NBLK; ++i) {
-      const int b = tid + i * NT;
-      const int rb = b % NRB, kb = b / NRB;
-      krow[i] = kb * 4;
-      voff[i] = (uint32_t)(((int64_t)(kb * 4) * ld + row0 + rb * 8) * 2);
-    }
+    krow = tid / CPR;
+    ch = tid % CPR;
+    voff = (uint32_t)(((int64_t)krow * ld + row0 + ch * 8) * 2);
   }
-  // issue units: unit i is one 4 x 8 block (four loads / its transposed stores)
-  static constexpr int NUNIT = NBLK;
-  // k rows >= kend (past K, or past this split's range) read as zeros
+  // issue units: unit i is one chunk (load / store)
+  static constexpr int NUNIT = NCH;
   __device__ __forceinline__ void load_unit(__amdgpu_buffer_rsrc_t rs, int64_t ld, int k0, int kend, int i) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t oob = (k0 + krow[i] + j < kend) ? 0u : OOB_SHIFT;
-      reg[i][j] = bload(rs, voff[i] + (uint32_t)(((int64_t)(k0 + j) * ld) * 2) + oob);
-    }
+    const int k = k0 + krow + i * KSTEP;
+    const uint32_t oob = k < kend ? 0u : OOB_SHIFT;
+    reg[i] = bload(rs, voff + (uint32_t)(((int64_t)(k0 + i * KSTEP) * ld) * 2) + oob);
   }
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t ld, int k0, int kend) {
 #pragma unroll
-    for (int i = 0; i < NBLK; ++i) load_unit(rs, ld, k0, kend, i);
+    for (int i = 0; i < NCH; ++i) load_unit(rs, ld, k0, kend, i);
+  }
+  __device__ __forceinline__ void store_unit(char* lds, int tid, int i) {
+    const int k = krow + i * KSTEP;
+    *reinterpret_cast<u32x4_t*>(lds + Lay<false>::off<R>(k, ch * 8)) = reg[i];
   }
   __device__ __forceinline__ void store(char* lds, int tid) {
 #pragma unroll
-    for (int i = 0; i < NBLK; ++i) store_unit(lds, tid, i);
-  }
-  __device__ __forceinline__ void store_unit(char* lds, int tid, int i) {
-    const int b = tid + i * NT;
-    const int rb = b % NRB, kb = b / NRB;
-    const int kc = kb >> 1, half = kb & 1;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      // rows 2q (low halves) and 2q+1 (high halves)
-      const uint32_t a0 = reg[i][0][q], a1 = reg[i][1][q], a2 = reg[i][2][q], a3 = reg[i][3][q];
-      const u32x2_t lo = u32x2_t{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-      const u32x2_t hi = u32x2_t{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-      const int r0 = rb * 8 + 2 * q;
-      *reinterpret_cast<u32x2_t*>(lds + Lay<false>::off(r0, kc) + half * 8) = lo;
-      *reinterpret_cast<u32x2_t*>(lds + Lay<false>::off(r0 + 1, kc) + half * 8) = hi;
-    }
+    for (int i = 0; i < NCH; ++i) store_unit(lds, tid, i);
   }
 };
 
@@ -378,10 +384,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(GemmParams p)
   // first MFMA of a substep waits for two reads only
   auto read_one = [&](const char* a_s, const char* b_s, int ks, int q, bf16x8_t (&af)[TM], bf16x8_t (&bfr)[TN]) {
     const int kc = ks * 2 + kh;
-    if (q >= 1 && q <= TN) bfr[q - 1] = *reinterpret_cast<const bf16x8_t*>(b_s + Lay<BKM>::off(brow + (q - 1) * 32, kc));
-    else {
+    if (q >= 1 && q <= TN) {
+      if constexpr (BKM) bfr[q - 1] = *reinterpret_cast<const bf16x8_t*>(b_s + Lay<true>::off(brow + (q - 1) * 32, kc));
+      else bfr[q - 1] = read_mm<BN>(b_s, wn * WN + (q - 1) * 32, ks, lane);
+    } else {
       const int i = q == 0 ? 0 : q - TN;
-      af[i] = *reinterpret_cast<const bf16x8_t*>(a_s + Lay<AK>::off(arow + i * 32, kc));
+      if constexpr (AK) af[i] = *reinterpret_cast<const bf16x8_t*>(a_s + Lay<true>::off(arow + i * 32, kc));
+      else af[i] = read_mm<BM>(a_s, wm * WM + i * 32, ks, lane);
     }
   };
 
@@ -915,23 +924,6 @@ rp_status gemm(const GemmDesc& dd, hipStream_t s) {
   const int64_t n_eff = d.epi == EPI_SWIGLU ? d.N / 2 : d.N;
   const int64_t big = cdiv(d.M, 256) * cdiv(n_eff, d.epi == EPI_SWIGLU ? 128 : 256);
   if (big < 240) return dispatch_epi<128, 128, 2, 2>(d, s);
-  if (!d.a_kmajor && !d.b_kmajor) {
-    // both operands M-major (weight gradients): transpose both through the
-    // scratch and run the K-major kernel, which is far faster than
-    // transposing tiles in registers on the way to LDS
-    if (d.tr && d.tr_bytes >= gemm_tr_bytes(d.M, d.N, d.K) && d.M % 8 == 0 && d.N % 8 == 0 && d.K % 8 == 0) {
-      GemmDesc e = d;
-      char* ta = reinterpret_cast<char*>(d.tr);
-      char* tb = ta + align_up((size_t)d.M * d.K * 2, 256);
-      RP_TRY(transpose_bf16(d.A, d.lda, ta, d.K, d.K, d.M, s));
-      RP_TRY(transpose_bf16(d.B, d.ldb, tb, d.K, d.K, d.N, s));
-      e.A = ta; e.lda = d.K; e.a_kmajor = true;
-      e.B = tb; e.ldb = d.K; e.b_kmajor = true;
-      e.tr = nullptr;
-      return dispatch_epi<256, 256, 2, 4>(e, s);
-    }
-    return dispatch_epi<256, 256, 2, 2>(d, s);
-  }
   return dispatch_epi<256, 256, 2, 4>(d, s);
 }
 

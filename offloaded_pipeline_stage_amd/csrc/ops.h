@@ -49,10 +49,6 @@ struct GemmDesc {
   void* C2 = nullptr; int64_t ldc2 = 0;
   float* tmp = nullptr;           // fp32 [M, N] scratch for the unfused fp32 path
   bool force_simple = false;      // use the generic kernel even for bf16
-  // scratch for bf16 products whose operands are both M-major (the weight
-  // gradients dY^T X): both are transposed into it (gemm_tr_bytes) and the
-  // K-major kernel runs on the copies
-  void* tr = nullptr; size_t tr_bytes = 0;
   float alpha = 1.f;              // C = alpha * A B^T (+ R): store / residual epilogues
   // split-K (bf16 operands, plain fp32 store): K is cut into split_k ranges,
   // each writes an fp32 partial into `partial` (splitk_bytes), and a fixed-

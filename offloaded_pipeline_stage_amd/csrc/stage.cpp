@@ -54,8 +54,6 @@ struct BwdTmp {
   float* Dbuf = nullptr;   // [nq, T]
   float* dm_tmp = nullptr; // fp32 [T, F] (unfused fp32 path)
   float* part = nullptr;   // RMSNorm dgamma partials
-  void* tr = nullptr;      // operand transposes of the weight-gradient products
-  size_t tr_bytes = 0;
   void* g_qkv = nullptr;   // LoRA: dq|dk|dv times B_q|B_k|B_v [T, 3r]
   void* g_o = nullptr;     // LoRA: dh1 B_o [T, r]
   float* splitk = nullptr; // split-K partials of the adapter-gradient products
@@ -158,14 +156,6 @@ void carve(Bump& bp, const Shape& s, int64_t T, int seq, int n_layers, bool keep
     if (s.dt == RP_DTYPE_F32) b.dm_tmp = bp.take<float>(T * s.F * 4);
     b.part = bp.take<float>(rmsnorm_bwd_part_bytes((int)T, s.H));
     if (s.qkn) b.qkpart = bp.take<float>(qknorm_part_bytes((int)T, s.nq + s.nkv, s.d));
-    if (s.dt == RP_DTYPE_BF16) {
-      // largest weight-gradient product: dW_gu [2F, H] over T tokens
-      size_t need = 0;
-      const int64_t shapes[4][2] = {{s.H, s.F}, {2 * (int64_t)s.F, s.H}, {s.H, s.Q}, {s.QKV, s.H}};
-      for (auto& mn : shapes) need = std::max(need, gemm_tr_bytes(mn[0], mn[1], T));
-      b.tr = bp.take(need);
-      b.tr_bytes = need;
-    }
     if (s.r > 0) {
       b.g_qkv = bp.take(T * 3 * s.r * s.es);
       b.g_o = bp.take(T * s.r * s.es);
@@ -353,8 +343,6 @@ rp_status wgrad(int M, int N, int K, const void* A, int64_t lda, const void* Bm,
                 int dt, const BwdTmp& B, float alpha, bool accum, hipStream_t st) {
   GemmDesc g = mk(M, N, K, A, lda, false, Bm, ldb, false, C, ldc, dt, RP_DTYPE_F32);
   g.accumulate = accum;
-  g.tr = B.tr;
-  g.tr_bytes = B.tr_bytes;
   g.alpha = alpha;
   if (B.splitk) {
     g.split_k = 0;  // automatic for the skinny adapter products
@@ -766,10 +754,7 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
     if (pre_tr) {
       RP_TRY(gemm(mk(vs, s.H, (int)T, dzt, (int)T, true, zzt, (int)T, true, w.g, s.H, dt, RP_DTYPE_F32), st));
     } else {
-      GemmDesc gw = mk(vs, s.H, (int)T, dz, vs, false, zz, s.H, false, w.g, s.H, dt, RP_DTYPE_F32);
-      gw.tr = tr;
-      gw.tr_bytes = tr_bytes;
-      RP_TRY(gemm(gw, st));
+      RP_TRY(gemm(mk(vs, s.H, (int)T, dz, vs, false, zz, s.H, false, w.g, s.H, dt, RP_DTYPE_F32), st));
     }
     RP_TRY(mark_consumed(c, w));
     RP_TRY(mark_grad_ready(c, w));
