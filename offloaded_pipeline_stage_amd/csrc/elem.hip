@@ -581,84 +581,6 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
 }
 
 // The cross-entropy gradient of a bf16 shard, also written transposed:
-// dz[t][v] as ce_grad_kernel computes it (the same operations, so the same
-// bits) and dzt[v][t] = dz[t][v], the K-major operand of the weight-gradient
-// product dW = dz^T x. Tiles of 128 rows x 64 columns: a lane takes the same
-// 8 columns of two pairs of adjacent rows, stores them to dz 16 bytes at a
-// time, and pairs each two rows into 32-bit words of the transposed rows in
-// the swizzled LDS tile of transpose_bf16_kernel. rows and Vs are multiples
-// of 8.
-__global__ __launch_bounds__(256) void ce_grad_tr_kernel(const float* __restrict__ z, int64_t ld, int rows, int Vs,
-                                                         int vlo, const int32_t* __restrict__ labels, int vocab,
-                                                         const float* __restrict__ lse,
-                                                         const float* __restrict__ inv_n, bf16* __restrict__ dz,
-                                                         int64_t ldz, bf16* __restrict__ dzt, int64_t ldt) {
-  __shared__ uint32_t tile[64 * 64];
-  const int r0 = blockIdx.y * 128, c0 = blockIdx.x * 64;
-  const int q = threadIdx.x & 7, c = c0 + 8 * q;
-  const float scn = inv_n[0];
-  // all loads first: rows r0 + 2w + i for w = lane / 8 + 32 h
-  float4 v[2][2][2];
-  float lt[2][2], sc[2][2];
-  int j0[2][2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int t = r0 + 2 * ((threadIdx.x >> 3) + 32 * h) + i;
-      v[h][i][0] = v[h][i][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-      lt[h][i] = 0.f;
-      sc[h][i] = 0.f;
-      j0[h][i] = -1;
-      if (t < rows && c < Vs) {
-        const float* zr = z + (int64_t)t * ld + c;
-        v[h][i][0] = *reinterpret_cast<const float4*>(zr);
-        v[h][i][1] = *reinterpret_cast<const float4*>(zr + 4);
-        const int y = labels[t];
-        const bool valid = y >= 0 && y < vocab;
-        lt[h][i] = lse[t];
-        sc[h][i] = valid ? scn : 0.f;
-        j0[h][i] = valid ? y - vlo - c : -1;  // the label's position among the 8 columns (may lie outside)
-      }
-    }
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int w = (threadIdx.x >> 3) + 32 * h;
-    uint32_t pk[2][4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float x[8] = {v[h][i][0].x, v[h][i][0].y, v[h][i][0].z, v[h][i][0].w,
-                          v[h][i][1].x, v[h][i][1].y, v[h][i][1].z, v[h][i][1].w};
-      float g[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        g[e] = __expf(x[e] - lt[h][i]) * sc[h][i];
-        if (j0[h][i] == e) g[e] -= sc[h][i];
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pk[i][e] = uint32_t(to_bf16(g[2 * e]).u) | (uint32_t(to_bf16(g[2 * e + 1]).u) << 16);
-      const int t = r0 + 2 * w + i;
-      if (t < rows && c < Vs)
-        *reinterpret_cast<uint4*>(dz + (int64_t)t * ldz + c) = make_uint4(pk[i][0], pk[i][1], pk[i][2], pk[i][3]);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      // transposed rows 8q + 2e (the low halves) and 8q + 2e + 1 (the high)
-      tile[tr_word(8 * q + 2 * e, w)] = (pk[0][e] & 0xffffu) | (pk[1][e] << 16);
-      tile[tr_word(8 * q + 2 * e + 1, w)] = (pk[0][e] >> 16) | (pk[1][e] & 0xffff0000u);
-    }
-  }
-  __syncthreads();
-  const int k = threadIdx.x & 15;
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const int cc = (threadIdx.x >> 4) + 16 * h;
-    if (c0 + cc >= Vs || r0 + 8 * k >= rows) continue;
-    *reinterpret_cast<uint4*>(dzt + (int64_t)(c0 + cc) * ldt + r0 + 8 * k) =
-        *reinterpret_cast<const uint4*>(&tile[tr_word(cc, 4 * k)]);
-  }
-}
-
 __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N, float* __restrict__ C,
                                      int64_t ldc, int accumulate) {
   const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
@@ -892,19 +814,6 @@ rp_status ce_grad(int dt, const float* logits, int64_t ld, int T, int Vs, int vl
     else
       RP_LAUNCH((ce_grad_kernel<float, false>), g, b, 0, s, logits, ld, Vs, vlo, labels, vocab, lse, inv_n, (float*)dz, ldz);
   }
-  return RP_OK;
-}
-
-rp_status ce_grad_tr(const float* logits, int64_t ld, int T, int Vs, int vlo, const int32_t* labels, int vocab,
-                     const float* lse, const float* inv_n, void* dz, int64_t ldz, void* dzt, int64_t ldt,
-                     hipStream_t s) {
-  if (T == 0 || Vs == 0) return RP_OK;
-  RP_CHECK(T % 8 == 0 && Vs % 8 == 0 && ld % 4 == 0 && ldz % 8 == 0 && ldt % 8 == 0 && ld >= Vs && ldz >= Vs &&
-               ldt >= T && ((uintptr_t)logits & 15) == 0 && ((uintptr_t)dz & 15) == 0 && ((uintptr_t)dzt & 15) == 0,
-           RP_ERR_UNSUPPORTED, "ce_grad_tr: rows and shard width multiples of 8, aligned 16-byte rows");
-  TraceScope ts(s, "ce_grad_tr_kernel", 0.0, (double)T * Vs * (4 + 2 + 2) + 8.0 * T);
-  RP_LAUNCH(ce_grad_tr_kernel, dim3((unsigned)cdiv(Vs, 64), (unsigned)cdiv(T, 128)), dim3(256), 0, s, logits, ld, T,
-            Vs, vlo, labels, vocab, lse, inv_n, (bf16*)dz, ldz, (bf16*)dzt, ldt);
   return RP_OK;
 }
 

@@ -955,8 +955,4 @@ size_t splitk_bytes(int64_t M, int64_t N, int64_t K, int split_k) {
   return (size_t)cdiv(K, kc) * M * N * sizeof(float);
 }
 
-size_t gemm_tr_bytes(int64_t M, int64_t N, int64_t K) {
-  return align_up((size_t)M * K * 2, 256) + align_up((size_t)N * K * 2, 256);
-}
-
 }  // namespace rp

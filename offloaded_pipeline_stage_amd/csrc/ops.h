@@ -73,9 +73,6 @@ size_t splitk_bytes(int64_t M, int64_t N, int64_t K, int split_k);
 rp_status splitk_reduce(const float* part, int splits, int M, int N, float* C, int64_t ldc, bool accumulate,
                         hipStream_t s);
 
-// scratch gemm() uses to transpose both operands of an M x N x K product
-size_t gemm_tr_bytes(int64_t M, int64_t N, int64_t K);
-
 rp_status gemm(const GemmDesc& d, hipStream_t s);
 rp_status gemm_validate(const GemmDesc& d);
 
@@ -162,11 +159,6 @@ rp_status ce_combine(int T, int n_shards, const float2* parts, const float* zlab
 rp_status ce_grad(int dt, const float* logits, int64_t ld, int T, int Vs, int vlo,
                   const int32_t* labels, int vocab, const float* lse, const float* inv_n,
                   void* dz, int64_t ldz, hipStream_t s);
-// bf16 only: ce_grad's dz (bit for bit) and its transpose dzt [Vs, ldt] in
-// one pass; T and Vs multiples of 8, 16-byte aligned rows
-rp_status ce_grad_tr(const float* logits, int64_t ld, int T, int Vs, int vlo, const int32_t* labels, int vocab,
-                     const float* lse, const float* inv_n, void* dz, int64_t ldz, void* dzt, int64_t ldt,
-                     hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // mixture of experts

@@ -700,8 +700,6 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
   void* dz = bp.take(T * vs_max * s.es);
   float* dxf = bp.take<float>(T * s.H * 4);
   float* part = bp.take<float>(rmsnorm_bwd_part_bytes((int)T, s.H));
-  const size_t tr_bytes = s.dt == RP_DTYPE_BF16 ? gemm_tr_bytes(vs_max, s.H, T) : 0;
-  void* tr = tr_bytes ? bp.take(tr_bytes) : nullptr;
   if (need) {
     *need = bp.off;
     return RP_OK;
@@ -730,32 +728,18 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
   }
   RP_TRY(ce_combine((int)T, ns, parts, zlab, labels, c->vocab, lse, loss, inv_n, st));
   RP_TRY(fill_zero(dxf, (size_t)T * s.H * 4, st));
-  // bf16 with sizes in multiples of 8: the weight-gradient products take
-  // K-major operands made here, x^T once for every shard and each shard's
-  // dz^T by the gradient kernel itself, in the transpose scratch
-  bool pre_tr = tr != nullptr && T % 8 == 0 && s.H % 8 == 0;
-  for (int i = 0; i < ns; ++i) pre_tr = pre_tr && (c->shard_lo[i + 1] - c->shard_lo[i]) % 8 == 0;
-  char* dzt = reinterpret_cast<char*>(tr);
-  char* zzt = pre_tr ? dzt + align_up((size_t)vs_max * T * 2, 256) : nullptr;
-  if (pre_tr) RP_TRY(transpose_bf16(zz, s.H, zzt, (int64_t)T, (int)T, s.H, st));
   for (int i = 0; i < ns; ++i) {
     const int lo = c->shard_lo[i], vs = c->shard_lo[i + 1] - lo;
     Slot& w = c->shards[i];
     RP_CHECK(w.g != nullptr, RP_ERR_INVALID, "lmhead: shard %d has no gradient buffer", i);
     RP_TRY(wait_grad_drained(c, w));
     const float* lg = logits + (size_t)i * T * vs_max;
-    if (pre_tr)
-      RP_TRY(ce_grad_tr(lg, vs, (int)T, vs, lo, labels, c->vocab, lse, inv_n, dz, vs, dzt, (int64_t)T, st));
-    else
-      RP_TRY(ce_grad(dt, lg, vs, (int)T, vs, lo, labels, c->vocab, lse, inv_n, dz, vs, st));
+    RP_TRY(ce_grad(dt, lg, vs, (int)T, vs, lo, labels, c->vocab, lse, inv_n, dz, vs, st));
     GemmDesc gx = mk((int)T, s.H, vs, dz, vs, true, w.w, s.H, false, dxf, s.H, dt, RP_DTYPE_F32);
     gx.accumulate = true;
     RP_TRY(gemm(gx, st));
-    if (pre_tr) {
-      RP_TRY(gemm(mk(vs, s.H, (int)T, dzt, (int)T, true, zzt, (int)T, true, w.g, s.H, dt, RP_DTYPE_F32), st));
-    } else {
-      RP_TRY(gemm(mk(vs, s.H, (int)T, dz, vs, false, zz, s.H, false, w.g, s.H, dt, RP_DTYPE_F32), st));
-    }
+    // dW_s = dz^T x: both operands M-major, read straight from dz and x
+    RP_TRY(gemm(mk(vs, s.H, (int)T, dz, vs, false, zz, s.H, false, w.g, s.H, dt, RP_DTYPE_F32), st));
     RP_TRY(mark_consumed(c, w));
     RP_TRY(mark_grad_ready(c, w));
   }
