@@ -169,7 +169,7 @@ rp_status rp_ctx_create(int device, const rp_layer_cfg* cfg, const rp_streams* s
   // a blocking stream: work enqueued on the legacy default stream before a
   // call runs before the call's kernels, and default-stream work enqueued
   // after it waits for them.
-  for (hipStream_t* ps : {&x->compute, &x->act_h2d, &x->act_d2h, &x->w_h2d, &x->g_d2h}) {
+  for (hipStream_t* ps : {&x->compute, &x->act_h2d, &x->act_d2h, &x->w_h2d, &x->g_d2h, &x->side}) {
     if (*ps) continue;
     rp_status st = new_queue_stream(device, ps);
     if (st != RP_OK) {
@@ -205,7 +205,7 @@ rp_status rp_ctx_streams(const rp_ctx* c, rp_streams* out) {
 
 rp_status rp_ctx_sync(rp_ctx* c) {
   CTX_ENTER(c);
-  hipStream_t ss[5] = {c->compute, c->act_h2d, c->act_d2h, c->w_h2d, c->g_d2h};
+  hipStream_t ss[6] = {c->compute, c->act_h2d, c->act_d2h, c->w_h2d, c->g_d2h, c->side};
   for (hipStream_t s : ss) RP_HIP(hipStreamSynchronize(s));
   RP_HIP(hipGetLastError());
   RP_CHECK(c->deferred.empty(), RP_ERR_STATE, "ctx_sync: %zu transfer windows still wait for activation tickets",
@@ -218,9 +218,9 @@ rp_status rp_ctx_destroy(rp_ctx* c) {
   if (trace_current() == &c->trace) trace_bind(nullptr);
   rp_status st = RP_OK;
   if (hipSetDevice(c->device) == hipSuccess) {
-    hipStream_t ss[5] = {c->compute, c->act_h2d, c->act_d2h, c->w_h2d, c->g_d2h};
+    hipStream_t ss[6] = {c->compute, c->act_h2d, c->act_d2h, c->w_h2d, c->g_d2h, c->side};
     for (hipStream_t s : ss)
-      if (hipStreamSynchronize(s) != hipSuccess) st = RP_ERR_HIP;
+      if (s && hipStreamSynchronize(s) != hipSuccess) st = RP_ERR_HIP;
     for (hipStream_t d : c->owned) (void)hipStreamDestroy(d);
     for (hipEvent_t e : c->all_events) (void)hipEventDestroy(e);
     for (void* p : c->stages) (void)hipFree(p);

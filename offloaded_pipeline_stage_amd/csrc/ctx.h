@@ -86,6 +86,11 @@ struct rp_ctx {
   rp_layer_cfg cfg{};
   rp::Shape sh{};
   hipStream_t compute = nullptr, act_h2d = nullptr, act_d2h = nullptr, w_h2d = nullptr, g_d2h = nullptr;
+  // a second compute stream of the context's own: memory-bound kernels of a
+  // call run on it beside the call's matrix products on `compute`, and every
+  // call joins it back into `compute` before it returns
+  hipStream_t side = nullptr;
+  std::vector<hipEvent_t> side_ev;  // fork/join events of the side stream (created once)
   // the device's fixed scratch of rp_op_attn_bwd_noalloc (looked up at creation)
   float* attn_scratch = nullptr;
   // transfer streams the context created (each on a hardware queue of its own)

@@ -697,7 +697,7 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
   float* zlab = bp.take<float>(T * 4);
   float* lse = bp.take<float>(T * 4);
   float* inv_n = bp.take<float>(4);
-  void* dz = bp.take(T * vs_max * s.es);
+  void* dzb[2] = {bp.take(T * vs_max * s.es), bp.take(T * vs_max * s.es)};
   float* dxf = bp.take<float>(T * s.H * 4);
   float* part = bp.take<float>(rmsnorm_bwd_part_bytes((int)T, s.H));
   if (need) {
@@ -717,6 +717,24 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
     RP_TRY(rmsnorm_fwd(dt, x, c->final_norm.w, z, rstd, (int)T, s.H, c->cfg.rms_eps, st));
     zz = z;
   }
+  // The memory-bound cross-entropy kernels run on the side stream beside the
+  // compute-bound shard products: each shard's statistics beside the next
+  // shard's logits product, each shard's dz beside the previous shard's
+  // input- and weight-gradient products (dz alternates between two buffers).
+  hipStream_t sd = c->side;
+  if ((int)c->side_ev.size() < 2 * ns + 2) {
+    c->side_ev.resize(2 * ns + 2, nullptr);
+    for (hipEvent_t& e : c->side_ev)
+      if (!e) {
+        e = c->new_event();
+        RP_CHECK(e != nullptr, RP_ERR_HIP, "lmhead: event creation failed");
+      }
+  }
+  auto fork = [&](hipStream_t from, hipStream_t to, int k) -> rp_status {  // `to` waits for `from`'s work so far
+    RP_HIP(hipEventRecord(c->side_ev[k], from));
+    RP_HIP(hipStreamWaitEvent(to, c->side_ev[k], 0));
+    return RP_OK;
+  };
   RP_TRY(fill_zero(zlab, T * 4, st));
   for (int i = 0; i < ns; ++i) {
     const int lo = c->shard_lo[i], vs = c->shard_lo[i + 1] - lo;
@@ -724,17 +742,29 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
     RP_TRY(wait_weights(c, w));
     float* lg = logits + (size_t)i * T * vs_max;
     RP_TRY(gemm(mk((int)T, vs, s.H, zz, s.H, true, w.w, s.H, true, lg, vs, dt, RP_DTYPE_F32), st));
-    RP_TRY(ce_shard_stats(lg, vs, (int)T, vs, lo, labels, c->vocab, parts + (size_t)i * T, zlab, st));
+    RP_TRY(fork(st, sd, i));
+    RP_TRY(ce_shard_stats(lg, vs, (int)T, vs, lo, labels, c->vocab, parts + (size_t)i * T, zlab, sd));
   }
+  RP_TRY(fork(sd, st, ns));
   RP_TRY(ce_combine((int)T, ns, parts, zlab, labels, c->vocab, lse, loss, inv_n, st));
   RP_TRY(fill_zero(dxf, (size_t)T * s.H * 4, st));
+  auto grad = [&](int i, hipStream_t on) -> rp_status {
+    const int lo = c->shard_lo[i], vs = c->shard_lo[i + 1] - lo;
+    return ce_grad(dt, logits + (size_t)i * T * vs_max, vs, (int)T, vs, lo, labels, c->vocab, lse, inv_n,
+                   dzb[i & 1], vs, on);
+  };
+  RP_TRY(grad(0, st));
   for (int i = 0; i < ns; ++i) {
     const int lo = c->shard_lo[i], vs = c->shard_lo[i + 1] - lo;
     Slot& w = c->shards[i];
     RP_CHECK(w.g != nullptr, RP_ERR_INVALID, "lmhead: shard %d has no gradient buffer", i);
+    if (i + 1 < ns) {
+      // shard i + 1's dz, into the buffer shard i - 1's products read
+      RP_TRY(fork(st, sd, ns + 1 + i));
+      RP_TRY(grad(i + 1, sd));
+    }
     RP_TRY(wait_grad_drained(c, w));
-    const float* lg = logits + (size_t)i * T * vs_max;
-    RP_TRY(ce_grad(dt, lg, vs, (int)T, vs, lo, labels, c->vocab, lse, inv_n, dz, vs, st));
+    const void* dz = dzb[i & 1];
     GemmDesc gx = mk((int)T, s.H, vs, dz, vs, true, w.w, s.H, false, dxf, s.H, dt, RP_DTYPE_F32);
     gx.accumulate = true;
     RP_TRY(gemm(gx, st));
@@ -742,6 +772,7 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
     RP_TRY(gemm(mk(vs, s.H, (int)T, dz, vs, false, zz, s.H, false, w.g, s.H, dt, RP_DTYPE_F32), st));
     RP_TRY(mark_consumed(c, w));
     RP_TRY(mark_grad_ready(c, w));
+    if (i + 1 < ns) RP_TRY(fork(sd, st, 2 * ns + 1));  // shard i + 1's dz is ready
   }
   if (fnorm) {
     RP_CHECK(c->final_norm.g != nullptr, RP_ERR_INVALID, "lmhead: final norm has no gradient buffer");
