@@ -243,7 +243,6 @@ def summarize_counters(dirs, title: str, commands, min_us: float = 20.0) -> str:
         dv = t["derived"]
         cells = " ".join(f"{dv[c]:11.3f}" if c in dv else f"{'-':>11}" for c in cols)
         lines.append(f"{t['launches']:6d} {t['mean_us']:8.1f} {t['vgpr']:4d} {t['agpr']:4d} {cells}  {n}")
-    lines += ["", "counters_json: " + json.dumps(table, sort_keys=True)]
     return "\n".join(lines) + "\n"
 
 

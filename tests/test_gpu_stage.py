@@ -117,11 +117,9 @@ def test_bf16_layer_fwd_bwd_matches_oracle(W, name, seq, batch, qkn):
 @pytest.mark.parametrize("seq,vocab,shards", [(320, 8192, 4), (200, 6176, 4), (100, 4096, 2)])
 def test_bf16_lmhead_sharded_matches_oracle(W, seq, vocab, shards):
     """LM head + CE with vocabulary shards at hidden 4096 (vocab reduced),
-    bf16: loss, dx and every shard's weight gradient. Token counts and shard
-    widths in multiples of 8 (bf16 shards always are) take the path whose
-    gradient kernel also writes dz transposed (320 tokens: a ragged 128-row
-    tile; 1544-row shards: a ragged 64-column tile); 100 tokens take the path
-    that transposes inside the product."""
+    bf16: loss, dx and every shard's weight gradient, at token counts and
+    shard widths that leave ragged tiles (320 tokens; 1544-row shards; 100
+    tokens, not a multiple of 8)."""
     say("bf16 lm head", seq, vocab, shards)
     cfg = synth.config("llama3_8b", seq=seq, vocab=vocab, n_shards=shards)
     x = synth.activation(cfg, "x")
