@@ -574,6 +574,17 @@ rp_status rp_op_moe_route(rp_ctx* ctx, int batch, int seq, const float* logits, 
  * RP_ERR_INVALID on misaligned arguments. */
 rp_status rp_op_copy(rp_ctx* ctx, void* dst, const void* src, size_t bytes);
 
+/* bf16 transpose, dst[c * ldd + r] = src[r * lds + c] for r < rows,
+ * c < cols (elements of dst outside that range untouched). The step that
+ * makes the activation operand of a weight-gradient product (dW = dY^T X,
+ * where dY and X are stored token-major) K-major ahead of the GEMM, so that
+ * only dY is read through transposing LDS reads. rows, cols, lds
+ * and ldd multiples of 8; pointers 16-byte aligned device memory, src and dst
+ * not overlapping. Enqueued on the compute stream; RP_ERR_UNSUPPORTED when
+ * the size or alignment rules are not met. */
+rp_status rp_op_transpose_bf16(rp_ctx* ctx, int rows, int cols, const void* src, int64_t lds,
+                               void* dst, int64_t ldd);
+
 /* ------------------------------------------------------------------------ */
 /* kernel trace                                                              */
 /* ------------------------------------------------------------------------ */

@@ -111,6 +111,7 @@ _SIGS = {
                                   C.c_int, C.c_int, C.c_int]),
     "rp_op_attn_fwd": (C.c_int, [_P, C.c_int, C.c_int, _P, _P, _P]),
     "rp_op_copy": (C.c_int, [_P, _P, _P, C.c_size_t]),
+    "rp_op_transpose_bf16": (C.c_int, [_P, C.c_int, C.c_int, _P, C.c_int64, _P, C.c_int64]),
     "rp_op_attn_bwd": (C.c_int, [_P, C.c_int, C.c_int, _P, _P, _P, _P, _P, _P, C.c_size_t]),
     "rp_op_attn_bwd_noalloc": (C.c_int, [_P, C.c_int, C.c_int, _P, _P, _P, _P, _P]),
     "rp_op_moe_route": (C.c_int, [_P, C.c_int, C.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _P, C.c_size_t]),
@@ -429,6 +430,18 @@ class Context:
         check(lib().rp_op_gemm_bf16(self.h, M, N, K, ptr(A), lda, int(a_kmajor), ptr(B), ldb, int(b_kmajor),
                                     ptr(Cm), ldc, int(out_f32), int(accumulate)))
         self._hold(A, B, Cm)
+
+    def op_transpose_bf16(self, src, dst):
+        """dst[:cols, :rows] = src[:rows, :cols].T for 2-D bf16 device tensors
+        with unit column stride."""
+        rows, cols = src.shape
+        if dst.dtype != torch.bfloat16 or src.dtype != torch.bfloat16 or src.stride(1) != 1 or dst.stride(1) != 1:
+            raise ValueError("op_transpose_bf16: bf16 tensors with unit column stride")
+        if dst.shape[0] < cols or dst.shape[1] < rows:
+            raise ValueError("op_transpose_bf16: dst too small")
+        self._order()
+        check(lib().rp_op_transpose_bf16(self.h, rows, cols, ptr(src), src.stride(0), ptr(dst), dst.stride(0)))
+        self._hold(src, dst)
 
     def op_copy(self, dst, src):
         self._order()

@@ -412,6 +412,13 @@ rp_status rp_op_copy(rp_ctx* c, void* dst, const void* src, size_t bytes) {
   return copy16(dst, src, bytes, c->compute);
 }
 
+rp_status rp_op_transpose_bf16(rp_ctx* c, int rows, int cols, const void* src, int64_t lds, void* dst, int64_t ldd) {
+  CTX_ENTER(c);
+  RP_CHECK(rows >= 0 && cols >= 0 && lds >= cols && ldd >= rows, RP_ERR_INVALID, "op_transpose: bad sizes");
+  RP_CHECK(rows == 0 || cols == 0 || (src && dst), RP_ERR_INVALID, "op_transpose: null pointer");
+  return transpose_bf16(src, lds, dst, ldd, rows, cols, c->compute);
+}
+
 rp_status rp_op_attn_fwd(rp_ctx* c, int batch, int seq, const void* qkv, void* o, float* lse) {
   CTX_ENTER(c);
   RP_CHECK(batch >= 1 && seq >= 1 && qkv && o && lse, RP_ERR_INVALID, "op_attn_fwd: bad arguments");

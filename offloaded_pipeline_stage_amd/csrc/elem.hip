@@ -527,6 +527,59 @@ __global__ void embed_bwd_kernel(const int32_t* ids, const T* dx0, float* dtable
   }
 }
 
+// 64 x 64 tile per 256-thread block through LDS: 16-byte loads along the
+// source rows, 16-byte stores along the destination rows
+// dst[c][r] = src[r][c] over tiles of 128 source rows x 64 source columns.
+// A thread loads the same 8 columns (16 bytes) of two adjacent source rows
+// and pairs them column by column into 32-bit words, each two consecutive
+// elements of one destination row; the tile is held destination-major as
+// [64 rows][64 words] and written out 16 bytes per lane. The tile's 16-byte
+// granules are XOR-swizzled by the destination row's group of 8, which
+// spreads both the 4-byte stores (lanes of one store differ in column group
+// and row pair) and the 16-byte reads (lanes differ in granule) over the
+// banks. rows and cols are multiples of 8, so a 16-byte chunk is wholly in
+// range or wholly out.
+__device__ __forceinline__ int tr_word(int c, int w) { return c * 64 + (((w >> 2) ^ (c >> 3)) << 2) + (w & 3); }
+
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src, int64_t lds,
+                                                             uint16_t* __restrict__ dst, int64_t ldd, int rows,
+                                                             int cols) {
+  __shared__ uint32_t tile[64 * 64];
+  const int r0 = blockIdx.y * 128, c0 = blockIdx.x * 64;
+  const int q = threadIdx.x & 7;  // column group: source columns c0 + 8q .. + 7
+  uint4 va[2], vb[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int w = (threadIdx.x >> 3) + 32 * h;  // word (row pair): source rows r0 + 2w, r0 + 2w + 1
+    const int r = r0 + 2 * w, c = c0 + 8 * q;
+    va[h] = vb[h] = make_uint4(0, 0, 0, 0);
+    if (r < rows && c < cols) {
+      va[h] = *reinterpret_cast<const uint4*>(src + (int64_t)r * lds + c);
+      vb[h] = *reinterpret_cast<const uint4*>(src + (int64_t)(r + 1) * lds + c);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int w = (threadIdx.x >> 3) + 32 * h;
+    const uint32_t a[4] = {va[h].x, va[h].y, va[h].z, va[h].w}, b[4] = {vb[h].x, vb[h].y, vb[h].z, vb[h].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // destination rows 8q + 2e (the low halves) and 8q + 2e + 1 (the high)
+      tile[tr_word(8 * q + 2 * e, w)] = (a[e] & 0xffffu) | (b[e] << 16);
+      tile[tr_word(8 * q + 2 * e + 1, w)] = (a[e] >> 16) | (b[e] & 0xffff0000u);
+    }
+  }
+  __syncthreads();
+  const int k = threadIdx.x & 15;  // granule: destination columns r0 + 8k .. + 7
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int c = (threadIdx.x >> 4) + 16 * h;  // destination row c0 + c
+    if (c0 + c >= cols || r0 + 8 * k >= rows) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(&tile[tr_word(c, 4 * k)]);
+    *reinterpret_cast<uint4*>(dst + (int64_t)(c0 + c) * ldd + r0 + 8 * k) = v;
+  }
+}
+
 __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N, float* __restrict__ C,
                                      int64_t ldc, int accumulate) {
   const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
@@ -783,6 +836,17 @@ rp_status embed_bwd(int dt, const int32_t* ids, const void* dx0, float* dtable, 
     RP_LAUNCH(embed_bwd_kernel<bf16>, dim3(V), dim3(256), 0, s, ids, (const bf16*)dx0, dtable, T, H);
   else
     RP_LAUNCH(embed_bwd_kernel<float>, dim3(V), dim3(256), 0, s, ids, (const float*)dx0, dtable, T, H);
+  return RP_OK;
+}
+
+rp_status transpose_bf16(const void* src, int64_t lds, void* dst, int64_t ldd, int rows, int cols, hipStream_t s) {
+  if (rows == 0 || cols == 0) return RP_OK;
+  RP_CHECK(rows % 8 == 0 && cols % 8 == 0 && lds % 8 == 0 && ldd % 8 == 0 && ((uintptr_t)src & 15) == 0 &&
+               ((uintptr_t)dst & 15) == 0,
+           RP_ERR_UNSUPPORTED, "transpose: sizes and leading dimensions must be multiples of 8, 16-byte aligned");
+  TraceScope ts(s, "transpose_bf16_kernel", 0.0, 4.0 * rows * cols);
+  RP_LAUNCH(transpose_bf16_kernel, dim3((unsigned)cdiv(cols, 64), (unsigned)cdiv(rows, 128)), dim3(256), 0, s,
+            (const uint16_t*)src, lds, (uint16_t*)dst, ldd, rows, cols);
   return RP_OK;
 }
 

@@ -126,21 +126,25 @@ __device__ __forceinline__ u32x4_t bload(__amdgpu_buffer_rsrc_t r, uint32_t voff
 // K-major operands: rows padded to 144 bytes (16-byte chunk kc at row*144 +
 // 16*kc); the 8 lanes of a read phase hit 8 distinct 16-byte bank groups and
 // fragment addresses step by immediates.
-// M-major operands are kept as they lie in memory: 64 k rows of R elements
-// (2R bytes each, so the tile takes R x 128 bytes like a K-major one without
-// padding), 16-byte chunk c of k row k at position c ^ 4 (k % 4). Fragments
-// come from transposing LDS reads (read_mm); the stores of whole rows and
-// the reads of four k rows x four chunks are both free of bank conflicts.
+// M-major operands are kept as they lie in memory: 64 k rows of R elements,
+// each padded by 64 bytes (2R + 64 bytes a row), so consecutive k rows start
+// 64 bytes apart in the 256-byte bank cycle. Fragments come from transposing
+// LDS reads (read_mm): a 16-lane group reads 32 bytes of each of four
+// consecutive k rows, which the padding puts into four distinct 64-byte bank
+// ranges, and the other group of the half-wave reads the next 32 bytes of
+// the same rows, so the reads are free of bank conflicts; so are the stores
+// of whole rows. The offset is linear in m and k, so a fragment's address is
+// the lane's own offset plus an immediate.
 template <bool KM> struct Lay;
 template <> struct Lay<true> {
-  static constexpr int RS = 144;
+  template <int R> static constexpr int BYTES = R * 144;  // tile of R operand rows
   __device__ __forceinline__ static int off(int row, int kc) { return row * 144 + kc * 16; }
 };
 template <> struct Lay<false> {
-  static constexpr int RS = 128;  // bytes per operand row (index m or n) of the tile
+  template <int R> static constexpr int BYTES = 64 * (2 * R + 64);  // tile of R operand rows
   template <int R>
-  __device__ __forceinline__ static int off(int k, int m) {  // element (m, k), m a multiple of 4
-    return k * (2 * R) + (((m >> 3) ^ (4 * (k & 3))) << 4) + (m & 4) * 2;
+  __device__ __forceinline__ static int off(int k, int m) {  // element (m, k)
+    return k * (2 * R + 64) + 2 * m;
   }
 };
 
@@ -300,7 +304,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(GemmParams p)
   constexpr int TM = WM / 32, TN = WN / 32;
   static_assert(TM >= 1 && TN >= 1 && (EPI != EPI_SWIGLU || TN % 2 == 0), "bad wave tile");
   constexpr bool SW = (EPI == EPI_SWIGLU);
-  constexpr int A_BUF = BM * Lay<AK>::RS, B_BUF = BN * Lay<BKM>::RS;
+  constexpr int A_BUF = Lay<AK>::template BYTES<BM>, B_BUF = Lay<BKM>::template BYTES<BN>;
   extern __shared__ __align__(16) char smem[];
   // [A buffer 0][A buffer 1][B buffer 0][B buffer 1]
   char* const sA0 = smem;
@@ -803,7 +807,7 @@ rp_status launch_mfma(const GemmDesc& d, hipStream_t s) {
     if (p.C2) v = v && p.ldc2 % 4 == 0 && al(p.C2, 8);
     p.vec = v ? 1 : 0;
   }
-  const size_t lds = 2 * ((size_t)BM * (AK ? 144 : 128) + (size_t)BN * (BKM ? 144 : 128));
+  const size_t lds = 2 * ((size_t)Lay<AK>::template BYTES<BM> + (size_t)Lay<BKM>::template BYTES<BN>);
   static bool attr_set = false;  // one instantiation per template: set once
   if (!attr_set) {
     RP_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_mfma_kernel<BM, BN, WGM, WGN, AK, BKM, EPI, OF32, GRP>),
@@ -824,6 +828,12 @@ rp_status launch_mfma(const GemmDesc& d, hipStream_t s) {
 
 template <int BM, int BN, int WGM, int WGN, int EPI, bool OF32>
 rp_status dispatch_layout(const GemmDesc& d, hipStream_t s) {
+  if constexpr (BM == 256 && BN == 256 && WGM == 2 && WGN == 4 && EPI != EPI_SWIGLU) {
+    // M-major A, K-major B: 64 x 128 wave tiles, so that the operand whose
+    // fragments take two transposing reads each is the one with fewer
+    // fragments per wave
+    if (!d.a_kmajor && d.b_kmajor) return launch_mfma<BM, BN, 4, 2, false, true, EPI, OF32>(d, s);
+  }
   if (d.a_kmajor && d.b_kmajor) return launch_mfma<BM, BN, WGM, WGN, true, true, EPI, OF32>(d, s);
   if (d.a_kmajor && !d.b_kmajor) return launch_mfma<BM, BN, WGM, WGN, true, false, EPI, OF32>(d, s);
   if (!d.a_kmajor && !d.b_kmajor) return launch_mfma<BM, BN, WGM, WGN, false, false, EPI, OF32>(d, s);

@@ -194,6 +194,7 @@ rp_status embed_bwd(int dt, const int32_t* ids, const void* dx0, float* dtable, 
                     int H, hipStream_t s);
 // dst [cols, rows] (leading dimension ldd) = src [rows, cols]^T (leading
 // dimension lds), bf16; rows, cols, lds, ldd multiples of 8, 16-byte aligned
+rp_status transpose_bf16(const void* src, int64_t lds, void* dst, int64_t ldd, int rows, int cols, hipStream_t s);
 // out (dtype dt) = a (fp32)
 rp_status cast_from_f32(int dt, const float* a, void* out, size_t n, hipStream_t s);
 

@@ -337,11 +337,25 @@ rp_status layer_fwd(rp_ctx* c, const LayerBinding& lb, const LoraBf16& lw, void*
   return RP_OK;
 }
 
-// a weight-gradient product dW = X^T Y (both operands M-major, fp32 out),
-// added to dW when accumulating over micro-batches
+// `to` waits for the work enqueued on `from` so far. The event is recorded
+// and waited on at once, so one event serves every such fork and join.
+rp_status stream_fork(rp_ctx* c, hipStream_t from, hipStream_t to) {
+  if (c->side_ev.empty()) {
+    hipEvent_t e = c->new_event();
+    RP_CHECK(e != nullptr, RP_ERR_HIP, "event creation failed");
+    c->side_ev.push_back(e);
+  }
+  RP_HIP(hipEventRecord(c->side_ev[0], from));
+  RP_HIP(hipStreamWaitEvent(to, c->side_ev[0], 0));
+  return RP_OK;
+}
+
+// a weight-gradient product dW = X^T Y (X M-major; Y M-major, or K-major
+// when b_kmajor: Y^T stored [N, K]; fp32 out), added to dW when
+// accumulating over micro-batches
 rp_status wgrad(int M, int N, int K, const void* A, int64_t lda, const void* Bm, int64_t ldb, float* C, int64_t ldc,
-                int dt, const BwdTmp& B, float alpha, bool accum, hipStream_t st) {
-  GemmDesc g = mk(M, N, K, A, lda, false, Bm, ldb, false, C, ldc, dt, RP_DTYPE_F32);
+                int dt, const BwdTmp& B, float alpha, bool accum, hipStream_t st, bool b_kmajor = false) {
+  GemmDesc g = mk(M, N, K, A, lda, false, Bm, ldb, b_kmajor, C, ldc, dt, RP_DTYPE_F32);
   g.accumulate = accum;
   g.alpha = alpha;
   if (B.splitk) {
@@ -395,6 +409,14 @@ rp_status layer_bwd(rp_ctx* c, LayerBinding& lb, const LoraBf16& lw, int T, int 
     RP_TRY(gemm_grouped(gb, st));
     RP_TRY(moe_uncombine(B.dbe, A.mr, T, k, s.H, B.gbuf, st));
   } else {
+    // dWgu = dgu^T b reads b as a K-major operand once b is transposed: on
+    // the side stream, beside the products before it, into dh1, which is
+    // free until the RMSNorm backward below
+    const bool b_tr = full && dt == RP_DTYPE_BF16 && T % 8 == 0 && s.H % 8 == 0;
+    if (b_tr) {
+      RP_TRY(stream_fork(c, st, c->side));
+      RP_TRY(transpose_bf16(A.b, s.H, B.dh1, T, T, s.H, c->side));
+    }
     // MLP: dm = dy Wd -> dgu (fused SwiGLU backward)
     GemmDesc g1 = mk(T, s.F, s.H, dy, s.H, true, wptr(w, cfg, RP_T_WD), s.F, false, B.dgu, F2, dt, dt,
                      EPI_SWIGLU_BWD);
@@ -406,7 +428,12 @@ rp_status layer_bwd(rp_ctx* c, LayerBinding& lb, const LoraBf16& lw, int T, int 
     RP_TRY(gemm(mk(T, s.H, F2, B.dgu, F2, true, wptr(w, cfg, RP_T_WGU), s.H, false, B.gbuf, s.H, dt, RP_DTYPE_F32),
                 st));
     // dWgu = dgu^T b
-    if (full) RP_TRY(wgrad(F2, s.H, T, B.dgu, F2, A.b, s.H, gptr(w, cfg, RP_T_WGU), s.H, dt, B, 1.f, accum, st));
+    if (b_tr) {
+      RP_TRY(stream_fork(c, c->side, st));
+      RP_TRY(wgrad(F2, s.H, T, B.dgu, F2, B.dh1, T, gptr(w, cfg, RP_T_WGU), s.H, dt, B, 1.f, accum, st, true));
+    } else if (full) {
+      RP_TRY(wgrad(F2, s.H, T, B.dgu, F2, A.b, s.H, gptr(w, cfg, RP_T_WGU), s.H, dt, B, 1.f, accum, st));
+    }
   }
   // dh1 = dy + RMSNorm2^T db ; dgamma2
   RP_TRY(rmsnorm_bwd(dt, B.gbuf, A.h1, wptr(w, cfg, RP_T_GAMMA2), A.rstd2, dy, dt, B.dh1f, B.dh1,
@@ -700,6 +727,9 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
   void* dzb[2] = {bp.take(T * vs_max * s.es), bp.take(T * vs_max * s.es)};
   float* dxf = bp.take<float>(T * s.H * 4);
   float* part = bp.take<float>(rmsnorm_bwd_part_bytes((int)T, s.H));
+  // x^T [H, T] for the weight-gradient products (bf16, sizes in multiples of 8)
+  const bool xt_fit = s.dt == RP_DTYPE_BF16 && T % 8 == 0 && s.H % 8 == 0;
+  void* zt = xt_fit ? bp.take(T * s.H * s.es) : nullptr;
   if (need) {
     *need = bp.off;
     return RP_OK;
@@ -722,8 +752,8 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
   // shard's logits product, each shard's dz beside the previous shard's
   // input- and weight-gradient products (dz alternates between two buffers).
   hipStream_t sd = c->side;
-  if ((int)c->side_ev.size() < 2 * ns + 2) {
-    c->side_ev.resize(2 * ns + 2, nullptr);
+  if ((int)c->side_ev.size() < 2 * ns + 3) {
+    c->side_ev.resize(2 * ns + 3, nullptr);
     for (hipEvent_t& e : c->side_ev)
       if (!e) {
         e = c->new_event();
@@ -735,6 +765,15 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
     RP_HIP(hipStreamWaitEvent(to, c->side_ev[k], 0));
     return RP_OK;
   };
+  // dW_s = dz^T x reads x as a K-major operand once x is transposed (once
+  // per call, on the side stream beside the first logits product), so that
+  // only dz goes through transposing LDS reads; otherwise both operands are
+  // read M-major.
+  const bool xt = xt_fit && ((uintptr_t)zz & 15) == 0;
+  if (xt) {
+    RP_TRY(fork(st, sd, 2 * ns + 2));
+    RP_TRY(transpose_bf16(zz, s.H, zt, T, (int)T, s.H, sd));
+  }
   RP_TRY(fill_zero(zlab, T * 4, st));
   for (int i = 0; i < ns; ++i) {
     const int lo = c->shard_lo[i], vs = c->shard_lo[i + 1] - lo;
@@ -768,8 +807,10 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
     GemmDesc gx = mk((int)T, s.H, vs, dz, vs, true, w.w, s.H, false, dxf, s.H, dt, RP_DTYPE_F32);
     gx.accumulate = true;
     RP_TRY(gemm(gx, st));
-    // dW_s = dz^T x: both operands M-major, read straight from dz and x
-    RP_TRY(gemm(mk(vs, s.H, (int)T, dz, vs, false, zz, s.H, false, w.g, s.H, dt, RP_DTYPE_F32), st));
+    if (xt)
+      RP_TRY(gemm(mk(vs, s.H, (int)T, dz, vs, false, zt, T, true, w.g, s.H, dt, RP_DTYPE_F32), st));
+    else
+      RP_TRY(gemm(mk(vs, s.H, (int)T, dz, vs, false, zz, s.H, false, w.g, s.H, dt, RP_DTYPE_F32), st));
     RP_TRY(mark_consumed(c, w));
     RP_TRY(mark_grad_ready(c, w));
     if (i + 1 < ns) RP_TRY(fork(sd, st, 2 * ns + 1));  // shard i + 1's dz is ready

@@ -68,6 +68,42 @@ def test_gemm_bf16_layouts(B, M, N, K, ak, bk):
     assert torch.equal(C16.cpu(), C32.cpu().to(torch.bfloat16))
 
 
+@pytest.mark.parametrize("rows,cols,pad", [
+    (8, 8, 0), (128, 64, 0), (136, 24, 8), (200, 4104, 0), (1000, 200, 16), (8, 1000, 8), (2056, 72, 0),
+])
+def test_transpose_bf16(B, rows, cols, pad):
+    """The weight-gradient activation transpose: bit-exact against torch on
+    single, ragged and several tiles (128 source rows x 64 columns), with
+    padded leading dimensions whose padding must stay untouched."""
+    say("transpose", rows, cols, pad)
+    ctx = _ctx(B)
+    dev = torch.device("cuda")
+    src_full = synth.normal((rows, cols + pad), 21, f"tr{rows}{cols}", dtype=torch.bfloat16).to(dev)
+    src = src_full[:, :cols]
+    dst = torch.full((cols, rows + pad), -7.0, dtype=torch.bfloat16, device=dev)
+    ctx.op_transpose_bf16(src, dst)
+    ctx.sync()
+    got = dst.cpu()
+    assert torch.equal(got[:, :rows], src.cpu().t())
+    assert torch.all(got[:, rows:] == -7.0)
+
+
+@pytest.mark.parametrize("rows,cols", [(8192, 4096), (8192, 32064), (8192, 28672)])
+def test_transpose_bf16_full_size(B, rows, cols):
+    """Transposes at the step's sizes (8192 tokens x the hidden width 4096,
+    and x the larger widths 28672, 32064), every element bit-exact,
+    compared on the device."""
+    say("transpose full size", rows, cols)
+    ctx = _ctx(B)
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev).manual_seed(rows + cols)
+    src = torch.randn(rows, cols, generator=g, device=dev).to(torch.bfloat16)
+    dst = torch.empty(cols, rows, dtype=torch.bfloat16, device=dev)
+    ctx.op_transpose_bf16(src, dst)
+    ctx.sync()
+    assert torch.equal(dst, src.t())
+
+
 def test_gemm_accumulate_and_strided_output(B):
     say("gemm accumulate")
     ctx = _ctx(B)
