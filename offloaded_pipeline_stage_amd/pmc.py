@@ -347,8 +347,75 @@ def summarize_kernels(d: str, title: str, commands, bench_line: str | None = Non
     return "\n".join(lines) + "\n"
 
 
+def summarize_configs(bench_line: str, commands) -> tuple[str, str | None]:
+    """Text summaries of a `bench.py --configs [--ablation] [--optimizer]`
+    line: the per-configuration table (and the host optimizer and streamed
+    figures the line carries), and the transfer-policy ablation table when
+    the line has one (else None)."""
+    d = json.loads(bench_line)
+    cf = d["configs"]
+    out = ["# Per-configuration throughput, weights resident (bench.py --configs)", ""] + [
+        f"command: {c}" for c in commands] + [
+        "", "Each configuration's own call sequence, wall time with the context synced, median of 3 after one warm-up;",
+        "tokens/s = T / time; TFLOP/s counts matrix products only (causal attention on its causal pairs, active experts "
+        "only,", "no weight-gradient products for the frozen LoRA base).", "",
+        "config             call                                      ms     tokens/s  TFLOP/s"]
+    notes = []
+    for name, c in cf.items():
+        for call, v in c.items():
+            if not isinstance(v, dict):
+                if call == "note":
+                    notes.append(f"{name}: {v}")
+                continue
+            tf = v.get("tflops")
+            out.append(f"{name:18s} {call:36s} {v['ms']:8.2f} {v['tokens_per_s']:12.0f} "
+                       f"{tf if tf is not None else '-':>8}")
+            if "note" in v:
+                notes.append(f"{name} {call}: {v['note']}")
+    out += [""] + notes
+    for key, label in (("optimizer", "host optimizer step (bench.py --optimizer)"),
+                       ("streamed", "streamed step, fp32 gradients"),
+                       ("streamed_bf16_grads", "streamed step, bf16 gradients")):
+        if key in d:
+            out.append(f"{label}: " + json.dumps(d[key]))
+    out += ["", "raw: " + json.dumps(cf)]
+    ab = d.get("ablation")
+    rows = None
+    if ab:
+        rows = ["# Transfer-policy ablation: Llama-3.1-8B-shaped layers on one MI355X", ""] + [
+            f"command: {c}" for c in commands] + ["", "workload: " + ab["workload"],
+            f"per stage: {ab['weights_GB_per_stage']} GB of bf16 weights up; per backward stage "
+            f"{ab['grads_GB_per_bwd_stage']} GB of fp32 gradients down;",
+            "activations and activation gradients go through pinned host memory between stages. Throughput = tokens "
+            "of one pass / wall time of one pass (mean of 2 after 1 warm-up).", "",
+            "| mbs | no_prefetch | prefetch | windowed | windowed / no_prefetch | windowed / prefetch |",
+            "|---|---|---|---|---|---|"]
+        for i, m in enumerate(ab["mbs"]):
+            rows.append(f"| {m} | {ab['no_prefetch'][i]:.0f} | {ab['prefetch'][i]:.0f} | {ab['windowed'][i]:.0f} | "
+                        f"{ab['windowed_over_no_prefetch'][i]:.3f} | {ab['windowed_over_prefetch'][i]:.3f} |")
+    return "\n".join(out) + "\n", (None if rows is None else "\n".join(rows) + "\n")
+
+
 if __name__ == "__main__":
     import sys
+    if len(sys.argv) > 1 and sys.argv[1] == "configs":
+        import argparse
+        ap = argparse.ArgumentParser(description="summarise a bench.py --configs line")
+        ap.add_argument("mode")
+        ap.add_argument("bench_log")
+        ap.add_argument("--command", action="append", default=[])
+        ap.add_argument("--out", required=True)
+        ap.add_argument("--ablation-out", default=None)
+        a = ap.parse_args()
+        line = [l for l in open(a.bench_log) if l.startswith("{")][-1]
+        txt, abl = summarize_configs(line, a.command)
+        with open(a.out, "w") as f:
+            f.write(txt)
+        if abl is not None and a.ablation_out:
+            with open(a.ablation_out, "w") as f:
+                f.write(abl)
+        print(txt)
+        sys.exit(0)
     if len(sys.argv) > 1 and sys.argv[1] == "kernels":
         import argparse
         ap = argparse.ArgumentParser(description="summarise a kernel trace")

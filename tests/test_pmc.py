@@ -1,5 +1,6 @@
 """Host-side reduction of rocprofv3 counter runs to per-launch HBM bytes."""
 import csv
+import json
 import os
 
 from offloaded_pipeline_stage_amd import pmc
@@ -75,3 +76,25 @@ def test_kernel_trace_summary(tmp_path):
     assert "    4      6.00    1500.0    1400.0    1600.0  60.0  gemm_mfma_kernel<256, 256, 2, 4, 1, 1, 0, 1, 0>" in txt
     assert "flash_dkdv_kernel" in txt and "1000.0" in txt
     assert "0.462 of the 2500 TFLOP/s peak" in txt
+
+
+def test_configs_summary():
+    """A bench line with configurations, the ablation, the optimizer and the
+    streamed figures gives both tables, every call on its own row."""
+    line = json.dumps({
+        "configs": {"a": {"tokens": 8, "fwd": {"ms": 2.0, "tokens_per_s": 4000.0, "tflops": 1.5},
+                          "note": "n1"},
+                    "b": {"tokens": 4, "x": {"ms": 1.0, "tokens_per_s": 4000.0, "tflops": None, "note": "n2"}}},
+        "optimizer": {"s_per_step": 0.3},
+        "streamed": {"ms_per_step": 60.0},
+        "ablation": {"workload": "w", "weights_GB_per_stage": 0.4, "grads_GB_per_bwd_stage": 0.8, "mbs": [1, 2],
+                     "no_prefetch": [10.0, 20.0], "prefetch": [11.0, 21.0], "windowed": [12.0, 22.0],
+                     "windowed_over_no_prefetch": [1.2, 1.1], "windowed_over_prefetch": [1.09, 1.05]}})
+    txt, abl = pmc.summarize_configs(line, ["cmd"])
+    assert "command: cmd" in txt
+    assert any(l.startswith("a ") and "fwd" in l and "2.00" in l for l in txt.splitlines())
+    assert any(l.startswith("b ") and l.rstrip().endswith("-") for l in txt.splitlines())
+    assert "a: n1" in txt and "b x: n2" in txt and "host optimizer step" in txt and "streamed step, fp32" in txt
+    assert "| 2 | 20 | 21 | 22 | 1.100 | 1.050 |" in abl
+    _, none = pmc.summarize_configs(json.dumps({"configs": {}}), [])
+    assert none is None
