@@ -223,14 +223,31 @@ __device__ __forceinline__ void dma16(i32x4_t r, const void* lds, uint32_t voff)
 // receives, in slot k, element c % 4 of the chunk addressed by lane
 // 4k + c / 4: so lane c of the group addresses row r0 + c / 4, d
 // d0 + 4 (c % 4), and every lane receives its own d for rows r0 .. r0 + 3.
-__device__ __forceinline__ bf16x8_t rd_trl(const char* t, int dt, int u, int j, int lane) {
+// The swizzle term of such a row depends on the lane only (r % 4 = (c / 4)
+// % 4 and (r / 4) % 4 = h, or h + 2 for the rows 8 further), and the d-tile
+// dt enters the chunk index as 4 dt, which XORs into it bit for bit; so the
+// lane's offsets for the four d-tiles are computed once (TrBase) and a read
+// adds only the sub-tile's and k-step's row offset, an immediate.
+struct TrBase {
+  int b0[4], b1[4];  // rows r and r + 8 of sub-tile 0, k-step 0, for d-tile dt
+};
+__device__ __forceinline__ TrBase tr_base(int lane) {
   const int grp = lane >> 4, c = lane & 15, h = lane >> 5;
-  const int d = 32 * dt + 16 * (grp & 1) + 4 * (c & 3);
-  const int r = 32 * u + 16 * j + 4 * h + (c >> 2);
-  const int off0 = r * 256 + (((d >> 3) ^ dr_swz(r)) << 4) + (d & 4) * 2;
-  const int off1 = (r + 8) * 256 + (((d >> 3) ^ dr_swz(r + 8)) << 4) + (d & 4) * 2;
-  const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t)(t + off0));
-  const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t)(t + off1));
+  const int s0 = 4 * ((c >> 2) & 3) + h;           // dr_swz of row r; row r + 8: s0 ^ 2
+  const int x = 2 * (grp & 1) + ((c & 3) >> 1);    // chunk of d within the d-tile
+  const int l = (4 * h + (c >> 2)) * 256 + (c & 1) * 8;
+  TrBase b;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    b.b0[dt] = l + (((4 * dt) ^ x ^ s0) << 4);
+    b.b1[dt] = l + 8 * 256 + (((4 * dt) ^ x ^ s0 ^ 2) << 4);
+  }
+  return b;
+}
+__device__ __forceinline__ bf16x8_t rd_trl(const char* t, const TrBase& tb, int dt, int u, int j) {
+  const char* row = t + (32 * u + 16 * j) * 256;
+  const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t)(row + tb.b0[dt]));
+  const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t)(row + tb.b1[dt]));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -249,6 +266,7 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
   extern __shared__ __align__(16) char smem[];
   __shared__ __align__(16) float sstat[NST][2 * TILE];   // lse and D of each stage's queries
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(tid), h = lane >> 5, n = lane & 31;
+  const TrBase tb = tr_base(lane);
   const int hk = blockIdx.x, b = blockIdx.z;
   const int kb = blockIdx.y;  // earliest keys (most queries) first
   const int G = p.nq / p.nkv;
@@ -426,8 +444,8 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          to[j][dt] = rd_trl(sO, dt, 0, j, lane);
-          tq[j][dt] = rd_trl(sQ, dt, 0, j, lane);
+          to[j][dt] = rd_trl(sO, tb, dt, 0, j);
+          tq[j][dt] = rd_trl(sQ, tb, dt, 0, j);
         }
       stats(lq1, dq1, 1, sL);
 #pragma unroll
@@ -450,8 +468,8 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          to[j][dt] = rd_trl(sO, dt, 1, j, lane);
-          tq[j][dt] = rd_trl(sQ, dt, 1, j, lane);
+          to[j][dt] = rd_trl(sO, tb, dt, 1, j);
+          tq[j][dt] = rd_trl(sQ, tb, dt, 1, j);
         }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -508,6 +526,7 @@ __global__ __launch_bounds__(NT) void flash_dq_kernel(FlashParams p, const bf16*
   constexpr int NDMA = 8;                // loads per wave per tile
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(tid), h = lane >> 5, n = lane & 31;
+  const TrBase tb = tr_base(lane);
   const int head = blockIdx.x, b = blockIdx.z;
   const int qb = p.n_blocks - 1 - blockIdx.y;  // longest rows first
   const int hk = head / (p.nq / p.nkv);
@@ -617,7 +636,7 @@ __global__ __launch_bounds__(NT) void flash_dq_kernel(FlashParams p, const bf16*
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) tk[j][dt] = rd_trl(sK, dt, 0, j, lane);
+        for (int dt = 0; dt < 4; ++dt) tk[j][dt] = rd_trl(sK, tb, dt, 0, j);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA,
@@ -633,7 +652,7 @@ __global__ __launch_bounds__(NT) void flash_dq_kernel(FlashParams p, const bf16*
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) tk[j][dt] = rd_trl(sK, dt, 1, j, lane);
+        for (int dt = 0; dt < 4; ++dt) tk[j][dt] = rd_trl(sK, tb, dt, 1, j);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -671,6 +690,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   constexpr int STAGE = 2 * TILE * 256;  // K, V
   __shared__ __align__(16) char smem[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(tid), h = lane >> 5, n = lane & 31;
+  const TrBase tb = tr_base(lane);
   const int head = blockIdx.x, b = blockIdx.z;
   const int qb = p.n_blocks - 1 - blockIdx.y;  // longest rows first
   const int hk = head / (p.nq / p.nkv);
@@ -786,7 +806,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         for (int j = 0; j < 2; ++j) {
           const bf16x8_t pb = to_operand(st[t], j);
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(rd_trl(sV, dt, t, j, lane), pb, acc[dt]);
+          for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(rd_trl(sV, tb, dt, t, j), pb, acc[dt]);
         }
     }
     sync_next();
