@@ -68,6 +68,16 @@ __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Register-class hints for the one-wave-per-SIMD kernels, which use more
+// than the 256 architectural registers: fragments that only ever feed MFMAs
+// (the wave's own rows, held for the whole kernel) go to the accumulation
+// registers, which MFMA operands may come from; score tiles, which the
+// vector ALU reads next, to the architectural ones. Without them the
+// compiler produced the score tiles in accumulation registers and copied
+// them out for every tile.
+__device__ __forceinline__ void to_acc_regs(bf16x8_t& f) { asm volatile("" : "+a"(f)); }
+__device__ __forceinline__ void to_arch_regs(f32x16_t& t) { asm volatile("" : "+v"(t)); }
+
 __device__ __forceinline__ f32x16_t zero16() {
   f32x16_t z;
 #pragma unroll
@@ -545,6 +555,11 @@ __global__ __launch_bounds__(NT) void flash_dq_kernel(FlashParams p, const bf16*
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = zero16();
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));  // Q, dO, lse and D landed (see dma16)
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    to_acc_regs(qf[s]);
+    to_acc_regs(dof[s]);
+  }
 
   const int klast = min(q0 + BROWS, p.seq) - 1;
   const int ntile = klast / TILE + 1;
@@ -621,6 +636,8 @@ __global__ __launch_bounds__(NT) void flash_dq_kernel(FlashParams p, const bf16*
         st0 = mfma(fk[s], qf[s], st0);
         dp0 = mfma(fv[s], dof[s], dp0);
       }
+      to_arch_regs(st0);
+      to_arch_regs(dp0);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         fk[s] = rd_rml(sK, 1, s, lane);
@@ -632,6 +649,8 @@ __global__ __launch_bounds__(NT) void flash_dq_kernel(FlashParams p, const bf16*
         st1 = mfma(fk[s], qf[s], st1);
         dp1 = mfma(fv[s], dof[s], dp1);
       }
+      to_arch_regs(st1);
+      to_arch_regs(dp1);
       dscore(st0, dp0, sb0, 0, k0, mask_c);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
