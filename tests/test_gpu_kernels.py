@@ -272,3 +272,34 @@ def test_gemm_epilogue_edges(B, M, N, K, ldc, out_f32, accumulate):
     tol = 1e-5 if out_f32 else 2 ** -8
     assert max_rel(C[:, :N], ref) < tol
     assert torch.equal(C[:, N:].cpu(), base[:, N:])  # columns past N untouched
+
+
+@pytest.mark.parametrize("ak,bk,ldc,out_f32,accumulate", [
+    (False, True, 4233, True, True),     # M-major A: the 64 x 128 wave tiles; element-wise epilogue
+    (False, True, 4232, False, False),   # the same tiles, bf16 four-column stores
+    (False, False, 4236, True, True),    # both operands M-major, aligned stride, accumulation
+    (True, False, 4233, True, False),    # M-major B
+])
+def test_gemm_mmajor_epilogue_edges(B, ak, bk, ldc, out_f32, accumulate):
+    """The layouts with an M-major operand (the weight- and input-gradient
+    products) at a size that takes the 256 x 256 tiles, with ragged edges, a
+    K tail, padded row strides and fp32 accumulation; columns past N are left
+    untouched."""
+    M, N, K = 4104, 4232, 136
+    say("gemm m-major epilogue", ak, bk, ldc, out_f32, accumulate)
+    ctx = _ctx(B)
+    dev = torch.device("cuda")
+    a_s, a = _operand(M, K, ak, 34, f"ma{M}{K}")
+    b_s, b = _operand(N, K, bk, 35, f"mb{N}{K}")
+    dt = torch.float32 if out_f32 else torch.bfloat16
+    base = synth.normal((M, ldc), 36, f"mc{M}{ldc}").to(dt)
+    C = base.clone().to(dev)
+    ctx.op_gemm_bf16(M, N, K, a_s.to(dev), K if ak else M, ak, b_s.to(dev), K if bk else N, bk, C, ldc,
+                     out_f32=out_f32, accumulate=accumulate)
+    ctx.sync()
+    ref = a @ b.T
+    if accumulate:
+        ref = ref + base[:, :N].double()
+    tol = 1e-5 if out_f32 else 2 ** -8
+    assert max_rel(C[:, :N], ref) < tol
+    assert torch.equal(C[:, N:].cpu(), base[:, N:])
