@@ -323,6 +323,48 @@ __global__ void rope_apply_kernel(T* buf, int64_t ld, int rows, int seq, int n_h
   base[i + half] = from_f<T>(b * cs.x + a * s);
 }
 
+// The same rotation for bf16 buffers, four pairs per thread: 8-byte loads
+// and stores of each half, the four (cos, sin) pairs in two 16-byte loads.
+// Needs d % 8 == 0, ld % 4 == 0 and an 8-byte aligned buffer.
+__global__ void rope_apply4_kernel(bf16* buf, int64_t ld, int rows, int seq, int n_heads, int d,
+                                   const float2* __restrict__ tab, int inverse) {
+  const int half = d / 2, q = half / 4;
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t per_row = (int64_t)n_heads * q;
+  if (idx >= (int64_t)rows * per_row) return;
+  const int row = (int)(idx / per_row);
+  const int rem = (int)(idx % per_row);
+  const int h = rem / q, i0 = 4 * (rem % q);
+  const int p = row % seq;
+  const float4 t01 = *reinterpret_cast<const float4*>(tab + (int64_t)p * half + i0);
+  const float4 t23 = *reinterpret_cast<const float4*>(tab + (int64_t)p * half + i0 + 2);
+  const float c[4] = {t01.x, t01.z, t23.x, t23.z};
+  float sn[4] = {t01.y, t01.w, t23.y, t23.w};
+  if (inverse)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sn[e] = -sn[e];
+  bf16* base = buf + (int64_t)row * ld + (int64_t)h * d + i0;
+  const uint2 ua = *reinterpret_cast<const uint2*>(base);
+  const uint2 ub = *reinterpret_cast<const uint2*>(base + half);
+  const uint32_t wa[2] = {ua.x, ua.y}, wb[2] = {ub.x, ub.y};
+  uint32_t oa[2], ob[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    float a2[2], b2[2], ra[2], rb[2];
+    a2[0] = __uint_as_float(wa[k] << 16); a2[1] = __uint_as_float(wa[k] & 0xffff0000u);
+    b2[0] = __uint_as_float(wb[k] << 16); b2[1] = __uint_as_float(wb[k] & 0xffff0000u);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      ra[e] = a2[e] * c[2 * k + e] - b2[e] * sn[2 * k + e];
+      rb[e] = b2[e] * c[2 * k + e] + a2[e] * sn[2 * k + e];
+    }
+    oa[k] = (uint32_t)to_bf16(ra[0]).u | ((uint32_t)to_bf16(ra[1]).u << 16);
+    ob[k] = (uint32_t)to_bf16(rb[0]).u | ((uint32_t)to_bf16(rb[1]).u << 16);
+  }
+  *reinterpret_cast<uint2*>(base) = make_uint2(oa[0], oa[1]);
+  *reinterpret_cast<uint2*>(base + half) = make_uint2(ob[0], ob[1]);
+}
+
 // ---------------------------------------------------------------------------
 // SwiGLU (unfused path)
 // ---------------------------------------------------------------------------
@@ -597,6 +639,15 @@ __global__ void cast_kernel(const float* a, T* out, size_t n) {
   if (i < n) out[i] = from_f<T>(a[i]);
 }
 
+// fp32 -> bf16, four elements per thread (16-byte loads, 8-byte stores)
+__global__ void cast4_bf16_kernel(const float4* __restrict__ a, uint2* __restrict__ out, size_t n4) {
+  const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  const float4 v = a[i];
+  out[i] = make_uint2((uint32_t)to_bf16(v.x).u | ((uint32_t)to_bf16(v.y).u << 16),
+                      (uint32_t)to_bf16(v.z).u | ((uint32_t)to_bf16(v.w).u << 16));
+}
+
 unsigned blocks_for(int64_t n, int per = 256) { return (unsigned)cdiv(n, per); }
 
 }  // namespace
@@ -741,8 +792,13 @@ rp_status rope_apply(int dt, void* buf, int64_t ld, int T, int seq, int n_heads,
                      const float2* tab, bool inverse, hipStream_t s) {
   const int64_t n = (int64_t)T * n_heads * (d / 2);
   if (n == 0) return RP_OK;
-  TraceScope ts(s, "rope_apply_kernel", 0.0, (double)n * 4 * dtype_size(dt));
-  if (dt == RP_DTYPE_BF16)
+  const bool v4 =
+      dt == RP_DTYPE_BF16 && d % 8 == 0 && ld % 4 == 0 && ((uintptr_t)buf & 7) == 0 && ((uintptr_t)tab & 15) == 0;
+  TraceScope ts(s, v4 ? "rope_apply4_kernel" : "rope_apply_kernel", 0.0, (double)n * 4 * dtype_size(dt));
+  if (v4)
+    RP_LAUNCH(rope_apply4_kernel, dim3(blocks_for(n / 4)), dim3(256), 0, s, (bf16*)buf, ld, T, seq, n_heads, d, tab,
+              inverse ? 1 : 0);
+  else if (dt == RP_DTYPE_BF16)
     RP_LAUNCH(rope_apply_kernel<bf16>, dim3(blocks_for(n)), dim3(256), 0, s, (bf16*)buf, ld, T, seq,
               n_heads, d, tab, inverse ? 1 : 0);
   else
@@ -861,8 +917,12 @@ rp_status splitk_reduce(const float* part, int splits, int M, int N, float* C, i
 
 rp_status cast_from_f32(int dt, const float* a, void* out, size_t n, hipStream_t s) {
   if (n == 0) return RP_OK;
-  TraceScope ts(s, "cast_kernel", 0.0, (double)n * (4 + dtype_size(dt)));
-  if (dt == RP_DTYPE_BF16)
+  const bool v4 = dt == RP_DTYPE_BF16 && n % 4 == 0 && ((uintptr_t)a & 15) == 0 && ((uintptr_t)out & 7) == 0;
+  TraceScope ts(s, v4 ? "cast4_bf16_kernel" : "cast_kernel", 0.0, (double)n * (4 + dtype_size(dt)));
+  if (v4)
+    RP_LAUNCH(cast4_bf16_kernel, dim3(blocks_for((int64_t)(n / 4))), dim3(256), 0, s, (const float4*)a, (uint2*)out,
+              n / 4);
+  else if (dt == RP_DTYPE_BF16)
     RP_LAUNCH(cast_kernel<bf16>, dim3(blocks_for(n)), dim3(256), 0, s, a, (bf16*)out, n);
   else
     RP_LAUNCH(cast_kernel<float>, dim3(blocks_for(n)), dim3(256), 0, s, a, (float*)out, n);
