@@ -478,7 +478,7 @@ __global__ __launch_bounds__(1024) void ce_combine_kernel(int rows, int n_shards
   s_cnt[threadIdx.x] = cnt;
   __syncthreads();
   for (int o = 512; o > 0; o >>= 1) {
-    if (threadIdx.x < o) {
+    if ((int)threadIdx.x < o) {
       s_loss[threadIdx.x] += s_loss[threadIdx.x + o];
       s_cnt[threadIdx.x] += s_cnt[threadIdx.x + o];
     }
