@@ -142,6 +142,19 @@ struct FlashParams {
   int n_blocks;      // row blocks of 128 per sequence
 };
 
+// Query head of workgroup column x of the forward grid: column
+// x = m n_kv + j runs head j G + m (G = n_q / n_kv), so the G query heads of
+// kv head j are the columns congruent to j modulo n_kv. Workgroups go to the
+// eight XCDs in turn by dispatch index; with n_q a multiple of 8 a column's
+// XCD is x % 8, and with n_kv dividing 8 every workgroup on XCD c then reads
+// kv head c % n_kv: they stream the same K and V tiles and share them in L2.
+// (The dQ kernel, whose streamed tiles are the same, measured no gain from
+// it and keeps column = head.)
+__device__ __forceinline__ int head_of_column(int x, int nq, int nkv) {
+  const int g = nq / nkv;
+  return (x % nkv) * g + x / nkv;
+}
+
 // ---------------------------------------------------------------------------
 // backward preprocessing: Dr[h][t] = sum_d dO[t, h, d] * O[t, h, d]
 // ---------------------------------------------------------------------------
@@ -710,7 +723,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   __shared__ __align__(16) char smem[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(tid), h = lane >> 5, n = lane & 31;
   const TrBase tb = tr_base(lane);
-  const int head = blockIdx.x, b = blockIdx.z;
+  const int head = head_of_column(blockIdx.x, p.nq, p.nkv), b = blockIdx.z;
   const int qb = p.n_blocks - 1 - blockIdx.y;  // longest rows first
   const int hk = head / (p.nq / p.nkv);
   const bf16* base = p.qkv + (int64_t)b * p.seq * p.ld;
