@@ -523,8 +523,7 @@ __global__ __launch_bounds__(256) void ce_grad_kernel(const float* __restrict__ 
   if constexpr (VEC) {
     const float4* z4 = reinterpret_cast<const float4*>(zr);
     const int n4 = Vs >> 2;
-    for (int c = threadIdx.x; c < n4; c += 256) {
-      const float4 v = z4[c];
+    auto emit = [&](int c, float4 v) __attribute__((always_inline)) {
       float o0 = __expf(v.x - lt) * sc, o1 = __expf(v.y - lt) * sc, o2 = __expf(v.z - lt) * sc,
             o3 = __expf(v.w - lt) * sc;
       const int j = yl - 4 * c;
@@ -533,7 +532,17 @@ __global__ __launch_bounds__(256) void ce_grad_kernel(const float* __restrict__ 
       if (j == 2) o2 -= sc;
       if (j == 3) o3 -= sc;
       store4<T>(dr + 4 * c, o0, o1, o2, o3);
+    };
+    // four loads in flight per thread before the first result is stored
+    int c = threadIdx.x;
+    for (; c + 768 < n4; c += 1024) {
+      const float4 a = z4[c], b = z4[c + 256], d = z4[c + 512], e = z4[c + 768];
+      emit(c, a);
+      emit(c + 256, b);
+      emit(c + 512, d);
+      emit(c + 768, e);
     }
+    for (; c < n4; c += 256) emit(c, z4[c]);
     c0 = n4 << 2;
   }
   for (int c = c0 + threadIdx.x; c < Vs; c += 256) {
