@@ -786,7 +786,6 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
   }
   RP_TRY(fork(sd, st, ns));
   RP_TRY(ce_combine((int)T, ns, parts, zlab, labels, c->vocab, lse, loss, inv_n, st));
-  RP_TRY(fill_zero(dxf, (size_t)T * s.H * 4, st));
   auto grad = [&](int i, hipStream_t on) -> rp_status {
     const int lo = c->shard_lo[i], vs = c->shard_lo[i + 1] - lo;
     return ce_grad(dt, logits + (size_t)i * T * vs_max, vs, (int)T, vs, lo, labels, c->vocab, lse, inv_n,
@@ -804,8 +803,10 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
     }
     RP_TRY(wait_grad_drained(c, w));
     const void* dz = dzb[i & 1];
+    // dX = sum over shards of dz_s W_s: the first shard's product writes dxf
+    // (no separate clearing pass), the others add to it
     GemmDesc gx = mk((int)T, s.H, vs, dz, vs, true, w.w, s.H, false, dxf, s.H, dt, RP_DTYPE_F32);
-    gx.accumulate = true;
+    gx.accumulate = i > 0;
     RP_TRY(gemm(gx, st));
     if (xt)
       RP_TRY(gemm(mk(vs, s.H, (int)T, dz, vs, false, zt, T, true, w.g, s.H, dt, RP_DTYPE_F32), st));
