@@ -61,6 +61,7 @@ struct GemmParams {
   const float2* rope_tab; // EPI_ROPE: (cos, sin) of position p, pair i at [p * 64 + i]
   int rope_seq, rope_heads;
   int vec;  // row strides of C, R and C2 (and F) multiples of 4 elements, bases aligned to 4 elements
+  int skip_c;  // EPI_SWIGLU: store only C2
 };
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
@@ -577,9 +578,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(GemmParams p)
           float mo[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) mo[e] = silu_f(a[e]) * bb[e];
-          bf16* gu = reinterpret_cast<bf16*>(p.C) + (int64_t)m * p.ldc;
-          st4(gu + f, cnt, p.vec, a);
-          st4(gu + p.F + f, cnt, p.vec, bb);
+          if (!p.skip_c) {
+            bf16* gu = reinterpret_cast<bf16*>(p.C) + (int64_t)m * p.ldc;
+            st4(gu + f, cnt, p.vec, a);
+            st4(gu + p.F + f, cnt, p.vec, bb);
+          }
           st4(reinterpret_cast<bf16*>(p.C2) + (int64_t)m * p.ldc2 + f, cnt, p.vec, mo);
         }
       }
@@ -761,6 +764,7 @@ rp_status launch_mfma(const GemmDesc& d, hipStream_t s) {
   p.C = d.C; p.ldc = d.ldc;
   p.R = d.R; p.ldr = d.ldr;
   p.C2 = d.C2; p.ldc2 = d.ldc2;
+  p.skip_c = EPI == EPI_SWIGLU && d.c_unused ? 1 : 0;
   p.accumulate = d.accumulate ? 1 : 0;
   p.alpha = d.alpha;
   p.kc = d.K;

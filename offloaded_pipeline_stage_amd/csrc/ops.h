@@ -47,6 +47,10 @@ struct GemmDesc {
   bool accumulate = false;
   const void* R = nullptr; int64_t ldr = 0;
   void* C2 = nullptr; int64_t ldc2 = 0;
+  // EPI_SWIGLU: the caller reads only C2 afterwards, so the fused path does
+  // not store the pre-activations into C (the unfused path still uses C as
+  // its scratch)
+  bool c_unused = false;
   float* tmp = nullptr;           // fp32 [M, N] scratch for the unfused fp32 path
   bool force_simple = false;      // use the generic kernel even for bf16
   float alpha = 1.f;              // C = alpha * A B^T (+ R): store / residual epilogues

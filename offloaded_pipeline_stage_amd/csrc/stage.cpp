@@ -226,7 +226,7 @@ GemmDesc mk(int M, int N, int K, const void* A, int64_t lda, bool ak, const void
 rp_status layer_fwd(rp_ctx* c, const LayerBinding& lb, const LoraBf16& lw, void* ye, void* lora_d,
                      const float* router, int T,
                     int seq, const void* x, const Acts& A, void* y, const float2* rope, hipStream_t st,
-                    const std::function<rp_status()>& after_qkv = {}) {
+                    bool keep_gu, const std::function<rp_status()>& after_qkv = {}) {
   const Shape& s = c->sh;
   const int dt = s.dt;
   const rp_layer_cfg& cfg = c->cfg;
@@ -314,6 +314,7 @@ rp_status layer_fwd(rp_ctx* c, const LayerBinding& lb, const LoraBf16& lw, void*
     GemmDesc gg = mk(T * k, 2 * Fe, s.H, A.b, s.H, true, wptr(w, cfg, RP_T_WGU), s.H, true, A.gu, 2 * Fe, dt, dt,
                      EPI_SWIGLU);
     gg.C2 = A.m; gg.ldc2 = Fe;
+    gg.c_unused = !keep_gu;
     gg.group = &grp;
     RP_TRY(gemm_grouped(gg, st));
     if (y == nullptr) return RP_OK;
@@ -329,6 +330,7 @@ rp_status layer_fwd(rp_ctx* c, const LayerBinding& lb, const LoraBf16& lw, void*
   GemmDesc gg = mk(T, 2 * s.F, s.H, A.b, s.H, true, wptr(w, cfg, RP_T_WGU), s.H, true, A.gu, 2 * s.F, dt, dt,
                    EPI_SWIGLU);
   gg.C2 = A.m; gg.ldc2 = s.F;
+  gg.c_unused = !keep_gu;  // the pre-activations are read only by a backward
   RP_TRY(gemm(gg, st));
   if (y == nullptr) return RP_OK;
   GemmDesc gd = mk(T, s.H, s.F, A.m, s.F, true, wptr(w, cfg, RP_T_WD), s.F, true, y, s.H, dt, dt, EPI_RESID);
@@ -588,7 +590,7 @@ rp_status stage_fwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* x
     // i - 1, whose checkpoint download must have finished
     if (!keep && ckpt_host && i >= 1 && i != n - 1) RP_HIP(hipStreamWaitEvent(st, d2h_done[i - 1], 0));
     RP_TRY(layer_fwd(c, lb, L.lw, L.ye, L.lora_d, s.E > 0 ? router[i] : nullptr, (int)T, seq, x, A, y, L.rope, st,
-                     download_ckpt));
+                     keep, download_ckpt));
     RP_TRY(mark_consumed(c, w));
     if (s.r > 0) RP_TRY(mark_consumed(c, lb.lora));
   }
@@ -689,7 +691,7 @@ rp_status stage_bwd(rp_ctx* c, int l0, int l1, int batch, int seq, const void* c
       x = ck_dev ? ckpt[i] : L.bt.ck[i & 1];
       // recompute the forward from the checkpoint (same kernels as the forward)
       RP_TRY(layer_fwd(c, lb, L.lw, L.ye, L.lora_d, s.E > 0 ? router[i] : nullptr, (int)T, seq, x, A, nullptr, L.rope,
-                       st));
+                       st, true));
     }
     // inter-layer gradients alternate gp[0], gp[1]; the stage input's goes to dx
     void* g_out = (i == 0) ? dx : L.bt.gp[(n - 1 - i) & 1];
