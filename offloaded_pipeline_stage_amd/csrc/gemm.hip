@@ -316,11 +316,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(GemmParams p)
   const int wm = wave / WGN, wn = wave % WGN;
 
   // tile order: contiguous ranges per XCD (workgroups are dealt round-robin
-  // over the 8 XCDs), grouped 8 tile-rows at a time for L2 reuse
+  // over the 8 XCDs), grouped 4 tile-rows at a time for L2 reuse, so that an
+  // XCD's 32 concurrent tiles span 4 rows and 8 columns (groups of 8 rows, 4
+  // columns: the Llama-8B-shaped step 0.37-0.40 ms longer; of 2 and 16 rows
+  // longer still)
   int pid = blockIdx.x;
   const int ntiles = p.tiles_m * p.tiles_n;
   if ((ntiles & 7) == 0) pid = (pid & 7) * (ntiles >> 3) + (pid >> 3);
-  constexpr int GROUP = 8;
+  constexpr int GROUP = 4;
   const int in_group = GROUP * p.tiles_n;
   const int gid = pid / in_group;
   const int first_m = gid * GROUP;
