@@ -40,6 +40,10 @@ GEMM_CASES = [
     (1000, 520, 72),
     (4096, 4096, 128),   # 256x256 tiles
     (4104, 4232, 200),   # 256x256 tiles with ragged edges
+    # 256x256 tiles, a tile count divisible by 8 (tiles dealt to the XCDs in
+    # contiguous ranges) and a last group of tile rows shorter than the others
+    (1272, 12288, 72),   # 5 x 48 tiles
+    (1496, 10240, 136),  # 6 x 40 tiles
 ]
 
 
