@@ -3,6 +3,7 @@
 // cross-entropy, token embedding. All HBM-bound: one wavefront per row with
 // 16-byte vector accesses, reductions by fixed-order butterflies so every
 // result is deterministic (recomputation must reproduce the forward exactly).
+#include <type_traits>
 #include <algorithm>
 
 #include "ops.h"
@@ -123,6 +124,42 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const T* __restrict__ 
 #pragma unroll
     for (int i = 0; i < V; ++i) v[i] = v[i] * r * g[i];
     store_vec<T>(yr + c, v);
+  }
+}
+
+// The same for bf16 rows of NV * 512 elements, the row held in registers:
+// each row is read from memory once (the two-pass kernel above reads it twice,
+// and its second read misses L2), every lane's loads issued together. The
+// lane owns the same elements and sums their squares in the same order, so
+// the results are bit-identical.
+template <int NV>
+__global__ __launch_bounds__(256) void rmsnorm_fwd_rows_kernel(const bf16* __restrict__ x,
+                                                               const bf16* __restrict__ gamma,
+                                                               bf16* __restrict__ y, float* __restrict__ rstd,
+                                                               int rows, int H, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const bf16* xr = x + (int64_t)row * H;
+  float v[NV][8];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) load_vec<bf16>(xr + (64 * j + lane) * 8, v[j]);
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss = fmaf(v[j][i], v[j][i], ss);
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+  if (lane == 0) rstd[row] = r;
+  bf16* yr = y + (int64_t)row * H;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    float g[8];
+    load_vec<bf16>(gamma + (64 * j + lane) * 8, g);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[j][i] = v[j][i] * r * g[i];
+    store_vec<bf16>(yr + (64 * j + lane) * 8, v[j]);
   }
 }
 
@@ -698,7 +735,24 @@ rp_status rmsnorm_fwd(int dt, const void* x, const void* gamma, void* y, float* 
   if (T == 0) return RP_OK;
   RP_CHECK(H % 8 == 0, RP_ERR_UNSUPPORTED, "rmsnorm: H %% 8 != 0");
   dim3 g(blocks_for(T, 4));
-  TraceScope ts(s, "rmsnorm_fwd_kernel", 0.0, (double)T * H * 2 * dtype_size(dt) + H * dtype_size(dt) + 4.0 * T);
+  const double bytes = (double)T * H * 2 * dtype_size(dt) + H * dtype_size(dt) + 4.0 * T;
+  if (dt == RP_DTYPE_BF16 && H % 512 == 0) {
+    auto rows = [&](auto nv_c) -> rp_status {
+      constexpr int NV = decltype(nv_c)::value;
+      TraceScope ts(s, "rmsnorm_fwd_rows_kernel", 0.0, bytes);
+      RP_LAUNCH(rmsnorm_fwd_rows_kernel<NV>, g, dim3(256), 0, s, (const bf16*)x, (const bf16*)gamma, (bf16*)y,
+                rstd, T, H, eps);
+      return RP_OK;
+    };
+    switch (H / 512) {
+      case 4: return rows(std::integral_constant<int, 4>{});
+      case 8: return rows(std::integral_constant<int, 8>{});
+      case 10: return rows(std::integral_constant<int, 10>{});
+      case 16: return rows(std::integral_constant<int, 16>{});
+      default: break;
+    }
+  }
+  TraceScope ts(s, "rmsnorm_fwd_kernel", 0.0, bytes);
   if (dt == RP_DTYPE_BF16)
     RP_LAUNCH(rmsnorm_fwd_kernel<bf16>, g, dim3(256), 0, s, (const bf16*)x, (const bf16*)gamma,
               (bf16*)y, rstd, T, H, eps);
