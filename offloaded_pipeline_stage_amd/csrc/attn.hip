@@ -210,12 +210,14 @@ rp_status attn_fwd(const AttnDesc& a, const void* qkv, void* o, float* lse, hipS
   return a.d == 128 ? fwd_simple<float, 2>(a, qkv, o, lse, s) : fwd_simple<float, 1>(a, qkv, o, lse, s);
 }
 
+bool attn_bwd_fuses_rope(const AttnDesc& a) { return a.dt == RP_DTYPE_BF16 && a.d == 128 && flash_supported(a); }
+
 rp_status attn_bwd(const AttnDesc& a, const void* qkv, const void* o, const void* dout, const float* lse,
-                   float* Dbuf, void* dqkv, hipStream_t s) {
+                   float* Dbuf, void* dqkv, hipStream_t s, const float2* rope_inv) {
   RP_TRY(check(a));
+  RP_CHECK(!rope_inv || attn_bwd_fuses_rope(a), RP_ERR_UNSUPPORTED, "attn_bwd: no fused rotation for this shape");
   if (a.batch * a.seq == 0) return RP_OK;
-  if (a.dt == RP_DTYPE_BF16 && a.d == 128 && flash_supported(a))
-    return flash_bwd(a, qkv, o, dout, lse, Dbuf, dqkv, s);
+  if (attn_bwd_fuses_rope(a)) return flash_bwd(a, qkv, o, dout, lse, Dbuf, dqkv, s, rope_inv);
   if (a.dt == RP_DTYPE_BF16)
     return a.d == 128 ? bwd_simple<bf16, 2>(a, qkv, o, dout, lse, Dbuf, dqkv, s)
                       : bwd_simple<bf16, 1>(a, qkv, o, dout, lse, Dbuf, dqkv, s);

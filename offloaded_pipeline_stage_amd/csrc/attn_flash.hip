@@ -116,19 +116,47 @@ __device__ __forceinline__ void load_rows_b(bf16x8_t (&f)[8], const bf16* g, int
 }
 
 // store a [128 d x 32 rows] accumulator (rows on lanes) scaled by `mul` into
-// row `row` of a strided bf16 matrix at column col
+// row `row` of a strided bf16 matrix at column col. With `rot` (a RoPE table,
+// (cos, sin) of position p and pair i at rot[64 p + i]) the values are first
+// taken back through the rotation of the row's position: the gradient of the
+// rotate-half pair (d, d + 64) is (a cos + b sin, b cos - a sin). A lane
+// holds both members of its pairs (d-tiles dt and dt + 2), so this needs no
+// exchange, and each value is rounded to bf16 once.
 __device__ __forceinline__ void store_acc_rows(const f32x16_t (&acc)[4], float mul, bf16* g, int64_t ld, int row,
-                                               int rmax, int col, int h) {
+                                               int rmax, int col, int h, const float2* rot = nullptr) {
   if (row >= rmax) return;
   bf16* out = g + (int64_t)row * ld + col;
+  float v[4][16];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[dt][r] = acc[dt][r] * mul;
+  if (rot) {
+    const float2* tr = rot + (int64_t)row * 64;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // pairs 32 dt + 8 q + 4 h + e, e = 0..3: two 16-byte table reads
+        const float4 t01 = *reinterpret_cast<const float4*>(tr + 32 * dt + 8 * q + 4 * h);
+        const float4 t23 = *reinterpret_cast<const float4*>(tr + 32 * dt + 8 * q + 4 * h + 2);
+        const float c[4] = {t01.x, t01.z, t23.x, t23.z}, sn[4] = {t01.y, t01.w, t23.y, t23.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = v[dt][4 * q + e], b = v[dt + 2][4 * q + e];
+          v[dt][4 * q + e] = a * c[e] + b * sn[e];
+          v[dt + 2][4 * q + e] = b * c[e] - a * sn[e];
+        }
+      }
+  }
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int d = 32 * dt + 8 * q + 4 * h;
       u32x2_t u;
-      u[0] = pack_bf16x2(acc[dt][4 * q + 0] * mul, acc[dt][4 * q + 1] * mul);
-      u[1] = pack_bf16x2(acc[dt][4 * q + 2] * mul, acc[dt][4 * q + 3] * mul);
+      u[0] = pack_bf16x2(v[dt][4 * q + 0], v[dt][4 * q + 1]);
+      u[1] = pack_bf16x2(v[dt][4 * q + 2], v[dt][4 * q + 3]);
       *reinterpret_cast<u32x2_t*>(out + d) = u;
     }
 }
@@ -140,6 +168,7 @@ struct FlashParams {
   float c2;          // scale * log2(e)
   float scale;
   int n_blocks;      // row blocks of 128 per sequence
+  const float2* rope;  // backward: RoPE table to take dQ and dK back through (null: none)
 };
 
 // Query head of workgroup column x of the forward grid: column
@@ -531,7 +560,7 @@ __global__ __launch_bounds__(NT) void flash_dkdv_kernel(FlashParams p, const bf1
   // drain the loads past the end before the workgroup exits
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
   bf16* dst = dqkv + (int64_t)b * p.seq * p.ld;
-  store_acc_rows(dk, p.scale, dst, p.ld, kpos, p.seq, kcol, h);
+  store_acc_rows(dk, p.scale, dst, p.ld, kpos, p.seq, kcol, h, p.rope);
   store_acc_rows(dv, 1.f, dst, p.ld, kpos, p.seq, vcol, h);
 }
 
@@ -705,7 +734,7 @@ __global__ __launch_bounds__(NT) void flash_dq_kernel(FlashParams p, const bf16*
   for (; kt < kfree; ++kt) tile(kt, std::false_type{});
   for (; kt < ntile; ++kt) tile(kt, std::true_type{});
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-  store_acc_rows(acc, p.scale, dqkv + (int64_t)b * p.seq * p.ld, p.ld, qpos, p.seq, head * D, h);
+  store_acc_rows(acc, p.scale, dqkv + (int64_t)b * p.seq * p.ld, p.ld, qpos, p.seq, head * D, h, p.rope);
 }
 
 // ---------------------------------------------------------------------------
@@ -863,6 +892,7 @@ FlashParams make_params(const AttnDesc& a, const void* qkv) {
   p.scale = 1.0f / sqrtf((float)D);
   p.c2 = p.scale * LOG2E;
   p.n_blocks = (int)cdiv(a.seq, BROWS);
+  p.rope = nullptr;
   return p;
 }
 
@@ -900,12 +930,14 @@ rp_status flash_fwd(const AttnDesc& a, const void* qkv, void* o, float* lse, hip
 }
 
 rp_status flash_bwd(const AttnDesc& a, const void* qkv, const void* o, const void* dout, const float* lse,
-                    float* Dbuf, void* dqkv, hipStream_t s) {
+                    float* Dbuf, void* dqkv, hipStream_t s, const float2* rope_inv) {
   RP_CHECK(((uintptr_t)qkv & 15) == 0 && ((uintptr_t)o & 15) == 0 && ((uintptr_t)dout & 15) == 0 &&
                ((uintptr_t)dqkv & 15) == 0,
            RP_ERR_INVALID, "flash attention: buffers must be 16-byte aligned");
+  RP_CHECK(((uintptr_t)rope_inv & 15) == 0, RP_ERR_INVALID, "flash attention: the RoPE table must be 16-byte aligned");
   RP_TRY(set_lds_limits());
-  const FlashParams p = make_params(a, qkv);
+  FlashParams p = make_params(a, qkv);
+  p.rope = rope_inv;
   const int T = a.batch * a.seq;
   const int64_t rows = (int64_t)T * a.n_q;
   {

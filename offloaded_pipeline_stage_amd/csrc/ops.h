@@ -137,9 +137,11 @@ struct AttnDesc {
   int batch = 1, seq = 0, n_q = 0, n_kv = 0, d = 0;
 };
 rp_status attn_fwd(const AttnDesc& a, const void* qkv, void* o, float* lse, hipStream_t s);
-// Dbuf: fp32 [n_q, T] scratch
+// Dbuf: fp32 [n_q, T] scratch. rope_inv (only where attn_bwd_fuses_rope):
+// a RoPE table that dQ and dK are taken back through before they are stored
 rp_status attn_bwd(const AttnDesc& a, const void* qkv, const void* o, const void* dout,
-                   const float* lse, float* Dbuf, void* dqkv, hipStream_t s);
+                   const float* lse, float* Dbuf, void* dqkv, hipStream_t s, const float2* rope_inv = nullptr);
+bool attn_bwd_fuses_rope(const AttnDesc& a);
 size_t attn_bwd_ws_bytes(const AttnDesc& a);
 // the allocation-free backward's fixed scratch: kAttnScratchFloats fp32 per
 // GPU (8 MiB: n_q * batch * seq <= 2^21); its device address for `device`,

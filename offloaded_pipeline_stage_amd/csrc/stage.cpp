@@ -455,7 +455,10 @@ rp_status layer_bwd(rp_ctx* c, LayerBinding& lb, const LoraBf16& lw, int T, int 
   }
   AttnDesc ad;
   ad.dt = dt; ad.batch = T / seq; ad.seq = seq; ad.n_q = s.nq; ad.n_kv = s.nkv; ad.d = s.d;
-  RP_TRY(attn_bwd(ad, A.qkv, A.o, B.dO, A.lse, B.Dbuf, B.dqkv, st));
+  // without QK-norm the rotation's backward rides in the attention
+  // backward's dQ and dK stores where the flash kernels run
+  const bool fused_rope = rope && !s.qkn && attn_bwd_fuses_rope(ad) && ((uintptr_t)rope & 15) == 0;
+  RP_TRY(attn_bwd(ad, A.qkv, A.o, B.dO, A.lse, B.Dbuf, B.dqkv, st, fused_rope ? rope : nullptr));
   if (s.qkn) {
     // the gains are base weights: trained in a full fine-tune, frozen with LoRA;
     // gamma_k's gradient directly follows gamma_q's in the gradient block
@@ -463,7 +466,7 @@ rp_status layer_bwd(rp_ctx* c, LayerBinding& lb, const LoraBf16& lw, int T, int 
     RP_CHECK(!dg || gptr(w, cfg, RP_T_KNORM) == dg + s.d, RP_ERR_STATE, "qk-norm: gain gradients not adjacent");
     RP_TRY(qknorm_rope_bwd(dt, B.dqkv, s.QKV, A.qkraw, A.qkrstd, wptr(w, cfg, RP_T_QNORM), wptr(w, cfg, RP_T_KNORM),
                            T, seq, s.nq, s.nkv, s.d, rope, dg, accum, B.qkpart, st));
-  } else {
+  } else if (!fused_rope) {
     RP_TRY(rope_apply(dt, B.dqkv, s.QKV, T, seq, s.nq + s.nkv, s.d, rope, true, st));
   }
   // da = dqkv Wqkv ; dWqkv = dqkv^T a
