@@ -114,12 +114,13 @@ def test_bf16_layer_fwd_bwd_matches_oracle(W, name, seq, batch, qkn):
         assert e < tol, (n, e)
 
 
-@pytest.mark.parametrize("seq,vocab,shards", [(320, 8192, 4), (200, 6176, 4), (100, 4096, 2)])
+@pytest.mark.parametrize("seq,vocab,shards", [(320, 8192, 4), (200, 6176, 4), (100, 4096, 2), (256, 2048, 1)])
 def test_bf16_lmhead_sharded_matches_oracle(W, seq, vocab, shards):
     """LM head + CE with vocabulary shards at hidden 4096 (vocab reduced),
     bf16: loss, dx and every shard's weight gradient, at token counts and
     shard widths that leave ragged tiles (320 tokens; 1544-row shards; 100
-    tokens, not a multiple of 8)."""
+    tokens, not a multiple of 8), and with a single shard, whose product
+    writes dx alone."""
     say("bf16 lm head", seq, vocab, shards)
     cfg = synth.config("llama3_8b", seq=seq, vocab=vocab, n_shards=shards)
     x = synth.activation(cfg, "x")
