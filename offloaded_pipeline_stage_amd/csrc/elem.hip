@@ -495,20 +495,58 @@ __global__ __launch_bounds__(1024) void ce_combine_kernel(int rows, int n_shards
   __shared__ int s_cnt[1024];
   float acc = 0.f;
   int cnt = 0;
-  for (int t = threadIdx.x; t < rows; t += 1024) {
-    float m = -INFINITY;
-    for (int s = 0; s < n_shards; ++s) m = fmaxf(m, parts[(int64_t)s * rows + t].x);
-    float l = 0.f;
-    for (int s = 0; s < n_shards; ++s) {
-      const float2 p = parts[(int64_t)s * rows + t];
-      l += p.y * __expf(p.x - m);
-    }
+  // one row's lse from its shards' (max, sum) pairs; the loss sum in row order
+  auto row_done = [&](int t, float m, float l, int y, float zl) __attribute__((always_inline)) {
     const float v = m + __logf(l);
     lse[t] = v;
-    const int y = labels[t];
     if (y >= 0 && y < vocab) {
-      acc += v - zlab[t];
+      acc += v - zl;
       cnt += 1;
+    }
+  };
+  constexpr int U = 8, MS = 4;  // rows per batch, shards held in registers
+  if (n_shards <= MS) {
+    // every load of U rows issued before the first use: the kernel is one
+    // block, and one dependent load after another would set its time
+    for (int t0 = threadIdx.x; t0 < rows; t0 += 1024 * U) {
+      float2 pv[U][MS];
+      int yv[U];
+      float zv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + 1024 * u;
+        const bool in = t < rows;
+#pragma unroll
+        for (int s = 0; s < MS; ++s)
+          pv[u][s] = in && s < n_shards ? parts[(int64_t)s * rows + t] : make_float2(-INFINITY, 0.f);
+        yv[u] = in ? labels[t] : -1;
+        zv[u] = in ? zlab[t] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + 1024 * u;
+        if (t >= rows) break;
+        float m = -INFINITY;
+#pragma unroll
+        for (int s = 0; s < MS; ++s)
+          if (s < n_shards) m = fmaxf(m, pv[u][s].x);
+        float l = 0.f;
+#pragma unroll
+        for (int s = 0; s < MS; ++s)
+          if (s < n_shards) l += pv[u][s].y * __expf(pv[u][s].x - m);
+        row_done(t, m, l, yv[u], zv[u]);
+      }
+    }
+  } else {
+    for (int t = threadIdx.x; t < rows; t += 1024) {
+      float m = -INFINITY;
+      for (int s = 0; s < n_shards; ++s) m = fmaxf(m, parts[(int64_t)s * rows + t].x);
+      float l = 0.f;
+      for (int s = 0; s < n_shards; ++s) {
+        const float2 p = parts[(int64_t)s * rows + t];
+        l += p.y * __expf(p.x - m);
+      }
+      row_done(t, m, l, labels[t], zlab[t]);
     }
   }
   s_loss[threadIdx.x] = acc;
