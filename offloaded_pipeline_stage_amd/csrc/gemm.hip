@@ -62,7 +62,6 @@ struct GemmParams {
   int rope_seq, rope_heads;
   int vec;  // row strides of C, R and C2 (and F) multiples of 4 elements, bases aligned to 4 elements
   int skip_c;  // EPI_SWIGLU: store only C2
-  int r_f32;   // EPI_RESID with bf16 output: R is fp32
 };
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.f + __expf(-g)); }
@@ -638,10 +637,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(GemmParams p)
         } else {
           if (EPI == EPI_RESID) {
             float x[4];
-            if (p.r_f32)
-              ld4(reinterpret_cast<const float*>(p.R) + (int64_t)m * p.ldr + n, cnt, p.vec, x);
-            else
-              ld4(reinterpret_cast<const bf16*>(p.R) + (int64_t)m * p.ldr + n, cnt, p.vec, x);
+            ld4(reinterpret_cast<const bf16*>(p.R) + (int64_t)m * p.ldr + n, cnt, p.vec, x);
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] += x[e];
           }
@@ -772,7 +768,6 @@ rp_status launch_mfma(const GemmDesc& d, hipStream_t s) {
   p.R = d.R; p.ldr = d.ldr;
   p.C2 = d.C2; p.ldc2 = d.ldc2;
   p.skip_c = EPI == EPI_SWIGLU && d.c_unused ? 1 : 0;
-  p.r_f32 = d.r_f32 ? 1 : 0;
   p.accumulate = d.accumulate ? 1 : 0;
   p.alpha = d.alpha;
   p.kc = d.K;
@@ -815,7 +810,7 @@ rp_status launch_mfma(const GemmDesc& d, hipStream_t s) {
     // the epilogue's four-element accesses: row strides and the column offset
     // F in multiples of 4 elements, bases aligned to 4 elements
     const size_t ce = OF32 ? 4 : 2;
-    const size_t re = EPI == EPI_RESID ? (d.r_f32 ? 4 : ce) : 2;
+    const size_t re = EPI == EPI_RESID ? ce : 2;
     auto al = [](const void* q, size_t b) { return reinterpret_cast<uintptr_t>(q) % b == 0; };
     bool v = p.ldc % 4 == 0 && al(p.C, 4 * ce) && p.c_split % 4 == 0 && p.F % 4 == 0;
     if (p.R) v = v && p.ldr % 4 == 0 && al(p.R, 4 * re);
@@ -901,9 +896,6 @@ rp_status gemm_validate(const GemmDesc& d) {
     if (d.epi == EPI_SWIGLU) RP_CHECK(d.N % 2 == 0, RP_ERR_INVALID, "swiglu: N must be even");
   }
   if (d.epi == EPI_RESID || d.epi == EPI_SWIGLU_BWD) RP_CHECK(d.R, RP_ERR_INVALID, "gemm: missing R");
-  RP_CHECK(!d.r_f32 || (d.epi == EPI_RESID && d.in_dtype == RP_DTYPE_BF16 && d.out_dtype == RP_DTYPE_BF16 &&
-                        !d.force_simple && d.split_k <= 1 && !d.accumulate && !d.group),
-           RP_ERR_UNSUPPORTED, "gemm: an fp32 addend only with bf16 operands and output, fused path");
   if (d.epi == EPI_SWIGLU) RP_CHECK(d.C2, RP_ERR_INVALID, "gemm: missing C2");
   if (d.epi == EPI_ROPE)
     RP_CHECK(d.in_dtype == RP_DTYPE_BF16 && d.out_dtype == RP_DTYPE_BF16 && !d.force_simple && d.a_kmajor &&

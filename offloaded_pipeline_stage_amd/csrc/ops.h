@@ -51,7 +51,6 @@ struct GemmDesc {
   // not store the pre-activations into C (the unfused path still uses C as
   // its scratch)
   bool c_unused = false;
-  bool r_f32 = false;  // EPI_RESID with bf16 operands and output: R is fp32
   float* tmp = nullptr;           // fp32 [M, N] scratch for the unfused fp32 path
   bool force_simple = false;      // use the generic kernel even for bf16
   float alpha = 1.f;              // C = alpha * A B^T (+ R): store / residual epilogues

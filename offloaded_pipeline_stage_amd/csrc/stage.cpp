@@ -791,7 +791,6 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
   }
   RP_TRY(fork(sd, st, ns));
   RP_TRY(ce_combine((int)T, ns, parts, zlab, labels, c->vocab, lse, loss, inv_n, st));
-  const bool dx_direct = !fnorm && dt == RP_DTYPE_BF16;
   auto grad = [&](int i, hipStream_t on) -> rp_status {
     const int lo = c->shard_lo[i], vs = c->shard_lo[i + 1] - lo;
     return ce_grad(dt, logits + (size_t)i * T * vs_max, vs, (int)T, vs, lo, labels, c->vocab, lse, inv_n,
@@ -810,19 +809,9 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
     RP_TRY(wait_grad_drained(c, w));
     const void* dz = dzb[i & 1];
     // dX = sum over shards of dz_s W_s: the first shard's product writes dxf
-    // (no separate clearing pass), the others add to it. Without a final
-    // norm the last one writes dx itself, its fp32 sum rounded once to bf16
-    // (dxf as an fp32 addend), instead of a separate cast pass.
-    const bool to_dx = dx_direct && i + 1 == ns;
-    GemmDesc gx = to_dx ? mk((int)T, s.H, vs, dz, vs, true, w.w, s.H, false, dx, s.H, dt, dt)
-                        : mk((int)T, s.H, vs, dz, vs, true, w.w, s.H, false, dxf, s.H, dt, RP_DTYPE_F32);
-    if (to_dx && i > 0) {
-      gx.epi = EPI_RESID;
-      gx.R = dxf;
-      gx.ldr = s.H;
-      gx.r_f32 = true;
-    }
-    if (!to_dx) gx.accumulate = i > 0;
+    // (no separate clearing pass), the others add to it
+    GemmDesc gx = mk((int)T, s.H, vs, dz, vs, true, w.w, s.H, false, dxf, s.H, dt, RP_DTYPE_F32);
+    gx.accumulate = i > 0;
     RP_TRY(gemm(gx, st));
     if (xt)
       RP_TRY(gemm(mk(vs, s.H, (int)T, dz, vs, false, zt, T, true, w.g, s.H, dt, RP_DTYPE_F32), st));
@@ -839,7 +828,7 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
                        false, part, (int)T, s.H, st));
     RP_TRY(mark_consumed(c, c->final_norm));
     RP_TRY(mark_grad_ready(c, c->final_norm));
-  } else if (!dx_direct) {
+  } else {
     RP_TRY(cast_from_f32(dt, dxf, dx, (size_t)T * s.H, st));
   }
   return ws_mark(c, ws);

@@ -119,8 +119,7 @@ def test_bf16_lmhead_sharded_matches_oracle(W, seq, vocab, shards):
     """LM head + CE with vocabulary shards at hidden 4096 (vocab reduced),
     bf16: loss, dx and every shard's weight gradient, at token counts and
     shard widths that leave ragged tiles (320 tokens; 1544-row shards; 100
-    tokens, not a multiple of 8), and with a single shard, whose product
-    writes dx alone."""
+    tokens, not a multiple of 8), and with a single shard."""
     say("bf16 lm head", seq, vocab, shards)
     cfg = synth.config("llama3_8b", seq=seq, vocab=vocab, n_shards=shards)
     x = synth.activation(cfg, "x")
