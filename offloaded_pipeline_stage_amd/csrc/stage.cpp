@@ -752,10 +752,11 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
     RP_TRY(rmsnorm_fwd(dt, x, c->final_norm.w, z, rstd, (int)T, s.H, c->cfg.rms_eps, st));
     zz = z;
   }
-  // The memory-bound cross-entropy kernels run on the side stream beside the
-  // compute-bound shard products: each shard's statistics beside the next
-  // shard's logits product, each shard's dz beside the previous shard's
-  // input- and weight-gradient products (dz alternates between two buffers).
+  // Each shard's statistics run in line after its logits product (beside
+  // the next one they slowed it by as much as they take alone, and the two
+  // stream hops cost more); each shard's dz runs on the side stream beside
+  // the previous shard's input- and weight-gradient products (dz alternates
+  // between two buffers).
   hipStream_t sd = c->side;
   if ((int)c->side_ev.size() < 2 * ns + 3) {
     c->side_ev.resize(2 * ns + 3, nullptr);
@@ -786,8 +787,7 @@ rp_status lmhead(rp_ctx* c, int batch, int seq, const void* x, const int32_t* la
     RP_TRY(wait_weights(c, w));
     float* lg = logits + (size_t)i * T * vs_max;
     RP_TRY(gemm(mk((int)T, vs, s.H, zz, s.H, true, w.w, s.H, true, lg, vs, dt, RP_DTYPE_F32), st));
-    RP_TRY(fork(st, sd, i));
-    RP_TRY(ce_shard_stats(lg, vs, (int)T, vs, lo, labels, c->vocab, parts + (size_t)i * T, zlab, sd));
+    RP_TRY(ce_shard_stats(lg, vs, (int)T, vs, lo, labels, c->vocab, parts + (size_t)i * T, zlab, st));
   }
   RP_TRY(fork(sd, st, ns));
   RP_TRY(ce_combine((int)T, ns, parts, zlab, labels, c->vocab, lse, loss, inv_n, st));
